@@ -1,0 +1,276 @@
+"""Plain CPU oracle of the W4A4 quantized linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this module.  The GPU library never calls it,
+and it shares no code with the GPU library: no kernels, no helpers, no tables.
+
+What is computed, and where the pages fix it
+---------------------------------------------
+* Rotation: each row of X is cut into contiguous blocks of ``b`` channels and
+  every block is multiplied by a Hadamard matrix whose first row is all ones,
+  so that a single-channel outlier becomes a constant offset over its block
+  (OffQ page, "Metodología", step 2 "Absorción mediante Desplazamiento", and
+  step 3 "Implementación por Grupos").  We take the Sylvester matrix
+  H[i, j] = (-1)^popcount(i & j), normalised by 1/sqrt(b) so that the rotation
+  keeps the L2 norm.  It is applied as a dense float64 matmul, not as a fast
+  transform, and rounded once to float32.
+* Activation quantization: per token ("on the fly") symmetric int4 with an
+  absmax scale (SERQ page, "Resumen técnico" §1 and §2 item 2: the main path
+  stays at 4 bits, INT4).  In float32: a = max|x|, s = a / 7, q = clamp(rint(x / s),
+  -7, 7) with round-half-to-even; when s is 0 every code is 0.
+* Weight preparation (offline): the same rotation, then symmetric
+  round-to-nearest int4 per output channel, or per group of ``g`` channels
+  along K (DynamicPTQ page, "Resultados": RTN weight quantizer).  The scale is
+  stored in its storage dtype, and the codes are taken against the stored
+  scale.
+* Packing: two's-complement nibbles, element 2j in the low nibble of byte j.
+* Integer GEMM: acc[m, n] = sum_k qx[m, k] * qw[n, k], computed as a float64
+  matmul of the integer codes, which is exact because every partial sum is an
+  integer of magnitude at most 64*K < 2^53.
+* Low-rank term: the single low-rank compensation added to the 4-bit product
+  (SERQ page, "Resumen técnico" §2 item 2).  Written as (X @ A) @ B in float64
+  on the unrotated input as given.
+* Epilogue: Y = s_x[m] * s_w[n] * acc[m, n] (or the sum over weight groups)
+  + low-rank term, in float64, rounded once to float32.
+
+Parity pins for every function live in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+from functools import lru_cache
+from typing import Optional
+
+import numpy as np
+
+QMAX = 7
+
+
+# ----------------------------------------------------------------------------
+# Rotation (OffQ page, "Metodología", steps 2-3)
+# ----------------------------------------------------------------------------
+@lru_cache(maxsize=16)
+def _hadamard_cached(b: int) -> np.ndarray:
+    return _hadamard_build(b)
+
+
+def hadamard_matrix(b: int) -> np.ndarray:
+    """Sylvester Hadamard matrix of order b: H[i, j] = (-1)^popcount(i & j).
+
+    Row 0 and column 0 are all ones (the property OffQ's offsetting uses).
+    """
+    return _hadamard_cached(int(b)).copy()
+
+
+def _hadamard_build(b: int) -> np.ndarray:
+    if b < 1 or (b & (b - 1)) != 0:
+        raise ValueError("Hadamard order must be a power of two")
+    i = np.arange(b, dtype=np.int64)
+    and_ = i[:, None] & i[None, :]
+    parity = np.zeros_like(and_)
+    v = and_.copy()
+    while np.any(v):
+        parity ^= v & 1
+        v >>= 1
+    return np.where(parity == 0, 1.0, -1.0)
+
+
+def rotate64(x: np.ndarray, b: int) -> np.ndarray:
+    """Block rotation in float64: every contiguous block of b channels of
+    every row becomes block @ H_b / sqrt(b).  No rounding to float32."""
+    x = np.asarray(x, dtype=np.float64)
+    M, K = x.shape
+    if K % b != 0:
+        raise ValueError("block size must divide K")
+    H = _hadamard_cached(int(b))
+    blocks = x.reshape(M * (K // b), b)
+    return (blocks @ H / np.sqrt(b)).reshape(M, K)
+
+
+def rotate(x: np.ndarray, b: int) -> np.ndarray:
+    """The oracle's rotated activations: rotate64 rounded once to float32."""
+    return rotate64(x, b).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Quantization (SERQ page, "Resumen técnico" §1-2)
+# ----------------------------------------------------------------------------
+def absmax_scale(v32: np.ndarray) -> np.float32:
+    """s = max|v| / 7 in float32 (IEEE division, round to nearest even)."""
+    a = np.float32(np.max(np.abs(v32))) if v32.size else np.float32(0.0)
+    return np.float32(a / np.float32(QMAX))
+
+
+def codes_against_scale(v32: np.ndarray, s32) -> np.ndarray:
+    """q = clamp(rint(v / s), -7, 7) with the quotient rounded to float32 and
+    rint rounding half to even.  A zero scale gives all-zero codes."""
+    s32 = np.float32(s32)
+    if s32 == 0:
+        return np.zeros(v32.shape, dtype=np.int8)
+    quot = (v32.astype(np.float32) / s32).astype(np.float32)
+    return np.clip(np.rint(quot), -QMAX, QMAX).astype(np.int8)
+
+
+def quantize_act(xrot32: np.ndarray):
+    """Per-token symmetric int4 of already-rotated float32 activations.
+
+    Returns (codes int8 [M,K] in [-7,7], scales float32 [M])."""
+    xrot32 = np.asarray(xrot32, dtype=np.float32)
+    M, K = xrot32.shape
+    s = _row_scales(xrot32)
+    return _codes_rows(xrot32, s), s
+
+
+def _row_scales(v32: np.ndarray) -> np.ndarray:
+    """absmax_scale applied to every row of a 2-D float32 array."""
+    if v32.shape[1] == 0:
+        return np.zeros(v32.shape[0], np.float32)
+    a = np.max(np.abs(v32), axis=1).astype(np.float32)
+    return (a / np.float32(QMAX)).astype(np.float32)
+
+
+def _codes_rows(v32: np.ndarray, s32: np.ndarray) -> np.ndarray:
+    """codes_against_scale applied to every row with its own float32 scale."""
+    s32 = np.asarray(s32, np.float32)
+    safe = np.where(s32 == 0, np.float32(1), s32).astype(np.float32)
+    quot = (v32 / safe[:, None]).astype(np.float32)
+    q = np.clip(np.rint(quot), -QMAX, QMAX).astype(np.int8)
+    q[s32 == 0, :] = 0
+    return q
+
+
+def quantize_weight(wrot32: np.ndarray, group: int, scale_dtype: str):
+    """Symmetric round-to-nearest int4 of rotated weights, one scale per
+    output channel (group == 0) or per group of ``group`` channels along K.
+
+    The scale is rounded to ``scale_dtype`` first and the codes are taken
+    against that stored value.  Returns (codes int8 [N,K], scales [N] or
+    [N, K/group] in scale_dtype)."""
+    wrot32 = np.asarray(wrot32, dtype=np.float32)
+    N, K = wrot32.shape
+    g = K if group == 0 else group
+    if K % g != 0:
+        raise ValueError("group must divide K")
+    G = K // g
+    segs = wrot32.reshape(N * G, g)
+    stored = _row_scales(segs).astype(np.dtype(scale_dtype))
+    q = _codes_rows(segs, stored.astype(np.float32)).reshape(N, K)
+    s = stored.reshape(N, G)
+    if group == 0:
+        s = s[:, 0]
+    return q, s
+
+
+# ----------------------------------------------------------------------------
+# Packing
+# ----------------------------------------------------------------------------
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """byte[.., j] = (q[.., 2j] & 0xF) | (q[.., 2j+1] & 0xF) << 4."""
+    q = np.asarray(q).astype(np.int16)
+    if q.shape[-1] % 2 != 0:
+        raise ValueError("even number of codes required")
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray) -> np.ndarray:
+    """Inverse of pack_int4: nibbles read as two's-complement 4-bit values."""
+    p = np.asarray(p, dtype=np.uint8).astype(np.int16)
+    lo = p & 0xF
+    hi = p >> 4
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Integer GEMM, low-rank term, epilogue (SERQ page, "Resumen técnico" §2-3)
+# ----------------------------------------------------------------------------
+def int_gemm(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k qx[m, k] * qw[n, k], exact, as int64."""
+    a = np.asarray(qx, dtype=np.float64)
+    w = np.asarray(qw, dtype=np.float64)
+    return (a @ w.T).astype(np.int64)
+
+
+def int_gemm_groups(qx: np.ndarray, qw: np.ndarray, group: int) -> np.ndarray:
+    """One exact int64 partial per K-group: [G, M, N]."""
+    K = qx.shape[1]
+    G = K // group
+    return np.stack([int_gemm(qx[:, j * group:(j + 1) * group],
+                              qw[:, j * group:(j + 1) * group]) for j in range(G)])
+
+
+def lowrank(x: np.ndarray, A: Optional[np.ndarray], B: Optional[np.ndarray]) -> np.ndarray:
+    """(X @ A) @ B in float64 on the values exactly as given; 0 without A."""
+    if A is None or B is None:
+        return None
+    t = np.asarray(x, np.float64) @ np.asarray(A, np.float64)
+    return t @ np.asarray(B, np.float64)
+
+
+def epilogue(acc_or_groups: np.ndarray, s_x: np.ndarray, s_w: np.ndarray,
+             lr: Optional[np.ndarray]) -> np.ndarray:
+    """Y = s_x[m] * s_w[n] * acc[m, n] (+ lr), float64, rounded once to float32.
+
+    With per-group weight scales, acc_or_groups is [G, M, N] and
+    Y = sum_j s_x[m] * s_w[n, j] * acc_j[m, n]."""
+    sx = np.asarray(s_x, np.float64)
+    sw = np.asarray(s_w, np.float64)
+    if sw.ndim == 1:
+        y = sx[:, None] * sw[None, :] * np.asarray(acc_or_groups, np.float64)
+    else:
+        acc = np.asarray(acc_or_groups, np.float64)
+        y = np.zeros(acc.shape[1:])
+        for j in range(acc.shape[0]):
+            y += sx[:, None] * sw[None, :, j] * acc[j]
+    if lr is not None:
+        y = y + lr
+    return y.astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Whole layer
+# ----------------------------------------------------------------------------
+def prepare_weight(W: np.ndarray, had_block: int, group: int, scale_dtype: str):
+    """Offline weight preparation: rotate, quantize, pack.
+
+    Returns (packed uint8 [N, K/2], scales, codes int8 [N, K])."""
+    wrot = rotate(W, had_block) if had_block > 1 else np.asarray(W, np.float32)
+    q, s = quantize_weight(wrot, group, scale_dtype)
+    return pack_int4(q), s, q
+
+
+def quantize_activation(X: np.ndarray, had_block: int):
+    """Rotate (had_block > 1) and quantize per token.
+
+    Returns (packed uint8 [M, K/2], scales float32 [M], codes, rotated fp32)."""
+    xrot = rotate(X, had_block) if had_block > 1 else np.asarray(X, np.float32)
+    q, s = quantize_act(xrot)
+    return pack_int4(q), s, q, xrot
+
+
+def qlinear_forward(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.ndarray,
+                    had_block: int, group: int, A=None, B=None) -> np.ndarray:
+    """The quantized forward Y [M, N] float32."""
+    _, s_x, qx, _ = quantize_activation(X, had_block)
+    qw = unpack_int4(wq_packed)
+    if group == 0:
+        acc = int_gemm(qx, qw)
+    else:
+        acc = int_gemm_groups(qx, qw, group)
+    return epilogue(acc, s_x, np.asarray(w_scale).astype(np.float32),
+                    lowrank(X, A, B))
+
+
+def qlinear_from_codes(qx: np.ndarray, s_x: np.ndarray, wq_packed: np.ndarray,
+                       w_scale: np.ndarray, group: int, X=None, A=None, B=None) -> np.ndarray:
+    """Epilogue of the layer evaluated on given activation codes and scales
+    (used to judge a GPU result on the GPU's own codes)."""
+    qw = unpack_int4(wq_packed)
+    acc = int_gemm(qx, qw) if group == 0 else int_gemm_groups(qx, qw, group)
+    lr = lowrank(X, A, B) if X is not None else None
+    return epilogue(acc, s_x, np.asarray(w_scale).astype(np.float32), lr)

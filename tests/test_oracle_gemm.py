@@ -1,0 +1,164 @@
+"""Pins of the oracle's integer GEMM, low-rank term, epilogue and whole layer.
+
+SERQ page, "Resumen técnico" §1-3: a 4-bit x 4-bit matrix product in the
+linear layer plus one low-rank compensation term; OffQ page, "Metodología",
+steps 2-3 for the rotation in front.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import w4a4_oracle as O
+from bit_gemm_block_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def triple_loop(a, b):
+    M, K = a.shape
+    N = b.shape[0]
+    out = np.zeros((M, N), dtype=np.int64)
+    for m in range(M):
+        for n in range(N):
+            t = 0
+            for k in range(K):
+                t += int(a[m, k]) * int(b[n, k])
+            out[m, n] = t
+    return out
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (8, 4, 64), (13, 9, 33)])
+def test_int_gemm_brute_force(M, N, K):
+    rng = np.random.default_rng(M * 100 + N * 10 + K)
+    a = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    b = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    want = triple_loop(a, b)
+    assert np.array_equal(O.int_gemm(a, b), want)
+    assert np.array_equal(a.astype(np.int64) @ b.astype(np.int64).T, want)
+
+
+def test_int_gemm_k1_exhaustive_table():
+    v = np.arange(-8, 8, dtype=np.int8)
+    a = v.reshape(16, 1)
+    acc = O.int_gemm(a, a)
+    assert np.array_equal(acc, np.outer(v.astype(np.int64), v.astype(np.int64)))
+
+
+def test_int_gemm_extremes_and_bound():
+    K = 14336
+    neg8 = np.full((1, K), -8, np.int8)
+    assert O.int_gemm(neg8, neg8)[0, 0] == 64 * K
+    seven = np.full((1, K), 7, np.int8)
+    assert O.int_gemm(seven, -seven)[0, 0] == -49 * K
+    rng = np.random.default_rng(7)
+    a = rng.integers(-7, 8, (4, 4096)).astype(np.int8)
+    b = rng.integers(-7, 8, (4, 4096)).astype(np.int8)
+    assert np.all(np.abs(O.int_gemm(a, b)) <= 49 * 4096)
+
+
+def test_groups_sum_to_full():
+    rng = np.random.default_rng(8)
+    a = rng.integers(-7, 8, (5, 512)).astype(np.int8)
+    b = rng.integers(-7, 8, (6, 512)).astype(np.int8)
+    g = O.int_gemm_groups(a, b, 128)
+    assert g.shape == (4, 5, 6)
+    assert np.array_equal(g.sum(axis=0), O.int_gemm(a, b))
+    assert np.array_equal(g[2], triple_loop(a[:, 256:384], b[:, 256:384]))
+
+
+def test_lowrank_alone_when_weight_codes_are_zero():
+    # With all-zero weight codes the layer reduces to X @ A @ B (torch fp64).
+    rng = np.random.default_rng(9)
+    M, K, N, r = 6, 128, 40, 8
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    A = (0.01 * rng.standard_normal((K, r))).astype(np.float16)
+    B = (0.01 * rng.standard_normal((r, N))).astype(np.float16)
+    wq = np.zeros((N, K // 2), np.uint8)
+    ws = np.ones(N, np.float16)
+    y = O.qlinear_forward(X, wq, ws, 128, 0, A, B)
+    want = (torch.from_numpy(X).double() @ torch.from_numpy(A).double()
+            @ torch.from_numpy(B).double()).float().numpy()
+    assert np.array_equal(y, want)
+
+
+def test_without_lowrank_term():
+    rng = np.random.default_rng(10)
+    X = rng.standard_normal((4, 64)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((8, 64))).astype(np.float32)
+    wq, ws, qw = O.prepare_weight(W, 64, 0, "float32")
+    y = O.qlinear_forward(X, wq, ws, 64, 0)
+    _, sx, qx, _ = O.quantize_activation(X, 64)
+    want = (sx[:, None].astype(np.float64) * ws[None, :].astype(np.float64)
+            * (qx.astype(np.int64) @ qw.astype(np.int64).T)).astype(np.float32)
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("b,g,sd", [(64, 0, "float32"), (16, 128, "float16"), (256, 64, "float16")])
+def test_lossless_grid_gives_exact_product(b, g, sd):
+    # Closed form: if the rotated activations and weights already sit on the
+    # int4 grid (power-of-two scales, every row/group reaching +-7), the whole
+    # pipeline is exact and Y equals the float64 product X~ W~^T.  b is a
+    # power of four so that 1/sqrt(b) is a power of two and X = X~ H / sqrt(b)
+    # is exactly representable in float32.
+    rng = np.random.default_rng(11)
+    M, N, K = 7, 9, 512
+    gg = K if g == 0 else g
+    qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    qx[:, 0] = 7
+    sx = np.float32(2.0 ** -3)
+    qw = rng.integers(-7, 8, (N, K)).astype(np.int8)
+    qw[:, ::gg] = -7
+    sw = np.float32(2.0 ** -6)
+    xt = sx * qx.astype(np.float64)
+    wt = sw * qw.astype(np.float64)
+    X = O.rotate64(xt, b)            # the rotation is an involution
+    W = O.rotate64(wt, b)
+    wq, ws, qw_back = O.prepare_weight(W.astype(np.float32), b, g, sd)
+    assert np.array_equal(qw_back, qw)
+    y = O.qlinear_forward(X.astype(np.float32), wq, ws, b, g)
+    assert np.array_equal(y, (xt @ wt.T).astype(np.float32))
+
+
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "hand_k4_example.json")) as f:
+        gd = json.load(f)
+    X = np.array(gd["X"], np.float32)
+    W = np.array(gd["W"], np.float32)
+    b = gd["had_block"]
+    xp, sx, qx, xr = O.quantize_activation(X, b)
+    assert np.allclose(xr, gd["x_rot"], rtol=1e-6, atol=1e-7)
+    assert qx.tolist() == gd["x_codes"]
+    assert xp.tolist() == gd["x_packed"]
+    assert np.allclose(sx, gd["x_scale"], rtol=1e-6)
+    wq, ws, qw = O.prepare_weight(W, b, 0, "float32")
+    assert qw.tolist() == gd["w_codes"]
+    assert np.allclose(ws, gd["w_scale"], rtol=1e-6)
+    assert O.int_gemm(qx, qw).tolist() == gd["acc"]
+    y = O.qlinear_forward(X, wq, ws, b, 0)
+    assert np.allclose(y, gd["y"], rtol=1e-6, atol=1e-6)
+    A = np.array(gd["A"], np.float32)
+    B = np.array(gd["B"], np.float32)
+    assert np.allclose(O.lowrank(X, A, B), gd["lowrank"], rtol=0, atol=0)
+    y2 = O.qlinear_forward(X, wq, ws, b, 0, A, B)
+    assert np.allclose(y2, np.array(gd["y"]) + np.array(gd["lowrank"]), rtol=1e-6, atol=1e-6)
+
+
+def test_rotation_reduces_error_on_outlier_inputs():
+    # Sanity of the method's premise (OffQ page, "Declaración del problema";
+    # DynamicPTQ page, "Planteamiento"): with massive channels the rotated
+    # W4A4 product is closer to X W^T than the unrotated one on ordinary rows.
+    w = synth.small("t", 64, 1024, 256, n_outlier=4, bos_factor=500.0)
+    d = synth.make_inputs(w)
+    X, W = d["X"], d["W"]
+    exact = X.astype(np.float64) @ W.astype(np.float64).T
+
+    def rel_err(b):
+        wq, ws, _ = O.prepare_weight(W, b, 0, "float16")
+        y = O.qlinear_forward(X, wq, ws, b, 0)
+        return np.linalg.norm(y[1:] - exact[1:]) / np.linalg.norm(exact[1:])
+
+    assert rel_err(128) < 0.9 * rel_err(1)
+    assert rel_err(1024) < 0.9 * rel_err(1)
