@@ -1,0 +1,284 @@
+// api.cpp — the C ABI declared in include/w4a4.h: argument validation,
+// kernel planning and stream-ordered launches.  No allocation happens here;
+// every buffer belongs to the caller.
+#include "../../include/w4a4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "w4a4_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxK = 16384;
+constexpr int64_t kMaxRank = 256;
+constexpr int64_t kMaxHad = 4096;
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+int ilog2(int64_t v) {
+  int r = 0;
+  while ((int64_t{1} << r) < v) ++r;
+  return r;
+}
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int d) { return d == W4A4_F32 || d == W4A4_F16; }
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return W4A4_ERR_HIP;
+}
+
+// Per-device cache: 0 unknown, 1 gfx950, 2 other.  Also the LDS limit.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_kind[kMaxDevices];
+std::atomic<int> g_dev_lds[kMaxDevices];
+
+// Returns W4A4_OK and the usable LDS bytes per workgroup for the current
+// device, or W4A4_ERR_UNSUPPORTED when there is no gfx950 device.
+int device_check(int* max_lds) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return W4A4_ERR_UNSUPPORTED;
+  }
+  int kind = g_dev_kind[dev].load(std::memory_order_acquire);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return W4A4_ERR_UNSUPPORTED;
+    }
+    kind = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    int lds = static_cast<int>(prop.sharedMemPerBlock);
+    if (lds > 160 * 1024) lds = 160 * 1024;
+    g_dev_lds[dev].store(lds, std::memory_order_relaxed);
+    g_dev_kind[dev].store(kind, std::memory_order_release);
+  }
+  if (kind != 1) return W4A4_ERR_UNSUPPORTED;
+  if (max_lds) *max_lds = g_dev_lds[dev].load(std::memory_order_relaxed);
+  return W4A4_OK;
+}
+
+// Shared checks of K and the Hadamard block.  had_block 0/1 means none.
+int check_k_had(int64_t K, int64_t had_block, bool need_rotation) {
+  if (K <= 0 || had_block < 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  if (need_rotation && had_block < 1) return W4A4_ERR_UNSUPPORTED;
+  if (had_block > 1 && (!is_pow2(had_block) || had_block > kMaxHad || K % had_block != 0))
+    return W4A4_ERR_UNSUPPORTED;
+  return W4A4_OK;
+}
+
+int check_group(int64_t K, int64_t g, bool pow2_only) {
+  if (g < 0) return W4A4_ERR_INVALID_ARG;
+  if (g == 0) return W4A4_OK;
+  if (g % 64 != 0 || K % g != 0) return W4A4_ERR_UNSUPPORTED;
+  if (pow2_only && !is_pow2(g)) return W4A4_ERR_UNSUPPORTED;
+  return W4A4_OK;
+}
+
+int plan_rotq(int64_t K, int64_t had_block, int64_t gsz, int max_lds, w4a4::RotqPlan* p) {
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  return w4a4::rotq_plan(K, log2b, gsz, max_lds, p) ? W4A4_OK : W4A4_ERR_UNSUPPORTED;
+}
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
+
+struct WsLayout {
+  size_t xq, sx, t, total;
+};
+WsLayout ws_layout(int64_t M, int64_t K, int64_t rank) {
+  WsLayout w;
+  w.xq = 0;
+  w.sx = align256(static_cast<size_t>(M) * static_cast<size_t>(K / 2));
+  w.t = w.sx + align256(static_cast<size_t>(M) * 4);
+  w.total = w.t + align256(static_cast<size_t>(M) * static_cast<size_t>(rank) * 4);
+  return w;
+}
+
+int quant_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                   uint8_t* xq, float* x_scale, hipStream_t st, int max_lds) {
+  w4a4::RotqPlan plan;
+  int s = plan_rotq(K, had_block, K, max_lds, &plan);
+  if (s != W4A4_OK) return s;
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT, K, false,
+                                   nullptr, xq, x_scale, plan, st);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int w4a4_abi_version(void) { return W4A4_ABI_VERSION; }
+
+const char* w4a4_status_string(int status) {
+  switch (status) {
+    case W4A4_OK: return "ok";
+    case W4A4_ERR_INVALID_ARG: return "invalid argument";
+    case W4A4_ERR_UNSUPPORTED: return "unsupported shape or device";
+    case W4A4_ERR_MISALIGNED: return "pointer not aligned to 16 bytes";
+    case W4A4_ERR_WORKSPACE: return "workspace too small";
+    case W4A4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int w4a4_last_hip_error(void) { return g_last_hip_error; }
+
+int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot, int64_t M, int64_t K,
+                         int64_t had_block, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0) return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, true);
+  if (s != W4A4_OK) return s;
+  if (M == 0) return W4A4_OK;
+  if (!x || !x_rot) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_rot)) return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, ilog2(had_block), w4a4::ROTQ_ROTATE,
+                                   K, false, x_rot, nullptr, nullptr, plan,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                           uint8_t* xq, float* x_scale, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0) return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if (M == 0) return W4A4_OK;
+  if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  return quant_act_impl(x, x_dtype, M, K, had_block, xq, x_scale,
+                        static_cast<hipStream_t>(stream), max_lds);
+}
+
+int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, int64_t had_block,
+                              int64_t w_group, uint8_t* wq, void* w_scale, int scale_dtype,
+                              void* stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || N < 0) return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if ((s = check_group(K, w_group, true)) != W4A4_OK) return s;
+  if (N == 0) return W4A4_OK;
+  if (!w || !wq || !w_scale) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)) return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  const int64_t gsz = w_group == 0 ? K : w_group;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(K, had_block, gsz, max_lds, &plan)) != W4A4_OK) return s;
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, w4a4::ROTQ_QUANT, gsz,
+                                   scale_dtype == W4A4_F16, nullptr, wq, w_scale, plan,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_lowrank_project(const void* x, int x_dtype, const void* A, int64_t M, int64_t K,
+                         int64_t rank, float* t, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0 || K <= 0 || rank < 1) return W4A4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || K > kMaxK || rank > kMaxRank) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0) return W4A4_OK;
+  if (!x || !A || !t) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(t)) return W4A4_ERR_MISALIGNED;
+  int s = device_check(nullptr);
+  if (s != W4A4_OK) return s;
+  hipError_t e = w4a4::launch_lowrank_project(x, x_dtype == W4A4_F16, A, M, K,
+                                              static_cast<int>(rank), t,
+                                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qgemm_w4a4(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                    const void* w_scale, int w_scale_dtype, int64_t w_group, int64_t M, int64_t N,
+                    int64_t K, float* y, int32_t* acc, void* stream) {
+  if (!dtype_ok(w_scale_dtype) || M < 0 || N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  int s = check_group(K, w_group, false);
+  if (s != W4A4_OK) return s;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
+  if (y && (!x_scale || !w_scale)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(wq) || (x_scale && !aligned16(x_scale)) ||
+      (w_scale && !aligned16(w_scale)) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
+    return W4A4_ERR_MISALIGNED;
+  if ((s = device_check(nullptr)) != W4A4_OK) return s;
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.sx = x_scale; g.wq = wq; g.sw = w_scale;
+  g.sw_f16 = w_scale_dtype == W4A4_F16;
+  g.group = static_cast<int>(w_group);
+  g.M = M; g.N = N; g.K = K;
+  g.y = y; g.acc = acc;
+  g.t = nullptr; g.B = nullptr; g.b_f16 = 0; g.rank = 0;
+  hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank) {
+  if (M <= 0 || N <= 0 || K <= 0 || rank < 0) return 0;
+  return ws_layout(M, K, rank).total;
+}
+
+int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const void* w_scale,
+                         int w_scale_dtype, int64_t M, int64_t N, int64_t K, int64_t had_block,
+                         int64_t w_group, const void* A, const void* B, int64_t rank, float* y,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || M < 0 || N < 0 || rank < 0)
+    return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if ((s = check_group(K, w_group, false)) != W4A4_OK) return s;
+  if (rank > kMaxRank) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !wq || !w_scale || !y || !workspace) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!A || !B)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace) || (rank > 0 && (!aligned16(A) || !aligned16(B))))
+    return W4A4_ERR_MISALIGNED;
+  const WsLayout L = ws_layout(M, K, rank);
+  if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws + L.xq;
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  float* t = reinterpret_cast<float*>(ws + L.t);
+
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT, K, false,
+                                   nullptr, xq, sx, plan, st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (rank > 0) {
+    e = w4a4::launch_lowrank_project(x, x_dtype == W4A4_F16, A, M, K, static_cast<int>(rank), t, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.sx = sx; g.wq = wq; g.sw = w_scale;
+  g.sw_f16 = w_scale_dtype == W4A4_F16;
+  g.group = static_cast<int>(w_group);
+  g.M = M; g.N = N; g.K = K;
+  g.y = y; g.acc = nullptr;
+  g.t = rank > 0 ? t : nullptr;
+  g.B = rank > 0 ? B : nullptr;
+  g.b_f16 = x_dtype == W4A4_F16;
+  g.rank = static_cast<int>(rank);
+  e = w4a4::launch_qgemm(g, st);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+}  // extern "C"

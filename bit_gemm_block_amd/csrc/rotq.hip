@@ -1,0 +1,362 @@
+// rotq.hip — block Hadamard rotation fused with symmetric int4 quantization.
+//
+// The rotation is the OffQ offsetting transform (OffQ page, "Metodología",
+// steps 2-3): every contiguous block of b channels of a row is multiplied by
+// the Sylvester Hadamard matrix (first row all ones) scaled by 1/sqrt(b).
+// The quantizer is the per-token (or per weight group) symmetric int4 absmax
+// quantizer of SERQ's 4-bit path (SERQ page, "Resumen técnico" §1-2).
+//
+// Work decomposition.  A row of K elements is cut into segments of S = L*R
+// elements; L consecutive lanes own a segment and every lane keeps R float32
+// values in registers.  The fast Walsh-Hadamard transform runs in three
+// passes, each on register-resident data with compile-time butterfly pairs:
+//   1. load pass: the row is read with coalesced 16-byte loads (V = 8 fp16 or
+//      4 fp32 elements per load); element bits [0, log2 V) are in registers;
+//   2. column pass: after a trip through LDS a lane holds, for a few fixed
+//      columns of the [L][R] view of the segment, all values of the row
+//      bits the block spans; element bits [log2 R, log2 b) are transformed;
+//   3. row pass: after a second trip a lane holds one row of R contiguous
+//      elements; element bits [log2 V, min(log2 b, log2 R)) are transformed.
+// The row pass layout is also the output layout: R contiguous codes per lane
+// pack into R/2 contiguous bytes.  LDS rows are XOR-swizzled at float4
+// granularity so that row reads (ds_read_b128) and column reads (ds_read_b32)
+// are free of bank conflicts for R = 64.
+//
+// Quantization is exact with respect to the float32 rule q = rint(x~ / s):
+// codes are first taken from t = y * (rs / s) with a magic-number rounding,
+// and every element certifies that t lies at least 2^-16 away from a
+// half-integer.  The combined relative error of the reciprocal form is below
+// 2^-18.8 of |t| <= 7, so a certified t rounds like the IEEE quotient; a lane
+// holding any uncertified element redoes its elements with true division.
+#include "w4a4_internal.h"
+
+#include <hip/hip_fp16.h>
+
+#pragma clang fp contract(off)
+
+namespace w4a4 {
+namespace {
+
+constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct Piece;
+template <> struct Piece<float> {
+  static constexpr int V = 4;
+  __device__ static void load(const float* p, float* out) {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    out[0] = f.x; out[1] = f.y; out[2] = f.z; out[3] = f.w;
+  }
+};
+template <> struct Piece<_Float16> {
+  static constexpr int V = 8;
+  __device__ static void load(const _Float16* p, float* out) {
+    const half8 h = *reinterpret_cast<const half8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = static_cast<float>(h[i]);
+  }
+};
+
+// Butterflies on register-index bits [lo, hi) of v: for every pair
+// (r, r | 2^st) with bit st of r clear, (a, b) -> (a + b, a - b).
+template <int N>
+__device__ __forceinline__ void fwht_reg_bits(float (&v)[N], int lo, int hi) {
+  constexpr int LOGN = ilog2(N);
+#pragma unroll
+  for (int st = 0; st < LOGN; ++st) {
+    if (st >= lo && st < hi) {
+#pragma unroll
+      for (int r = 0; r < N; ++r) {
+        if ((r & (1 << st)) == 0) {
+          const float a = v[r], b = v[r | (1 << st)];
+          v[r] = a + b;
+          v[r | (1 << st)] = a - b;
+        }
+      }
+    }
+  }
+}
+
+struct RotqKArgs {
+  const void* x;
+  int64_t M;
+  int K;
+  int log2b;
+  float rs;          // float32(1 / sqrt(b))
+  int mode;          // RotqMode
+  int gsz;           // elements per scale group (K = one scale per row)
+  int scale_f16;
+  float* xrot;
+  uint8_t* q;
+  void* scale;
+  int segs_per_row;
+  int rows_per_wg;
+  int nslots;
+};
+
+// Swizzled float offset of element (i, j) of a segment stored as [L][R].
+template <int R>
+__device__ __forceinline__ int lds_off(int i, int j) {
+  constexpr int R4 = R / 4;
+  return i * R + ((((j >> 2) ^ (i & (R4 - 1)))) << 2) + (j & 3);
+}
+
+template <typename TIn, int L, int R>
+__global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
+  constexpr int V = Piece<TIn>::V;
+  constexpr int S = L * R;
+  constexpr int LOGR = ilog2(R);
+  constexpr int LOGV = ilog2(V);
+  constexpr int PPL = R / V;  // 16-byte pieces per lane
+  constexpr int R4 = R / 4;
+  static_assert(R >= 8 && R <= 64 && (R % V) == 0, "segment shape");
+
+  extern __shared__ float lds[];
+  const int tid = threadIdx.x;
+  const int segs_wg = a.segs_per_row * a.rows_per_wg;
+  const int seg_wg = tid / L;
+  const int lam = tid % L;
+  const bool on = seg_wg < segs_wg;
+  const int row_wg = on ? seg_wg / a.segs_per_row : 0;
+  const int seg_row = on ? seg_wg % a.segs_per_row : 0;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * a.rows_per_wg + row_wg;
+  const bool valid = on && row < a.M;
+  float* seg = lds + static_cast<size_t>(on ? seg_wg : 0) * S;
+  uint32_t* slots = reinterpret_cast<uint32_t*>(lds + static_cast<size_t>(segs_wg) * S);
+  if (tid < a.nslots) slots[tid] = 0u;
+
+  const int k0 = seg_row * S;
+  float v[R];
+
+  // 1. Coalesced load and the in-piece butterflies.
+  if (valid) {
+    const TIn* src = reinterpret_cast<const TIn*>(a.x) + row * a.K + k0;
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) Piece<TIn>::load(src + (j * L + lam) * V, &v[j * V]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = 0.f;
+  }
+  fwht_reg_bits(v, 0, min(LOGV, a.log2b));
+  if (on) {
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      const int e = (j * L + lam) * V;
+      const int i = e >> LOGR;
+      const int c4 = (e & (R - 1)) >> 2;
+#pragma unroll
+      for (int u = 0; u < V / 4; ++u) {
+        float4 f = make_float4(v[j * V + 4 * u], v[j * V + 4 * u + 1], v[j * V + 4 * u + 2],
+                               v[j * V + 4 * u + 3]);
+        *reinterpret_cast<float4*>(seg + i * R + (((c4 + u) ^ (i & (R4 - 1))) << 2)) = f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. Column pass over element bits [log2 R, log2 b).
+  const int cb = a.log2b - LOGR;
+  if (cb > 0) {
+    if (on) {
+      const int cmask = (1 << cb) - 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int g = (r >> cb) * L + lam;
+        const int i = ((g >> LOGR) << cb) + (r & cmask);
+        v[r] = seg[lds_off<R>(i, g & (R - 1))];
+      }
+      fwht_reg_bits(v, 0, cb);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int g = (r >> cb) * L + lam;
+        const int i = ((g >> LOGR) << cb) + (r & cmask);
+        seg[lds_off<R>(i, g & (R - 1))] = v[r];
+      }
+    }
+    __syncthreads();
+  }
+
+  // 3. Row pass: lane lam holds elements [lam * R, lam * R + R) of the segment.
+  if (on) {
+#pragma unroll
+    for (int c4 = 0; c4 < R4; ++c4) {
+      const float4 f =
+          *reinterpret_cast<const float4*>(seg + lam * R + ((c4 ^ (lam & (R4 - 1))) << 2));
+      v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
+    }
+  }
+  fwht_reg_bits(v, LOGV, min(a.log2b, LOGR));
+
+  const int kfirst = k0 + lam * R;  // first element of this lane's run
+
+  if (a.mode == ROTQ_ROTATE) {
+    if (valid) {
+      float* dst = a.xrot + row * a.K + kfirst;
+#pragma unroll
+      for (int c4 = 0; c4 < R4; ++c4)
+        *reinterpret_cast<float4*>(dst + 4 * c4) =
+            make_float4(v[4 * c4] * a.rs, v[4 * c4 + 1] * a.rs, v[4 * c4 + 2] * a.rs,
+                        v[4 * c4 + 3] * a.rs);
+    }
+    return;
+  }
+
+  // 4. absmax of the scale group (max |y|; the rotated value is y * rs).
+  float m = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) m = fmaxf(m, fabsf(v[r]));
+  const int gsz = a.gsz;
+  const int span_lanes = (gsz < S ? gsz : S) / R;
+  for (int o = 1; o < span_lanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (gsz > S) {
+    const int slot = row_wg * (a.K / gsz) + kfirst / gsz;
+    if (valid && lam == 0) atomicMax(&slots[slot], __float_as_uint(m));
+    __syncthreads();
+    if (on) m = __uint_as_float(slots[slot]);
+  }
+
+  // 5. Scale: s = max|x~| / 7 with max|x~| = RN(max|y| * rs).
+  const float amax = m * a.rs;
+  const float s = __fdiv_rn(amax, 7.0f);
+  float s_eff = s;
+  __half s_h = __float2half_rn(s);
+  if (a.scale_f16) s_eff = __half2float(s_h);
+  if (valid && (kfirst % gsz) == 0) {
+    const int64_t si = row * (a.K / gsz) + kfirst / gsz;
+    if (a.scale_f16)
+      reinterpret_cast<__half*>(a.scale)[si] = s_h;
+    else
+      reinterpret_cast<float*>(a.scale)[si] = s;
+  }
+
+  // 6. Codes, packed 8 per dword (element 8d+t in nibble t).
+  uint32_t pk[R / 8];
+  if (s_eff == 0.f) {
+#pragma unroll
+    for (int d = 0; d < R / 8; ++d) pk[d] = 0u;
+  } else {
+    const float kk = a.rs * __frcp_rn(s_eff);
+    float dev = 0.f;
+#pragma unroll
+    for (int d = 0; d < R / 8; ++d) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float tq = v[8 * d + t] * kk;
+        const float u = tq + kMagic;
+        const float w = u - kMagic;
+        dev = fmaxf(dev, fabsf(tq - w));
+        const float uc = __builtin_amdgcn_fmed3f(u, kMagic - 7.0f, kMagic + 7.0f);
+        acc = __builtin_amdgcn_alignbit(__float_as_uint(uc), acc, 4);
+      }
+      pk[d] = acc;
+    }
+    const bool certified = (dev < 0.5f - 0x1p-16f) && (kk <= 0x1p100f);
+    if (!certified) {
+#pragma unroll
+      for (int d = 0; d < R / 8; ++d) {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const float xt = v[8 * d + t] * a.rs;
+          float qf = rintf(__fdiv_rn(xt, s_eff));
+          qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+          const uint32_t nib = static_cast<uint32_t>(static_cast<int>(qf)) & 0xFu;
+          acc = (acc >> 4) | (nib << 28);
+        }
+        pk[d] = acc;
+      }
+    }
+  }
+  if (valid) {
+    uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
+    if constexpr (R == 8) {
+      *reinterpret_cast<uint32_t*>(dst) = pk[0];
+    } else if constexpr (R == 16) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+    } else {
+#pragma unroll
+      for (int d = 0; d < R / 8; d += 4)
+        *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+    }
+  }
+}
+
+struct Shape { int L, R; };
+// Preference order: larger segments first, then more registers per lane.
+constexpr Shape kMenu[] = {{64, 64}, {32, 64}, {64, 32}, {16, 64}, {32, 32}, {64, 16}, {8, 64},
+                           {16, 32}, {32, 16}, {8, 32},  {16, 16}, {8, 16},  {8, 8}};
+
+template <typename TIn>
+hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((M + p.rows_per_wg - 1) / p.rows_per_wg));
+  const dim3 block(p.threads);
+#define W4A4_ROTQ_CASE(LL, RR)                                                        \
+  if (p.L == LL && p.R == RR) {                                                     \
+    hipLaunchKernelGGL((rotq_kernel<TIn, LL, RR>), grid, block, p.lds_bytes, st, ka); \
+    return hipGetLastError();                                                       \
+  }
+  W4A4_ROTQ_CASE(64, 64) W4A4_ROTQ_CASE(32, 64) W4A4_ROTQ_CASE(64, 32) W4A4_ROTQ_CASE(16, 64)
+  W4A4_ROTQ_CASE(32, 32) W4A4_ROTQ_CASE(64, 16) W4A4_ROTQ_CASE(8, 64) W4A4_ROTQ_CASE(16, 32)
+  W4A4_ROTQ_CASE(32, 16) W4A4_ROTQ_CASE(8, 32) W4A4_ROTQ_CASE(16, 16) W4A4_ROTQ_CASE(8, 16)
+  W4A4_ROTQ_CASE(8, 8)
+#undef W4A4_ROTQ_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool rotq_plan(int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan) {
+  const int64_t b = int64_t{1} << log2b;
+  for (const Shape& sh : kMenu) {
+    const int64_t S = static_cast<int64_t>(sh.L) * sh.R;
+    if (K % S != 0 || b > S || b > static_cast<int64_t>(sh.R) * sh.R) continue;
+    if (gsz != K && (gsz < sh.R || (gsz & (gsz - 1)) != 0 || K % gsz != 0)) continue;
+    const int64_t segs_per_row = K / S;
+    if (segs_per_row * sh.L > 256) continue;
+    const int64_t slots_per_row = gsz > S ? K / gsz : 0;
+    const int64_t row_bytes = K * 4 + slots_per_row * 4;
+    int64_t rows = 256 / (segs_per_row * sh.L);
+    if (rows < 1) rows = 1;
+    while (rows > 1 && rows * row_bytes > max_lds) --rows;
+    if (rows * row_bytes > max_lds) continue;
+    const int64_t threads = ((rows * segs_per_row * sh.L + 63) / 64) * 64;
+    if (threads > 256) continue;
+    plan->L = sh.L;
+    plan->R = sh.R;
+    plan->segs_per_row = static_cast<int>(segs_per_row);
+    plan->rows_per_wg = static_cast<int>(rows);
+    plan->threads = static_cast<int>(threads);
+    plan->lds_bytes = static_cast<int>(rows * row_bytes);
+    plan->nslots = static_cast<int>(rows * slots_per_row);
+    return true;
+  }
+  return false;
+}
+
+hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2b, int mode,
+                       int64_t gsz, bool scale_f16, float* xrot, uint8_t* q, void* scale,
+                       const RotqPlan& plan, hipStream_t st) {
+  RotqKArgs ka;
+  ka.x = x;
+  ka.M = M;
+  ka.K = static_cast<int>(K);
+  ka.log2b = log2b;
+  ka.rs = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(int64_t{1} << log2b)));
+  ka.mode = mode;
+  ka.gsz = static_cast<int>(gsz);
+  ka.scale_f16 = scale_f16 ? 1 : 0;
+  ka.xrot = xrot;
+  ka.q = q;
+  ka.scale = scale;
+  ka.segs_per_row = plan.segs_per_row;
+  ka.rows_per_wg = plan.rows_per_wg;
+  ka.nslots = plan.nslots;
+  if (x_f16) return launch_typed<_Float16>(ka, plan, M, st);
+  return launch_typed<float>(ka, plan, M, st);
+}
+
+}  // namespace w4a4

@@ -1,0 +1,200 @@
+"""Python binding of libw4a4.so: argument marshalling only.
+
+Every function takes torch tensors that live on a ROCm device, checks dtype,
+shape and contiguity, and calls the C entry point of the same name on the
+current HIP stream of that device.  No arithmetic of the layer happens here;
+outputs that the caller does not pass are allocated with torch (device memory
+plumbing only).  When the shared library is missing every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libw4a4.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
+F32, F16 = 0, 1
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SIGS = {
+    "w4a4_abi_version": (_INT, []),
+    "w4a4_status_string": (ctypes.c_char_p, [_INT]),
+    "w4a4_last_hip_error": (_INT, []),
+    "w4a4_hadamard_rotate": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P]),
+    "w4a4_quantize_act_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_quantize_weight_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT, _P]),
+    "w4a4_lowrank_project": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P, _P]),
+    "w4a4_qgemm_w4a4": (_INT, [_P, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_qlinear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
+                                    _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+}
+
+
+class W4A4Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().w4a4_status_string(status).decode()
+        if status == ERR_HIP:
+            msg += f" (hipError {lib().w4a4_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [status {status}]")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_gemm_block_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/w4a4.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(w4a4_\w+)\s*\(", text, re.M)))
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise W4A4Error(fn, status)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def hadamard_rotate(x: torch.Tensor, had_block: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, "x")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=x.device)
+    _dev(out, "out")
+    _check("hadamard_rotate", lib().w4a4_hadamard_rotate(
+        _ptr(x), _dt(x), _ptr(out), M, K, had_block, _stream(x)))
+    return out
+
+
+def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor] = None,
+                      x_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    _dev(x, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("quantize_act_int4", lib().w4a4_quantize_act_int4(
+        _ptr(x), _dt(x), M, K, had_block, _ptr(xq), _ptr(x_scale), _stream(x)))
+    return xq, x_scale
+
+
+def quantize_weight_int4(w: torch.Tensor, had_block: int, w_group: int,
+                         scale_dtype: torch.dtype = torch.float16) -> Tuple[torch.Tensor, torch.Tensor]:
+    _dev(w, "w")
+    N, K = w.shape
+    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    shape = (N,) if w_group == 0 else (N, K // w_group)
+    ws = torch.empty(shape, dtype=scale_dtype, device=w.device)
+    _check("quantize_weight_int4", lib().w4a4_quantize_weight_int4(
+        _ptr(w), _dt(w), N, K, had_block, w_group, _ptr(wq), _ptr(ws), _dt(ws), _stream(w)))
+    return wq, ws
+
+
+def lowrank_project(x: torch.Tensor, A: torch.Tensor, t: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, "x")
+    _dev(A, "A")
+    M, K = x.shape
+    if A.dtype != x.dtype or A.shape[0] != K:
+        raise ValueError("A must be [K, rank] in x's dtype")
+    rank = A.shape[1]
+    if t is None:
+        t = torch.empty((M, rank), dtype=torch.float32, device=x.device)
+    _check("lowrank_project", lib().w4a4_lowrank_project(
+        _ptr(x), _dt(x), _ptr(A), M, K, rank, _ptr(t), _stream(x)))
+    return t
+
+
+def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tensor,
+               w_scale: Optional[torch.Tensor], w_group: int, want_y: bool = True,
+               want_acc: bool = False, y: Optional[torch.Tensor] = None,
+               acc: Optional[torch.Tensor] = None):
+    _dev(xq, "xq")
+    _dev(wq, "wq")
+    M, K2 = xq.shape
+    N = wq.shape[0]
+    K = 2 * K2
+    if wq.shape[1] != K2:
+        raise ValueError("xq and wq disagree on K")
+    if want_y and y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if want_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    wst = _dt(w_scale) if w_scale is not None else F32
+    _check("qgemm_w4a4", lib().w4a4_qgemm_w4a4(
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), wst, w_group, M, N, K,
+        _ptr(y), _ptr(acc), _stream(xq)))
+    return y, acc
+
+
+def qlinear_workspace_size(M: int, N: int, K: int, rank: int) -> int:
+    return int(lib().w4a4_qlinear_workspace_size(M, N, K, rank))
+
+
+def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, had_block: int,
+                    w_group: int, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, "x")
+    _dev(wq, "wq")
+    M, K = x.shape
+    N = wq.shape[0]
+    rank = 0 if A is None else A.shape[1]
+    if rank and (B is None or A.dtype != x.dtype or B.dtype != x.dtype):
+        raise ValueError("A and B must both be given in x's dtype")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = qlinear_workspace_size(M, N, K, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check("qlinear_forward", lib().w4a4_qlinear_forward(
+        _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
+        _ptr(A), _ptr(B), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
+    return y

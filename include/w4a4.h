@@ -1,0 +1,170 @@
+/*
+ * w4a4.h — C ABI of the W4A4 quantized linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (SERQ page, "Resumen técnico" §1-3; OffQ page, "Metodología"
+ * steps 2-3):
+ *   1. rotate every row of the activation X [M, K] by a block Hadamard
+ *      transform over contiguous groups of b channels (Sylvester matrix,
+ *      whose first row is all ones, scaled by 1/sqrt(b));
+ *   2. quantize each rotated row ("on the fly", per token) to symmetric int4
+ *      with an absmax scale;
+ *   3. multiply the int4 codes by pre-quantized int4 weight codes W [N, K]
+ *      (int32 accumulation) and dequantize with the activation and weight
+ *      scales;
+ *   4. optionally add the single low-rank compensation term X . A . B of
+ *      rank r on the unrotated X.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers:   every data pointer is a DEVICE pointer owned by the caller,
+ *             row-major and contiguous, aligned to 16 bytes.  The library
+ *             never allocates, frees or keeps a pointer past the call.
+ * Streams:    `stream` is a hipStream_t passed as void* (NULL = the null
+ *             stream).  Every call only enqueues work on that stream and
+ *             returns; buffers must stay alive until the stream has run it.
+ *             A non-OK status means nothing was enqueued.
+ * Sizes:      M (tokens) and N (output channels) may be 0 (nothing is
+ *             enqueued); K must be a positive multiple of 64 and at most
+ *             16384.
+ * dtypes:     W4A4_F32 = float32, W4A4_F16 = IEEE binary16.
+ * Packing:    int4 codes are two's-complement nibbles, element 2j in the low
+ *             nibble of byte j: a [R, K] code matrix is stored as uint8
+ *             [R, K/2].  Produced codes are always in [-7, 7]; the GEMM also
+ *             multiplies -8 correctly.
+ * Rotation:   had_block b is 0 or 1 for "no rotation" (input already
+ *             rotated), otherwise a power of two, at most 4096, dividing K.
+ * Quantizer:  s = max|x~| / 7 in float32 (IEEE division); each code is
+ *             clamp(rint(x~ / s), -7, 7) with the quotient rounded to float32
+ *             and ties to even; a zero scale gives all-zero codes.
+ * Errors:     no exceptions cross the ABI; every call returns a w4a4_status.
+ * Threads:    the library is stateless apart from a per-device cache of the
+ *             device check; calls are reentrant.
+ */
+#ifndef W4A4_H
+#define W4A4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4A4_ABI_VERSION 1
+
+typedef enum {
+  W4A4_OK = 0,
+  W4A4_ERR_INVALID_ARG = 1, /* null required pointer, bad dtype, negative size,
+                               K not positive, rank > 0 without A or B */
+  W4A4_ERR_UNSUPPORTED = 2, /* shape outside the kernels' domain (K not a
+                               multiple of 64 or above 16384, bad Hadamard
+                               block or weight group, rank above 256), or a
+                               device that is not gfx950 / no device */
+  W4A4_ERR_MISALIGNED = 3,  /* a pointer not aligned to 16 bytes */
+  W4A4_ERR_WORKSPACE = 4,   /* workspace smaller than required */
+  W4A4_ERR_HIP = 5          /* a HIP runtime error while launching */
+} w4a4_status;
+
+typedef enum { W4A4_F32 = 0, W4A4_F16 = 1 } w4a4_dtype;
+
+/* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
+int w4a4_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* w4a4_status_string(int status);
+
+/* HIP error code (hipError_t) behind the last W4A4_ERR_HIP returned on this
+ * thread, 0 if none. */
+int w4a4_last_hip_error(void);
+
+/*
+ * Block Hadamard rotation (OffQ page, "Metodología" steps 2-3).
+ *   x      [M, K] in dtype x_dtype.
+ *   x_rot  [M, K] float32 output: every block of b contiguous channels of a
+ *          row becomes block . H_b / sqrt(b), computed in float32 by a fast
+ *          Walsh-Hadamard transform.
+ *   had_block must be a power of two >= 2.
+ */
+int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot,
+                         int64_t M, int64_t K, int64_t had_block, void* stream);
+
+/*
+ * Per-token symmetric int4 quantization of activations, with the block
+ * Hadamard rotation fused in front (SERQ page, "Resumen técnico" §1-2: 4-bit
+ * activations quantized on the fly; OffQ page, steps 2-3).
+ *   x        [M, K] in dtype x_dtype.
+ *   had_block 0/1: x is already rotated (codes then follow the quantizer rule
+ *            exactly); otherwise the rotation above is applied first.
+ *   xq       [M, K/2] uint8 output, packed codes.
+ *   x_scale  [M] float32 output, one scale per row.
+ */
+int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
+                           int64_t had_block, uint8_t* xq, float* x_scale,
+                           void* stream);
+
+/*
+ * Offline weight preparation: rotation (had_block > 1) and symmetric
+ * round-to-nearest int4 (DynamicPTQ page, "Resultados": RTN weights).
+ *   w        [N, K] in dtype w_dtype.
+ *   w_group  0: one scale per output channel; otherwise a power of two >= 64
+ *            dividing K: one scale per group of w_group channels along K.
+ *   wq       [N, K/2] uint8 output, packed codes.
+ *   w_scale  [N] or [N, K/w_group] output in dtype scale_dtype.  The scale is
+ *            rounded to scale_dtype first and the codes are taken against the
+ *            stored value.
+ */
+int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K,
+                              int64_t had_block, int64_t w_group, uint8_t* wq,
+                              void* w_scale, int scale_dtype, void* stream);
+
+/*
+ * First half of the low-rank term (SERQ page, "Resumen técnico" §2 item 2):
+ *   t [M, rank] float32 = x [M, K] . A [K, rank], with x and A in dtype
+ *   x_dtype, float32 accumulation.  1 <= rank <= 256.
+ */
+int w4a4_lowrank_project(const void* x, int x_dtype, const void* A, int64_t M,
+                         int64_t K, int64_t rank, float* t, void* stream);
+
+/*
+ * int4 x int4 GEMM with the dequantizing epilogue (SERQ page, "Resumen
+ * técnico" §3: 4-bit matrix multiplication in the linear layer).
+ *   xq [M, K/2], x_scale [M] float32: activation codes and scales.
+ *   wq [N, K/2], w_scale [N] (w_group 0) or [N, K/w_group] in w_scale_dtype.
+ *   w_group 0 or a multiple of 64 dividing K.
+ *   y   [M, N] float32 output, or NULL:
+ *         y[m,n] = x_scale[m] * sum_j w_scale[n,j] * acc_j[m,n]
+ *       where acc_j is the exact int32 product over K-group j.
+ *   acc [M, N] int32 output, or NULL: the exact full-K integer product
+ *       sum_k qx[m,k] * qw[n,k].
+ *   At least one of y and acc must be non-NULL.
+ */
+int w4a4_qgemm_w4a4(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                    const void* w_scale, int w_scale_dtype, int64_t w_group,
+                    int64_t M, int64_t N, int64_t K, float* y, int32_t* acc,
+                    void* stream);
+
+/* Bytes of workspace qlinear_forward needs for these sizes (0 if M or N is
+ * 0). */
+size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank);
+
+/*
+ * The whole layer: rotate + quantize X, int4 GEMM, dequant, + X.A.B.
+ *   x [M, K] in x_dtype; A [K, rank] and B [rank, N] in x_dtype (or NULL when
+ *   rank is 0); wq / w_scale as prepared by w4a4_quantize_weight_int4 with
+ *   the same had_block and w_group.  y [M, N] float32 output.
+ *   workspace: device scratch of at least w4a4_qlinear_workspace_size bytes,
+ *   used for the activation codes, scales and X.A; its contents on entry do
+ *   not matter.
+ */
+int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
+                         const void* w_scale, int w_scale_dtype, int64_t M,
+                         int64_t N, int64_t K, int64_t had_block,
+                         int64_t w_group, const void* A, const void* B,
+                         int64_t rank, float* y, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A4_H */

@@ -1,0 +1,111 @@
+"""The C ABI loads, exports every declared entry point and rejects bad
+arguments with the documented status before touching a device.
+
+These tests run without a GPU.  The pointers passed are fake addresses; every
+call but the last one carries an argument error, so nothing is launched.  The
+last one (all arguments valid) is only run where no GPU is present, and
+checks that the library reports the missing device instead of launching.
+"""
+import pytest
+import torch
+
+from bit_gemm_block_amd import w4a4 as W
+
+P = 0x10000      # a 16-byte-aligned fake address (never dereferenced)
+Q = 0x10001      # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return W.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = W.header_functions()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(W._SIGS)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.w4a4_abi_version() == 1
+    assert lib.w4a4_status_string(0) == b"ok"
+    for s in range(1, 6):
+        assert lib.w4a4_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.w4a4_status_string(99) == b"unknown status"
+    assert lib.w4a4_last_hip_error() == 0
+
+
+def test_quantize_act_argument_errors(lib):
+    f = lib.w4a4_quantize_act_int4
+    assert f(P, 7, 4, 256, 0, P, P, None) == W.ERR_INVALID_ARG          # dtype
+    assert f(P, W.F16, -1, 256, 0, P, P, None) == W.ERR_INVALID_ARG     # M < 0
+    assert f(P, W.F16, 4, 0, 0, P, P, None) == W.ERR_INVALID_ARG        # K = 0
+    assert f(None, W.F16, 4, 256, 0, P, P, None) == W.ERR_INVALID_ARG   # null x
+    assert f(P, W.F16, 4, 256, 0, None, P, None) == W.ERR_INVALID_ARG   # null xq
+    assert f(P, W.F16, 4, 100, 0, P, P, None) == W.ERR_UNSUPPORTED      # K % 64
+    assert f(P, W.F16, 4, 32768, 0, P, P, None) == W.ERR_UNSUPPORTED    # K too big
+    assert f(P, W.F16, 4, 256, 3, P, P, None) == W.ERR_UNSUPPORTED      # b not pow2
+    assert f(P, W.F16, 4, 8192, 8192, P, P, None) == W.ERR_UNSUPPORTED  # b > 4096
+    assert f(P, W.F16, 4, 192, 128, P, P, None) == W.ERR_UNSUPPORTED    # b does not divide K
+    assert f(Q, W.F16, 4, 256, 0, P, P, None) == W.ERR_MISALIGNED
+    assert f(P, W.F16, 4, 256, 0, P, Q, None) == W.ERR_MISALIGNED
+    assert f(None, W.F16, 0, 256, 64, None, None, None) == W.OK         # empty: no-op
+
+
+def test_rotate_and_weight_argument_errors(lib):
+    r = lib.w4a4_hadamard_rotate
+    assert r(P, W.F32, P, 4, 256, 0, None) == W.ERR_UNSUPPORTED         # rotation needed
+    assert r(P, W.F32, None, 4, 256, 256, None) == W.ERR_INVALID_ARG
+    assert r(P, W.F32, Q, 4, 256, 256, None) == W.ERR_MISALIGNED
+    w = lib.w4a4_quantize_weight_int4
+    assert w(P, W.F32, 8, 256, 0, 96, P, P, W.F16, None) == W.ERR_UNSUPPORTED   # group % 64
+    assert w(P, W.F32, 8, 192, 0, 128, P, P, W.F16, None) == W.ERR_UNSUPPORTED  # group | K
+    assert w(P, W.F32, 8, 384, 0, 192, P, P, W.F16, None) == W.ERR_UNSUPPORTED  # not pow2
+    assert w(P, W.F32, 8, 256, 0, -64, P, P, W.F16, None) == W.ERR_INVALID_ARG
+    assert w(P, W.F32, 8, 256, 0, 0, P, P, 5, None) == W.ERR_INVALID_ARG       # scale dtype
+    assert w(P, W.F32, 8, 256, 0, 0, P, None, W.F16, None) == W.ERR_INVALID_ARG
+    assert w(P, W.F32, 0, 256, 0, 0, None, None, W.F16, None) == W.OK
+
+
+def test_gemm_and_lowrank_argument_errors(lib):
+    g = lib.w4a4_qgemm_w4a4
+    assert g(P, P, P, P, W.F16, 0, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
+    assert g(P, None, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
+    assert g(P, P, P, P, W.F16, 96, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, P, P, P, W.F16, 0, 4, 8, 200, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, P, Q, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
+    assert g(None, None, None, None, W.F16, 0, 4, 0, 256, None, None, None) == W.OK
+    lr = lib.w4a4_lowrank_project
+    assert lr(P, W.F16, P, 4, 256, 0, P, None) == W.ERR_INVALID_ARG
+    assert lr(P, W.F16, P, 4, 256, 257, P, None) == W.ERR_UNSUPPORTED
+    assert lr(P, W.F16, None, 4, 256, 8, P, None) == W.ERR_INVALID_ARG
+
+
+def test_qlinear_argument_errors(lib):
+    f = lib.w4a4_qlinear_forward
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
+    assert need >= 16 * 128 + 16 * 4 + 16 * 8 * 4
+    assert lib.w4a4_qlinear_workspace_size(0, 32, 256, 8) == 0
+    args = [P, W.F16, P, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P, need, None]
+    bad = list(args); bad[10] = None                                  # rank > 0 without A
+    assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[12] = 300
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[15] = need - 1
+    assert f(*bad) == W.ERR_WORKSPACE
+    bad = list(args); bad[14] = Q
+    assert f(*bad) == W.ERR_MISALIGNED
+    bad = list(args); bad[9] = 100
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[5] = 0
+    assert f(*bad) == W.OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_unsupported(lib):
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
+    assert lib.w4a4_qlinear_forward(P, W.F16, P, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P,
+                                    need, None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, P, None) == W.ERR_UNSUPPORTED

@@ -1,0 +1,276 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (oracle readings, see the oracle module header):
+* integer and byte results (codes, packed bytes, int32 accumulators) and the
+  scales of the quantizer when both sides start from the same float32 input
+  (the oracle's rotated activations, had_block 0): bit-exact;
+* the float32 fast Walsh-Hadamard rotation against the float64 dense one:
+  per block, max |delta| <= 2 (log2 b + 2) 2^-24 ||x~_block||_2 (first-order
+  error bound of log2 b rounded butterfly stages plus the final scaling);
+* the fused rotate+quantize path: at most 0.01% of codes differ, each by
+  exactly one step, scales within 1e-6 relative;
+* the float32 output: max |Y_gpu - epilogue(GPU codes and scales)| <=
+  1e-3 * RMS(Y_oracle); the distance to the oracle's own Y is reported.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import w4a4_oracle as O
+from bit_gemm_block_amd import synth
+from bit_gemm_block_amd import w4a4 as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def np_dtype(name):
+    return np.float16 if name == "float16" else np.float32
+
+
+def rotation_bound(x, b):
+    ref = O.rotate64(x, b)
+    M, K = ref.shape
+    blk = np.linalg.norm(ref.reshape(M, K // b, b), axis=2)
+    lb = int(np.log2(b))
+    bound = 2 * (lb + 2) * 2.0 ** -24 * blk
+    return ref, np.repeat(bound, b, axis=1).reshape(M, K)
+
+
+# --------------------------------------------------------------------------
+# Rotation
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,b,dt", [
+    (16, 256, 256, "float32"), (5, 4096, 4096, "float16"), (33, 4096, 128, "float16"),
+    (9, 14336, 128, "float16"), (3, 14336, 2048, "float16"), (7, 192, 64, "float32"),
+    (4, 1024, 2, "float16"), (2, 512, 512, "float32")])
+def test_hadamard_rotate_within_bound(M, K, b, dt):
+    w = synth.small("r", M, K, 8, x_dtype=dt, n_outlier=2, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    got = host(W.hadamard_rotate(dev(X), b))
+    ref, bound = rotation_bound(X, b)
+    assert np.all(np.abs(got - ref) <= bound)
+
+
+# --------------------------------------------------------------------------
+# Quantizers: exact on the oracle's rotated input
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,b,dt", [
+    (16, 256, 256, "float32"), (37, 4096, 4096, "float16"), (20, 14336, 128, "float16"),
+    (3, 192, 64, "float32"), (1, 64, 2, "float16")])
+def test_quantize_act_exact_on_oracle_rotation(M, K, b, dt):
+    w = synth.small("q", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xr = O.rotate(X, b)
+    xq, sx = W.quantize_act_int4(dev(xr), 0)
+    pq, ps, _, _ = O.quantize_activation(xr, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(host(xq), pq)
+
+
+def test_quantize_act_exact_unrotated_fp16_and_edge_rows():
+    rng = np.random.default_rng(3)
+    X = (rng.standard_normal((6, 512)) * 3).astype(np.float16)
+    X[1] = 0                                # zero row
+    X[2, :] = 0
+    X[2, 17] = np.float16(-2.0)             # single element
+    X[3] = np.float16(6e-8)                 # fp16 subnormals
+    X[4, ::2] = np.float16(1.5)             # ties after scaling
+    X[4, 1::2] = np.float16(-10.5)
+    xq, sx = W.quantize_act_int4(dev(X), 1)
+    pq, ps, _, _ = O.quantize_activation(X.astype(np.float32), 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(host(xq), pq)
+
+
+def test_quantize_act_tie_breaking_matches_division():
+    # Rows built on the boundary cases where x*(1/s) and x/s round apart.
+    f = np.float32
+    rows = []
+    for a in (3.0, 1.0, 0.3, 5.0, 11.0):
+        s = f(f(a) / f(7))
+        r = f(f(1) / s)
+        row = [f(a)]
+        for n in range(7):
+            xv = f((n + 0.5) * float(s))
+            for _ in range(9):
+                row.append(xv)
+                row.append(-xv)
+                xv = np.nextafter(xv, f(np.inf), dtype=np.float32)
+        row = (row + [f(0)] * 256)[:256]
+        rows.append(row)
+    X = np.array(rows, np.float32)
+    xq, sx = W.quantize_act_int4(dev(X), 0)
+    pq, ps, _, _ = O.quantize_activation(X, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(host(xq), pq)
+
+
+@pytest.mark.parametrize("N,K,g,sd", [(64, 256, 0, "float32"), (96, 4096, 0, "float16"),
+                                      (40, 14336, 128, "float16"), (24, 512, 64, "float16"),
+                                      (8, 4096, 4096, "float32")])
+def test_quantize_weight_exact_on_oracle_rotation(N, K, g, sd):
+    rng = np.random.default_rng(N + K)
+    Wt = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    Wt[:, 5] *= 30
+    wr = O.rotate(Wt, 128)
+    wq, ws = W.quantize_weight_int4(dev(wr), 0, g, torch.float16 if sd == "float16" else torch.float32)
+    oq, os_ = O.quantize_weight(wr, g, sd)
+    assert np.array_equal(host(ws), os_)
+    assert np.array_equal(host(wq), O.pack_int4(oq))
+
+
+@pytest.mark.parametrize("N,K,b,g", [(64, 4096, 4096, 0), (48, 14336, 128, 128), (32, 256, 256, 0)])
+def test_quantize_weight_fused_rotation(N, K, b, g):
+    rng = np.random.default_rng(7)
+    Wt = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    wq, ws = W.quantize_weight_int4(dev(Wt), b, g, torch.float16)
+    _, os_, oq = O.prepare_weight(Wt, b, g, "float16")
+    gq = O.unpack_int4(host(wq))
+    diff = gq.astype(np.int16) - oq
+    assert np.all(np.abs(diff) <= 1)
+    assert np.count_nonzero(diff) <= 1e-4 * diff.size
+    rel = np.abs(host(ws).astype(np.float64) - os_.astype(np.float64)) / os_.astype(np.float64)
+    assert np.all(rel <= 1e-3)   # fp16 storage: equal or one fp16 ulp apart
+
+
+@pytest.mark.parametrize("M,K,b,dt", [(16, 256, 256, "float32"), (64, 4096, 4096, "float16"),
+                                      (48, 14336, 128, "float16")])
+def test_quantize_act_fused_rotation(M, K, b, dt):
+    w = synth.small("f", M, K, 8, x_dtype=dt, n_outlier=4, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xq, sx = W.quantize_act_int4(dev(X), b)
+    _, ps, pc, _ = O.quantize_activation(X, b)
+    gc = O.unpack_int4(host(xq)).astype(np.int16)
+    diff = gc - pc
+    assert np.all(np.abs(diff) <= 1)
+    assert np.count_nonzero(diff) <= 1e-4 * diff.size
+    assert np.all(np.abs(host(sx).astype(np.float64) - ps) <= 1e-6 * ps)
+
+
+# --------------------------------------------------------------------------
+# Integer GEMM
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (7, 33, 192), (130, 260, 384), (16, 256, 256),
+                                   (257, 129, 4096), (64, 64, 14336)])
+def test_qgemm_int32_exact(M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    qx[0, :] = -8
+    qw[0, :] = -8
+    _, acc = W.qgemm_w4a4(dev(O.pack_int4(qx)), None, dev(O.pack_int4(qw)), None, 0,
+                          want_y=False, want_acc=True)
+    assert np.array_equal(host(acc), O.int_gemm(qx, qw))
+
+
+@pytest.mark.parametrize("M,N,K,g,sd", [(33, 70, 256, 0, "float32"), (128, 256, 4096, 0, "float16"),
+                                        (40, 96, 1024, 128, "float16"), (17, 50, 384, 64, "float32"),
+                                        (64, 128, 14336, 128, "float16")])
+def test_qgemm_dequant(M, N, K, g, sd):
+    rng = np.random.default_rng(M + N + K + g)
+    qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-7, 8, (N, K)).astype(np.int8)
+    sx = rng.uniform(0.01, 2.0, M).astype(np.float32)
+    shape = (N,) if g == 0 else (N, K // g)
+    sw = rng.uniform(1e-3, 0.05, shape).astype(np_dtype(sd))
+    y, acc = W.qgemm_w4a4(dev(O.pack_int4(qx)), dev(sx), dev(O.pack_int4(qw)), dev(sw), g,
+                          want_y=True, want_acc=True)
+    assert np.array_equal(host(acc), O.int_gemm(qx, qw))
+    accs = O.int_gemm(qx, qw) if g == 0 else O.int_gemm_groups(qx, qw, g)
+    ref = O.epilogue(accs, sx, sw.astype(np.float32), None).astype(np.float64)
+    # float32 epilogue: a few roundings per group term
+    G = 1 if g == 0 else K // g
+    mag = np.abs(sx)[:, None] * (np.abs(sw.astype(np.float64)).reshape(N, -1).max(axis=1)[None, :]) * 49 * K
+    assert np.all(np.abs(host(y) - ref) <= (G + 3) * 2.0 ** -23 * mag)
+
+
+# --------------------------------------------------------------------------
+# Low-rank projection
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,r,dt", [(16, 256, 8, "float32"), (8, 4096, 64, "float16"),
+                                      (100, 4096, 32, "float16"), (5, 192, 256, "float16")])
+def test_lowrank_project(M, K, r, dt):
+    w = synth.small("l", M, K, 8, x_dtype=dt, rank=r)
+    d = synth.make_inputs(w)
+    t = host(W.lowrank_project(dev(d["X"]), dev(d["A"])))
+    X64, A64 = d["X"].astype(np.float64), d["A"].astype(np.float64)
+    ref = X64 @ A64
+    bound = K * 2.0 ** -23 * (np.abs(X64) @ np.abs(A64))
+    assert np.all(np.abs(t - ref) <= bound)
+
+
+# --------------------------------------------------------------------------
+# Whole layer
+# --------------------------------------------------------------------------
+def run_layer(w, rows=None):
+    """GPU qlinear_forward vs the oracle on one workload; returns stats."""
+    d = synth.make_inputs(w, rows)
+    X, Wt, A, B = d["X"], d["W"], d["A"], d["B"]
+    wq, ws, _ = O.prepare_weight(Wt, w.had_block, w.w_group, w.w_scale_dtype)
+    Xd, wqd, wsd = dev(X), dev(wq), dev(ws)
+    Ad = dev(A) if A is not None else None
+    Bd = dev(B) if B is not None else None
+    y = host(W.qlinear_forward(Xd, wqd, wsd, w.had_block, w.w_group, Ad, Bd))
+    gxq, gsx = W.quantize_act_int4(Xd, w.had_block)
+    gxq, gsx = host(gxq), host(gsx)
+    _, ps, pc, _ = O.quantize_activation(X, w.had_block)
+    gc = O.unpack_int4(gxq).astype(np.int16)
+    y_on_gpu_codes = O.qlinear_from_codes(gc, gsx, wq, ws, w.w_group, X, A, B)
+    y_oracle = O.qlinear_forward(X, wq, ws, w.had_block, w.w_group, A, B)
+    rms = float(np.sqrt(np.mean(y_oracle.astype(np.float64) ** 2)))
+    diff = gc - pc
+    return dict(y=y, y_codes=y_on_gpu_codes, y_oracle=y_oracle, rms=rms, diff=diff,
+                gsx=gsx, psx=ps)
+
+
+def check_layer(st):
+    assert np.all(np.abs(st["diff"]) <= 1)
+    assert np.count_nonzero(st["diff"]) <= 1e-4 * st["diff"].size
+    assert np.all(np.abs(st["gsx"].astype(np.float64) - st["psx"]) <= 1e-6 * st["psx"])
+    err = np.max(np.abs(st["y"].astype(np.float64) - st["y_codes"]))
+    assert err <= 1e-3 * st["rms"], (err, st["rms"])
+
+
+@pytest.mark.parametrize("w", [synth.TINY, synth.DECODE], ids=lambda w: w.name)
+def test_qlinear_full_size(w):
+    st = run_layer(w)
+    check_layer(st)
+    print(w.name, "max|Y-Y_oracle|/RMS =",
+          float(np.max(np.abs(st["y"] - st["y_oracle"])) / st["rms"]))
+
+
+def test_qlinear_prefill_full_size():
+    st = run_layer(synth.PREFILL)
+    check_layer(st)
+    print("prefill max|Y-Y_oracle|/RMS =",
+          float(np.max(np.abs(st["y"] - st["y_oracle"])) / st["rms"]))
+
+
+@pytest.mark.parametrize("M,K,N,b,g,r,dt", [
+    (1, 256, 64, 256, 0, 0, "float16"), (7, 192, 33, 64, 64, 4, "float32"),
+    (130, 1024, 260, 128, 128, 16, "float16"), (33, 4096, 100, 4096, 0, 64, "float16"),
+    (65, 14336, 96, 128, 128, 32, "float16"), (16, 512, 48, 1, 0, 8, "float16")])
+def test_qlinear_ragged_shapes(M, K, N, b, g, r, dt):
+    w = synth.small("rag", M, K, N, x_dtype=dt, had_block=b, w_group=g, rank=r,
+                    w_scale_dtype="float16" if dt == "float16" else "float32")
+    check_layer(run_layer(w))
+
+
+def test_qlinear_empty_is_noop():
+    y = torch.full((0, 16), 3.0, device=DEV)
+    out = W.qlinear_forward(torch.empty((0, 256), dtype=torch.float16, device=DEV),
+                            torch.zeros((16, 128), dtype=torch.uint8, device=DEV),
+                            torch.ones(16, dtype=torch.float16, device=DEV), 256, 0, y=y,
+                            workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert out.shape == (0, 16)
