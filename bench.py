@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A4 quantized linear layer on one MI355X.
+
+Headline: qlinear_forward on the prefill workload (X fp16 2048 x 4096, W
+4096 x 4096 int4 per-channel fp16 scales, Hadamard block 4096, no low-rank
+term) in int TOP/s (2*M*N*K per call).  Beside it: the decode workload
+(X 8 x 4096, rank-64 X.A.B term) in algorithmic HBM GB/s, with the weights
+rotated through enough distinct copies that the 256 MB last-level cache
+cannot serve them.
+
+One step = one qlinear_forward call (rotate + quantize, [X.A], int4 GEMM with
+the dequant and low-rank epilogue).  Inputs and pre-quantized weights are
+resident in device memory before the timed region.  The timed region is a
+captured HIP graph of exactly --steps calls, bracketed by device
+synchronisation and timed with events on the stream the kernels run on.
+
+The roofline object is the GEMM kernel alone (the dominant kernel): its
+average launch duration from events around --steps back-to-back launches,
+against the chip's dense int8 matrix peak.  cpu_baseline is the float64 CPU
+oracle timed on a bounded row sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from bit_gemm_block_amd import synth  # noqa: E402
+from bit_gemm_block_amd import w4a4 as W  # noqa: E402
+
+PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 matrix peak, TOP/s
+PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
+LLC_BYTES = 256 << 20     # MI355X Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Layer:
+    """Device-resident inputs of one workload with weights quantized on GPU."""
+
+    def __init__(self, wl: synth.Workload, copies: int = 1):
+        self.wl = wl
+        d = synth.make_inputs(wl)
+        dev = "cuda:0"
+        self.x = torch.from_numpy(d["X"]).to(dev)
+        self.A = torch.from_numpy(d["A"]).to(dev) if d["A"] is not None else None
+        self.B = torch.from_numpy(d["B"]).to(dev) if d["B"] is not None else None
+        Wd = torch.from_numpy(d["W"]).to(dev)
+        sdt = torch.float16 if wl.w_scale_dtype == "float16" else torch.float32
+        wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt)
+        del Wd
+        # Distinct copies of the weights (and low-rank factors) so a decode
+        # loop streams them from HBM rather than from the last-level cache.
+        self.sets = [(wq, ws, self.A, self.B)]
+        for _ in range(copies - 1):
+            self.sets.append((wq.clone(), ws.clone(),
+                              self.A.clone() if self.A is not None else None,
+                              self.B.clone() if self.B is not None else None))
+        self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
+        need = W.qlinear_workspace_size(wl.M, wl.N, wl.K, wl.rank)
+        self.ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def forward(self, i: int = 0):
+        wq, ws, A, B = self.sets[i % len(self.sets)]
+        W.qlinear_forward(self.x, wq, ws, self.wl.had_block, self.wl.w_group, A, B,
+                          y=self.y, workspace=self.ws)
+
+    def algorithmic_bytes(self) -> int:
+        wl = self.wl
+        xb = 2 if wl.x_dtype == "float16" else 4
+        sb = 2 if wl.w_scale_dtype == "float16" else 4
+        nsc = wl.N if wl.w_group == 0 else wl.N * (wl.K // wl.w_group)
+        lr = (wl.K * wl.rank + wl.rank * wl.N) * xb
+        return wl.M * wl.K * xb + wl.N * wl.K // 2 + nsc * sb + lr + wl.M * wl.N * 4
+
+    def ops(self) -> int:
+        return 2 * self.wl.M * self.wl.N * self.wl.K
+
+
+def time_graph(fn, steps: int, warmup: int) -> float:
+    """Seconds per step: `steps` calls of fn(i) captured in one HIP graph."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()                      # untimed replay: first-launch costs
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    start.record(cur)
+    g.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def time_eager(fn, steps: int, warmup: int) -> float:
+    """Seconds per launch of fn(i) issued back to back on the current stream."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    start.record(cur)
+    for i in range(steps):
+        fn(i)
+    end.record(cur)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps
+
+
+def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
+    """Average duration of each kernel of the path launched alone."""
+    wl = layer.wl
+    ws = layer.ws
+    xq = ws[: wl.M * wl.K // 2].view(wl.M, wl.K // 2)
+    off = ((wl.M * wl.K // 2) + 255) // 256 * 256
+    sx = ws[off: off + 4 * wl.M].view(torch.float32)
+    wq, wsc, A, B = layer.sets[0]
+    layer.forward(0)
+    torch.cuda.synchronize()
+    out = {}
+    out["rotq"] = time_eager(lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx),
+                             steps, warmup)
+    out["qgemm"] = time_eager(
+        lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
+                               layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y),
+        steps, warmup)
+    return out
+
+
+def cpu_baseline(wl: synth.Workload, rows: int) -> dict:
+    """The float64 oracle on the first `rows` rows of the workload."""
+    from oracle import w4a4_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    d = synth.make_inputs(wl)
+    X = d["X"][:rows]
+    wq, ws, _ = O.prepare_weight(d["W"], wl.had_block, wl.w_group, wl.w_scale_dtype)
+    A, B = d["A"], d["B"]
+    O.qlinear_forward(X[:8], wq, ws, wl.had_block, wl.w_group, A, B)  # warm caches
+    t0 = time.perf_counter()
+    O.qlinear_forward(X, wq, ws, wl.had_block, wl.w_group, A, B)
+    t = time.perf_counter() - t0
+    return {"value": 2 * rows * wl.N * wl.K / t / 1e12, "unit": "TOP/s", "cores": int(threads),
+            "kind": "oracle", "seconds": t,
+            "sample": f"first {rows} of {wl.M} rows of {wl.name} (weights prepared untimed)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the W4A4 linear path of this library runs on a "
+              "single device and has no multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        return 2
+    W.lib()
+
+    # ---- prefill: the headline ------------------------------------------------
+    pre = Layer(synth.PREFILL)
+    log(f"prefill: {pre.wl.name} timing {args.steps} steps")
+    t_step = time_graph(pre.forward, args.steps, args.warmup)
+    kt = kernel_times(pre, args.steps, args.warmup)
+    tops = pre.ops() / t_step / 1e12
+    gemm_tops = pre.ops() / kt["qgemm"] / 1e12
+    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M
+    log(f"prefill: {t_step * 1e6:.2f} us/step, {tops:.1f} TOP/s; qgemm {kt['qgemm'] * 1e6:.2f} us "
+        f"({gemm_tops:.1f} TOP/s), rotq {kt['rotq'] * 1e6:.2f} us "
+        f"({rot_bytes / kt['rotq'] / 1e9:.0f} GB/s)")
+
+    # ---- decode ----------------------------------------------------------------
+    decode = None
+    if not args.no_decode:
+        probe = synth.DECODE
+        per_set = probe.N * probe.K // 2 + probe.N * 2 + 2 * (probe.K + probe.N) * probe.rank * 2
+        copies = int(np.ceil(3 * LLC_BYTES / per_set))
+        dec = Layer(probe, copies=copies)
+        log(f"decode: {dec.wl.name} with {copies} weight copies, timing {args.steps} steps")
+        t_dec = time_graph(dec.forward, args.steps, args.warmup)
+        kd = kernel_times(dec, args.steps, args.warmup)
+        gbs = dec.algorithmic_bytes() / t_dec / 1e9
+        log(f"decode: {t_dec * 1e6:.2f} us/step, {gbs:.0f} GB/s")
+        decode = {
+            "metric": "W4A4 qlinear HBM GB/s (M=8)", "value": gbs, "unit": "GB/s",
+            "ms_per_step": t_dec * 1e3, "frac_of_hbm": gbs / PEAK_HBM_GBS,
+            "bytes_per_step": dec.algorithmic_bytes(), "weight_copies": copies,
+            "kernels_us": {k: v * 1e6 for k, v in kd.items()},
+            "config": {"workload": dec.wl.name, "M": dec.wl.M, "N": dec.wl.N, "K": dec.wl.K,
+                       "had_block": dec.wl.had_block, "w_group": dec.wl.w_group,
+                       "rank": dec.wl.rank},
+        }
+        del dec
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(synth.PREFILL, args.cpu_rows)
+
+    out = {
+        "metric": "W4A4 qlinear TOPS (M=2048), K=N=4096",
+        "value": tops,
+        "unit": "TOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4",
+        "data": "synthetic",
+        "config": {"workload": pre.wl.name, "M": pre.wl.M, "N": pre.wl.N, "K": pre.wl.K,
+                   "had_block": pre.wl.had_block, "w_group": pre.wl.w_group,
+                   "rank": pre.wl.rank, "x_dtype": pre.wl.x_dtype},
+        "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
+        "roofline": {"bound": "mfma", "kernel": "qgemm_kernel", "achieved": gemm_tops,
+                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
+                     "ops_per_launch": pre.ops(), "us_per_launch": kt["qgemm"] * 1e6,
+                     "traffic": None},
+        "kernels_us": {k: v * 1e6 for k, v in kt.items()},
+        "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
