@@ -54,8 +54,9 @@ class Layer:
         d = synth.make_inputs(wl)
         dev = "cuda:0"
         self.x = torch.from_numpy(d["X"]).to(dev)
-        self.A = torch.from_numpy(d["A"]).to(dev) if d["A"] is not None else None
-        self.B = torch.from_numpy(d["B"]).to(dev) if d["B"] is not None else None
+        # Low-rank factors are stored transposed (At [r, K], Bt [N, r]).
+        self.A = torch.from_numpy(d["A"].T.copy()).to(dev) if d["A"] is not None else None
+        self.B = torch.from_numpy(d["B"].T.copy()).to(dev) if d["B"] is not None else None
         Wd = torch.from_numpy(d["W"]).to(dev)
         sdt = torch.float16 if wl.w_scale_dtype == "float16" else torch.float32
         wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt)
@@ -131,21 +132,20 @@ def time_eager(fn, steps: int, warmup: int) -> float:
 
 
 def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
-    """Average duration of each kernel of the path launched alone."""
+    """Average duration of each kernel of the path, launched alone with the
+    same arguments and code layout as inside qlinear_forward."""
     wl = layer.wl
-    ws = layer.ws
-    xq = ws[: wl.M * wl.K // 2].view(wl.M, wl.K // 2)
-    off = ((wl.M * wl.K // 2) + 255) // 256 * 256
-    sx = ws[off: off + 4 * wl.M].view(torch.float32)
-    wq, wsc, A, B = layer.sets[0]
-    layer.forward(0)
+    xq = torch.empty((wl.M, wl.K), dtype=torch.uint8, device="cuda:0")
+    sx = torch.empty((wl.M,), dtype=torch.float32, device="cuda:0")
+    W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout="i8")
     torch.cuda.synchronize()
     out = {}
-    out["rotq"] = time_eager(lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx),
-                             steps, warmup)
+    out["rotq"] = time_eager(
+        lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout="i8"), steps, warmup)
     out["qgemm"] = time_eager(
         lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
-                               layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y),
+                               layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
+                               layout="i8"),
         steps, warmup)
     return out
 
@@ -196,7 +196,7 @@ def main() -> int:
     kt = kernel_times(pre, args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
-    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M
+    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K + 4 * pre.wl.M  # X in, int8 codes + scales out
     log(f"prefill: {t_step * 1e6:.2f} us/step, {tops:.1f} TOP/s; qgemm {kt['qgemm'] * 1e6:.2f} us "
         f"({gemm_tops:.1f} TOP/s), rotq {kt['rotq'] * 1e6:.2f} us "
         f"({rot_bytes / kt['rotq'] / 1e9:.0f} GB/s)")

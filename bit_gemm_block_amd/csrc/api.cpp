@@ -1,7 +1,7 @@
 // api.cpp — the C ABI declared in include/w4a4.h: argument validation,
 // kernel planning and stream-ordered launches.  No allocation happens here;
 // every buffer belongs to the caller.
-#include "../../include/w4a4.h"
+#include "w4a4.h"
 
 #include <hip/hip_runtime.h>
 
@@ -94,22 +94,13 @@ struct WsLayout {
 WsLayout ws_layout(int64_t M, int64_t K, int64_t rank) {
   WsLayout w;
   w.xq = 0;
-  w.sx = align256(static_cast<size_t>(M) * static_cast<size_t>(K / 2));
+  w.sx = align256(static_cast<size_t>(M) * static_cast<size_t>(K));  // int8 codes
   w.t = w.sx + align256(static_cast<size_t>(M) * 4);
   w.total = w.t + align256(static_cast<size_t>(M) * static_cast<size_t>(rank) * 4);
   return w;
 }
 
-int quant_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
-                   uint8_t* xq, float* x_scale, hipStream_t st, int max_lds) {
-  w4a4::RotqPlan plan;
-  int s = plan_rotq(K, had_block, K, max_lds, &plan);
-  if (s != W4A4_OK) return s;
-  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT, K, false,
-                                   nullptr, xq, x_scale, plan, st);
-  return e == hipSuccess ? W4A4_OK : hip_fail(e);
-}
+bool layout_ok(int l) { return l == W4A4_CODES_PACKED || l == W4A4_CODES_I8; }
 
 }  // namespace
 
@@ -150,8 +141,8 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot, int64_t M, in
 }
 
 int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
-                           uint8_t* xq, float* x_scale, void* stream) {
-  if (!dtype_ok(x_dtype) || M < 0) return W4A4_ERR_INVALID_ARG;
+                           uint8_t* xq, int codes_layout, float* x_scale, void* stream) {
+  if (!dtype_ok(x_dtype) || !layout_ok(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if (M == 0) return W4A4_OK;
@@ -159,8 +150,13 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
-  return quant_act_impl(x, x_dtype, M, K, had_block, xq, x_scale,
-                        static_cast<hipStream_t>(stream), max_lds);
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  const int mode = codes_layout == W4A4_CODES_I8 ? w4a4::ROTQ_QUANT_I8 : w4a4::ROTQ_QUANT;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, mode, K, false, nullptr, xq,
+                                   x_scale, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
 int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, int64_t had_block,
@@ -185,25 +181,26 @@ int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, 
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
-int w4a4_lowrank_project(const void* x, int x_dtype, const void* A, int64_t M, int64_t K,
+int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M, int64_t K,
                          int64_t rank, float* t, void* stream) {
   if (!dtype_ok(x_dtype) || M < 0 || K <= 0 || rank < 1) return W4A4_ERR_INVALID_ARG;
   if (K % 64 != 0 || K > kMaxK || rank > kMaxRank) return W4A4_ERR_UNSUPPORTED;
   if (M == 0) return W4A4_OK;
-  if (!x || !A || !t) return W4A4_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(A) || !aligned16(t)) return W4A4_ERR_MISALIGNED;
+  if (!x || !At || !t) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(At) || !aligned16(t)) return W4A4_ERR_MISALIGNED;
   int s = device_check(nullptr);
   if (s != W4A4_OK) return s;
-  hipError_t e = w4a4::launch_lowrank_project(x, x_dtype == W4A4_F16, A, M, K,
-                                              static_cast<int>(rank), t,
+  hipError_t e = w4a4::launch_lowrank_project(x, x_dtype == W4A4_F16, At, M, K,
+                                              static_cast<int>(rank), t, false,
                                               static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
-int w4a4_qgemm_w4a4(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, const uint8_t* wq,
                     const void* w_scale, int w_scale_dtype, int64_t w_group, int64_t M, int64_t N,
                     int64_t K, float* y, int32_t* acc, void* stream) {
-  if (!dtype_ok(w_scale_dtype) || M < 0 || N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (!dtype_ok(w_scale_dtype) || !layout_ok(codes_layout) || M < 0 || N < 0 || K <= 0)
+    return W4A4_ERR_INVALID_ARG;
   if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
   int s = check_group(K, w_group, false);
   if (s != W4A4_OK) return s;
@@ -220,7 +217,8 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
   g.group = static_cast<int>(w_group);
   g.M = M; g.N = N; g.K = K;
   g.y = y; g.acc = acc;
-  g.t = nullptr; g.B = nullptr; g.b_f16 = 0; g.rank = 0;
+  g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
+  g.a_i8 = codes_layout == W4A4_CODES_I8;
   hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
@@ -232,19 +230,19 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
 
 int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const void* w_scale,
                          int w_scale_dtype, int64_t M, int64_t N, int64_t K, int64_t had_block,
-                         int64_t w_group, const void* A, const void* B, int64_t rank, float* y,
+                         int64_t w_group, const void* At, const void* Bt, int64_t rank, float* y,
                          void* workspace, size_t ws_bytes, void* stream) {
   if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || M < 0 || N < 0 || rank < 0)
     return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if ((s = check_group(K, w_group, false)) != W4A4_OK) return s;
-  if (rank > kMaxRank) return W4A4_ERR_UNSUPPORTED;
+  if (rank > kMaxRank || (x_dtype == W4A4_F16 && rank % 8 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!x || !wq || !w_scale || !y || !workspace) return W4A4_ERR_INVALID_ARG;
-  if (rank > 0 && (!A || !B)) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!At || !Bt)) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
-      !aligned16(workspace) || (rank > 0 && (!aligned16(A) || !aligned16(B))))
+      !aligned16(workspace) || (rank > 0 && (!aligned16(At) || !aligned16(Bt))))
     return W4A4_ERR_MISALIGNED;
   const WsLayout L = ws_layout(M, K, rank);
   if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
@@ -257,14 +255,15 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const vo
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* xq = ws + L.xq;
   float* sx = reinterpret_cast<float*>(ws + L.sx);
-  float* t = reinterpret_cast<float*>(ws + L.t);
+  void* t = ws + L.t;
+  const bool f16 = x_dtype == W4A4_F16;
 
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT, K, false,
-                                   nullptr, xq, sx, plan, st);
+  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b, w4a4::ROTQ_QUANT_I8, K, false, nullptr, xq,
+                                   sx, plan, st);
   if (e != hipSuccess) return hip_fail(e);
   if (rank > 0) {
-    e = w4a4::launch_lowrank_project(x, x_dtype == W4A4_F16, A, M, K, static_cast<int>(rank), t, st);
+    e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
     if (e != hipSuccess) return hip_fail(e);
   }
   w4a4::GemmArgs g{};
@@ -274,9 +273,10 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const vo
   g.M = M; g.N = N; g.K = K;
   g.y = y; g.acc = nullptr;
   g.t = rank > 0 ? t : nullptr;
-  g.B = rank > 0 ? B : nullptr;
-  g.b_f16 = x_dtype == W4A4_F16;
+  g.B = rank > 0 ? Bt : nullptr;
+  g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
   g.rank = static_cast<int>(rank);
+  g.a_i8 = 1;
   e = w4a4::launch_qgemm(g, st);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }

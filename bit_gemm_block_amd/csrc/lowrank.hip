@@ -1,47 +1,117 @@
 // lowrank.hip — T = X . A, the first factor of the single low-rank
 // compensation term of SERQ (SERQ page, "Resumen técnico" §2 item 2), on the
-// unrotated activations.  float32 accumulation; X and A are fp16 or fp32.
+// unrotated activations.  A is stored transposed, At [rank, K], so both
+// operands are contiguous along the contraction like the int4 weights.
 //
-// A workgroup owns 16 rows of X and 64 columns of A.  K is walked in chunks
-// of 64: the X chunk [16 x 64] and the A chunk [64 x 64] are staged in LDS as
-// float32 and every thread accumulates 4 outputs (4 rows of one column).
+// fp16 inputs: v_mfma_f32_16x16x32_f16 with float32 accumulation.  A
+// workgroup owns 16 rows of X and NCB blocks of 16 columns of T; its KW waves
+// split K and their partial 16x16 tiles are summed in LDS in a fixed order.
+// T is written as an fp16 pair (t_hi = fp16(T), t_lo = fp16(T - t_hi)) so
+// that the GEMM epilogue can form T . B with two fp16 MFMAs at about 22 bits
+// of precision.
+//
+// fp32 inputs: LDS-tiled float32 FMA, T written as float32.
 #include "w4a4_internal.h"
 
 namespace w4a4 {
 namespace {
 
-constexpr int TR = 16;  // rows of X per workgroup
-constexpr int TC = 64;  // columns of A per workgroup
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NCB, int KW>
+__global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __restrict__ x,
+                                                             const _Float16* __restrict__ at,
+                                                             int64_t M, int64_t K, int rank,
+                                                             void* __restrict__ t, int pair_out) {
+  __shared__ f32x4 red[KW][NCB][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int c0 = blockIdx.y * NCB * 16;  // first column of T
+  const int64_t mrow = m0 + (lane & 15);
+  const int koff = (lane >> 4) * 8;
+  const bool row_ok = mrow < M;
+
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nchunks = K / 32;
+  const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t ch = wave; ch < nchunks; ch += KW) {
+    const int64_t k = ch * 32 + koff;
+    const half8 xa = row_ok ? *reinterpret_cast<const half8*>(x + mrow * K + k) : zero8;
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int j = c0 + c * 16 + (lane & 15);
+      const half8 ab = j < rank ? *reinterpret_cast<const half8*>(at + static_cast<int64_t>(j) * K + k)
+                                : zero8;
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ab, acc[c], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) red[wave][c][lane] = acc[c];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      f32x4 s = red[0][c][lane];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) s += red[w][c][lane];
+      // Output fragment: rows 4*(lane>>4)+i, column lane&15.
+      const int j = c0 + c * 16 + (lane & 15);
+      if (j < rank) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + (lane >> 4) * 4 + i;
+          if (m < M) {
+            if (pair_out) {
+              const _Float16 hi = static_cast<_Float16>(s[i]);
+              const _Float16 lo = static_cast<_Float16>(s[i] - static_cast<float>(hi));
+              static_cast<_Float16*>(t)[m * rank + j] = hi;
+              static_cast<_Float16*>(t)[M * rank + m * rank + j] = lo;
+            } else {
+              static_cast<float*>(t)[m * rank + j] = s[i];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+constexpr int TR = 16;  // rows of X per workgroup (fp32 path)
+constexpr int TC = 64;  // columns of T per workgroup
 constexpr int KC = 64;  // K chunk
 
-template <typename T>
-__global__ void __launch_bounds__(256) lowrank_project_kernel(const T* __restrict__ x,
-                                                             const T* __restrict__ A, int64_t M,
-                                                             int64_t K, int rank,
-                                                             float* __restrict__ t) {
+__global__ void __launch_bounds__(256) lowrank_f32_kernel(const float* __restrict__ x,
+                                                         const float* __restrict__ at, int64_t M,
+                                                         int64_t K, int rank,
+                                                         float* __restrict__ t) {
   __shared__ float xs[TR][KC + 1];
-  __shared__ float as[KC][TC + 1];
+  __shared__ float as[TC][KC + 1];
   const int tid = threadIdx.x;
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * TR;
   const int c0 = blockIdx.y * TC;
   const int col = tid % TC;
-  const int rg = (tid / TC) * 4;  // first of this thread's 4 rows
+  const int rg = (tid / TC) * 4;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-
   for (int64_t k0 = 0; k0 < K; k0 += KC) {
     for (int e = tid; e < TR * KC; e += 256) {
       const int i = e / KC, k = e % KC;
       const int64_t m = r0 + i;
-      xs[i][k] = m < M ? static_cast<float>(x[m * K + k0 + k]) : 0.f;
+      xs[i][k] = m < M ? x[m * K + k0 + k] : 0.f;
     }
-    for (int e = tid; e < KC * TC; e += 256) {
-      const int k = e / TC, c = e % TC;
-      as[k][c] = (c0 + c) < rank ? static_cast<float>(A[(k0 + k) * rank + c0 + c]) : 0.f;
+    for (int e = tid; e < TC * KC; e += 256) {
+      const int c = e / KC, k = e % KC;
+      as[c][k] = (c0 + c) < rank ? at[static_cast<int64_t>(c0 + c) * K + k0 + k] : 0.f;
     }
     __syncthreads();
 #pragma unroll 8
     for (int k = 0; k < KC; ++k) {
-      const float av = as[k][col];
+      const float av = as[col][k];
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = fmaf(xs[rg + q][k], av, acc[q]);
     }
@@ -56,18 +126,41 @@ __global__ void __launch_bounds__(256) lowrank_project_kernel(const T* __restric
   }
 }
 
+template <int NCB>
+hipError_t launch_f16(const _Float16* x, const _Float16* at, int64_t M, int64_t K, int rank,
+                      void* t, int pair, hipStream_t st) {
+  const int64_t row_tiles = (M + 15) / 16;
+  const int col_groups = (rank + NCB * 16 - 1) / (NCB * 16);
+  const dim3 grid(static_cast<unsigned>(row_tiles), static_cast<unsigned>(col_groups));
+  if (row_tiles >= 64) {
+    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 4>), grid, dim3(256), 0, st, x, at, M, K, rank, t, pair);
+  } else {
+    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 8>), grid, dim3(512), 0, st, x, at, M, K, rank, t, pair);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* A, int64_t M, int64_t K,
-                                  int rank, float* t, hipStream_t st) {
+hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* at, int64_t M, int64_t K,
+                                  int rank, void* t, bool pair_out, hipStream_t st) {
+  if (x_f16) {
+    const _Float16* xh = static_cast<const _Float16*>(x);
+    const _Float16* ah = static_cast<const _Float16*>(at);
+    const int pair = pair_out ? 1 : 0;
+    const int64_t row_tiles = (M + 15) / 16;
+    const int blocks = (rank + 15) / 16;
+    // Few row tiles: one 16-column block per workgroup for parallelism.
+    // Many row tiles: all columns in one workgroup so X is read once.
+    if (row_tiles < 64 || blocks == 1) return launch_f16<1>(xh, ah, M, K, rank, t, pair, st);
+    if (blocks <= 2) return launch_f16<2>(xh, ah, M, K, rank, t, pair, st);
+    if (blocks <= 4) return launch_f16<4>(xh, ah, M, K, rank, t, pair, st);
+    if (blocks <= 8) return launch_f16<8>(xh, ah, M, K, rank, t, pair, st);
+    return launch_f16<16>(xh, ah, M, K, rank, t, pair, st);
+  }
   const dim3 grid(static_cast<unsigned>((M + TR - 1) / TR), static_cast<unsigned>((rank + TC - 1) / TC));
-  if (x_f16)
-    hipLaunchKernelGGL(lowrank_project_kernel<_Float16>, grid, dim3(256), 0, st,
-                       static_cast<const _Float16*>(x), static_cast<const _Float16*>(A), M, K, rank,
-                       t);
-  else
-    hipLaunchKernelGGL(lowrank_project_kernel<float>, grid, dim3(256), 0, st,
-                       static_cast<const float*>(x), static_cast<const float*>(A), M, K, rank, t);
+  hipLaunchKernelGGL(lowrank_f32_kernel, grid, dim3(256), 0, st, static_cast<const float*>(x),
+                     static_cast<const float*>(at), M, K, rank, static_cast<float*>(t));
   return hipGetLastError();
 }
 

@@ -4,7 +4,7 @@
 // compensation matrix added to it).
 //
 //   acc[m, n] = sum_k qx[m, k] * qw[n, k]          (exact int32)
-//   y[m, n]   = sx[m] * sum_j sw[n, j] * acc_j[m, n] + (T . B)[m, n]
+//   y[m, n]   = sx[m] * sum_j sw[n, j] * acc_j[m, n] + (T . Bt^T)[m, n]
 //
 // Both operands are packed int4, K-contiguous ([rows, K/2] bytes).  There is
 // no int4 matrix instruction on CDNA4, so codes are widened to int8 in
@@ -16,10 +16,21 @@
 // lanes of the instruction, i.e. the K order inside one instruction is
 // permuted; A and B use the same permutation, so the dot products are exact.
 //
-// Tiling: a 256-thread workgroup owns a BM x BN output tile; its four waves
-// form a 2 x 2 grid of (BM/2) x (BN/2) wave tiles.  K advances 128 codes
-// (64 bytes per row, two MFMA K steps) per iteration through double-buffered
-// LDS tiles.
+// Large M: a 256-thread workgroup owns a (32 TM) x (32 TN) output tile; its
+// four waves form a 2 x 2 grid of (16 TM) x (16 TN) wave tiles.  K advances
+// 128 codes (64 bytes per row, two MFMA K steps) per iteration through
+// double-buffered LDS tiles.  Tiles are handed to workgroups so that the
+// workgroups resident on one XCD (each XCD has its own L2) cover a compact
+// block of output tiles and share their A and B panels in that L2.
+//
+// Small M (decode, M <= 32): a workgroup owns 16 output columns and its waves
+// split K; every lane streams its weight bytes straight from memory into
+// registers (no LDS staging), the waves' partial tiles are reduced in LDS.
+//
+// Low-rank term.  fp16 path: T is given as an fp16 pair (t_hi, t_lo) [M, r]
+// and Bt [N, r] is fp16; each 16x16 output block adds t_hi.Bt^T and
+// t_lo.Bt^T with v_mfma_f32_16x16x32_f16, using the dequantized tile as the
+// accumulator input.  fp32 path: float32 FMA loop.
 #include "w4a4_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -28,8 +39,12 @@ namespace w4a4 {
 namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-constexpr int BK_BYTES = 64;  // 128 int4 codes per row per K step
+constexpr int BK_BYTES = 64;  // 128 int4 codes per row per K iteration
+constexpr float kInv256 = 0.00390625f;  // both operands carry 16*q
+constexpr float kInv16 = 0.0625f;       // only the weights carry 16*q
 
 __device__ __forceinline__ float load_scale(const void* p, int64_t i, int f16) {
   if (f16) return __half2float(reinterpret_cast<const __half*>(p)[i]);
@@ -43,30 +58,118 @@ __device__ __forceinline__ i32x4 widen(uint32_t p0, uint32_t p1) {
                static_cast<int32_t>((p1 << 4) & 0xF0F0F0F0u), static_cast<int32_t>(p1 & 0xF0F0F0F0u)};
 }
 
-// LDS tile rows hold 64 bytes (128 codes).  Lane group g (lanes 16g..16g+15)
-// of an MFMA reads one 16-byte chunk: its first 8 bytes are codes
-// [16g, 16g+16) of K step 0 (codes 0..63 of the row) and its last 8 bytes the
-// same slice of K step 1 (codes 64..127), so that each K step is a contiguous
-// range of 64 codes.  Chunks are XOR-swizzled by row to spread LDS banks.
+// LDS tile layout ("fragment-major").  A K iteration covers 128 codes
+// (64 bytes) of each tile row.  The 16-byte piece lane group g
+// (lanes 16g..16g+15) of an MFMA reads holds codes [16g, 16g+16) of K step 0
+// (codes 0..63 of the iteration) in its first 8 bytes and the same slice of
+// K step 1 (codes 64..127) in its last 8 bytes, so that each K step is a
+// contiguous range of 64 codes.  Pieces are stored as
+// [row block (16 rows)][g (4)][row in block (16)][16 bytes], so the 64 lanes
+// of one fragment read touch 1 KB of consecutive LDS and never collide in a
+// bank; each ds_write_b64 of the staging writes two 256-byte runs.
 //
-// Physical byte offset of 16-byte chunk c of tile row r.
-__device__ __forceinline__ int tile_off(int r, int c) {
-  return r * BK_BYTES + ((c ^ ((r >> 2) & 3)) << 4);
+// Byte offset of the piece read by lane group g for tile row r.
+__device__ __forceinline__ int frag_off(int r, int g) {
+  return (((r >> 4) * 4 + g) << 8) + ((r & 15) << 4);
 }
-// Physical byte offset of logical 8-byte piece p (bytes [8p, 8p+8)) of row r.
+// Byte offset of the logical 8 bytes [8p, 8p + 8) of tile row r.
 __device__ __forceinline__ int piece_off(int r, int p) {
-  return tile_off(r, p & 3) + ((p >> 2) << 3);
+  return frag_off(r, p & 3) + ((p >> 2) << 3);
 }
 
-template <int BM, int BN, bool GROUPED>
+// int8 activation tiles (a_i8): a K iteration covers 128 bytes of each row;
+// K step h, lane group g reads codes [64h + 16g, 64h + 16g + 16), stored as
+// [row block][h (2)][g (4)][row in block (16)][16 bytes].
+__device__ __forceinline__ int a8_off(int r, int h, int g) {
+  return ((((r >> 4) * 2 + h) * 4 + g) << 8) + ((r & 15) << 4);
+}
+
+// Adds the low-rank term of one 16x16 output block to its dequantized values.
+// Fragment layout of a 16x16 MFMA result: lane holds rows 4*(lane>>4)+i of
+// column lane&15.
+template <int LRMODE>
+__device__ __forceinline__ f32x4 add_lowrank(const GemmArgs& a, f32x4 v, int64_t mblk, int64_t nblk,
+                                             int lane) {
+  if constexpr (LRMODE == LR_F16) {
+    const int64_t mr = mblk + (lane & 15);  // operand row (A side)
+    const int64_t nr = nblk + (lane & 15);  // operand row of Bt (B side)
+    const int koff = (lane >> 4) * 8;
+    const _Float16* th = static_cast<const _Float16*>(a.t);
+    const _Float16* tl = th + a.M * a.rank;
+    const _Float16* bt = static_cast<const _Float16*>(a.B);
+    const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int c = 0; c < a.rank; c += 32) {
+      const int j = c + koff;
+      const bool jok = j < a.rank;
+      const half8 hi = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(th + mr * a.rank + j) : z;
+      const half8 lo = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(tl + mr * a.rank + j) : z;
+      const half8 bb = (jok && nr < a.N) ? *reinterpret_cast<const half8*>(bt + nr * a.rank + j) : z;
+      v = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo, bb, v, 0, 0, 0);
+      v = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi, bb, v, 0, 0, 0);
+    }
+  } else if constexpr (LRMODE == LR_F32) {
+    const int64_t n = nblk + (lane & 15);
+    if (n < a.N) {
+      const float* t = static_cast<const float*>(a.t);
+      const float* bt = static_cast<const float*>(a.B) + n * a.rank;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mblk + (lane >> 4) * 4 + i;
+        if (m < a.M) {
+          float s = 0.f;
+          for (int q = 0; q < a.rank; ++q) s = fmaf(t[m * a.rank + q], bt[q], s);
+          v[i] += s;
+        }
+      }
+    }
+  }
+  return v;
+}
+
+// Writes one 16x16 block (int32 total >> shift and/or float32 y).
+__device__ __forceinline__ void store_block(const GemmArgs& a, int64_t mblk, int64_t nblk, int lane,
+                                            i32x4 total, f32x4 yv, int shift) {
+  const int64_t n = nblk + (lane & 15);
+  if (n >= a.N) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t m = mblk + (lane >> 4) * 4 + i;
+    if (m < a.M) {
+      if (a.acc) a.acc[m * a.N + n] = total[i] >> shift;
+      if (a.y) a.y[m * a.N + n] = yv[i];
+    }
+  }
+}
+
+// Maps a workgroup index to an output tile: consecutive workgroup indices go
+// to different XCDs (round robin), so the tiles of one XCD are taken as one
+// contiguous range of a grouped ordering (groups of GM tile rows, tile
+// columns fastest inside a group) and land as a compact block.
+__device__ __forceinline__ void tile_of(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t* tm,
+                                        int64_t* tn) {
+  const int64_t T = tiles_m * tiles_n;
+  int64_t L = bid;
+  if ((T & 7) == 0) L = (bid & 7) * (T >> 3) + (bid >> 3);
+  constexpr int64_t GM = 4;
+  const int64_t per_group = GM * tiles_n;
+  const int64_t g = L / per_group;
+  const int64_t first_m = g * GM;
+  const int64_t gsize = (tiles_m - first_m) < GM ? (tiles_m - first_m) : GM;
+  const int64_t r = L % per_group;
+  *tm = first_m + r % gsize;
+  *tn = r / gsize;
+}
+
+template <int TM, int TN, bool GROUPED, int LRMODE, bool AI8>
 __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int A_UNITS = BM * BK_BYTES / 16 / 256;  // 16-byte loads per thread
+  constexpr int WM = TM * 16, WN = TN * 16;
+  constexpr int BM = 2 * WM, BN = 2 * WN;
+  constexpr int A_ROW = AI8 ? 2 * BK_BYTES : BK_BYTES;  // A bytes per row per iteration
+  constexpr int A_UNITS = BM * A_ROW / 16 / 256;       // 16-byte loads per thread
   constexpr int B_UNITS = BN * BK_BYTES / 16 / 256;
   static_assert(A_UNITS >= 1 && B_UNITS >= 1, "tile too small");
 
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * BK_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * A_ROW];
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * BK_BYTES];
 
   const int tid = threadIdx.x;
@@ -75,60 +178,84 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
   const int wm0 = (wave >> 1) * WM;
   const int wn0 = (wave & 1) * WN;
 
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t tiles_n = (a.N + BN - 1) / BN;
-  const int64_t tile = blockIdx.x;
-  const int64_t m0 = (tile / tiles_n) * BM;
-  const int64_t n0 = (tile % tiles_n) * BN;
+  int64_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = tmi * BM;
+  const int64_t n0 = tni * BN;
   const int64_t K = a.K;
-  const int64_t row_bytes = K / 2;
+  const int64_t row_bytes = K / 2;                 // packed rows
+  const int64_t a_row_bytes = AI8 ? K : K / 2;     // activation rows
   const int nkt = static_cast<int>((K + 127) / 128);
-  const int ksteps = static_cast<int>(K / 64);
+  const bool k_tail = (K & 127) != 0;  // last iteration holds 64 codes
+
+  // Staging pointers.  Rows past M (or N) are clamped to the last row: they
+  // only feed output rows (columns) that are never stored.
+  const uint8_t* pa[A_UNITS];
+  const uint8_t* pb[B_UNITS];
+  int sa[A_UNITS][2], sb[B_UNITS][2];  // LDS byte offsets (of the two halves)
+#pragma unroll
+  for (int i = 0; i < A_UNITS; ++i) {
+    const int u = tid + 256 * i;
+    if constexpr (AI8) {
+      const int r = u >> 3, c = u & 7;
+      const int64_t m = (m0 + r) < a.M ? (m0 + r) : (a.M - 1);
+      pa[i] = a.xq + m * a_row_bytes + c * 16;
+      sa[i][0] = a8_off(r, c >> 2, c & 3);
+      sa[i][1] = 0;
+    } else {
+      const int r = u >> 2, c = u & 3;
+      const int64_t m = (m0 + r) < a.M ? (m0 + r) : (a.M - 1);
+      pa[i] = a.xq + m * a_row_bytes + c * 16;
+      sa[i][0] = piece_off(r, 2 * c);
+      sa[i][1] = piece_off(r, 2 * c + 1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < B_UNITS; ++i) {
+    const int u = tid + 256 * i;
+    const int r = u >> 2, c = u & 3;
+    const int64_t n = (n0 + r) < a.N ? (n0 + r) : (a.N - 1);
+    pb[i] = a.wq + n * row_bytes + c * 16;
+    sb[i][0] = piece_off(r, 2 * c);
+    sb[i][1] = piece_off(r, 2 * c + 1);
+  }
+  // Units of this thread that lie in codes 64..127 of an iteration.
+  const bool a_hi = AI8 ? (tid & 7) >= 4 : (tid & 3) >= 2;
+  const bool b_hi = (tid & 3) >= 2;
 
   uint4 ra[A_UNITS], rb[B_UNITS];
   auto gload = [&](int kt) {
+    const bool last = k_tail && kt == nkt - 1;
+    const int64_t aoff = static_cast<int64_t>(kt) * A_ROW;
+    const int64_t boff = static_cast<int64_t>(kt) * BK_BYTES;
 #pragma unroll
-    for (int i = 0; i < A_UNITS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u >> 2, c = u & 3;
-      const int64_t m = m0 + r;
-      const int64_t kb = static_cast<int64_t>(kt) * BK_BYTES + c * 16;
-      if (m < a.M && kb < row_bytes)
-        ra[i] = *reinterpret_cast<const uint4*>(a.xq + m * row_bytes + kb);
-      else
-        ra[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < A_UNITS; ++i)
+      ra[i] = (last && a_hi) ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(pa[i] + aoff);
 #pragma unroll
-    for (int i = 0; i < B_UNITS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u >> 2, c = u & 3;
-      const int64_t n = n0 + r;
-      const int64_t kb = static_cast<int64_t>(kt) * BK_BYTES + c * 16;
-      if (n < a.N && kb < row_bytes)
-        rb[i] = *reinterpret_cast<const uint4*>(a.wq + n * row_bytes + kb);
-      else
-        rb[i] = make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < B_UNITS; ++i)
+      rb[i] = (last && b_hi) ? make_uint4(0, 0, 0, 0) : *reinterpret_cast<const uint4*>(pb[i] + boff);
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_UNITS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u >> 2, p = (u & 3) * 2;
-      *reinterpret_cast<uint2*>(&As[buf][piece_off(r, p)]) = make_uint2(ra[i].x, ra[i].y);
-      *reinterpret_cast<uint2*>(&As[buf][piece_off(r, p + 1)]) = make_uint2(ra[i].z, ra[i].w);
+      if constexpr (AI8) {
+        *reinterpret_cast<uint4*>(&As[buf][sa[i][0]]) = ra[i];
+      } else {
+        *reinterpret_cast<uint2*>(&As[buf][sa[i][0]]) = make_uint2(ra[i].x, ra[i].y);
+        *reinterpret_cast<uint2*>(&As[buf][sa[i][1]]) = make_uint2(ra[i].z, ra[i].w);
+      }
     }
 #pragma unroll
     for (int i = 0; i < B_UNITS; ++i) {
-      const int u = tid + 256 * i;
-      const int r = u >> 2, p = (u & 3) * 2;
-      *reinterpret_cast<uint2*>(&Bs[buf][piece_off(r, p)]) = make_uint2(rb[i].x, rb[i].y);
-      *reinterpret_cast<uint2*>(&Bs[buf][piece_off(r, p + 1)]) = make_uint2(rb[i].z, rb[i].w);
+      *reinterpret_cast<uint2*>(&Bs[buf][sb[i][0]]) = make_uint2(rb[i].x, rb[i].y);
+      *reinterpret_cast<uint2*>(&Bs[buf][sb[i][1]]) = make_uint2(rb[i].z, rb[i].w);
     }
   };
 
   i32x4 acc[TM][TN];
-  float facc[GROUPED ? TM : 1][GROUPED ? TN : 1][4];
-  i32x4 full[GROUPED ? TM : 1][GROUPED ? TN : 1];  // full-K sum (for the acc output)
+  f32x4 facc[GROUPED ? TM : 1][GROUPED ? TN : 1];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -137,66 +264,64 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        full[i][j] = i32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) facc[i][j][r] = 0.f;
-      }
+      for (int j = 0; j < TN; ++j) facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const bool want_y = a.y != nullptr;  // scales are only read when y is written
   const int gsteps = GROUPED ? a.group / 64 : 1;
   const int64_t ngroups = GROUPED ? K / a.group : 1;
+  const int ksteps = static_cast<int>(K / 64);
 
   gload(0);
   lstore(0);
   __syncthreads();
 
   const int frow = lane & 15;  // fragment row within a 16-row block
-  const int fchk = lane >> 4;  // 16-byte chunk of the 64-byte tile row
+  const int fg = lane >> 4;    // lane group
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nkt) gload(kt + 1);
 
-    uint4 fa[TM], fb[TN];
+    uint4 fa[AI8 ? 1 : TM], fb[TN];
+    if constexpr (!AI8) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-      fa[i] = *reinterpret_cast<const uint4*>(&As[buf][tile_off(wm0 + i * 16 + frow, fchk)]);
+      for (int i = 0; i < TM; ++i)
+        fa[i] = *reinterpret_cast<const uint4*>(&As[buf][frag_off(wm0 + i * 16 + frow, fg)]);
+    }
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      fb[j] = *reinterpret_cast<const uint4*>(&Bs[buf][tile_off(wn0 + j * 16 + frow, fchk)]);
+      fb[j] = *reinterpret_cast<const uint4*>(&Bs[buf][frag_off(wn0 + j * 16 + frow, fg)]);
 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int kstep = kt * 2 + h;
-      if (kstep < ksteps) {
-        i32x4 opa[TM], opb[TN];
+      i32x4 opb[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) opa[i] = h ? widen(fa[i].z, fa[i].w) : widen(fa[i].x, fa[i].y);
+      for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
+      for (int i = 0; i < TM; ++i) {
+        i32x4 opa;
+        if constexpr (AI8)
+          opa = *reinterpret_cast<const i32x4*>(&As[buf][a8_off(wm0 + i * 16 + frow, h, fg)]);
+        else
+          opa = h ? widen(fa[i].z, fa[i].w) : widen(fa[i].x, fa[i].y);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa, opb[j], acc[i][j], 0, 0, 0);
+      }
+      if constexpr (GROUPED) {
+        const int kstep = kt * 2 + h;
+        if (kstep < ksteps && (kstep + 1) % gsteps == 0) {
+          const int64_t grp = (kstep + 1) / gsteps - 1;
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], acc[i][j], 0, 0, 0);
-
-        if constexpr (GROUPED) {
-          if ((kstep + 1) % gsteps == 0) {
-            const int64_t grp = (kstep + 1) / gsteps - 1;
+          for (int j = 0; j < TN; ++j) {
+            int64_t n = n0 + wn0 + j * 16 + frow;
+            n = n < a.N ? n : a.N - 1;
+            const float sw = load_scale(a.sw, n * ngroups + grp, a.sw_f16);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              const int64_t n = n0 + wn0 + j * 16 + frow;
-              const float sw =
-                  (want_y && n < a.N) ? load_scale(a.sw, n * ngroups + grp, a.sw_f16) : 0.f;
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-              for (int i = 0; i < TM; ++i) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
-                full[i][j] += acc[i][j];
-                acc[i][j] = i32x4{0, 0, 0, 0};
-              }
+              for (int r = 0; r < 4; ++r)
+                facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
+              acc[i][j] = i32x4{0, 0, 0, 0};
             }
           }
         }
@@ -207,56 +332,562 @@ __global__ void __launch_bounds__(256) qgemm_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  // Epilogue.  Output fragment (i, j) of lane holds rows 4*(lane>>4)+r, column lane&15.
-  const int ecol = lane & 15;
-  const int erow = (lane >> 4) * 4;
+  // Epilogue.  Output fragment (i, j) of this lane: rows
+  // m0 + wm0 + 16 i + 4 (lane >> 4) + r (r < 4), column n0 + wn0 + 16 j + (lane & 15).
+  const bool want_y = a.y != nullptr;
+  const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
+  const int64_t nlane = n0 + wn0 + (lane & 15);
+  const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+  float sxr[TM][4];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = mlane + i * 16 + r;
+      sxr[i][r] = (want_y && m < a.M) ? a.sx[m] * (AI8 ? kInv16 : kInv256) : 0.f;
+    }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
-    const int64_t n = n0 + wn0 + j * 16 + ecol;
-    if (n >= a.N) continue;
-    const float swn = (GROUPED || !want_y) ? 1.f : load_scale(a.sw, n, a.sw_f16);
+    const int64_t n = nlane + j * 16;
+    const bool n_ok = n < a.N;
+    const float swn = (GROUPED || !want_y || !n_ok) ? 1.f : load_scale(a.sw, n, a.sw_f16);
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      f32x4 yv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + wm0 + i * 16 + erow + r;
-        if (m >= a.M) continue;
-        const int32_t total = GROUPED ? full[GROUPED ? i : 0][GROUPED ? j : 0][r] : acc[i][j][r];
-        if (a.acc) a.acc[m * a.N + n] = total >> 8;
-        if (a.y) {
-          float val;
-          if constexpr (GROUPED)
-            val = facc[i][j][r] * (a.sx[m] * 0.00390625f);
-          else
-            val = static_cast<float>(total) * (a.sx[m] * swn * 0.00390625f);
-          if (a.rank > 0) {
-            float lr = 0.f;
-            const float* trow = a.t + m * a.rank;
-            for (int q = 0; q < a.rank; ++q)
-              lr = fmaf(trow[q], load_scale(a.B, static_cast<int64_t>(q) * a.N + n, a.b_f16), lr);
-            val += lr;
+        if constexpr (GROUPED)
+          yv[r] = facc[i][j][r] * sxr[i][r];
+        else
+          yv[r] = static_cast<float>(acc[i][j][r]) * (sxr[i][r] * swn);
+      }
+      if constexpr (LRMODE != LR_NONE) {
+        if (want_y) yv = add_lowrank<LRMODE>(a, yv, mlane - (lane >> 4) * 4 + i * 16, nlane - (lane & 15) + j * 16, lane);
+      }
+      const int64_t mb = mlane + i * 16;
+      if (interior) {
+        float* yp = a.y + mb * a.N + n;
+        int32_t* ap = a.acc + mb * a.N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (want_y) yp[r * a.N] = yv[r];
+          if (!GROUPED && a.acc) ap[r * a.N] = acc[i][j][r] >> (AI8 ? 4 : 8);
+        }
+      } else if (n_ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (mb + r < a.M) {
+            if (want_y) a.y[(mb + r) * a.N + n] = yv[r];
+            if (!GROUPED && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> (AI8 ? 4 : 8);
           }
-          a.y[m * a.N + n] = val;
         }
       }
     }
   }
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(const GemmArgs& a, hipStream_t st) {
+// ---------------------------------------------------------------------------
+// Pipelined kernel for int8 activation codes, K % 128 == 0 and weight groups
+// that are multiples of 128.  Global memory is copied straight into LDS with
+// global_load_lds_dwordx4 (each lane's 16 bytes land at lane * 16 of a 1 KB
+// run), through a ring of STAGES LDS buffers, so loads run STAGES - 1
+// iterations ahead of the matrix instructions without staging registers.
+//
+// K mapping of one 128-code iteration: K step h, lane group g covers codes
+// [32g + 16h, 32g + 16h + 16): the int8 activation operand is the 16 bytes at
+// that offset, the weight operand the h-th half of the 16 packed bytes
+// [16g, 16g + 16) (codes [32g, 32g + 32)) after widening.
+//
+// LDS stage: A as [row block][h][g][16 rows][16 B], B as [row block][g][16
+// rows][16 B]; every 1 KB run is filled by one wave instruction and read by
+// one conflict-free ds_read_b128.
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at
+// their maximum); vmcnt is split over bits [3:0] and [15:14].
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(N));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l writes
+// [lds_base + 16 l, lds_base + 16 l + 16).  Issued from asm so that the
+// compiler does not treat the copy as an LDS store it must wait for before
+// every LDS read; the kernel waits for the copies itself (wait_vmcnt).  The
+// asm writes no register, so nothing it produces can be consumed early.
+__device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier that also waits for this wave's own LDS reads: no wave
+// passes it while another may still read a stage that is about to be
+// refilled.  Written as asm with a memory clobber so that the compiler keeps
+// LDS accesses on their side of it and adds no wait for the in-flight
+// direct-to-LDS copies (each stage is its own LDS array, so it can tell the
+// stage being read from the stages being filled).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE>
+__global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
+  constexpr int WM = TM * 16, WN = TN * 16;
+  constexpr int BM = 2 * WM, BN = 2 * WN;
+  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 64;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int A_RUNS = BM / 16 * 2, B_RUNS = BN / 16;
+  constexpr int RUNS = A_RUNS + B_RUNS;
+  static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
+  static_assert(STAGES >= 2 && STAGES <= 8, "stages");
+  constexpr int RUNS_PER_WAVE = RUNS / 4;
+  static_assert((STAGES - 2) * RUNS_PER_WAVE < 64, "in-flight copies exceed vmcnt");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGES > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[STAGES > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st4[STAGES > 4 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st5[STAGES > 5 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st6[STAGES > 6 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st7[STAGES > 7 ? STAGE : 16];
+  auto stage = [&](int sidx) -> uint8_t* {
+    switch (sidx) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      case 3: return st3;
+      case 4: return st4;
+      case 5: return st5;
+      case 6: return st6;
+      default: return st7;
+    }
+  };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm0 = (wave >> 1) * WM;
+  const int wn0 = (wave & 1) * WN;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (a.N + BN - 1) / BN;
+  int64_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = tmi * BM;
+  const int64_t n0 = tni * BN;
+  const int64_t K = a.K;
+  const int nkt = static_cast<int>(K / 128);
+
+  // Source pointer (at iteration 0) and LDS offset of each run this wave copies.
+  const uint8_t* src[RUNS_PER_WAVE];
+  int dst[RUNS_PER_WAVE];
+  int step[RUNS_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < RUNS_PER_WAVE; ++q) {
+    const int run = wave + 4 * q;
+    const int g = lane >> 4, rr = lane & 15;
+    if (run < A_RUNS) {
+      const int blk = run >> 1, h = run & 1;
+      int64_t m = m0 + blk * 16 + rr;
+      m = m < a.M ? m : a.M - 1;
+      src[q] = a.xq + m * K + 32 * g + 16 * h;
+      dst[q] = ((blk * 2 + h) * 4) << 8;
+      step[q] = 128;
+    } else {
+      const int blk = run - A_RUNS;
+      int64_t n = n0 + blk * 16 + rr;
+      n = n < a.N ? n : a.N - 1;
+      src[q] = a.wq + n * (K / 2) + 16 * g;
+      dst[q] = A_BYTES + ((blk * 4) << 8);
+      step[q] = 64;
+    }
+  }
+  // Workgroups that share an A or B panel start at different K positions,
+  // so that a panel slice is fetched from memory by one of them and found in
+  // L2 by the others instead of all of them waiting on the same miss.
+  const int iters_per_group0 = GROUPED ? a.group / 128 : 1;
+  int k_rot = 0;
+  if (nkt >= 8) {
+    const int span = ((nkt / 8) / iters_per_group0) * iters_per_group0;
+    k_rot = static_cast<int>((tmi + tni) & 7) * span;
+  }
+  auto kpos = [&](int kt) { const int k = kt + k_rot; return k >= nkt ? k - nkt : k; };
+  auto issue = [&](int kt, uint8_t* base) {
+    const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
+    const int64_t kp = kpos(kt);
+#pragma unroll
+    for (int q = 0; q < RUNS_PER_WAVE; ++q)
+      dma16(src[q] + kp * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
+  };
+
+  i32x4 acc[TM][TN];
+  f32x4 facc[GROUPED ? TM : 1][GROUPED ? TN : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int iters_per_group = GROUPED ? a.group / 128 : 1;
+  const int64_t ngroups = GROUPED ? K / a.group : 1;
+
+#pragma unroll
+  for (int sidx = 0; sidx < STAGES - 1; ++sidx)
+    if (sidx < nkt) issue(sidx, stage(sidx));
+
+  const int frow = lane & 15;
+  const int fg = lane >> 4;
+  for (int kt0 = 0; kt0 < nkt; kt0 += STAGES) {
+#pragma unroll
+    for (int sidx = 0; sidx < STAGES; ++sidx) {
+      const int kt = kt0 + sidx;
+      if (kt < nkt) {
+        // Stage kt has landed once at most the later stages' runs are in flight.
+        if (kt + STAGES - 1 <= nkt)
+          wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
+        else
+          wait_vmcnt<0>();
+        stage_barrier();
+        if (kt + STAGES - 1 < nkt) issue(kt + STAGES - 1, stage((sidx + STAGES - 1) % STAGES));
+
+        const uint8_t* As = stage(sidx);
+        const uint8_t* Bs = As + A_BYTES;
+        uint4 fb[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          fb[j] = *reinterpret_cast<const uint4*>(Bs + ((((wn0 >> 4) + j) * 4 + fg) << 8) + (frow << 4));
+        i32x4 fa[2][TM];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+            fa[h][i] = *reinterpret_cast<const i32x4*>(
+                As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          i32x4 opb[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][i], opb[j], acc[i][j], 0, 0, 0);
+        }
+        if constexpr (GROUPED) {
+          const int kp = kpos(kt);
+          if ((kp + 1) % iters_per_group == 0) {
+            const int64_t grp = (kp + 1) / iters_per_group - 1;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+              int64_t n = n0 + wn0 + j * 16 + frow;
+              n = n < a.N ? n : a.N - 1;
+              const float sw = load_scale(a.sw, n * ngroups + grp, a.sw_f16);
+#pragma unroll
+              for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
+                acc[i][j] = i32x4{0, 0, 0, 0};
+              }
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // Epilogue (accumulators hold 16 * acc: only the weights carry the factor).
+  const bool want_y = a.y != nullptr;
+  const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
+  const int64_t nlane = n0 + wn0 + (lane & 15);
+  const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+  float sxr[TM][4];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = mlane + i * 16 + r;
+      sxr[i][r] = (want_y && m < a.M) ? a.sx[m] * kInv16 : 0.f;
+    }
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t n = nlane + j * 16;
+    const bool n_ok = n < a.N;
+    const float swn = (GROUPED || !want_y || !n_ok) ? 1.f : load_scale(a.sw, n, a.sw_f16);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      f32x4 yv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (GROUPED)
+          yv[r] = facc[i][j][r] * sxr[i][r];
+        else
+          yv[r] = static_cast<float>(acc[i][j][r]) * (sxr[i][r] * swn);
+      }
+      if constexpr (LRMODE != LR_NONE) {
+        if (want_y)
+          yv = add_lowrank<LRMODE>(a, yv, m0 + wm0 + i * 16, n0 + wn0 + j * 16, lane);
+      }
+      const int64_t mb = mlane + i * 16;
+      if (interior) {
+        float* yp = a.y + mb * a.N + n;
+        int32_t* ap = a.acc + mb * a.N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (want_y) yp[r * a.N] = yv[r];
+          if (!GROUPED && a.acc) ap[r * a.N] = acc[i][j][r] >> 4;
+        }
+      } else if (n_ok) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (mb + r < a.M) {
+            if (want_y) a.y[(mb + r) * a.N + n] = yv[r];
+            if (!GROUPED && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> 4;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Small M: 16 output columns per workgroup, KW waves split K.  MB row blocks
+// of 16 cover M <= 16 * MB.  Every lane loads, per 128-code K pair t, the 16
+// bytes [64t + 16g, 64t + 16g + 16) of its weight row (g = lane >> 4) and of
+// its activation rows; K step 0 of the pair uses the first 8 bytes and K
+// step 1 the last 8, identically on both sides.
+template <int MB, int KW, bool GROUPED, int LRMODE, bool AI8>
+__global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
+  constexpr int CH = 8;  // K pairs loaded per batch
+  __shared__ i32x4 ired[KW][MB][64];
+  __shared__ f32x4 fred[GROUPED ? KW : 1][GROUPED ? MB : 1][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t row_bytes = a.K / 2;
+  const int64_t npairs = (a.K + 127) / 128;
+  const int g = lane >> 4;
+  const int64_t nrow = n0 + (lane & 15);
+  const bool n_ok = nrow < a.N;
+  const bool want_y = a.y != nullptr;
+  const int64_t ngroups = GROUPED ? a.K / a.group : 1;
+  const int64_t pairs_per_group = GROUPED ? a.group / 128 : 1;
+
+  // Contiguous pair range of this wave.
+  const int64_t p_begin = npairs * wave / KW;
+  const int64_t p_end = npairs * (wave + 1) / KW;
+
+  i32x4 acc[MB];
+  f32x4 facc[GROUPED ? MB : 1];
+  i32x4 full[GROUPED ? MB : 1];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) acc[b] = i32x4{0, 0, 0, 0};
+  if constexpr (GROUPED) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      facc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      full[b] = i32x4{0, 0, 0, 0};
+    }
+  }
+
+  for (int64_t p0 = p_begin; p0 < p_end; p0 += CH) {
+    uint4 wv[CH], xv[CH][MB][AI8 ? 2 : 1];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int64_t p = p0 + c;
+      const int64_t kb = p * 64 + g * 16;
+      const bool ok = p < p_end && kb < row_bytes;
+      wv[c] = (ok && n_ok) ? *reinterpret_cast<const uint4*>(a.wq + nrow * row_bytes + kb)
+                           : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int64_t m = b * 16 + (lane & 15);
+        const bool xok = ok && m < a.M;
+        if constexpr (AI8) {
+          const uint8_t* xp = a.xq + m * a.K + 2 * kb;  // int8 codes [2kb, 2kb + 32)
+          xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
+          xv[c][b][1] = xok ? *reinterpret_cast<const uint4*>(xp + 16) : make_uint4(0, 0, 0, 0);
+        } else {
+          xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(a.xq + m * row_bytes + kb)
+                            : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const i32x4 w0 = widen(wv[c].x, wv[c].y);
+      const i32x4 w1 = widen(wv[c].z, wv[c].w);
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        i32x4 x0, x1;
+        if constexpr (AI8) {
+          x0 = *reinterpret_cast<const i32x4*>(&xv[c][b][0]);
+          x1 = *reinterpret_cast<const i32x4*>(&xv[c][b][AI8 ? 1 : 0]);
+        } else {
+          x0 = widen(xv[c][b][0].x, xv[c][b][0].y);
+          x1 = widen(xv[c][b][0].z, xv[c][b][0].w);
+        }
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, w0, acc[b], 0, 0, 0);
+        acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, w1, acc[b], 0, 0, 0);
+      }
+      if constexpr (GROUPED) {
+        const int64_t p = p0 + c;
+        if (p < p_end && (p + 1) % pairs_per_group == 0) {
+          const int64_t grp = p / pairs_per_group;
+          const float sw = (want_y && n_ok) ? load_scale(a.sw, nrow * ngroups + grp, a.sw_f16) : 0.f;
+#pragma unroll
+          for (int b = 0; b < MB; ++b) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) facc[b][r] = fmaf(static_cast<float>(acc[b][r]), sw, facc[b][r]);
+            full[b] += acc[b];
+            acc[b] = i32x4{0, 0, 0, 0};
+          }
+        }
+      }
+    }
+  }
+  if constexpr (GROUPED) {
+    // A group straddling this wave's last pair and the next wave's first is
+    // flushed by both waves, each with its part of the sum.
+    if (p_end > p_begin && p_end % pairs_per_group != 0) {
+      const int64_t grp = (p_end - 1) / pairs_per_group;
+      const float sw = (want_y && n_ok) ? load_scale(a.sw, nrow * ngroups + grp, a.sw_f16) : 0.f;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) facc[b][r] = fmaf(static_cast<float>(acc[b][r]), sw, facc[b][r]);
+        full[b] += acc[b];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+      ired[wave][b][lane] = full[b];
+      fred[wave][b][lane] = facc[b];
+    }
+  } else {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) ired[wave][b][lane] = acc[b];
+  }
+  __syncthreads();
+  if (wave < MB) {
+    const int b = wave;
+    i32x4 total = ired[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) total += ired[w][b][lane];
+    f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int64_t mblk = b * 16;
+    if (want_y) {
+      f32x4 fsum = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (GROUPED) {
+        fsum = fred[0][b][lane];
+#pragma unroll
+        for (int w = 1; w < KW; ++w) fsum += fred[w][b][lane];
+      }
+      const int64_t n = n0 + (lane & 15);
+      const float swn = (GROUPED || n >= a.N) ? 1.f : load_scale(a.sw, n, a.sw_f16);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mblk + (lane >> 4) * 4 + r;
+        const float sxm = m < a.M ? a.sx[m] * (AI8 ? kInv16 : kInv256) : 0.f;
+        yv[r] = GROUPED ? fsum[r] * sxm : static_cast<float>(total[r]) * (sxm * swn);
+      }
+      yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
+    }
+    store_block(a, mblk, n0, lane, total, yv, AI8 ? 4 : 8);
+  }
+}
+
+template <int TM, int TN, bool AI8>
+hipError_t launch_tiles_a(const GemmArgs& a, hipStream_t st) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  if (a.group > 0)
-    hipLaunchKernelGGL((qgemm_kernel<BM, BN, true>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                       st, a);
-  else
-    hipLaunchKernelGGL((qgemm_kernel<BM, BN, false>), dim3(static_cast<unsigned>(tiles)), dim3(256), 0,
-                       st, a);
-  return hipGetLastError();
+  const dim3 grid(static_cast<unsigned>(tiles));
+#define W4A4_GEMM_CASE(G, LR)                                                         \
+  if ((a.group > 0) == G && a.lr_mode == LR) {                                       \
+    hipLaunchKernelGGL((qgemm_kernel<TM, TN, G, LR, AI8>), grid, dim3(256), 0, st, a); \
+    return hipGetLastError();                                                         \
+  }
+  W4A4_GEMM_CASE(false, LR_NONE) W4A4_GEMM_CASE(false, LR_F16) W4A4_GEMM_CASE(false, LR_F32)
+  W4A4_GEMM_CASE(true, LR_NONE) W4A4_GEMM_CASE(true, LR_F16) W4A4_GEMM_CASE(true, LR_F32)
+#undef W4A4_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int TM, int TN>
+hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
+  return a.a_i8 ? launch_tiles_a<TM, TN, true>(a, st) : launch_tiles_a<TM, TN, false>(a, st);
+}
+
+template <int TM, int TN, int STAGES>
+hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const dim3 grid(static_cast<unsigned>(tiles));
+#define W4A4_PIPE_CASE(G, LR)                                                                     \
+  if ((a.group > 0) == G && a.lr_mode == LR) {                                                     \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR>), grid, dim3(256), 0, st, a);     \
+    return hipGetLastError();                                                                     \
+  }
+  W4A4_PIPE_CASE(false, LR_NONE) W4A4_PIPE_CASE(false, LR_F16) W4A4_PIPE_CASE(false, LR_F32)
+  W4A4_PIPE_CASE(true, LR_NONE) W4A4_PIPE_CASE(true, LR_F16) W4A4_PIPE_CASE(true, LR_F32)
+#undef W4A4_PIPE_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int MB, bool AI8>
+hipError_t launch_skinny_a(const GemmArgs& a, hipStream_t st) {
+  constexpr int KW = 4;
+  const dim3 grid(static_cast<unsigned>((a.N + 15) / 16));
+#define W4A4_SKINNY_CASE(G, LR)                                                                  \
+  if ((a.group > 0) == G && a.lr_mode == LR) {                                                    \
+    hipLaunchKernelGGL((qgemm_skinny_kernel<MB, KW, G, LR, AI8>), grid, dim3(64 * KW), 0, st, a); \
+    return hipGetLastError();                                                                    \
+  }
+  W4A4_SKINNY_CASE(false, LR_NONE) W4A4_SKINNY_CASE(false, LR_F16) W4A4_SKINNY_CASE(false, LR_F32)
+  W4A4_SKINNY_CASE(true, LR_NONE) W4A4_SKINNY_CASE(true, LR_F16) W4A4_SKINNY_CASE(true, LR_F32)
+#undef W4A4_SKINNY_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int MB>
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+  return a.a_i8 ? launch_skinny_a<MB, true>(a, st) : launch_skinny_a<MB, false>(a, st);
 }
 
 }  // namespace
 
-hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) { return launch_tile<128, 128>(a, st); }
+hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
+  // The skinny kernel flushes weight groups at 128-code granularity.
+  const bool skinny_ok = a.group == 0 || a.group % 128 == 0;
+  if (a.M <= 16 && skinny_ok) return launch_skinny<1>(a, st);
+  if (a.M <= 32 && skinny_ok) return launch_skinny<2>(a, st);
+  // The tiled kernels write the int32 product only when ungrouped: a grouped
+  // request for acc runs the ungrouped kernel for it (the integer product
+  // does not depend on the weight groups).
+  if (a.group > 0 && a.acc) {
+    GemmArgs ia = a;
+    ia.group = 0;
+    ia.y = nullptr;
+    ia.lr_mode = LR_NONE;
+    hipError_t e = launch_tiles<4, 4>(ia, st);
+    if (e != hipSuccess) return e;
+    if (!a.y) return hipSuccess;
+  }
+  GemmArgs ya = a;
+  if (a.group > 0) ya.acc = nullptr;
+  // int8 codes, whole 128-code iterations: the pipelined direct-to-LDS kernel.
+  if (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0 && a.M > 32) {
+    return launch_pipe<4, 4, 3>(ya, st);
+  }
+  const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+  if (a.group == 0 && a.M >= 256 && big_tiles >= 200) return launch_tiles<8, 4>(ya, st);
+  return launch_tiles<4, 4>(ya, st);
+}
 
 }  // namespace w4a4

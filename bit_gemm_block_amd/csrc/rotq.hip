@@ -232,46 +232,45 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       reinterpret_cast<float*>(a.scale)[si] = s;
   }
 
-  // 6. Codes, packed 8 per dword (element 8d+t in nibble t).
-  uint32_t pk[R / 8];
+  // 6. Codes.  code[r] holds the code of element r in its low bits (two's
+  // complement: low nibble = q & 0xF, low byte = q & 0xFF).
+  uint32_t code[R];
   if (s_eff == 0.f) {
 #pragma unroll
-    for (int d = 0; d < R / 8; ++d) pk[d] = 0u;
+    for (int r = 0; r < R; ++r) code[r] = 0u;
   } else {
     const float kk = a.rs * __frcp_rn(s_eff);
     float dev = 0.f;
 #pragma unroll
-    for (int d = 0; d < R / 8; ++d) {
-      uint32_t acc = 0u;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float tq = v[8 * d + t] * kk;
-        const float u = tq + kMagic;
-        const float w = u - kMagic;
-        dev = fmaxf(dev, fabsf(tq - w));
-        const float uc = __builtin_amdgcn_fmed3f(u, kMagic - 7.0f, kMagic + 7.0f);
-        acc = __builtin_amdgcn_alignbit(__float_as_uint(uc), acc, 4);
-      }
-      pk[d] = acc;
+    for (int r = 0; r < R; ++r) {
+      const float tq = v[r] * kk;
+      const float u = tq + kMagic;
+      const float w = u - kMagic;
+      dev = fmaxf(dev, fabsf(tq - w));
+      code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - 7.0f, kMagic + 7.0f));
     }
     const bool certified = (dev < 0.5f - 0x1p-16f) && (kk <= 0x1p100f);
     if (!certified) {
 #pragma unroll
-      for (int d = 0; d < R / 8; ++d) {
-        uint32_t acc = 0u;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float xt = v[8 * d + t] * a.rs;
-          float qf = rintf(__fdiv_rn(xt, s_eff));
-          qf = fminf(fmaxf(qf, -7.0f), 7.0f);
-          const uint32_t nib = static_cast<uint32_t>(static_cast<int>(qf)) & 0xFu;
-          acc = (acc >> 4) | (nib << 28);
-        }
-        pk[d] = acc;
+      for (int r = 0; r < R; ++r) {
+        const float xt = v[r] * a.rs;
+        float qf = rintf(__fdiv_rn(xt, s_eff));
+        qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+        code[r] = static_cast<uint32_t>(static_cast<int>(qf));
       }
     }
   }
-  if (valid) {
+  if (!valid) return;
+  if (a.mode == ROTQ_QUANT) {
+    // Packed nibbles: element 8d+t in nibble t of dword d.
+    uint32_t pk[R / 8];
+#pragma unroll
+    for (int d = 0; d < R / 8; ++d) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_alignbit(code[8 * d + t], acc, 4);
+      pk[d] = acc;
+    }
     uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
     if constexpr (R == 8) {
       *reinterpret_cast<uint32_t*>(dst) = pk[0];
@@ -280,6 +279,29 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
     } else {
 #pragma unroll
       for (int d = 0; d < R / 8; d += 4)
+        *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+    }
+  } else {
+    // One int8 code per byte, each group of 8 elements stored in the order
+    // 0,2,4,6,1,3,5,7: the K order in which the GEMM widens packed weights.
+    uint32_t pk[R / 4];
+#pragma unroll
+    for (int d = 0; d < R / 8; ++d) {
+      uint32_t e = 0u, o = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        e = __builtin_amdgcn_alignbit(code[8 * d + 2 * t], e, 8);
+        o = __builtin_amdgcn_alignbit(code[8 * d + 2 * t + 1], o, 8);
+      }
+      pk[2 * d] = e;
+      pk[2 * d + 1] = o;
+    }
+    uint8_t* dst = a.q + row * a.K + kfirst;
+    if constexpr (R == 8) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+    } else {
+#pragma unroll
+      for (int d = 0; d < R / 4; d += 4)
         *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
     }
   }

@@ -22,19 +22,26 @@ struct RotqPlan {
 // Chooses the segment shape for (K, b, group); returns false if none fits.
 bool rotq_plan(int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan);
 
-enum RotqMode { ROTQ_ROTATE = 0, ROTQ_QUANT = 1 };
+// ROTQ_QUANT_I8 writes one int8 code per byte, each group of 8 elements in
+// the order 0,2,4,6,1,3,5,7 (the K order of the GEMM's nibble widening): the
+// activation operand format the fused layer hands to the GEMM.
+enum RotqMode { ROTQ_ROTATE = 0, ROTQ_QUANT = 1, ROTQ_QUANT_I8 = 2 };
 
 // x: [M, K] (f16 if x_f16 else f32).  mode ROTATE writes xrot [M, K] f32;
-// mode QUANT writes q [M, K/2] and one scale per group of gsz elements
-// (gsz == K: per row) as f32 or f16 (scale_f16).
+// mode QUANT writes q [M, K/2] (QUANT_I8: q [M, K]) and one scale per group of
+// gsz elements (gsz == K: per row) as f32 or f16 (scale_f16).
 hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K,
                        int log2b, int mode, int64_t gsz, bool scale_f16,
                        float* xrot, uint8_t* q, void* scale,
                        const RotqPlan& plan, hipStream_t st);
 
 // ---- int4 GEMM (qgemm.hip) -------------------------------------------------
+// Low-rank epilogue kinds: none; fp16 (t = fp16 pair t_hi [M, r] followed by
+// t_lo [M, r], B = Bt [N, r] fp16); fp32 (t = [M, r], B = Bt [N, r] fp32).
+enum LowRankMode { LR_NONE = 0, LR_F16 = 1, LR_F32 = 2 };
+
 struct GemmArgs {
-  const uint8_t* xq;     // [M, K/2]
+  const uint8_t* xq;     // [M, K/2] packed, or [M, K] int8 when a_i8
   const float* sx;       // [M]
   const uint8_t* wq;     // [N, K/2]
   const void* sw;        // [N] or [N, K/group]
@@ -43,17 +50,21 @@ struct GemmArgs {
   int64_t M, N, K;
   float* y;              // [M, N] or null
   int32_t* acc;          // [M, N] or null
-  const float* t;        // [M, rank] (X.A) or null
-  const void* B;         // [rank, N] or null
-  int b_f16;
+  const void* t;         // X.A as described by lr_mode, or null
+  const void* B;         // Bt [N, rank], or null
+  int lr_mode;           // LowRankMode
   int rank;
+  int a_i8;              // activation codes as int8 (ROTQ_QUANT_I8 layout)
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
 
 // ---- low-rank projection (lowrank.hip) -------------------------------------
-hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* A,
-                                  int64_t M, int64_t K, int rank, float* t,
-                                  hipStream_t st);
+// t = x [M, K] . At[rank, K]^T.  fp16 inputs: pair_out writes the fp16 pair
+// (t_hi [M, rank], then t_lo [M, rank]) into t, otherwise float32 [M, rank].
+// fp32 inputs always write float32.
+hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* at,
+                                  int64_t M, int64_t K, int rank, void* t,
+                                  bool pair_out, hipStream_t st);
 
 }  // namespace w4a4

@@ -21,6 +21,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, F16 = 0, 1
+CODES_PACKED, CODES_I8 = 0, 1
+_LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -32,10 +34,10 @@ _SIGS = {
     "w4a4_status_string": (ctypes.c_char_p, [_INT]),
     "w4a4_last_hip_error": (_INT, []),
     "w4a4_hadamard_rotate": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P]),
-    "w4a4_quantize_act_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_quantize_act_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
     "w4a4_quantize_weight_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT, _P]),
     "w4a4_lowrank_project": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P, _P]),
-    "w4a4_qgemm_w4a4": (_INT, [_P, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_qgemm_w4a4": (_INT, [_P, _INT, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "w4a4_qlinear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
@@ -114,15 +116,20 @@ def hadamard_rotate(x: torch.Tensor, had_block: int, out: Optional[torch.Tensor]
 
 
 def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor] = None,
-                      x_scale: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                      x_scale: Optional[torch.Tensor] = None,
+                      layout: str = "packed") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Codes in layout "packed" ([M, K/2] nibbles) or "i8" ([M, K] int8 in
+    the GEMM's K order), and one float32 scale per row."""
     _dev(x, "x")
     M, K = x.shape
+    lay = _LAYOUTS[layout]
     if xq is None:
-        xq = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        xq = torch.empty((M, K // 2 if lay == CODES_PACKED else K), dtype=torch.uint8,
+                         device=x.device)
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check("quantize_act_int4", lib().w4a4_quantize_act_int4(
-        _ptr(x), _dt(x), M, K, had_block, _ptr(xq), _ptr(x_scale), _stream(x)))
+        _ptr(x), _dt(x), M, K, had_block, _ptr(xq), lay, _ptr(x_scale), _stream(x)))
     return xq, x_scale
 
 
@@ -138,30 +145,32 @@ def quantize_weight_int4(w: torch.Tensor, had_block: int, w_group: int,
     return wq, ws
 
 
-def lowrank_project(x: torch.Tensor, A: torch.Tensor, t: Optional[torch.Tensor] = None) -> torch.Tensor:
+def lowrank_project(x: torch.Tensor, At: torch.Tensor, t: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """t = x . A with A given transposed, At [rank, K]."""
     _dev(x, "x")
-    _dev(A, "A")
+    _dev(At, "At")
     M, K = x.shape
-    if A.dtype != x.dtype or A.shape[0] != K:
-        raise ValueError("A must be [K, rank] in x's dtype")
-    rank = A.shape[1]
+    if At.dtype != x.dtype or At.shape[1] != K:
+        raise ValueError("At must be [rank, K] in x's dtype")
+    rank = At.shape[0]
     if t is None:
         t = torch.empty((M, rank), dtype=torch.float32, device=x.device)
     _check("lowrank_project", lib().w4a4_lowrank_project(
-        _ptr(x), _dt(x), _ptr(A), M, K, rank, _ptr(t), _stream(x)))
+        _ptr(x), _dt(x), _ptr(At), M, K, rank, _ptr(t), _stream(x)))
     return t
 
 
 def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tensor,
                w_scale: Optional[torch.Tensor], w_group: int, want_y: bool = True,
                want_acc: bool = False, y: Optional[torch.Tensor] = None,
-               acc: Optional[torch.Tensor] = None):
+               acc: Optional[torch.Tensor] = None, layout: str = "packed"):
     _dev(xq, "xq")
     _dev(wq, "wq")
-    M, K2 = xq.shape
+    lay = _LAYOUTS[layout]
+    M = xq.shape[0]
     N = wq.shape[0]
-    K = 2 * K2
-    if wq.shape[1] != K2:
+    K = 2 * wq.shape[1]
+    if xq.shape[1] != (K // 2 if lay == CODES_PACKED else K):
         raise ValueError("xq and wq disagree on K")
     if want_y and y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
@@ -169,7 +178,7 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     wst = _dt(w_scale) if w_scale is not None else F32
     _check("qgemm_w4a4", lib().w4a4_qgemm_w4a4(
-        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), wst, w_group, M, N, K,
+        _ptr(xq), lay, _ptr(x_scale), _ptr(wq), _ptr(w_scale), wst, w_group, M, N, K,
         _ptr(y), _ptr(acc), _stream(xq)))
     return y, acc
 
@@ -179,16 +188,23 @@ def qlinear_workspace_size(M: int, N: int, K: int, rank: int) -> int:
 
 
 def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, had_block: int,
-                    w_group: int, A: Optional[torch.Tensor] = None, B: Optional[torch.Tensor] = None,
-                    y: Optional[torch.Tensor] = None,
+                    w_group: int, At: Optional[torch.Tensor] = None,
+                    Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = dequant(int4 GEMM(rotate+quantize(x), wq)) + x . A . B, with the
+    low-rank factors given transposed: At [rank, K], Bt [N, rank]."""
     _dev(x, "x")
     _dev(wq, "wq")
     M, K = x.shape
     N = wq.shape[0]
-    rank = 0 if A is None else A.shape[1]
-    if rank and (B is None or A.dtype != x.dtype or B.dtype != x.dtype):
-        raise ValueError("A and B must both be given in x's dtype")
+    rank = 0 if At is None else At.shape[0]
+    if rank:
+        if Bt is None or At.dtype != x.dtype or Bt.dtype != x.dtype:
+            raise ValueError("At and Bt must both be given in x's dtype")
+        if tuple(At.shape) != (rank, K) or tuple(Bt.shape) != (N, rank):
+            raise ValueError("At must be [rank, K] and Bt [N, rank]")
+        _dev(At, "At")
+        _dev(Bt, "Bt")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
     need = qlinear_workspace_size(M, N, K, rank)
@@ -196,5 +212,5 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check("qlinear_forward", lib().w4a4_qlinear_forward(
         _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
-        _ptr(A), _ptr(B), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
+        _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
     return y

@@ -58,14 +58,25 @@ typedef enum {
                                K not positive, rank > 0 without A or B */
   W4A4_ERR_UNSUPPORTED = 2, /* shape outside the kernels' domain (K not a
                                multiple of 64 or above 16384, bad Hadamard
-                               block or weight group, rank above 256), or a
-                               device that is not gfx950 / no device */
+                               block or weight group, rank above 256 or an
+                               fp16 rank not a multiple of 8), or a device
+                               that is not gfx950 / no device */
   W4A4_ERR_MISALIGNED = 3,  /* a pointer not aligned to 16 bytes */
   W4A4_ERR_WORKSPACE = 4,   /* workspace smaller than required */
   W4A4_ERR_HIP = 5          /* a HIP runtime error while launching */
 } w4a4_status;
 
 typedef enum { W4A4_F32 = 0, W4A4_F16 = 1 } w4a4_dtype;
+
+/* Layouts of activation codes.
+ *   W4A4_CODES_PACKED: [M, K/2] uint8, two nibbles per byte (see Packing).
+ *   W4A4_CODES_I8:     [M, K] int8, one code per byte; inside every group of
+ *                      8 consecutive channels the bytes hold channels
+ *                      0,2,4,6,1,3,5,7 of the group.  This is the K order in
+ *                      which the GEMM widens packed weight nibbles, so these
+ *                      codes feed the int8 matrix instructions unchanged; it
+ *                      is the layout w4a4_qlinear_forward uses internally. */
+typedef enum { W4A4_CODES_PACKED = 0, W4A4_CODES_I8 = 1 } w4a4_codes_layout;
 
 /* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
 int w4a4_abi_version(void);
@@ -95,12 +106,12 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot,
  *   x        [M, K] in dtype x_dtype.
  *   had_block 0/1: x is already rotated (codes then follow the quantizer rule
  *            exactly); otherwise the rotation above is applied first.
- *   xq       [M, K/2] uint8 output, packed codes.
+ *   xq       output codes in codes_layout ([M, K/2] packed or [M, K] int8).
  *   x_scale  [M] float32 output, one scale per row.
  */
 int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
-                           int64_t had_block, uint8_t* xq, float* x_scale,
-                           void* stream);
+                           int64_t had_block, uint8_t* xq, int codes_layout,
+                           float* x_scale, void* stream);
 
 /*
  * Offline weight preparation: rotation (had_block > 1) and symmetric
@@ -119,16 +130,18 @@ int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K,
 
 /*
  * First half of the low-rank term (SERQ page, "Resumen técnico" §2 item 2):
- *   t [M, rank] float32 = x [M, K] . A [K, rank], with x and A in dtype
- *   x_dtype, float32 accumulation.  1 <= rank <= 256.
+ *   t [M, rank] float32 = x [M, K] . A, with A passed transposed as
+ *   At [rank, K] (row j of At is column j of A, so that it is contiguous
+ *   along K like the weights).  x and At in dtype x_dtype; float32
+ *   accumulation (fp16 matrix instructions for fp16 inputs).  1 <= rank <= 256.
  */
-int w4a4_lowrank_project(const void* x, int x_dtype, const void* A, int64_t M,
+int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M,
                          int64_t K, int64_t rank, float* t, void* stream);
 
 /*
  * int4 x int4 GEMM with the dequantizing epilogue (SERQ page, "Resumen
  * técnico" §3: 4-bit matrix multiplication in the linear layer).
- *   xq [M, K/2], x_scale [M] float32: activation codes and scales.
+ *   xq in codes_layout, x_scale [M] float32: activation codes and scales.
  *   wq [N, K/2], w_scale [N] (w_group 0) or [N, K/w_group] in w_scale_dtype.
  *   w_group 0 or a multiple of 64 dividing K.
  *   y   [M, N] float32 output, or NULL:
@@ -138,10 +151,10 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* A, int64_t M,
  *       sum_k qx[m,k] * qw[n,k].
  *   At least one of y and acc must be non-NULL.
  */
-int w4a4_qgemm_w4a4(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
-                    const void* w_scale, int w_scale_dtype, int64_t w_group,
-                    int64_t M, int64_t N, int64_t K, float* y, int32_t* acc,
-                    void* stream);
+int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale,
+                    const uint8_t* wq, const void* w_scale, int w_scale_dtype,
+                    int64_t w_group, int64_t M, int64_t N, int64_t K, float* y,
+                    int32_t* acc, void* stream);
 
 /* Bytes of workspace qlinear_forward needs for these sizes (0 if M or N is
  * 0). */
@@ -149,9 +162,15 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
 
 /*
  * The whole layer: rotate + quantize X, int4 GEMM, dequant, + X.A.B.
- *   x [M, K] in x_dtype; A [K, rank] and B [rank, N] in x_dtype (or NULL when
- *   rank is 0); wq / w_scale as prepared by w4a4_quantize_weight_int4 with
- *   the same had_block and w_group.  y [M, N] float32 output.
+ *   x [M, K] in x_dtype; wq / w_scale as prepared by
+ *   w4a4_quantize_weight_int4 with the same had_block and w_group.
+ *   The rank-r factors are passed transposed so that both are contiguous
+ *   along their contraction: At [rank, K] (At[j, k] = A[k, j]) and
+ *   Bt [N, rank] (Bt[n, j] = B[j, n]), in x_dtype, or NULL when rank is 0.
+ *   With fp16 inputs rank must be a multiple of 8; T = X.A is kept as an
+ *   fp16 pair (hi + lo, about 22 significant bits) for the fp16 matrix
+ *   instructions of the epilogue.
+ *   y [M, N] float32 output.
  *   workspace: device scratch of at least w4a4_qlinear_workspace_size bytes,
  *   used for the activation codes, scales and X.A; its contents on entry do
  *   not matter.
@@ -159,7 +178,7 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
 int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          const void* w_scale, int w_scale_dtype, int64_t M,
                          int64_t N, int64_t K, int64_t had_block,
-                         int64_t w_group, const void* A, const void* B,
+                         int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace,
                          size_t ws_bytes, void* stream);
 

@@ -39,19 +39,21 @@ def test_version_and_status_strings(lib):
 
 def test_quantize_act_argument_errors(lib):
     f = lib.w4a4_quantize_act_int4
-    assert f(P, 7, 4, 256, 0, P, P, None) == W.ERR_INVALID_ARG          # dtype
-    assert f(P, W.F16, -1, 256, 0, P, P, None) == W.ERR_INVALID_ARG     # M < 0
-    assert f(P, W.F16, 4, 0, 0, P, P, None) == W.ERR_INVALID_ARG        # K = 0
-    assert f(None, W.F16, 4, 256, 0, P, P, None) == W.ERR_INVALID_ARG   # null x
-    assert f(P, W.F16, 4, 256, 0, None, P, None) == W.ERR_INVALID_ARG   # null xq
-    assert f(P, W.F16, 4, 100, 0, P, P, None) == W.ERR_UNSUPPORTED      # K % 64
-    assert f(P, W.F16, 4, 32768, 0, P, P, None) == W.ERR_UNSUPPORTED    # K too big
-    assert f(P, W.F16, 4, 256, 3, P, P, None) == W.ERR_UNSUPPORTED      # b not pow2
-    assert f(P, W.F16, 4, 8192, 8192, P, P, None) == W.ERR_UNSUPPORTED  # b > 4096
-    assert f(P, W.F16, 4, 192, 128, P, P, None) == W.ERR_UNSUPPORTED    # b does not divide K
-    assert f(Q, W.F16, 4, 256, 0, P, P, None) == W.ERR_MISALIGNED
-    assert f(P, W.F16, 4, 256, 0, P, Q, None) == W.ERR_MISALIGNED
-    assert f(None, W.F16, 0, 256, 64, None, None, None) == W.OK         # empty: no-op
+    L = W.CODES_PACKED
+    assert f(P, 7, 4, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG          # dtype
+    assert f(P, W.F16, 4, 256, 0, P, 5, P, None) == W.ERR_INVALID_ARG      # layout
+    assert f(P, W.F16, -1, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG     # M < 0
+    assert f(P, W.F16, 4, 0, 0, P, L, P, None) == W.ERR_INVALID_ARG        # K = 0
+    assert f(None, W.F16, 4, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG   # null x
+    assert f(P, W.F16, 4, 256, 0, None, L, P, None) == W.ERR_INVALID_ARG   # null xq
+    assert f(P, W.F16, 4, 100, 0, P, L, P, None) == W.ERR_UNSUPPORTED      # K % 64
+    assert f(P, W.F16, 4, 32768, 0, P, L, P, None) == W.ERR_UNSUPPORTED    # K too big
+    assert f(P, W.F16, 4, 256, 3, P, L, P, None) == W.ERR_UNSUPPORTED      # b not pow2
+    assert f(P, W.F16, 4, 8192, 8192, P, L, P, None) == W.ERR_UNSUPPORTED  # b > 4096
+    assert f(P, W.F16, 4, 192, 128, P, L, P, None) == W.ERR_UNSUPPORTED    # b does not divide K
+    assert f(Q, W.F16, 4, 256, 0, P, L, P, None) == W.ERR_MISALIGNED
+    assert f(P, W.F16, 4, 256, 0, P, L, Q, None) == W.ERR_MISALIGNED
+    assert f(None, W.F16, 0, 256, 64, None, L, None, None) == W.OK         # empty: no-op
 
 
 def test_rotate_and_weight_argument_errors(lib):
@@ -71,12 +73,14 @@ def test_rotate_and_weight_argument_errors(lib):
 
 def test_gemm_and_lowrank_argument_errors(lib):
     g = lib.w4a4_qgemm_w4a4
-    assert g(P, P, P, P, W.F16, 0, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
-    assert g(P, None, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
-    assert g(P, P, P, P, W.F16, 96, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
-    assert g(P, P, P, P, W.F16, 0, 4, 8, 200, P, None, None) == W.ERR_UNSUPPORTED
-    assert g(P, P, Q, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
-    assert g(None, None, None, None, W.F16, 0, 4, 0, 256, None, None, None) == W.OK
+    L = W.CODES_I8
+    assert g(P, L, P, P, P, W.F16, 0, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
+    assert g(P, 9, P, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG    # layout
+    assert g(P, L, None, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
+    assert g(P, L, P, P, P, W.F16, 96, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, L, P, P, P, W.F16, 0, 4, 8, 200, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, L, P, Q, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
+    assert g(None, L, None, None, None, W.F16, 0, 4, 0, 256, None, None, None) == W.OK
     lr = lib.w4a4_lowrank_project
     assert lr(P, W.F16, P, 4, 256, 0, P, None) == W.ERR_INVALID_ARG
     assert lr(P, W.F16, P, 4, 256, 257, P, None) == W.ERR_UNSUPPORTED
@@ -108,4 +112,5 @@ def test_valid_call_without_device_reports_unsupported(lib):
     need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
     assert lib.w4a4_qlinear_forward(P, W.F16, P, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P,
                                     need, None) == W.ERR_UNSUPPORTED
-    assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, P, None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P,
+                                      None) == W.ERR_UNSUPPORTED

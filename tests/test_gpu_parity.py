@@ -38,6 +38,23 @@ def np_dtype(name):
     return np.float16 if name == "float16" else np.float32
 
 
+def i8_from_codes(q):
+    """Codes [M, K] -> the W4A4_CODES_I8 byte layout: inside every group of 8
+    channels, channels 0,2,4,6 then 1,3,5,7 (the documented order)."""
+    M, K = q.shape
+    g = q.reshape(M, K // 8, 8)
+    return np.concatenate([g[:, :, 0::2], g[:, :, 1::2]], axis=2).reshape(M, K).astype(np.int8)
+
+
+def codes_from_i8(b):
+    M, K = b.shape
+    g = b.view(np.int8).reshape(M, K // 8, 8)
+    out = np.empty_like(g)
+    out[:, :, 0::2] = g[:, :, :4]
+    out[:, :, 1::2] = g[:, :, 4:]
+    return out.reshape(M, K)
+
+
 def rotation_bound(x, b):
     ref = O.rotate64(x, b)
     M, K = ref.shape
@@ -76,6 +93,19 @@ def test_quantize_act_exact_on_oracle_rotation(M, K, b, dt):
     pq, ps, _, _ = O.quantize_activation(xr, 0)
     assert np.array_equal(host(sx), ps)
     assert np.array_equal(host(xq), pq)
+
+
+@pytest.mark.parametrize("M,K,b,dt", [(37, 4096, 4096, "float16"), (20, 14336, 128, "float16"),
+                                      (3, 192, 64, "float32"), (1, 64, 2, "float16")])
+def test_quantize_act_i8_layout_exact(M, K, b, dt):
+    w = synth.small("q8", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xr = O.rotate(X, b)
+    xq, sx = W.quantize_act_int4(dev(xr), 0, layout="i8")
+    _, ps, pc, _ = O.quantize_activation(xr, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(codes_from_i8(host(xq)), pc)
+    assert np.array_equal(host(xq).view(np.int8), i8_from_codes(pc))
 
 
 def test_quantize_act_exact_unrotated_fp16_and_edge_rows():
@@ -162,7 +192,9 @@ def test_quantize_act_fused_rotation(M, K, b, dt):
 # Integer GEMM
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,K", [(1, 1, 64), (7, 33, 192), (130, 260, 384), (16, 256, 256),
-                                   (257, 129, 4096), (64, 64, 14336)])
+                                   (257, 129, 4096), (64, 64, 14336), (8, 4096, 4096),
+                                   (17, 300, 14336), (32, 64, 192), (1000, 6500, 256),
+                                   (2048, 4096, 256)])
 def test_qgemm_int32_exact(M, N, K):
     rng = np.random.default_rng(M * N + K)
     qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
@@ -174,18 +206,36 @@ def test_qgemm_int32_exact(M, N, K):
     assert np.array_equal(host(acc), O.int_gemm(qx, qw))
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (7, 33, 192), (130, 260, 384), (16, 4096, 4096),
+                                   (32, 64, 192), (300, 129, 320), (1000, 6500, 256),
+                                   (2048, 4096, 4096)])
+def test_qgemm_i8_codes_int32_exact(M, N, K):
+    rng = np.random.default_rng(M * N + K + 1)
+    qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    qx[0, :] = -8
+    qw[0, :] = -8
+    _, acc = W.qgemm_w4a4(dev(i8_from_codes(qx).view(np.uint8)), None, dev(O.pack_int4(qw)), None, 0,
+                          want_y=False, want_acc=True, layout="i8")
+    assert np.array_equal(host(acc), O.int_gemm(qx, qw))
+
+
 @pytest.mark.parametrize("M,N,K,g,sd", [(33, 70, 256, 0, "float32"), (128, 256, 4096, 0, "float16"),
                                         (40, 96, 1024, 128, "float16"), (17, 50, 384, 64, "float32"),
-                                        (64, 128, 14336, 128, "float16")])
-def test_qgemm_dequant(M, N, K, g, sd):
+                                        (64, 128, 14336, 128, "float16"), (8, 4096, 4096, 0, "float16"),
+                                        (16, 200, 14336, 128, "float16"), (24, 100, 512, 256, "float32"),
+                                        (1000, 6500, 256, 128, "float16"), (5, 40, 1024, 64, "float16")])
+@pytest.mark.parametrize("layout", ["packed", "i8"])
+def test_qgemm_dequant(M, N, K, g, sd, layout):
     rng = np.random.default_rng(M + N + K + g)
     qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
     qw = rng.integers(-7, 8, (N, K)).astype(np.int8)
     sx = rng.uniform(0.01, 2.0, M).astype(np.float32)
     shape = (N,) if g == 0 else (N, K // g)
     sw = rng.uniform(1e-3, 0.05, shape).astype(np_dtype(sd))
-    y, acc = W.qgemm_w4a4(dev(O.pack_int4(qx)), dev(sx), dev(O.pack_int4(qw)), dev(sw), g,
-                          want_y=True, want_acc=True)
+    xin = O.pack_int4(qx) if layout == "packed" else i8_from_codes(qx).view(np.uint8)
+    y, acc = W.qgemm_w4a4(dev(xin), dev(sx), dev(O.pack_int4(qw)), dev(sw), g,
+                          want_y=True, want_acc=True, layout=layout)
     assert np.array_equal(host(acc), O.int_gemm(qx, qw))
     accs = O.int_gemm(qx, qw) if g == 0 else O.int_gemm_groups(qx, qw, g)
     ref = O.epilogue(accs, sx, sw.astype(np.float32), None).astype(np.float64)
@@ -203,7 +253,7 @@ def test_qgemm_dequant(M, N, K, g, sd):
 def test_lowrank_project(M, K, r, dt):
     w = synth.small("l", M, K, 8, x_dtype=dt, rank=r)
     d = synth.make_inputs(w)
-    t = host(W.lowrank_project(dev(d["X"]), dev(d["A"])))
+    t = host(W.lowrank_project(dev(d["X"]), dev(d["A"].T)))
     X64, A64 = d["X"].astype(np.float64), d["A"].astype(np.float64)
     ref = X64 @ A64
     bound = K * 2.0 ** -23 * (np.abs(X64) @ np.abs(A64))
@@ -219,8 +269,8 @@ def run_layer(w, rows=None):
     X, Wt, A, B = d["X"], d["W"], d["A"], d["B"]
     wq, ws, _ = O.prepare_weight(Wt, w.had_block, w.w_group, w.w_scale_dtype)
     Xd, wqd, wsd = dev(X), dev(wq), dev(ws)
-    Ad = dev(A) if A is not None else None
-    Bd = dev(B) if B is not None else None
+    Ad = dev(A.T) if A is not None else None   # the ABI takes At [r, K], Bt [N, r]
+    Bd = dev(B.T) if B is not None else None
     y = host(W.qlinear_forward(Xd, wqd, wsd, w.had_block, w.w_group, Ad, Bd))
     gxq, gsx = W.quantize_act_int4(Xd, w.had_block)
     gxq, gsx = host(gxq), host(gsx)
@@ -260,7 +310,10 @@ def test_qlinear_prefill_full_size():
 @pytest.mark.parametrize("M,K,N,b,g,r,dt", [
     (1, 256, 64, 256, 0, 0, "float16"), (7, 192, 33, 64, 64, 4, "float32"),
     (130, 1024, 260, 128, 128, 16, "float16"), (33, 4096, 100, 4096, 0, 64, "float16"),
-    (65, 14336, 96, 128, 128, 32, "float16"), (16, 512, 48, 1, 0, 8, "float16")])
+    (65, 14336, 96, 128, 128, 32, "float16"), (16, 512, 48, 1, 0, 8, "float16"),
+    (20, 4096, 520, 128, 128, 24, "float16"), (300, 1024, 1030, 256, 0, 40, "float16"),
+    (520, 4096, 700, 4096, 0, 8, "float16"), (9, 384, 50, 128, 0, 256, "float16"),
+    (300, 320, 200, 64, 64, 8, "float16"), (40, 192, 100, 64, 0, 0, "float32")])
 def test_qlinear_ragged_shapes(M, K, N, b, g, r, dt):
     w = synth.small("rag", M, K, N, x_dtype=dt, had_block=b, w_group=g, rank=r,
                     w_scale_dtype="float16" if dt == "float16" else "float32")
