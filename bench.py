@@ -49,8 +49,9 @@ def log(*a):
 class Layer:
     """Device-resident inputs of one workload with weights quantized on GPU."""
 
-    def __init__(self, wl: synth.Workload, copies: int = 1):
+    def __init__(self, wl: synth.Workload, copies: int = 1, w_layout: str = "tiled"):
         self.wl = wl
+        self.w_layout = w_layout
         d = synth.make_inputs(wl)
         dev = "cuda:0"
         self.x = torch.from_numpy(d["X"]).to(dev)
@@ -59,7 +60,7 @@ class Layer:
         self.B = torch.from_numpy(d["B"].T.copy()).to(dev) if d["B"] is not None else None
         Wd = torch.from_numpy(d["W"]).to(dev)
         sdt = torch.float16 if wl.w_scale_dtype == "float16" else torch.float32
-        wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt)
+        wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt, layout=w_layout)
         del Wd
         # Distinct copies of the weights (and low-rank factors) so a decode
         # loop streams them from HBM rather than from the last-level cache.
@@ -76,7 +77,7 @@ class Layer:
     def forward(self, i: int = 0):
         wq, ws, A, B = self.sets[i % len(self.sets)]
         W.qlinear_forward(self.x, wq, ws, self.wl.had_block, self.wl.w_group, A, B,
-                          y=self.y, workspace=self.ws)
+                          y=self.y, workspace=self.ws, w_layout=self.w_layout)
 
     def algorithmic_bytes(self) -> int:
         wl = self.wl
@@ -135,23 +136,26 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     """Average duration of each kernel of the path, launched alone with the
     same arguments and code layout as inside qlinear_forward."""
     wl = layer.wl
-    xq = torch.empty((wl.M, wl.K), dtype=torch.uint8, device="cuda:0")
+    tiled = layer.w_layout == "tiled"
+    lay = "i8_tiled" if tiled else "i8"
+    xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K), dtype=torch.uint8, device="cuda:0")
     sx = torch.empty((wl.M,), dtype=torch.float32, device="cuda:0")
-    W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout="i8")
+    W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay)
     torch.cuda.synchronize()
     out = {}
     out["rotq"] = time_eager(
-        lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout="i8"), steps, warmup)
+        lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay), steps, warmup)
     out["qgemm"] = time_eager(
         lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
                                layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
-                               layout="i8"),
+                               layout=lay, w_layout=layer.w_layout),
         steps, warmup)
     return out
 
 
-def cpu_baseline(wl: synth.Workload, rows: int) -> dict:
-    """The float64 oracle on the first `rows` rows of the workload."""
+def cpu_baseline(wl: synth.Workload, seconds: float) -> dict:
+    """The float64 oracle on the whole workload, repeated until `seconds` of
+    CPU time have passed (at least once)."""
     from oracle import w4a4_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -159,16 +163,22 @@ def cpu_baseline(wl: synth.Workload, rows: int) -> dict:
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     d = synth.make_inputs(wl)
-    X = d["X"][:rows]
+    X = d["X"]
     wq, ws, _ = O.prepare_weight(d["W"], wl.had_block, wl.w_group, wl.w_scale_dtype)
     A, B = d["A"], d["B"]
     O.qlinear_forward(X[:8], wq, ws, wl.had_block, wl.w_group, A, B)  # warm caches
+    calls = 0
     t0 = time.perf_counter()
-    O.qlinear_forward(X, wq, ws, wl.had_block, wl.w_group, A, B)
-    t = time.perf_counter() - t0
-    return {"value": 2 * rows * wl.N * wl.K / t / 1e12, "unit": "TOP/s", "cores": int(threads),
-            "kind": "oracle", "seconds": t,
-            "sample": f"first {rows} of {wl.M} rows of {wl.name} (weights prepared untimed)"}
+    while True:
+        O.qlinear_forward(X, wq, ws, wl.had_block, wl.w_group, A, B)
+        calls += 1
+        t = time.perf_counter() - t0
+        if t >= seconds:
+            break
+    return {"value": calls * 2 * wl.M * wl.N * wl.K / t / 1e12, "unit": "TOP/s",
+            "cores": int(threads), "kind": "oracle", "seconds": t,
+            "sample": f"{calls} oracle calls on the whole {wl.M}-row {wl.name} workload "
+                      f"(weights prepared untimed)"}
 
 
 def main() -> int:
@@ -176,7 +186,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--w-layout", choices=["tiled", "rowmajor"], default="tiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     args = ap.parse_args()
@@ -190,7 +201,7 @@ def main() -> int:
     W.lib()
 
     # ---- prefill: the headline ------------------------------------------------
-    pre = Layer(synth.PREFILL)
+    pre = Layer(synth.PREFILL, w_layout=args.w_layout)
     log(f"prefill: {pre.wl.name} timing {args.steps} steps")
     t_step = time_graph(pre.forward, args.steps, args.warmup)
     kt = kernel_times(pre, args.steps, args.warmup)
@@ -207,7 +218,7 @@ def main() -> int:
         probe = synth.DECODE
         per_set = probe.N * probe.K // 2 + probe.N * 2 + 2 * (probe.K + probe.N) * probe.rank * 2
         copies = int(np.ceil(3 * LLC_BYTES / per_set))
-        dec = Layer(probe, copies=copies)
+        dec = Layer(probe, copies=copies, w_layout=args.w_layout)
         log(f"decode: {dec.wl.name} with {copies} weight copies, timing {args.steps} steps")
         t_dec = time_graph(dec.forward, args.steps, args.warmup)
         kd = kernel_times(dec, args.steps, args.warmup)
@@ -226,8 +237,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
-        cpu = cpu_baseline(synth.PREFILL, args.cpu_rows)
+        log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(synth.PREFILL, args.cpu_seconds)
 
     out = {
         "metric": "W4A4 qlinear TOPS (M=2048), K=N=4096",
@@ -244,7 +255,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": pre.wl.name, "M": pre.wl.M, "N": pre.wl.N, "K": pre.wl.K,
                    "had_block": pre.wl.had_block, "w_group": pre.wl.w_group,
-                   "rank": pre.wl.rank, "x_dtype": pre.wl.x_dtype},
+                   "rank": pre.wl.rank, "x_dtype": pre.wl.x_dtype,
+                   "w_layout": args.w_layout},
         "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
         "roofline": {"bound": "mfma", "kernel": "qgemm_kernel", "achieved": gemm_tops,
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,

@@ -94,13 +94,17 @@ struct WsLayout {
 WsLayout ws_layout(int64_t M, int64_t K, int64_t rank) {
   WsLayout w;
   w.xq = 0;
-  w.sx = align256(static_cast<size_t>(M) * static_cast<size_t>(K));  // int8 codes
+  // int8 codes, rows padded to a multiple of 16 for the tiled layout
+  w.sx = align256(static_cast<size_t>((M + 15) / 16 * 16) * static_cast<size_t>(K));
   w.t = w.sx + align256(static_cast<size_t>(M) * 4);
   w.total = w.t + align256(static_cast<size_t>(M) * static_cast<size_t>(rank) * 4);
   return w;
 }
 
-bool layout_ok(int l) { return l == W4A4_CODES_PACKED || l == W4A4_CODES_I8; }
+bool layout_ok(int l) {
+  return l == W4A4_CODES_PACKED || l == W4A4_CODES_I8 || l == W4A4_CODES_I8_TILED;
+}
+bool wlayout_ok(int l) { return l == W4A4_WEIGHTS_ROWMAJOR || l == W4A4_WEIGHTS_TILED; }
 
 }  // namespace
 
@@ -145,6 +149,7 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   if (!dtype_ok(x_dtype) || !layout_ok(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
+  if (codes_layout == W4A4_CODES_I8_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if (M == 0) return W4A4_OK;
   if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
@@ -153,18 +158,22 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   w4a4::RotqPlan plan;
   if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  const int mode = codes_layout == W4A4_CODES_I8 ? w4a4::ROTQ_QUANT_I8 : w4a4::ROTQ_QUANT;
+  const int mode = codes_layout == W4A4_CODES_I8         ? w4a4::ROTQ_QUANT_I8
+                   : codes_layout == W4A4_CODES_I8_TILED ? w4a4::ROTQ_QUANT_I8_TILED
+                                                         : w4a4::ROTQ_QUANT;
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, mode, K, false, nullptr, xq,
                                    x_scale, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
 int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, int64_t had_block,
-                              int64_t w_group, uint8_t* wq, void* w_scale, int scale_dtype,
-                              void* stream) {
-  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || N < 0) return W4A4_ERR_INVALID_ARG;
+                              int64_t w_group, uint8_t* wq, int w_layout, void* w_scale,
+                              int scale_dtype, void* stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || !wlayout_ok(w_layout) || N < 0)
+    return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
+  if (w_layout == W4A4_WEIGHTS_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if ((s = check_group(K, w_group, true)) != W4A4_OK) return s;
   if (N == 0) return W4A4_OK;
   if (!w || !wq || !w_scale) return W4A4_ERR_INVALID_ARG;
@@ -175,7 +184,8 @@ int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, 
   w4a4::RotqPlan plan;
   if ((s = plan_rotq(K, had_block, gsz, max_lds, &plan)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, w4a4::ROTQ_QUANT, gsz,
+  const int mode = w_layout == W4A4_WEIGHTS_TILED ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT;
+  hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, mode, gsz,
                                    scale_dtype == W4A4_F16, nullptr, wq, w_scale, plan,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
@@ -197,13 +207,17 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M, 
 }
 
 int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, const uint8_t* wq,
-                    const void* w_scale, int w_scale_dtype, int64_t w_group, int64_t M, int64_t N,
-                    int64_t K, float* y, int32_t* acc, void* stream) {
-  if (!dtype_ok(w_scale_dtype) || !layout_ok(codes_layout) || M < 0 || N < 0 || K <= 0)
+                    int w_layout, const void* w_scale, int w_scale_dtype, int64_t w_group,
+                    int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, void* stream) {
+  if (!dtype_ok(w_scale_dtype) || !layout_ok(codes_layout) || !wlayout_ok(w_layout) || M < 0 ||
+      N < 0 || K <= 0)
     return W4A4_ERR_INVALID_ARG;
   if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
   int s = check_group(K, w_group, false);
   if (s != W4A4_OK) return s;
+  const bool tiled = w_layout == W4A4_WEIGHTS_TILED;
+  if (tiled != (codes_layout == W4A4_CODES_I8_TILED)) return W4A4_ERR_INVALID_ARG;
+  if (tiled && (K % 128 != 0 || w_group % 128 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
   if (y && (!x_scale || !w_scale)) return W4A4_ERR_INVALID_ARG;
@@ -218,7 +232,8 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, c
   g.M = M; g.N = N; g.K = K;
   g.y = y; g.acc = acc;
   g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
-  g.a_i8 = codes_layout == W4A4_CODES_I8;
+  g.a_i8 = codes_layout != W4A4_CODES_PACKED;
+  g.tiled = tiled;
   hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
@@ -228,15 +243,18 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
   return ws_layout(M, K, rank).total;
 }
 
-int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const void* w_scale,
-                         int w_scale_dtype, int64_t M, int64_t N, int64_t K, int64_t had_block,
-                         int64_t w_group, const void* At, const void* Bt, int64_t rank, float* y,
-                         void* workspace, size_t ws_bytes, void* stream) {
-  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || M < 0 || N < 0 || rank < 0)
+int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+                         const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
+                         int64_t had_block, int64_t w_group, const void* At, const void* Bt,
+                         int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok(w_layout) || M < 0 || N < 0 ||
+      rank < 0)
     return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if ((s = check_group(K, w_group, false)) != W4A4_OK) return s;
+  const bool tiled = w_layout == W4A4_WEIGHTS_TILED;
+  if (tiled && (K % 128 != 0 || w_group % 128 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (rank > kMaxRank || (x_dtype == W4A4_F16 && rank % 8 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!x || !wq || !w_scale || !y || !workspace) return W4A4_ERR_INVALID_ARG;
@@ -259,8 +277,9 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const vo
   const bool f16 = x_dtype == W4A4_F16;
 
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b, w4a4::ROTQ_QUANT_I8, K, false, nullptr, xq,
-                                   sx, plan, st);
+  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b,
+                                   tiled ? w4a4::ROTQ_QUANT_I8_TILED : w4a4::ROTQ_QUANT_I8, K, false,
+                                   nullptr, xq, sx, plan, st);
   if (e != hipSuccess) return hip_fail(e);
   if (rank > 0) {
     e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
@@ -277,6 +296,7 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, const vo
   g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
   g.rank = static_cast<int>(rank);
   g.a_i8 = 1;
+  g.tiled = tiled;
   e = w4a4::launch_qgemm(g, st);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }

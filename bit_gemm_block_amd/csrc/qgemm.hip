@@ -432,7 +432,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE>
+template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   constexpr int WM = TM * 16, WN = TN * 16;
   constexpr int BM = 2 * WM, BN = 2 * WN;
@@ -479,46 +479,52 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   const int64_t K = a.K;
   const int nkt = static_cast<int>(K / 128);
 
-  // Source pointer (at iteration 0) and LDS offset of each run this wave copies.
+  // Source pointer (at iteration 0) and LDS offset of each run this wave
+  // copies.  Row-major operands: a run is 16 rows x 64 bytes.  Tiled
+  // operands: a run is one contiguous 1 KB block already in fragment order.
   const uint8_t* src[RUNS_PER_WAVE];
   int dst[RUNS_PER_WAVE];
   int step[RUNS_PER_WAVE];
+  const int64_t mblocks = (a.M + 15) / 16, nblocks = (a.N + 15) / 16;
 #pragma unroll
   for (int q = 0; q < RUNS_PER_WAVE; ++q) {
     const int run = wave + 4 * q;
     const int g = lane >> 4, rr = lane & 15;
     if (run < A_RUNS) {
       const int blk = run >> 1, h = run & 1;
-      int64_t m = m0 + blk * 16 + rr;
-      m = m < a.M ? m : a.M - 1;
-      src[q] = a.xq + m * K + 32 * g + 16 * h;
+      if constexpr (TILED) {
+        int64_t mb = m0 / 16 + blk;
+        mb = mb < mblocks ? mb : mblocks - 1;
+        src[q] = a.xq + (mb * nkt * 2 + h) * 1024 + 16 * lane;
+        step[q] = 2048;
+      } else {
+        int64_t m = m0 + blk * 16 + rr;
+        m = m < a.M ? m : a.M - 1;
+        src[q] = a.xq + m * K + 32 * g + 16 * h;
+        step[q] = 128;
+      }
       dst[q] = ((blk * 2 + h) * 4) << 8;
-      step[q] = 128;
     } else {
       const int blk = run - A_RUNS;
-      int64_t n = n0 + blk * 16 + rr;
-      n = n < a.N ? n : a.N - 1;
-      src[q] = a.wq + n * (K / 2) + 16 * g;
+      if constexpr (TILED) {
+        int64_t nb = n0 / 16 + blk;
+        nb = nb < nblocks ? nb : nblocks - 1;
+        src[q] = a.wq + nb * nkt * 1024 + 16 * lane;
+        step[q] = 1024;
+      } else {
+        int64_t n = n0 + blk * 16 + rr;
+        n = n < a.N ? n : a.N - 1;
+        src[q] = a.wq + n * (K / 2) + 16 * g;
+        step[q] = 64;
+      }
       dst[q] = A_BYTES + ((blk * 4) << 8);
-      step[q] = 64;
     }
   }
-  // Workgroups that share an A or B panel start at different K positions,
-  // so that a panel slice is fetched from memory by one of them and found in
-  // L2 by the others instead of all of them waiting on the same miss.
-  const int iters_per_group0 = GROUPED ? a.group / 128 : 1;
-  int k_rot = 0;
-  if (nkt >= 8) {
-    const int span = ((nkt / 8) / iters_per_group0) * iters_per_group0;
-    k_rot = static_cast<int>((tmi + tni) & 7) * span;
-  }
-  auto kpos = [&](int kt) { const int k = kt + k_rot; return k >= nkt ? k - nkt : k; };
   auto issue = [&](int kt, uint8_t* base) {
     const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
-    const int64_t kp = kpos(kt);
 #pragma unroll
     for (int q = 0; q < RUNS_PER_WAVE; ++q)
-      dma16(src[q] + kp * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
+      dma16(src[q] + static_cast<int64_t>(kt) * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
   };
 
   i32x4 acc[TM][TN];
@@ -580,9 +586,8 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
               acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][i], opb[j], acc[i][j], 0, 0, 0);
         }
         if constexpr (GROUPED) {
-          const int kp = kpos(kt);
-          if ((kp + 1) % iters_per_group == 0) {
-            const int64_t grp = (kp + 1) / iters_per_group - 1;
+          if ((kt + 1) % iters_per_group == 0) {
+            const int64_t grp = (kt + 1) / iters_per_group - 1;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
               int64_t n = n0 + wn0 + j * 16 + frow;
@@ -661,8 +666,9 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 // bytes [64t + 16g, 64t + 16g + 16) of its weight row (g = lane >> 4) and of
 // its activation rows; K step 0 of the pair uses the first 8 bytes and K
 // step 1 the last 8, identically on both sides.
-template <int MB, int KW, bool GROUPED, int LRMODE, bool AI8>
+template <int MB, int KW, bool GROUPED, int LRMODE, bool AI8, bool TILED>
 __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
+  static_assert(!TILED || AI8, "tiled weights pair with tiled int8 codes");
   constexpr int CH = 8;  // K pairs loaded per batch
   __shared__ i32x4 ired[KW][MB][64];
   __shared__ f32x4 fred[GROUPED ? KW : 1][GROUPED ? MB : 1][64];
@@ -701,21 +707,35 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int64_t p = p0 + c;
-      const int64_t kb = p * 64 + g * 16;
-      const bool ok = p < p_end && kb < row_bytes;
-      wv[c] = (ok && n_ok) ? *reinterpret_cast<const uint4*>(a.wq + nrow * row_bytes + kb)
-                           : make_uint4(0, 0, 0, 0);
+      if constexpr (TILED) {
+        // One contiguous 1 KB block per (16-row block, K pair) and wave.
+        const bool ok = p < p_end;
+        wv[c] = ok ? *reinterpret_cast<const uint4*>(a.wq + (n0 / 16 * npairs + p) * 1024 + 16 * lane)
+                   : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const int64_t m = b * 16 + (lane & 15);
-        const bool xok = ok && m < a.M;
-        if constexpr (AI8) {
-          const uint8_t* xp = a.xq + m * a.K + 2 * kb;  // int8 codes [2kb, 2kb + 32)
-          xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
-          xv[c][b][1] = xok ? *reinterpret_cast<const uint4*>(xp + 16) : make_uint4(0, 0, 0, 0);
-        } else {
-          xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(a.xq + m * row_bytes + kb)
-                            : make_uint4(0, 0, 0, 0);
+        for (int b = 0; b < MB; ++b) {
+          const int64_t mb = b < (a.M + 15) / 16 ? b : (a.M + 15) / 16 - 1;
+          const uint8_t* xp = a.xq + (mb * npairs + p) * 2048 + 16 * lane;
+          xv[c][b][0] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
+          xv[c][b][AI8 ? 1 : 0] = ok ? *reinterpret_cast<const uint4*>(xp + 1024) : make_uint4(0, 0, 0, 0);
+        }
+      } else {
+        const int64_t kb = p * 64 + g * 16;
+        const bool ok = p < p_end && kb < row_bytes;
+        wv[c] = (ok && n_ok) ? *reinterpret_cast<const uint4*>(a.wq + nrow * row_bytes + kb)
+                             : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const int64_t m = b * 16 + (lane & 15);
+          const bool xok = ok && m < a.M;
+          if constexpr (AI8) {
+            const uint8_t* xp = a.xq + m * a.K + 2 * kb;  // int8 codes [2kb, 2kb + 32)
+            xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
+            xv[c][b][AI8 ? 1 : 0] = xok ? *reinterpret_cast<const uint4*>(xp + 16) : make_uint4(0, 0, 0, 0);
+          } else {
+            xv[c][b][0] = xok ? *reinterpret_cast<const uint4*>(a.xq + m * row_bytes + kb)
+                              : make_uint4(0, 0, 0, 0);
+          }
         }
       }
     }
@@ -829,25 +849,30 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles));
-#define W4A4_PIPE_CASE(G, LR)                                                                     \
-  if ((a.group > 0) == G && a.lr_mode == LR) {                                                     \
-    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR>), grid, dim3(256), 0, st, a);     \
+#define W4A4_PIPE_CASE(G, LR, T)                                                                   \
+  if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T) {                             \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T>), grid, dim3(256), 0, st, a);  \
     return hipGetLastError();                                                                     \
   }
-  W4A4_PIPE_CASE(false, LR_NONE) W4A4_PIPE_CASE(false, LR_F16) W4A4_PIPE_CASE(false, LR_F32)
-  W4A4_PIPE_CASE(true, LR_NONE) W4A4_PIPE_CASE(true, LR_F16) W4A4_PIPE_CASE(true, LR_F32)
+  W4A4_PIPE_CASE(false, LR_NONE, false) W4A4_PIPE_CASE(false, LR_F16, false)
+  W4A4_PIPE_CASE(false, LR_F32, false) W4A4_PIPE_CASE(true, LR_NONE, false)
+  W4A4_PIPE_CASE(true, LR_F16, false) W4A4_PIPE_CASE(true, LR_F32, false)
+  W4A4_PIPE_CASE(false, LR_NONE, true) W4A4_PIPE_CASE(false, LR_F16, true)
+  W4A4_PIPE_CASE(false, LR_F32, true) W4A4_PIPE_CASE(true, LR_NONE, true)
+  W4A4_PIPE_CASE(true, LR_F16, true) W4A4_PIPE_CASE(true, LR_F32, true)
 #undef W4A4_PIPE_CASE
   return hipErrorInvalidValue;
 }
 
-template <int MB, bool AI8>
+template <int MB, bool AI8, bool TILED>
 hipError_t launch_skinny_a(const GemmArgs& a, hipStream_t st) {
   constexpr int KW = 4;
   const dim3 grid(static_cast<unsigned>((a.N + 15) / 16));
-#define W4A4_SKINNY_CASE(G, LR)                                                                  \
-  if ((a.group > 0) == G && a.lr_mode == LR) {                                                    \
-    hipLaunchKernelGGL((qgemm_skinny_kernel<MB, KW, G, LR, AI8>), grid, dim3(64 * KW), 0, st, a); \
-    return hipGetLastError();                                                                    \
+#define W4A4_SKINNY_CASE(G, LR)                                                              \
+  if ((a.group > 0) == G && a.lr_mode == LR) {                                                \
+    hipLaunchKernelGGL((qgemm_skinny_kernel<MB, KW, G, LR, AI8, TILED>), grid, dim3(64 * KW), \
+                       0, st, a);                                                             \
+    return hipGetLastError();                                                                \
   }
   W4A4_SKINNY_CASE(false, LR_NONE) W4A4_SKINNY_CASE(false, LR_F16) W4A4_SKINNY_CASE(false, LR_F32)
   W4A4_SKINNY_CASE(true, LR_NONE) W4A4_SKINNY_CASE(true, LR_F16) W4A4_SKINNY_CASE(true, LR_F32)
@@ -857,7 +882,8 @@ hipError_t launch_skinny_a(const GemmArgs& a, hipStream_t st) {
 
 template <int MB>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-  return a.a_i8 ? launch_skinny_a<MB, true>(a, st) : launch_skinny_a<MB, false>(a, st);
+  if (a.tiled) return launch_skinny_a<MB, true, true>(a, st);
+  return a.a_i8 ? launch_skinny_a<MB, true, false>(a, st) : launch_skinny_a<MB, false, false>(a, st);
 }
 
 }  // namespace
@@ -875,14 +901,15 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
     ia.group = 0;
     ia.y = nullptr;
     ia.lr_mode = LR_NONE;
-    hipError_t e = launch_tiles<4, 4>(ia, st);
+    hipError_t e = a.tiled ? launch_pipe<4, 4, 3>(ia, st) : launch_tiles<4, 4>(ia, st);
     if (e != hipSuccess) return e;
     if (!a.y) return hipSuccess;
   }
   GemmArgs ya = a;
   if (a.group > 0) ya.acc = nullptr;
-  // int8 codes, whole 128-code iterations: the pipelined direct-to-LDS kernel.
-  if (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0 && a.M > 32) {
+  // int8 codes, whole 128-code iterations: the pipelined direct-to-LDS kernel
+  // (the only one that reads tiled operands).
+  if (a.tiled || (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0)) {
     return launch_pipe<4, 4, 3>(ya, st);
   }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);

@@ -261,7 +261,10 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
     }
   }
   if (!valid) return;
-  if (a.mode == ROTQ_QUANT) {
+  const bool tiled = a.mode == ROTQ_QUANT_TILED || a.mode == ROTQ_QUANT_I8_TILED;
+  const int64_t nkit = a.K / 128;               // 128-code K iterations per row
+  const int64_t rblk = row >> 4, rin = row & 15;  // 16-row block, row inside it
+  if (a.mode == ROTQ_QUANT || a.mode == ROTQ_QUANT_TILED) {
     // Packed nibbles: element 8d+t in nibble t of dword d.
     uint32_t pk[R / 8];
 #pragma unroll
@@ -271,15 +274,33 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_alignbit(code[8 * d + t], acc, 4);
       pk[d] = acc;
     }
-    uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
-    if constexpr (R == 8) {
-      *reinterpret_cast<uint32_t*>(dst) = pk[0];
-    } else if constexpr (R == 16) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
-    } else {
+    if (!tiled) {
+      uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
+      if constexpr (R == 8) {
+        *reinterpret_cast<uint32_t*>(dst) = pk[0];
+      } else if constexpr (R == 16) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+      } else {
 #pragma unroll
-      for (int d = 0; d < R / 8; d += 4)
-        *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+        for (int d = 0; d < R / 8; d += 4)
+          *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+      }
+    } else {
+      // Packed byte j of the row sits in the 1 KB block (rblk, j / 64) at
+      // ((j % 64) / 16 * 16 + rin) * 16 + j % 16.
+#pragma unroll
+      for (int c = 0; c < (R >= 32 ? R / 32 : 1); ++c) {
+        const int64_t j = (kfirst >> 1) + c * 16;
+        uint8_t* dst = a.q + (rblk * nkit + (j >> 6)) * 1024 + ((((j & 63) >> 4) * 16 + rin) << 4) +
+                       (j & 15);
+        if constexpr (R == 8) {
+          *reinterpret_cast<uint32_t*>(dst) = pk[0];
+        } else if constexpr (R == 16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
+        }
+      }
     }
   } else {
     // One int8 code per byte, each group of 8 elements stored in the order
@@ -296,13 +317,29 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       pk[2 * d] = e;
       pk[2 * d + 1] = o;
     }
-    uint8_t* dst = a.q + row * a.K + kfirst;
-    if constexpr (R == 8) {
-      *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
-    } else {
+    if (!tiled) {
+      uint8_t* dst = a.q + row * a.K + kfirst;
+      if constexpr (R == 8) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+      } else {
 #pragma unroll
-      for (int d = 0; d < R / 4; d += 4)
-        *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+        for (int d = 0; d < R / 4; d += 4)
+          *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+      }
+    } else {
+      // Code k of the row sits in the 2 KB block (rblk, k / 128) at
+      // (((k % 32) / 16 * 4 + (k % 128) / 32) * 16 + rin) * 16 + k % 16.
+#pragma unroll
+      for (int c = 0; c < (R >= 16 ? R / 16 : 1); ++c) {
+        const int64_t k = kfirst + c * 16;
+        uint8_t* dst = a.q + (rblk * nkit + (k >> 7)) * 2048 +
+                       ((((((k & 31) >> 4) << 2) + ((k & 127) >> 5)) * 16 + rin) << 4) + (k & 15);
+        if constexpr (R == 8) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
+        }
+      }
     }
   }
 }

@@ -24,8 +24,16 @@ bool rotq_plan(int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan);
 
 // ROTQ_QUANT_I8 writes one int8 code per byte, each group of 8 elements in
 // the order 0,2,4,6,1,3,5,7 (the K order of the GEMM's nibble widening): the
-// activation operand format the fused layer hands to the GEMM.
-enum RotqMode { ROTQ_ROTATE = 0, ROTQ_QUANT = 1, ROTQ_QUANT_I8 = 2 };
+// activation operand format the fused layer hands to the GEMM.  The _TILED
+// modes write the same bytes in 16-row x 128-code tiles (see include/w4a4.h,
+// W4A4_WEIGHTS_TILED and W4A4_CODES_I8_TILED).
+enum RotqMode {
+  ROTQ_ROTATE = 0,
+  ROTQ_QUANT = 1,
+  ROTQ_QUANT_I8 = 2,
+  ROTQ_QUANT_TILED = 3,
+  ROTQ_QUANT_I8_TILED = 4
+};
 
 // x: [M, K] (f16 if x_f16 else f32).  mode ROTATE writes xrot [M, K] f32;
 // mode QUANT writes q [M, K/2] (QUANT_I8: q [M, K]) and one scale per group of
@@ -55,6 +63,7 @@ struct GemmArgs {
   int lr_mode;           // LowRankMode
   int rank;
   int a_i8;              // activation codes as int8 (ROTQ_QUANT_I8 layout)
+  int tiled;             // int8 codes and weights both in the 16 x 128 tiled layouts
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);

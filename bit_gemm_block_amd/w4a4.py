@@ -21,8 +21,10 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, F16 = 0, 1
-CODES_PACKED, CODES_I8 = 0, 1
-_LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8}
+CODES_PACKED, CODES_I8, CODES_I8_TILED = 0, 1, 2
+WEIGHTS_ROWMAJOR, WEIGHTS_TILED = 0, 1
+_LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8, "i8_tiled": CODES_I8_TILED}
+_WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -35,11 +37,13 @@ _SIGS = {
     "w4a4_last_hip_error": (_INT, []),
     "w4a4_hadamard_rotate": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P]),
     "w4a4_quantize_act_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
-    "w4a4_quantize_weight_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT, _P]),
+    "w4a4_quantize_weight_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
+                                         _P]),
     "w4a4_lowrank_project": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P, _P]),
-    "w4a4_qgemm_w4a4": (_INT, [_P, _INT, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_qgemm_w4a4": (_INT, [_P, _INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _P, _P,
+                               _P]),
     "w4a4_qlinear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
-    "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
+    "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
 }
 
@@ -74,6 +78,11 @@ def header_functions() -> list[str]:
     with open(HEADER) as f:
         text = f.read()
     return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(w4a4_\w+)\s*\(", text, re.M)))
+
+
+def pad16(n: int) -> int:
+    """Rows of a tiled layout: n rounded up to a multiple of 16."""
+    return (n + 15) // 16 * 16
 
 
 def _check(fn: str, status: int) -> None:
@@ -118,13 +127,15 @@ def hadamard_rotate(x: torch.Tensor, had_block: int, out: Optional[torch.Tensor]
 def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor] = None,
                       x_scale: Optional[torch.Tensor] = None,
                       layout: str = "packed") -> Tuple[torch.Tensor, torch.Tensor]:
-    """Codes in layout "packed" ([M, K/2] nibbles) or "i8" ([M, K] int8 in
-    the GEMM's K order), and one float32 scale per row."""
+    """Codes in layout "packed" ([M, K/2] nibbles), "i8" ([M, K] int8 in
+    the GEMM's K order) or "i8_tiled" ([pad16(M), K] in 2 KB tiles), and one
+    float32 scale per row."""
     _dev(x, "x")
     M, K = x.shape
     lay = _LAYOUTS[layout]
     if xq is None:
-        xq = torch.empty((M, K // 2 if lay == CODES_PACKED else K), dtype=torch.uint8,
+        rows = pad16(M) if lay == CODES_I8_TILED else M
+        xq = torch.empty((rows, K // 2 if lay == CODES_PACKED else K), dtype=torch.uint8,
                          device=x.device)
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
@@ -134,14 +145,20 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
 
 
 def quantize_weight_int4(w: torch.Tensor, had_block: int, w_group: int,
-                         scale_dtype: torch.dtype = torch.float16) -> Tuple[torch.Tensor, torch.Tensor]:
+                         scale_dtype: torch.dtype = torch.float16,
+                         layout: str = "rowmajor") -> Tuple[torch.Tensor, torch.Tensor]:
+    """Packed codes in layout "rowmajor" ([N, K/2]) or "tiled" ([pad16(N),
+    K/2] in 1 KB tiles), and the scales [N] or [N, K/w_group]."""
     _dev(w, "w")
     N, K = w.shape
-    wq = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    wl = _WLAYOUTS[layout]
+    wq = torch.empty((pad16(N) if wl == WEIGHTS_TILED else N, K // 2), dtype=torch.uint8,
+                     device=w.device)
     shape = (N,) if w_group == 0 else (N, K // w_group)
     ws = torch.empty(shape, dtype=scale_dtype, device=w.device)
     _check("quantize_weight_int4", lib().w4a4_quantize_weight_int4(
-        _ptr(w), _dt(w), N, K, had_block, w_group, _ptr(wq), _ptr(ws), _dt(ws), _stream(w)))
+        _ptr(w), _dt(w), N, K, had_block, w_group, _ptr(wq), wl, _ptr(ws), _dt(ws),
+        _stream(w)))
     return wq, ws
 
 
@@ -163,22 +180,32 @@ def lowrank_project(x: torch.Tensor, At: torch.Tensor, t: Optional[torch.Tensor]
 def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tensor,
                w_scale: Optional[torch.Tensor], w_group: int, want_y: bool = True,
                want_acc: bool = False, y: Optional[torch.Tensor] = None,
-               acc: Optional[torch.Tensor] = None, layout: str = "packed"):
+               acc: Optional[torch.Tensor] = None, layout: str = "packed",
+               w_layout: str = "rowmajor", M: Optional[int] = None, N: Optional[int] = None):
+    """M and N default to x_scale's and w_scale's lengths (else xq's and wq's
+    rows, which tiled layouts pad to a multiple of 16)."""
     _dev(xq, "xq")
     _dev(wq, "wq")
     lay = _LAYOUTS[layout]
-    M = xq.shape[0]
-    N = wq.shape[0]
+    wl = _WLAYOUTS[w_layout]
+    if M is None:
+        M = x_scale.shape[0] if x_scale is not None else xq.shape[0]
+    if N is None:
+        N = w_scale.shape[0] if w_scale is not None else wq.shape[0]
     K = 2 * wq.shape[1]
     if xq.shape[1] != (K // 2 if lay == CODES_PACKED else K):
         raise ValueError("xq and wq disagree on K")
+    if xq.shape[0] < (pad16(M) if lay == CODES_I8_TILED else M):
+        raise ValueError("xq has too few rows")
+    if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
+        raise ValueError("wq has too few rows")
     if want_y and y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     if want_acc and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     wst = _dt(w_scale) if w_scale is not None else F32
     _check("qgemm_w4a4", lib().w4a4_qgemm_w4a4(
-        _ptr(xq), lay, _ptr(x_scale), _ptr(wq), _ptr(w_scale), wst, w_group, M, N, K,
+        _ptr(xq), lay, _ptr(x_scale), _ptr(wq), wl, _ptr(w_scale), wst, w_group, M, N, K,
         _ptr(y), _ptr(acc), _stream(xq)))
     return y, acc
 
@@ -190,13 +217,19 @@ def qlinear_workspace_size(M: int, N: int, K: int, rank: int) -> int:
 def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, had_block: int,
                     w_group: int, At: Optional[torch.Tensor] = None,
                     Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None,
+                    w_layout: str = "rowmajor") -> torch.Tensor:
     """Y = dequant(int4 GEMM(rotate+quantize(x), wq)) + x . A . B, with the
-    low-rank factors given transposed: At [rank, K], Bt [N, rank]."""
+    low-rank factors given transposed: At [rank, K], Bt [N, rank].  N is
+    w_scale's length."""
     _dev(x, "x")
     _dev(wq, "wq")
+    _dev(w_scale, "w_scale")
+    wl = _WLAYOUTS[w_layout]
     M, K = x.shape
-    N = wq.shape[0]
+    N = w_scale.shape[0]
+    if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N) or wq.shape[1] != K // 2:
+        raise ValueError("wq does not match w_scale and x")
     rank = 0 if At is None else At.shape[0]
     if rank:
         if Bt is None or At.dtype != x.dtype or Bt.dtype != x.dtype:
@@ -211,6 +244,6 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check("qlinear_forward", lib().w4a4_qlinear_forward(
-        _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
+        _ptr(x), _dt(x), _ptr(wq), wl, _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
         _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
     return y

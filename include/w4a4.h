@@ -76,7 +76,30 @@ typedef enum { W4A4_F32 = 0, W4A4_F16 = 1 } w4a4_dtype;
  *                      which the GEMM widens packed weight nibbles, so these
  *                      codes feed the int8 matrix instructions unchanged; it
  *                      is the layout w4a4_qlinear_forward uses internally. */
-typedef enum { W4A4_CODES_PACKED = 0, W4A4_CODES_I8 = 1 } w4a4_codes_layout;
+typedef enum {
+  W4A4_CODES_PACKED = 0,
+  W4A4_CODES_I8 = 1,
+  W4A4_CODES_I8_TILED = 2
+} w4a4_codes_layout;
+
+/* Tiled layouts (K a multiple of 128).  Rows are taken in blocks of 16 and K
+ * in iterations of 128 codes; every (row block, iteration) tile is stored
+ * contiguously, row blocks outermost, in the order in which one 64-lane
+ * wave reads it: lane l = 16 g + r holds row r of the block.  Rows past the
+ * end of the last block are padding with unspecified bytes.
+ *   W4A4_CODES_I8_TILED (activations, [ceil(M/16)*16, K] bytes): tile
+ *     (b, t) is 2048 bytes at (b*(K/128) + t)*2048; inside it, for
+ *     h in {0,1}, g in {0..3}, r in {0..15}, the 16 bytes at
+ *     ((4h + g)*16 + r)*16 are the W4A4_CODES_I8 bytes of codes
+ *     [128t + 32g + 16h, +16) of row 16b + r.
+ *   W4A4_WEIGHTS_TILED (weights, [ceil(N/16)*16, K/2] bytes): tile (b, t) is
+ *     1024 bytes at (b*(K/128) + t)*1024; inside it, for g in {0..3},
+ *     r in {0..15}, the 16 bytes at (16g + r)*16 are the packed bytes
+ *     [64t + 16g, +16) of row 16b + r.
+ * With these layouts every 1 KB of a GEMM operand tile is one contiguous
+ * copy, which the strided row-major layouts cannot offer; tiled weights are
+ * used with tiled int8 activation codes. */
+typedef enum { W4A4_WEIGHTS_ROWMAJOR = 0, W4A4_WEIGHTS_TILED = 1 } w4a4_weight_layout;
 
 /* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
 int w4a4_abi_version(void);
@@ -106,7 +129,8 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot,
  *   x        [M, K] in dtype x_dtype.
  *   had_block 0/1: x is already rotated (codes then follow the quantizer rule
  *            exactly); otherwise the rotation above is applied first.
- *   xq       output codes in codes_layout ([M, K/2] packed or [M, K] int8).
+ *   xq       output codes in codes_layout ([M, K/2] packed, [M, K] int8 or
+ *            tiled int8).
  *   x_scale  [M] float32 output, one scale per row.
  */
 int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
@@ -119,14 +143,15 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
  *   w        [N, K] in dtype w_dtype.
  *   w_group  0: one scale per output channel; otherwise a power of two >= 64
  *            dividing K: one scale per group of w_group channels along K.
- *   wq       [N, K/2] uint8 output, packed codes.
+ *   wq       packed codes in w_layout: [N, K/2] row-major, or tiled.
  *   w_scale  [N] or [N, K/w_group] output in dtype scale_dtype.  The scale is
  *            rounded to scale_dtype first and the codes are taken against the
  *            stored value.
  */
 int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K,
                               int64_t had_block, int64_t w_group, uint8_t* wq,
-                              void* w_scale, int scale_dtype, void* stream);
+                              int w_layout, void* w_scale, int scale_dtype,
+                              void* stream);
 
 /*
  * First half of the low-rank term (SERQ page, "Resumen técnico" §2 item 2):
@@ -142,7 +167,9 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M,
  * int4 x int4 GEMM with the dequantizing epilogue (SERQ page, "Resumen
  * técnico" §3: 4-bit matrix multiplication in the linear layer).
  *   xq in codes_layout, x_scale [M] float32: activation codes and scales.
- *   wq [N, K/2], w_scale [N] (w_group 0) or [N, K/w_group] in w_scale_dtype.
+ *   wq in w_layout, w_scale [N] (w_group 0) or [N, K/w_group] in
+ *   w_scale_dtype.  Tiled weights need W4A4_CODES_I8_TILED codes and a
+ *   w_group of 0 or a multiple of 128.
  *   w_group 0 or a multiple of 64 dividing K.
  *   y   [M, N] float32 output, or NULL:
  *         y[m,n] = x_scale[m] * sum_j w_scale[n,j] * acc_j[m,n]
@@ -152,9 +179,9 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M,
  *   At least one of y and acc must be non-NULL.
  */
 int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale,
-                    const uint8_t* wq, const void* w_scale, int w_scale_dtype,
-                    int64_t w_group, int64_t M, int64_t N, int64_t K, float* y,
-                    int32_t* acc, void* stream);
+                    const uint8_t* wq, int w_layout, const void* w_scale,
+                    int w_scale_dtype, int64_t w_group, int64_t M, int64_t N,
+                    int64_t K, float* y, int32_t* acc, void* stream);
 
 /* Bytes of workspace qlinear_forward needs for these sizes (0 if M or N is
  * 0). */
@@ -162,8 +189,10 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
 
 /*
  * The whole layer: rotate + quantize X, int4 GEMM, dequant, + X.A.B.
- *   x [M, K] in x_dtype; wq / w_scale as prepared by
- *   w4a4_quantize_weight_int4 with the same had_block and w_group.
+ *   x [M, K] in x_dtype; wq (in w_layout) / w_scale as prepared by
+ *   w4a4_quantize_weight_int4 with the same had_block and w_group.  Tiled
+ *   weights take the fastest GEMM (K a multiple of 128, w_group 0 or a
+ *   multiple of 128).
  *   The rank-r factors are passed transposed so that both are contiguous
  *   along their contraction: At [rank, K] (At[j, k] = A[k, j]) and
  *   Bt [N, rank] (Bt[n, j] = B[j, n]), in x_dtype, or NULL when rank is 0.
@@ -176,8 +205,8 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
  *   not matter.
  */
 int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
-                         const void* w_scale, int w_scale_dtype, int64_t M,
-                         int64_t N, int64_t K, int64_t had_block,
+                         int w_layout, const void* w_scale, int w_scale_dtype,
+                         int64_t M, int64_t N, int64_t K, int64_t had_block,
                          int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace,
                          size_t ws_bytes, void* stream);

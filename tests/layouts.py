@@ -1,0 +1,62 @@
+"""Host-side byte layouts of the library's operands, written from their
+definitions in include/w4a4.h (test helpers: pure permutations, no
+arithmetic of the layer)."""
+import numpy as np
+
+
+def pad16(n):
+    return (n + 15) // 16 * 16
+
+
+def i8_from_codes(q):
+    """Codes [M, K] -> the W4A4_CODES_I8 byte layout: inside every group of 8
+    channels, channels 0,2,4,6 then 1,3,5,7 (the documented order)."""
+    M, K = q.shape
+    g = q.reshape(M, K // 8, 8)
+    return np.concatenate([g[:, :, 0::2], g[:, :, 1::2]], axis=2).reshape(M, K).astype(np.int8)
+
+
+def codes_from_i8(b):
+    M, K = b.shape
+    g = b.view(np.int8).reshape(M, K // 8, 8)
+    out = np.empty_like(g)
+    out[:, :, 0::2] = g[:, :, :4]
+    out[:, :, 1::2] = g[:, :, 4:]
+    return out.reshape(M, K)
+
+
+def tile_codes_i8(i8, rng=None):
+    """[M, K] W4A4_CODES_I8 bytes -> W4A4_CODES_I8_TILED ([pad16(M), K]):
+    tile (blk, t) holds, at ((4h + g) 16 + r) 16, codes [128t + 32g + 16h,
+    +16) of row 16 blk + r.  Padding rows get random bytes."""
+    M, K = i8.shape
+    Mp = pad16(M)
+    full = np.empty((Mp, K), np.uint8)
+    full[:M] = i8.view(np.uint8)
+    full[M:] = (rng or np.random.default_rng(0)).integers(0, 256, (Mp - M, K), dtype=np.uint8)
+    t = full.reshape(Mp // 16, 16, K // 128, 4, 2, 16).transpose(0, 2, 4, 3, 1, 5)
+    return np.ascontiguousarray(t).reshape(Mp, K)
+
+
+def untile_codes_i8(tiled, M):
+    Mp, K = tiled.shape
+    t = tiled.reshape(Mp // 16, K // 128, 2, 4, 16, 16).transpose(0, 4, 1, 3, 2, 5)
+    return np.ascontiguousarray(t).reshape(Mp, K)[:M]
+
+
+def tile_weights(packed, rng=None):
+    """[N, K/2] packed codes -> W4A4_WEIGHTS_TILED ([pad16(N), K/2]): tile
+    (blk, t) holds, at (16g + r) 16, bytes [64t + 16g, +16) of row 16 blk + r."""
+    N, H = packed.shape
+    Np = pad16(N)
+    full = np.empty((Np, H), np.uint8)
+    full[:N] = packed
+    full[N:] = (rng or np.random.default_rng(1)).integers(0, 256, (Np - N, H), dtype=np.uint8)
+    t = full.reshape(Np // 16, 16, H // 64, 4, 16).transpose(0, 2, 3, 1, 4)
+    return np.ascontiguousarray(t).reshape(Np, H)
+
+
+def untile_weights(tiled, N):
+    Np, H = tiled.shape
+    t = tiled.reshape(Np // 16, H // 64, 4, 16, 16).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(t).reshape(Np, H)[:N]

@@ -62,25 +62,34 @@ def test_rotate_and_weight_argument_errors(lib):
     assert r(P, W.F32, None, 4, 256, 256, None) == W.ERR_INVALID_ARG
     assert r(P, W.F32, Q, 4, 256, 256, None) == W.ERR_MISALIGNED
     w = lib.w4a4_quantize_weight_int4
-    assert w(P, W.F32, 8, 256, 0, 96, P, P, W.F16, None) == W.ERR_UNSUPPORTED   # group % 64
-    assert w(P, W.F32, 8, 192, 0, 128, P, P, W.F16, None) == W.ERR_UNSUPPORTED  # group | K
-    assert w(P, W.F32, 8, 384, 0, 192, P, P, W.F16, None) == W.ERR_UNSUPPORTED  # not pow2
-    assert w(P, W.F32, 8, 256, 0, -64, P, P, W.F16, None) == W.ERR_INVALID_ARG
-    assert w(P, W.F32, 8, 256, 0, 0, P, P, 5, None) == W.ERR_INVALID_ARG       # scale dtype
-    assert w(P, W.F32, 8, 256, 0, 0, P, None, W.F16, None) == W.ERR_INVALID_ARG
-    assert w(P, W.F32, 0, 256, 0, 0, None, None, W.F16, None) == W.OK
+    assert w(P, W.F32, 8, 256, 0, 96, P, 0, P, W.F16, None) == W.ERR_UNSUPPORTED   # group % 64
+    assert w(P, W.F32, 8, 192, 0, 128, P, 0, P, W.F16, None) == W.ERR_UNSUPPORTED  # group | K
+    assert w(P, W.F32, 8, 384, 0, 192, P, 0, P, W.F16, None) == W.ERR_UNSUPPORTED  # not pow2
+    assert w(P, W.F32, 8, 256, 0, -64, P, 0, P, W.F16, None) == W.ERR_INVALID_ARG
+    assert w(P, W.F32, 8, 256, 0, 0, P, 0, P, 5, None) == W.ERR_INVALID_ARG       # scale dtype
+    assert w(P, W.F32, 8, 256, 0, 0, P, 0, None, W.F16, None) == W.ERR_INVALID_ARG
+    assert w(P, W.F32, 0, 256, 0, 0, None, 0, None, W.F16, None) == W.OK
 
 
 def test_gemm_and_lowrank_argument_errors(lib):
     g = lib.w4a4_qgemm_w4a4
     L = W.CODES_I8
-    assert g(P, L, P, P, P, W.F16, 0, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
-    assert g(P, 9, P, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG    # layout
-    assert g(P, L, None, P, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
-    assert g(P, L, P, P, P, W.F16, 96, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
-    assert g(P, L, P, P, P, W.F16, 0, 4, 8, 200, P, None, None) == W.ERR_UNSUPPORTED
-    assert g(P, L, P, Q, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
-    assert g(None, L, None, None, None, W.F16, 0, 4, 0, 256, None, None, None) == W.OK
+    assert g(P, L, P, P, 0, P, W.F16, 0, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
+    assert g(P, 9, P, P, 0, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG    # layout
+    assert g(P, L, None, P, 0, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
+    assert g(P, L, P, P, 0, P, W.F16, 96, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, L, P, P, 0, P, W.F16, 0, 4, 8, 200, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, L, P, Q, 0, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
+    assert g(None, L, None, None, 0, None, W.F16, 0, 4, 0, 256, None, None, None) == W.OK
+    T, WT = W.CODES_I8_TILED, W.WEIGHTS_TILED
+    assert g(P, L, P, P, 7, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG    # w layout
+    assert g(P, L, P, P, WT, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG   # mixed
+    assert g(P, T, P, P, 0, P, W.F16, 0, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG    # mixed
+    assert g(P, T, P, P, WT, P, W.F16, 0, 4, 8, 192, P, None, None) == W.ERR_UNSUPPORTED   # K % 128
+    assert g(P, T, P, P, WT, P, W.F16, 64, 4, 8, 256, P, None, None) == W.ERR_UNSUPPORTED  # group
+    assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 192, 0, P, T, P, None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_quantize_weight_int4(P, W.F32, 8, 192, 0, 0, P, WT, P, W.F16,
+                                         None) == W.ERR_UNSUPPORTED
     lr = lib.w4a4_lowrank_project
     assert lr(P, W.F16, P, 4, 256, 0, P, None) == W.ERR_INVALID_ARG
     assert lr(P, W.F16, P, 4, 256, 257, P, None) == W.ERR_UNSUPPORTED
@@ -92,25 +101,29 @@ def test_qlinear_argument_errors(lib):
     need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
     assert need >= 16 * 128 + 16 * 4 + 16 * 8 * 4
     assert lib.w4a4_qlinear_workspace_size(0, 32, 256, 8) == 0
-    args = [P, W.F16, P, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P, need, None]
-    bad = list(args); bad[10] = None                                  # rank > 0 without A
+    args = [P, W.F16, P, 0, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P, need, None]
+    bad = list(args); bad[11] = None                                  # rank > 0 without A
     assert f(*bad) == W.ERR_INVALID_ARG
-    bad = list(args); bad[12] = 300
+    bad = list(args); bad[13] = 300
     assert f(*bad) == W.ERR_UNSUPPORTED
-    bad = list(args); bad[15] = need - 1
+    bad = list(args); bad[16] = need - 1
     assert f(*bad) == W.ERR_WORKSPACE
-    bad = list(args); bad[14] = Q
+    bad = list(args); bad[15] = Q
     assert f(*bad) == W.ERR_MISALIGNED
-    bad = list(args); bad[9] = 100
+    bad = list(args); bad[10] = 100
     assert f(*bad) == W.ERR_UNSUPPORTED
-    bad = list(args); bad[5] = 0
+    bad = list(args); bad[3] = 2                                      # weight layout
+    assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[3] = W.WEIGHTS_TILED; bad[10] = 64          # tiled needs group % 128
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[6] = 0
     assert f(*bad) == W.OK
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
 def test_valid_call_without_device_reports_unsupported(lib):
     need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
-    assert lib.w4a4_qlinear_forward(P, W.F16, P, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P,
-                                    need, None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_qlinear_forward(P, W.F16, P, 0, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P,
+                                    P, need, None) == W.ERR_UNSUPPORTED
     assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P,
                                       None) == W.ERR_UNSUPPORTED

@@ -19,6 +19,8 @@ import torch
 from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
+from layouts import (codes_from_i8, i8_from_codes, tile_codes_i8, tile_weights, untile_codes_i8,
+                     untile_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,23 +38,6 @@ def host(t):
 
 def np_dtype(name):
     return np.float16 if name == "float16" else np.float32
-
-
-def i8_from_codes(q):
-    """Codes [M, K] -> the W4A4_CODES_I8 byte layout: inside every group of 8
-    channels, channels 0,2,4,6 then 1,3,5,7 (the documented order)."""
-    M, K = q.shape
-    g = q.reshape(M, K // 8, 8)
-    return np.concatenate([g[:, :, 0::2], g[:, :, 1::2]], axis=2).reshape(M, K).astype(np.int8)
-
-
-def codes_from_i8(b):
-    M, K = b.shape
-    g = b.view(np.int8).reshape(M, K // 8, 8)
-    out = np.empty_like(g)
-    out[:, :, 0::2] = g[:, :, :4]
-    out[:, :, 1::2] = g[:, :, 4:]
-    return out.reshape(M, K)
 
 
 def rotation_bound(x, b):
@@ -108,6 +93,25 @@ def test_quantize_act_i8_layout_exact(M, K, b, dt):
     assert np.array_equal(host(xq).view(np.int8), i8_from_codes(pc))
 
 
+@pytest.mark.parametrize("M,K,b,dt", [(37, 4096, 4096, "float16"), (20, 14336, 128, "float16"),
+                                      (3, 256, 64, "float32"), (16, 128, 2, "float16"),
+                                      (1, 128, 128, "float32")])
+def test_quantize_act_i8_tiled_exact(M, K, b, dt):
+    w = synth.small("qt", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xr = O.rotate(X, b)
+    xq, sx = W.quantize_act_int4(dev(xr), 0, layout="i8_tiled")
+    assert tuple(xq.shape) == (W.pad16(M), K)
+    _, ps, pc, _ = O.quantize_activation(xr, 0)
+    assert np.array_equal(host(sx), ps)
+    got = host(xq)
+    assert np.array_equal(untile_codes_i8(got, M).view(np.int8), i8_from_codes(pc))
+    # the host tiling of the same bytes agrees on every real row
+    ref = tile_codes_i8(i8_from_codes(pc))
+    real = untile_codes_i8(ref, M)
+    assert np.array_equal(real, untile_codes_i8(got, M))
+
+
 def test_quantize_act_exact_unrotated_fp16_and_edge_rows():
     rng = np.random.default_rng(3)
     X = (rng.standard_normal((6, 512)) * 3).astype(np.float16)
@@ -158,6 +162,21 @@ def test_quantize_weight_exact_on_oracle_rotation(N, K, g, sd):
     oq, os_ = O.quantize_weight(wr, g, sd)
     assert np.array_equal(host(ws), os_)
     assert np.array_equal(host(wq), O.pack_int4(oq))
+
+
+@pytest.mark.parametrize("N,K,g,sd", [(64, 256, 0, "float32"), (100, 4096, 0, "float16"),
+                                      (40, 14336, 128, "float16"), (8, 4096, 4096, "float32")])
+def test_quantize_weight_tiled_exact(N, K, g, sd):
+    rng = np.random.default_rng(N + K + 3)
+    Wt = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
+    Wt[:, 9] *= 30
+    wr = O.rotate(Wt, 128)
+    wq, ws = W.quantize_weight_int4(dev(wr), 0, g, torch.float16 if sd == "float16" else torch.float32,
+                                    layout="tiled")
+    assert tuple(wq.shape) == (W.pad16(N), K // 2)
+    oq, os_ = O.quantize_weight(wr, g, sd)
+    assert np.array_equal(host(ws), os_)
+    assert np.array_equal(untile_weights(host(wq), N), O.pack_int4(oq))
 
 
 @pytest.mark.parametrize("N,K,b,g", [(64, 4096, 4096, 0), (48, 14336, 128, 128), (32, 256, 256, 0)])
@@ -245,6 +264,30 @@ def test_qgemm_dequant(M, N, K, g, sd, layout):
     assert np.all(np.abs(host(y) - ref) <= (G + 3) * 2.0 ** -23 * mag)
 
 
+@pytest.mark.parametrize("M,N,K,g", [(1, 1, 128, 0), (8, 4096, 4096, 0), (16, 300, 14336, 128),
+                                     (17, 33, 256, 0), (32, 4096, 4096, 128), (33, 70, 384, 128),
+                                     (130, 260, 384, 0), (300, 129, 1024, 256),
+                                     (1000, 6500, 256, 128), (2048, 4096, 4096, 0)])
+def test_qgemm_tiled_exact_and_dequant(M, N, K, g):
+    rng = np.random.default_rng(M * 7 + N + K + g)
+    qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    qx[0, :] = -8
+    qw[0, :] = -8
+    sx = rng.uniform(0.01, 2.0, M).astype(np.float32)
+    shape = (N,) if g == 0 else (N, K // g)
+    sw = rng.uniform(1e-3, 0.05, shape).astype(np.float16)
+    y, acc = W.qgemm_w4a4(dev(tile_codes_i8(i8_from_codes(qx), rng)), dev(sx),
+                          dev(tile_weights(O.pack_int4(qw), rng)), dev(sw), g,
+                          want_y=True, want_acc=True, layout="i8_tiled", w_layout="tiled")
+    assert np.array_equal(host(acc), O.int_gemm(qx, qw))
+    accs = O.int_gemm(qx, qw) if g == 0 else O.int_gemm_groups(qx, qw, g)
+    ref = O.epilogue(accs, sx, sw.astype(np.float32), None).astype(np.float64)
+    G = 1 if g == 0 else K // g
+    mag = np.abs(sx)[:, None] * (np.abs(sw.astype(np.float64)).reshape(N, -1).max(axis=1)[None, :]) * 64 * K
+    assert np.all(np.abs(host(y) - ref) <= (G + 3) * 2.0 ** -23 * mag)
+
+
 # --------------------------------------------------------------------------
 # Low-rank projection
 # --------------------------------------------------------------------------
@@ -263,15 +306,16 @@ def test_lowrank_project(M, K, r, dt):
 # --------------------------------------------------------------------------
 # Whole layer
 # --------------------------------------------------------------------------
-def run_layer(w, rows=None):
+def run_layer(w, rows=None, w_layout="rowmajor"):
     """GPU qlinear_forward vs the oracle on one workload; returns stats."""
     d = synth.make_inputs(w, rows)
     X, Wt, A, B = d["X"], d["W"], d["A"], d["B"]
     wq, ws, _ = O.prepare_weight(Wt, w.had_block, w.w_group, w.w_scale_dtype)
-    Xd, wqd, wsd = dev(X), dev(wq), dev(ws)
+    Xd, wsd = dev(X), dev(ws)
+    wqd = dev(tile_weights(wq) if w_layout == "tiled" else wq)
     Ad = dev(A.T) if A is not None else None   # the ABI takes At [r, K], Bt [N, r]
     Bd = dev(B.T) if B is not None else None
-    y = host(W.qlinear_forward(Xd, wqd, wsd, w.had_block, w.w_group, Ad, Bd))
+    y = host(W.qlinear_forward(Xd, wqd, wsd, w.had_block, w.w_group, Ad, Bd, w_layout=w_layout))
     gxq, gsx = W.quantize_act_int4(Xd, w.had_block)
     gxq, gsx = host(gxq), host(gsx)
     _, ps, pc, _ = O.quantize_activation(X, w.had_block)
@@ -292,19 +336,32 @@ def check_layer(st):
     assert err <= 1e-3 * st["rms"], (err, st["rms"])
 
 
+@pytest.mark.parametrize("wl", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("w", [synth.TINY, synth.DECODE], ids=lambda w: w.name)
-def test_qlinear_full_size(w):
-    st = run_layer(w)
+def test_qlinear_full_size(w, wl):
+    st = run_layer(w, w_layout=wl)
     check_layer(st)
-    print(w.name, "max|Y-Y_oracle|/RMS =",
+    print(w.name, wl, "max|Y-Y_oracle|/RMS =",
           float(np.max(np.abs(st["y"] - st["y_oracle"])) / st["rms"]))
 
 
-def test_qlinear_prefill_full_size():
-    st = run_layer(synth.PREFILL)
+@pytest.mark.parametrize("wl", ["rowmajor", "tiled"])
+def test_qlinear_prefill_full_size(wl):
+    st = run_layer(synth.PREFILL, w_layout=wl)
     check_layer(st)
-    print("prefill max|Y-Y_oracle|/RMS =",
+    print("prefill", wl, "max|Y-Y_oracle|/RMS =",
           float(np.max(np.abs(st["y"] - st["y_oracle"])) / st["rms"]))
+
+
+@pytest.mark.parametrize("M,K,N,b,g,r,dt", [
+    (1, 256, 64, 256, 0, 0, "float16"), (130, 1024, 260, 128, 128, 16, "float16"),
+    (33, 4096, 100, 4096, 0, 64, "float16"), (65, 14336, 96, 128, 128, 32, "float16"),
+    (20, 4096, 520, 128, 128, 24, "float16"), (300, 1024, 1030, 256, 0, 40, "float16"),
+    (40, 384, 100, 128, 0, 0, "float32"), (16, 512, 48, 1, 0, 8, "float16")])
+def test_qlinear_tiled_weights_ragged(M, K, N, b, g, r, dt):
+    w = synth.small("ragt", M, K, N, x_dtype=dt, had_block=b, w_group=g, rank=r,
+                    w_scale_dtype="float16" if dt == "float16" else "float32")
+    check_layer(run_layer(w, w_layout="tiled"))
 
 
 @pytest.mark.parametrize("M,K,N,b,g,r,dt", [

@@ -1,0 +1,35 @@
+"""The layout helpers the GPU parity tests use are inverse permutations and
+put bytes where include/w4a4.h says they go."""
+import numpy as np
+
+from layouts import (codes_from_i8, i8_from_codes, tile_codes_i8, tile_weights, untile_codes_i8,
+                     untile_weights)
+
+
+def test_i8_order_is_even_then_odd_channels():
+    q = np.arange(16, dtype=np.int8).reshape(1, 16) - 8
+    b = i8_from_codes(q)
+    assert b[0].tolist() == [-8, -6, -4, -2, -7, -5, -3, -1, 0, 2, 4, 6, 1, 3, 5, 7]
+    assert np.array_equal(codes_from_i8(b.view(np.uint8)), q)
+
+
+def test_tiling_helpers_are_inverse_permutations():
+    rng = np.random.default_rng(5)
+    a = rng.integers(0, 256, (37, 384), dtype=np.uint8)
+    assert np.array_equal(untile_codes_i8(tile_codes_i8(a), 37), a)
+    wq = rng.integers(0, 256, (21, 192), dtype=np.uint8)
+    assert np.array_equal(untile_weights(tile_weights(wq), 21), wq)
+    # every byte sits at the offset the header documents
+    t = tile_codes_i8(a).reshape(-1)
+    K = a.shape[1]
+    for m in range(a.shape[0]):
+        for k in range(K):
+            blk, r, tt = m // 16, m % 16, k // 128
+            g, h = (k % 128) // 32, (k % 32) // 16
+            assert t[(blk * (K // 128) + tt) * 2048 + ((4 * h + g) * 16 + r) * 16 + k % 16] == a[m, k]
+    tw = tile_weights(wq).reshape(-1)
+    H = wq.shape[1]
+    for n in range(wq.shape[0]):
+        for j in range(H):
+            off = ((n // 16) * (H // 64) + j // 64) * 1024 + (16 * ((j % 64) // 16) + n % 16) * 16 + j % 16
+            assert tw[off] == wq[n, j]
