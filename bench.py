@@ -91,6 +91,18 @@ class Layer:
         return 2 * self.wl.M * self.wl.N * self.wl.K
 
 
+def gemm_bytes(wl: synth.Workload) -> int:
+    """Bytes the GEMM must move once: int8 codes and scales of X, packed
+    weights and their scales, float32 Y."""
+    sb = 2 if wl.w_scale_dtype == "float16" else 4
+    nsc = wl.N if wl.w_group == 0 else wl.N * (wl.K // wl.w_group)
+    return wl.M * wl.K + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N
+
+
+def gemm_kernel_name(layer: "Layer") -> str:
+    return "qgemm_pipe_kernel" if layer.w_layout == "tiled" or layer.wl.M > 32 else "qgemm_skinny_kernel"
+
+
 def time_graph(fn, steps: int, warmup: int) -> float:
     """Seconds per step: `steps` calls of fn(i) captured in one HIP graph."""
     for i in range(warmup):
@@ -153,6 +165,57 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     return out
 
 
+CALIB_BYTES = 256 << 20   # the calibration copy reads and writes this much
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_prefill_traffic.txt")
+GEMM_SOURCES = [os.path.join(ROOT, "bit_gemm_block_amd", "csrc", f)
+                for f in ("qgemm.hip", "w4a4_internal.h")]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_kernels(steps: int, w_layout: str) -> None:
+    """Launch the prefill kernels alone (for hardware counters): rotate +
+    quantize and the GEMM `steps` times each, then a plain elementwise copy
+    of CALIB_BYTES, whose counter readings calibrate the byte counters."""
+    pre = Layer(synth.PREFILL, w_layout=w_layout)
+    kernel_times(pre, steps, 2)
+    src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"profiled {steps} launches of each prefill kernel and 5 copies of {CALIB_BYTES} bytes")
+
+
+def read_traffic(algorithmic: float) -> dict | None:
+    """HBM bytes per GEMM launch from the committed counter summary, or None
+    when the summary is missing or the GEMM source changed since it was made."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+        return None
+    try:
+        fetch = float(kv["gemm_fetch_bytes_per_launch"])
+        write = float(kv["gemm_write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+    return {"fetch_bytes": fetch, "write_bytes": write, "bytes": fetch + write,
+            "vs_algorithmic": (fetch + write) / algorithmic}
+
+
 def cpu_baseline(wl: synth.Workload, seconds: float) -> dict:
     """The float64 oracle on the whole workload, repeated until `seconds` of
     CPU time have passed (at least once)."""
@@ -190,6 +253,8 @@ def main() -> int:
     ap.add_argument("--w-layout", choices=["tiled", "rowmajor"], default="tiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="only launch the prefill kernels and a calibration copy (for counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the W4A4 linear path of this library runs on a "
@@ -199,6 +264,9 @@ def main() -> int:
         print("bench.py needs a ROCm GPU", file=sys.stderr)
         return 2
     W.lib()
+    if args.profile_kernels:
+        profile_kernels(args.steps, args.w_layout)
+        return 0
 
     # ---- prefill: the headline ------------------------------------------------
     pre = Layer(synth.PREFILL, w_layout=args.w_layout)
@@ -258,10 +326,11 @@ def main() -> int:
                    "rank": pre.wl.rank, "x_dtype": pre.wl.x_dtype,
                    "w_layout": args.w_layout},
         "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
-        "roofline": {"bound": "mfma", "kernel": "qgemm_kernel", "achieved": gemm_tops,
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(pre), "achieved": gemm_tops,
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
                      "ops_per_launch": pre.ops(), "us_per_launch": kt["qgemm"] * 1e6,
-                     "traffic": None},
+                     "algorithmic_bytes_per_launch": gemm_bytes(pre.wl),
+                     "traffic": read_traffic(gemm_bytes(pre.wl))},
         "kernels_us": {k: v * 1e6 for k, v in kt.items()},
         "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,
         "decode": decode,
