@@ -22,12 +22,14 @@
 // granularity so that row reads (ds_read_b128) and column reads (ds_read_b32)
 // are free of bank conflicts for R = 64.
 //
-// Quantization is exact with respect to the float32 rule q = rint(x~ / s):
-// codes are first taken from t = y * (rs / s) with a magic-number rounding,
-// and every element certifies that t lies at least 2^-16 away from a
-// half-integer.  The combined relative error of the reciprocal form is below
-// 2^-18.8 of |t| <= 7, so a certified t rounds like the IEEE quotient; a lane
-// holding any uncertified element redoes its elements with true division.
+// Quantization is exact with respect to the float32 rule
+// q = clamp(rint(fl(x~ / s)), -7, 7) with x~ = RN(y * rs): the quotient is
+// formed as x~ * RN(1/s) and refined twice by Markstein's step (residual
+// r = x~ - q s by fma, then q' = RN(q + r RN(1/s))); once q is within one ulp
+// of x~ / s, the refined value is the correctly rounded quotient.  Quotients
+// of magnitude >= 1/4 keep every intermediate normal for 2^-100 <= s <= 2^100,
+// and smaller ones give code 0 whatever their last bits; scales outside that
+// range take the IEEE division.
 #include "w4a4_internal.h"
 
 #include <hip/hip_fp16.h>
@@ -60,22 +62,34 @@ template <> struct Piece<_Float16> {
   }
 };
 
-// Butterflies on register-index bits [lo, hi) of v: for every pair
-// (r, r | 2^st) with bit st of r clear, (a, b) -> (a + b, a - b).
-template <int N>
-__device__ __forceinline__ void fwht_reg_bits(float (&v)[N], int lo, int hi) {
-  constexpr int LOGN = ilog2(N);
+// Butterflies on register-index bits [LO, HI) of v: for every pair
+// (r, r | 2^st) with bit st of r clear, (a, b) -> (a + b, a - b).  The stage
+// range is a compile-time constant so that all stages form one straight-line
+// block in which the register allocator renames instead of copying.
+template <int LO, int HI, int N>
+__device__ __forceinline__ void fwht_stages(float (&v)[N]) {
 #pragma unroll
-  for (int st = 0; st < LOGN; ++st) {
-    if (st >= lo && st < hi) {
+  for (int st = LO; st < HI; ++st) {
 #pragma unroll
-      for (int r = 0; r < N; ++r) {
-        if ((r & (1 << st)) == 0) {
-          const float a = v[r], b = v[r | (1 << st)];
-          v[r] = a + b;
-          v[r | (1 << st)] = a - b;
-        }
+    for (int r = 0; r < N; ++r) {
+      if ((r & (1 << st)) == 0) {
+        const float a = v[r], b = v[r | (1 << st)];
+        v[r] = a + b;
+        v[r | (1 << st)] = a - b;
       }
+    }
+  }
+}
+
+// Stages [LO, hi) for a run-time hi in [LO, HI]: one uniform branch picks a
+// fully unrolled stage sequence.
+template <int LO, int HI, int N>
+__device__ __forceinline__ void fwht_bits_upto(float (&v)[N], int hi) {
+  if constexpr (HI > LO) {
+    if (hi >= HI) {
+      fwht_stages<LO, HI>(v);
+    } else {
+      fwht_bits_upto<LO, HI - 1>(v, hi);
     }
   }
 }
@@ -140,7 +154,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) v[r] = 0.f;
   }
-  fwht_reg_bits(v, 0, min(LOGV, a.log2b));
+  fwht_bits_upto<0, LOGV>(v, a.log2b);
   if (on) {
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
@@ -168,7 +182,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         const int i = ((g >> LOGR) << cb) + (r & cmask);
         v[r] = seg[lds_off<R>(i, g & (R - 1))];
       }
-      fwht_reg_bits(v, 0, cb);
+      fwht_bits_upto<0, LOGR>(v, cb);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int g = (r >> cb) * L + lam;
@@ -188,7 +202,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       v[4 * c4] = f.x; v[4 * c4 + 1] = f.y; v[4 * c4 + 2] = f.z; v[4 * c4 + 3] = f.w;
     }
   }
-  fwht_reg_bits(v, LOGV, min(a.log2b, LOGR));
+  fwht_bits_upto<LOGV, LOGR>(v, a.log2b);
 
   const int kfirst = k0 + lam * R;  // first element of this lane's run
 
@@ -234,30 +248,28 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 
   // 6. Codes.  code[r] holds the code of element r in its low bits (two's
   // complement: low nibble = q & 0xF, low byte = q & 0xFF).
+  // A zero scale (an all-zero group) takes the reciprocal 0, so every
+  // quotient and code is 0.  The rint is the magic-number addition: the low
+  // mantissa bits of q + 1.5 * 2^23 are rint(q) in two's complement.
   uint32_t code[R];
-  if (s_eff == 0.f) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) code[r] = 0u;
-  } else {
-    const float kk = a.rs * __frcp_rn(s_eff);
-    float dev = 0.f;
+  if (s_eff == 0.f || (s_eff >= 0x1p-100f && s_eff <= 0x1p100f)) {
+    const float rc = s_eff == 0.f ? 0.f : __frcp_rn(s_eff);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const float tq = v[r] * kk;
-      const float u = tq + kMagic;
-      const float w = u - kMagic;
-      dev = fmaxf(dev, fabsf(tq - w));
+      const float xt = v[r] * a.rs;
+      float q = xt * rc;
+      q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
+      q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
+      const float u = q + kMagic;
       code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - 7.0f, kMagic + 7.0f));
     }
-    const bool certified = (dev < 0.5f - 0x1p-16f) && (kk <= 0x1p100f);
-    if (!certified) {
+  } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float xt = v[r] * a.rs;
-        float qf = rintf(__fdiv_rn(xt, s_eff));
-        qf = fminf(fmaxf(qf, -7.0f), 7.0f);
-        code[r] = static_cast<uint32_t>(static_cast<int>(qf));
-      }
+    for (int r = 0; r < R; ++r) {
+      const float xt = v[r] * a.rs;
+      float qf = rintf(__fdiv_rn(xt, s_eff));
+      qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+      code[r] = static_cast<uint32_t>(static_cast<int>(qf));
     }
   }
   if (!valid) return;

@@ -150,6 +150,47 @@ def test_quantize_act_tie_breaking_matches_division():
     assert np.array_equal(host(xq), pq)
 
 
+@pytest.mark.parametrize("e", [-125, -110, -98, -60, 0, 60, 98, 110, 121])
+def test_quantize_act_exact_extreme_scales(e):
+    # Rows of fp32 values scaled by 2^e: scales on both sides of the range in
+    # which the quotient is refined from a reciprocal.
+    rng = np.random.default_rng(1000 + e)
+    X = (rng.standard_normal((48, 512)) * np.float64(2.0) ** e).astype(np.float32)
+    X[5] = 0
+    xq, sx = W.quantize_act_int4(dev(X), 0)
+    pq, ps, _, _ = O.quantize_activation(X, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(host(xq), pq)
+
+
+def test_quantize_act_exact_random_near_ties():
+    # Every element sits within a few ulps of a half-integer multiple of its
+    # row's scale: the cases where a reciprocal-based quotient can round the
+    # other way.
+    rng = np.random.default_rng(11)
+    f = np.float32
+    M, K = 64, 1024
+    X = np.empty((M, K), np.float32)
+    for m in range(M):
+        amax = f(rng.uniform(0.5, 2.0) * 2.0 ** rng.integers(-20, 20))
+        s = f(amax / f(7))
+        n = rng.integers(-7, 7, K).astype(np.float64) + 0.5
+        base = (n * np.float64(s)).astype(np.float32)
+        ulps = rng.integers(-3, 4, K)
+        row = base.copy()
+        for _ in range(3):
+            row = np.where(ulps > 0, np.nextafter(row, f(np.inf)), row)
+            row = np.where(ulps < 0, np.nextafter(row, f(-np.inf)), row)
+            ulps = ulps - np.sign(ulps)
+        row[0] = amax
+        row = np.clip(row, -amax, amax)
+        X[m] = row
+    xq, sx = W.quantize_act_int4(dev(X), 0, layout="i8")
+    _, ps, pc, _ = O.quantize_activation(X, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(codes_from_i8(host(xq)), pc)
+
+
 @pytest.mark.parametrize("N,K,g,sd", [(64, 256, 0, "float32"), (96, 4096, 0, "float16"),
                                       (40, 14336, 128, "float16"), (24, 512, 64, "float16"),
                                       (8, 4096, 4096, "float32")])
