@@ -19,7 +19,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int NCB, int KW>
+template <int NCB, int KW, int PF>
 __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __restrict__ x,
                                                              const _Float16* __restrict__ at,
                                                              int64_t M, int64_t K, int rank,
@@ -38,18 +38,33 @@ __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __
 #pragma unroll
   for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave owns a contiguous range of 32-wide K chunks and issues the
+  // loads of PF chunks before their matrix instructions, so that a short
+  // range costs one memory latency rather than one per chunk.
   const int64_t nchunks = K / 32;
+  const int64_t c_begin = nchunks * wave / KW;
+  const int64_t c_end = nchunks * (wave + 1) / KW;
   const half8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t ch = wave; ch < nchunks; ch += KW) {
-    const int64_t k = ch * 32 + koff;
-    const half8 xa = row_ok ? *reinterpret_cast<const half8*>(x + mrow * K + k) : zero8;
+  for (int64_t cb = c_begin; cb < c_end; cb += PF) {
+    half8 xa[PF], ab[PF][NCB];
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const int j = c0 + c * 16 + (lane & 15);
-      const half8 ab = j < rank ? *reinterpret_cast<const half8*>(at + static_cast<int64_t>(j) * K + k)
-                                : zero8;
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ab, acc[c], 0, 0, 0);
+    for (int u = 0; u < PF; ++u) {
+      const bool ok = cb + u < c_end;
+      const int64_t k = (cb + u) * 32 + koff;
+      xa[u] = ok && row_ok ? *reinterpret_cast<const half8*>(x + mrow * K + k) : zero8;
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int j = c0 + c * 16 + (lane & 15);
+        ab[u][c] = ok && j < rank
+                       ? *reinterpret_cast<const half8*>(at + static_cast<int64_t>(j) * K + k)
+                       : zero8;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < PF; ++u)
+#pragma unroll
+      for (int c = 0; c < NCB; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[u], ab[u][c], acc[c], 0, 0, 0);
   }
 #pragma unroll
   for (int c = 0; c < NCB; ++c) red[wave][c][lane] = acc[c];
@@ -78,6 +93,69 @@ __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __
           }
         }
       }
+    }
+  }
+}
+
+// Few rows (M <= 16), fp16: one workgroup per column j of T.  Lane l of wave
+// w reads the 16 bytes at channel 8 (64 w + l) + 2048 c of X's rows and of
+// row j of At, so that every load instruction is one contiguous 1 KB run,
+// and accumulates x . a with fp16 pair dot products in float32.  Partial sums
+// are reduced across lanes and then across the four waves in a fixed order.
+template <int MR>
+__global__ void __launch_bounds__(256) lowrank_rows_kernel(const _Float16* __restrict__ x,
+                                                          const _Float16* __restrict__ at,
+                                                          int64_t M, int64_t K, int rank,
+                                                          void* __restrict__ t, int pair_out) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  __shared__ float red[4][MR];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = blockIdx.x;
+  const _Float16* arow = at + static_cast<int64_t>(j) * K;
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+#pragma unroll 2
+  for (int64_t k = 8 * tid; k < K; k += 2048) {
+    const half8 av = *reinterpret_cast<const half8*>(arow + k);
+    half8 xv[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      xv[m] = m < M ? *reinterpret_cast<const half8*>(x + m * K + k) : half8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const half2v xa = {xv[m][2 * p], xv[m][2 * p + 1]};
+        const half2v aa = {av[2 * p], av[2 * p + 1]};
+        acc[m] = __builtin_amdgcn_fdot2(xa, aa, acc[m], false);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    float v = acc[m];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    acc[m] = v;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) red[wave][m] = acc[m];
+  }
+  __syncthreads();
+  if (tid < MR && tid < M) {
+    const float sum = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    const int64_t m = tid;
+    if (pair_out) {
+      const _Float16 hi = static_cast<_Float16>(sum);
+      const _Float16 lo = static_cast<_Float16>(sum - static_cast<float>(hi));
+      static_cast<_Float16*>(t)[m * rank + j] = hi;
+      static_cast<_Float16*>(t)[M * rank + m * rank + j] = lo;
+    } else {
+      static_cast<float*>(t)[m * rank + j] = sum;
     }
   }
 }
@@ -132,11 +210,18 @@ hipError_t launch_f16(const _Float16* x, const _Float16* at, int64_t M, int64_t 
   const int64_t row_tiles = (M + 15) / 16;
   const int col_groups = (rank + NCB * 16 - 1) / (NCB * 16);
   const dim3 grid(static_cast<unsigned>(row_tiles), static_cast<unsigned>(col_groups));
-  if (row_tiles >= 64) {
-    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 4>), grid, dim3(256), 0, st, x, at, M, K, rank, t, pair);
-  } else {
-    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 8>), grid, dim3(512), 0, st, x, at, M, K, rank, t, pair);
+  constexpr int PF = NCB >= 4 ? 2 : 8 / NCB;
+  if constexpr (NCB == 1) {
+    if (row_tiles < 64) {
+      // Few workgroups: sixteen waves each split K so that every wave has a
+      // short range whose loads are all in flight at once.
+      hipLaunchKernelGGL((lowrank_f16_kernel<1, 16, PF>), grid, dim3(1024), 0, st, x, at, M, K,
+                         rank, t, pair);
+      return hipGetLastError();
+    }
   }
+  hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 4, PF>), grid, dim3(256), 0, st, x, at, M, K, rank,
+                     t, pair);
   return hipGetLastError();
 }
 
@@ -150,6 +235,16 @@ hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* at, int
     const int pair = pair_out ? 1 : 0;
     const int64_t row_tiles = (M + 15) / 16;
     const int blocks = (rank + 15) / 16;
+    if (M <= 8) {
+      hipLaunchKernelGGL((lowrank_rows_kernel<8>), dim3(rank), dim3(256), 0, st, xh, ah, M, K,
+                         rank, t, pair);
+      return hipGetLastError();
+    }
+    if (M <= 16) {
+      hipLaunchKernelGGL((lowrank_rows_kernel<16>), dim3(rank), dim3(256), 0, st, xh, ah, M, K,
+                         rank, t, pair);
+      return hipGetLastError();
+    }
     // Few row tiles: one 16-column block per workgroup for parallelism.
     // Many row tiles: all columns in one workgroup so X is read once.
     if (row_tiles < 64 || blocks == 1) return launch_f16<1>(xh, ah, M, K, rank, t, pair, st);

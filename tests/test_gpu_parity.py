@@ -333,7 +333,9 @@ def test_qgemm_tiled_exact_and_dequant(M, N, K, g):
 # Low-rank projection
 # --------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,r,dt", [(16, 256, 8, "float32"), (8, 4096, 64, "float16"),
-                                      (100, 4096, 32, "float16"), (5, 192, 256, "float16")])
+                                      (100, 4096, 32, "float16"), (5, 192, 256, "float16"),
+                                      (1, 64, 8, "float16"), (16, 14336, 40, "float16"),
+                                      (11, 2112, 24, "float16"), (17, 4096, 64, "float16")])
 def test_lowrank_project(M, K, r, dt):
     w = synth.small("l", M, K, 8, x_dtype=dt, rank=r)
     d = synth.make_inputs(w)
