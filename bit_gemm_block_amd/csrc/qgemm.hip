@@ -443,7 +443,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
   static_assert(STAGES >= 2 && STAGES <= 8, "stages");
   constexpr int RUNS_PER_WAVE = RUNS / 4;
-  static_assert((STAGES - 2) * RUNS_PER_WAVE < 64, "in-flight copies exceed vmcnt");
+  static_assert((STAGES - 1) * RUNS_PER_WAVE < 64, "in-flight copies exceed vmcnt");
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st2[STAGES > 2 ? STAGE : 16];
@@ -542,67 +542,95 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   const int iters_per_group = GROUPED ? a.group / 128 : 1;
   const int64_t ngroups = GROUPED ? K / a.group : 1;
 
-#pragma unroll
-  for (int sidx = 0; sidx < STAGES - 1; ++sidx)
-    if (sidx < nkt) issue(sidx, stage(sidx));
-
   const int frow = lane & 15;
   const int fg = lane >> 4;
-  for (int kt0 = 0; kt0 < nkt; kt0 += STAGES) {
+  auto read_frags = [&](const uint8_t* As, i32x4 (&fa)[2][TM], uint4 (&fb)[TN]) {
+    const uint8_t* Bs = As + A_BYTES;
 #pragma unroll
-    for (int sidx = 0; sidx < STAGES; ++sidx) {
-      const int kt = kt0 + sidx;
-      if (kt < nkt) {
-        // Stage kt has landed once at most the later stages' runs are in flight.
-        if (kt + STAGES - 1 <= nkt)
-          wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
-        else
-          wait_vmcnt<0>();
-        stage_barrier();
-        if (kt + STAGES - 1 < nkt) issue(kt + STAGES - 1, stage((sidx + STAGES - 1) % STAGES));
-
-        const uint8_t* As = stage(sidx);
-        const uint8_t* Bs = As + A_BYTES;
-        uint4 fb[TN];
+    for (int j = 0; j < TN; ++j)
+      fb[j] = *reinterpret_cast<const uint4*>(Bs + ((((wn0 >> 4) + j) * 4 + fg) << 8) + (frow << 4));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        fa[h][i] = *reinterpret_cast<const i32x4*>(
+            As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
+  };
+  auto compute = [&](int kt, const i32x4 (&fa)[2][TM], const uint4 (&fb)[TN]) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      i32x4 opb[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          fb[j] = *reinterpret_cast<const uint4*>(Bs + ((((wn0 >> 4) + j) * 4 + fg) << 8) + (frow << 4));
-        i32x4 fa[2][TM];
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][i], opb[j], acc[i][j], 0, 0, 0);
+    }
+    if constexpr (GROUPED) {
+      if ((kt + 1) % iters_per_group == 0) {
+        const int64_t grp = (kt + 1) / iters_per_group - 1;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int j = 0; j < TN; ++j) {
+          int64_t n = n0 + wn0 + j * 16 + frow;
+          n = n < a.N ? n : a.N - 1;
+          const float sw = load_scale(a.sw, n * ngroups + grp, a.sw_f16);
 #pragma unroll
-          for (int i = 0; i < TM; ++i)
-            fa[h][i] = *reinterpret_cast<const i32x4*>(
-                As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
+          for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          i32x4 opb[TN];
-#pragma unroll
-          for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][i], opb[j], acc[i][j], 0, 0, 0);
-        }
-        if constexpr (GROUPED) {
-          if ((kt + 1) % iters_per_group == 0) {
-            const int64_t grp = (kt + 1) / iters_per_group - 1;
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-              int64_t n = n0 + wn0 + j * 16 + frow;
-              n = n < a.N ? n : a.N - 1;
-              const float sw = load_scale(a.sw, n * ngroups + grp, a.sw_f16);
-#pragma unroll
-              for (int i = 0; i < TM; ++i) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                  facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
-                acc[i][j] = i32x4{0, 0, 0, 0};
-              }
-            }
+            for (int r = 0; r < 4; ++r)
+              facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
+            acc[i][j] = i32x4{0, 0, 0, 0};
           }
         }
+      }
+    }
+  };
+
+  // Prologue: the first STAGES stages in flight, stage 0 visible, its
+  // fragments read.
+#pragma unroll
+  for (int sidx = 0; sidx < STAGES; ++sidx)
+    if (sidx < nkt) issue(sidx, stage(sidx));
+  if (nkt >= STAGES)
+    wait_vmcnt<(STAGES - 1) * RUNS_PER_WAVE>();
+  else
+    wait_vmcnt<0>();
+  stage_barrier();
+  i32x4 fa0[2][TM], fa1[2][TM];
+  uint4 fb0[TN], fb1[TN];
+  read_frags(stage(0), fa0, fb0);
+
+  // Iteration kt (stage buffer s = kt % STAGES): once stage kt + 1 has landed
+  // and the barrier has retired every wave's reads of stage kt, the buffer
+  // of stage kt is refilled with stage kt + STAGES and stage kt + 1's
+  // fragments are read into the other register set; stage kt's matrix
+  // instructions then run while those reads are in flight.
+  auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[2][TM], uint4 (&fbc)[TN], i32x4 (&fan)[2][TM],
+                     uint4 (&fbn)[TN]) {
+    // The reads are unconditional (on the last iteration they read a stale,
+    // in-bounds buffer) so that no branch joins between them and the matrix
+    // instructions, where the compiler would wait for them.
+    if (kt + STAGES <= nkt)
+      wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
+    read_frags(stage((sbuf + 1) % STAGES), fan, fbn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+    compute(kt, fac, fbc);
+  };
+  for (int kt0 = 0; kt0 < nkt; kt0 += 2 * STAGES) {
+#pragma unroll
+    for (int u = 0; u < 2 * STAGES; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nkt) {
+        if (u & 1)
+          iterate(kt, u % STAGES, fa1, fb1, fa0, fb0);
+        else
+          iterate(kt, u % STAGES, fa0, fb0, fa1, fb1);
       }
     }
   }
