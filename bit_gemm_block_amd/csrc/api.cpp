@@ -81,9 +81,10 @@ int check_group(int64_t K, int64_t g, bool pow2_only) {
   return W4A4_OK;
 }
 
-int plan_rotq(int64_t K, int64_t had_block, int64_t gsz, int max_lds, w4a4::RotqPlan* p) {
+int plan_rotq(int64_t M, int64_t K, int64_t had_block, int64_t gsz, int max_lds,
+              w4a4::RotqPlan* p) {
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  return w4a4::rotq_plan(K, log2b, gsz, max_lds, p) ? W4A4_OK : W4A4_ERR_UNSUPPORTED;
+  return w4a4::rotq_plan(M, K, log2b, gsz, max_lds, p) ? W4A4_OK : W4A4_ERR_UNSUPPORTED;
 }
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
@@ -137,7 +138,7 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot, int64_t M, in
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, ilog2(had_block), w4a4::ROTQ_ROTATE,
                                    K, false, x_rot, nullptr, nullptr, plan,
                                    static_cast<hipStream_t>(stream));
@@ -156,7 +157,7 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
   const int mode = codes_layout == W4A4_CODES_I8         ? w4a4::ROTQ_QUANT_I8
                    : codes_layout == W4A4_CODES_I8_TILED ? w4a4::ROTQ_QUANT_I8_TILED
@@ -182,7 +183,7 @@ int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, 
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   const int64_t gsz = w_group == 0 ? K : w_group;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(K, had_block, gsz, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(N, K, had_block, gsz, max_lds, &plan)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
   const int mode = w_layout == W4A4_WEIGHTS_TILED ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT;
   hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, mode, gsz,
@@ -267,7 +268,7 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);

@@ -172,7 +172,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   __syncthreads();
 
   // 2. Column pass over element bits [log2 R, log2 b).
-  const int cb = a.log2b - LOGR;
+  const int cb = min(a.log2b - LOGR, LOGR);
   if (cb > 0) {
     if (on) {
       const int cmask = (1 << cb) - 1;
@@ -191,6 +191,37 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       }
     }
     __syncthreads();
+  }
+  // Blocks larger than R^2 (segments spanning several waves): further column
+  // passes over element bits [lo, lo + LOGR), lo = 2 LOGR, 3 LOGR, ...  In the
+  // [L][R] view these are bits [o, o + cb2) of the row index i, o = lo - LOGR;
+  // a lane holds the 2^cb2 values of (R >> cb2) (column, other row bits)
+  // combinations.
+  if constexpr (L >= 128) {
+  for (int lo = 2 * LOGR; lo < a.log2b; lo += LOGR) {
+    const int cb2 = min(a.log2b - lo, LOGR);
+    const int o = lo - LOGR;
+    if (on) {
+      const int cmask = (1 << cb2) - 1;
+      const int omask = (1 << o) - 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int g = (r >> cb2) * L + lam;
+        const int rest = g >> LOGR;
+        const int i = ((rest >> o) << (o + cb2)) | ((r & cmask) << o) | (rest & omask);
+        v[r] = seg[lds_off<R>(i, g & (R - 1))];
+      }
+      fwht_bits_upto<0, LOGR>(v, cb2);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int g = (r >> cb2) * L + lam;
+        const int rest = g >> LOGR;
+        const int i = ((rest >> o) << (o + cb2)) | ((r & cmask) << o) | (rest & omask);
+        seg[lds_off<R>(i, g & (R - 1))] = v[r];
+      }
+    }
+    __syncthreads();
+  }
   }
 
   // 3. Row pass: lane lam holds elements [lam * R, lam * R + R) of the segment.
@@ -223,11 +254,14 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) m = fmaxf(m, fabsf(v[r]));
   const int gsz = a.gsz;
+  // Lanes sharing one scale: shuffles inside a wave, then an LDS atomic max
+  // when the group spans several waves or segments.
   const int span_lanes = (gsz < S ? gsz : S) / R;
-  for (int o = 1; o < span_lanes; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (gsz > S) {
+  const int span_wave = span_lanes < 64 ? span_lanes : 64;
+  for (int o = 1; o < span_wave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (gsz > S || span_lanes > 64) {
     const int slot = row_wg * (a.K / gsz) + kfirst / gsz;
-    if (valid && lam == 0) atomicMax(&slots[slot], __float_as_uint(m));
+    if (valid && (lam & (span_wave - 1)) == 0) atomicMax(&slots[slot], __float_as_uint(m));
     __syncthreads();
     if (on) m = __uint_as_float(slots[slot]);
   }
@@ -360,6 +394,10 @@ struct Shape { int L, R; };
 // Preference order: larger segments first, then more registers per lane.
 constexpr Shape kMenu[] = {{64, 64}, {32, 64}, {64, 32}, {16, 64}, {32, 32}, {64, 16}, {8, 64},
                            {16, 32}, {32, 16}, {8, 32},  {16, 16}, {8, 16},  {8, 8}};
+// Few rows: segments spread over up to four waves so that a row's transform
+// is shared by more lanes (blocks above R^2 take extra column passes).
+constexpr Shape kWideMenu[] = {{256, 16}, {128, 16}, {128, 32}, {256, 8}};
+constexpr int64_t kWideRows = 64;  // at most this many rows use the wide menu
 
 template <typename TIn>
 hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipStream_t st) {
@@ -373,38 +411,53 @@ hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipSt
   W4A4_ROTQ_CASE(64, 64) W4A4_ROTQ_CASE(32, 64) W4A4_ROTQ_CASE(64, 32) W4A4_ROTQ_CASE(16, 64)
   W4A4_ROTQ_CASE(32, 32) W4A4_ROTQ_CASE(64, 16) W4A4_ROTQ_CASE(8, 64) W4A4_ROTQ_CASE(16, 32)
   W4A4_ROTQ_CASE(32, 16) W4A4_ROTQ_CASE(8, 32) W4A4_ROTQ_CASE(16, 16) W4A4_ROTQ_CASE(8, 16)
-  W4A4_ROTQ_CASE(8, 8)
+  W4A4_ROTQ_CASE(8, 8) W4A4_ROTQ_CASE(256, 16) W4A4_ROTQ_CASE(128, 16) W4A4_ROTQ_CASE(128, 32)
+  W4A4_ROTQ_CASE(256, 8)
 #undef W4A4_ROTQ_CASE
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool rotq_plan(int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan) {
+namespace {
+
+bool try_shape(const Shape& sh, bool wide, int64_t K, int log2b, int64_t gsz, int max_lds,
+               RotqPlan* plan) {
   const int64_t b = int64_t{1} << log2b;
-  for (const Shape& sh : kMenu) {
-    const int64_t S = static_cast<int64_t>(sh.L) * sh.R;
-    if (K % S != 0 || b > S || b > static_cast<int64_t>(sh.R) * sh.R) continue;
-    if (gsz != K && (gsz < sh.R || (gsz & (gsz - 1)) != 0 || K % gsz != 0)) continue;
-    const int64_t segs_per_row = K / S;
-    if (segs_per_row * sh.L > 256) continue;
-    const int64_t slots_per_row = gsz > S ? K / gsz : 0;
-    const int64_t row_bytes = K * 4 + slots_per_row * 4;
-    int64_t rows = 256 / (segs_per_row * sh.L);
-    if (rows < 1) rows = 1;
-    while (rows > 1 && rows * row_bytes > max_lds) --rows;
-    if (rows * row_bytes > max_lds) continue;
-    const int64_t threads = ((rows * segs_per_row * sh.L + 63) / 64) * 64;
-    if (threads > 256) continue;
-    plan->L = sh.L;
-    plan->R = sh.R;
-    plan->segs_per_row = static_cast<int>(segs_per_row);
-    plan->rows_per_wg = static_cast<int>(rows);
-    plan->threads = static_cast<int>(threads);
-    plan->lds_bytes = static_cast<int>(rows * row_bytes);
-    plan->nslots = static_cast<int>(rows * slots_per_row);
-    return true;
+  const int64_t S = static_cast<int64_t>(sh.L) * sh.R;
+  if (K % S != 0 || b > S) return false;
+  if (!wide && b > static_cast<int64_t>(sh.R) * sh.R) return false;
+  if (gsz != K && (gsz < sh.R || (gsz & (gsz - 1)) != 0 || K % gsz != 0)) return false;
+  const int64_t segs_per_row = K / S;
+  if (segs_per_row * sh.L > 256) return false;
+  const int64_t span_lanes = (gsz < S ? gsz : S) / sh.R;
+  const int64_t slots_per_row = (gsz > S || span_lanes > 64) ? K / gsz : 0;
+  const int64_t row_bytes = K * 4 + slots_per_row * 4;
+  int64_t rows = 256 / (segs_per_row * sh.L);
+  if (rows < 1) rows = 1;
+  while (rows > 1 && rows * row_bytes > max_lds) --rows;
+  if (rows * row_bytes > max_lds) return false;
+  const int64_t threads = ((rows * segs_per_row * sh.L + 63) / 64) * 64;
+  if (threads > 256) return false;
+  plan->L = sh.L;
+  plan->R = sh.R;
+  plan->segs_per_row = static_cast<int>(segs_per_row);
+  plan->rows_per_wg = static_cast<int>(rows);
+  plan->threads = static_cast<int>(threads);
+  plan->lds_bytes = static_cast<int>(rows * row_bytes);
+  plan->nslots = static_cast<int>(rows * slots_per_row);
+  return true;
+}
+
+}  // namespace
+
+bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan) {
+  if (M <= kWideRows) {
+    for (const Shape& sh : kWideMenu)
+      if (try_shape(sh, true, K, log2b, gsz, max_lds, plan)) return true;
   }
+  for (const Shape& sh : kMenu)
+    if (try_shape(sh, false, K, log2b, gsz, max_lds, plan)) return true;
   return false;
 }
 

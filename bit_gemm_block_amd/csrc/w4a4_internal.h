@@ -20,7 +20,7 @@ struct RotqPlan {
 };
 
 // Chooses the segment shape for (K, b, group); returns false if none fits.
-bool rotq_plan(int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan);
+bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan);
 
 // ROTQ_QUANT_I8 writes one int8 code per byte, each group of 8 elements in
 // the order 0,2,4,6,1,3,5,7 (the K order of the GEMM's nibble widening): the

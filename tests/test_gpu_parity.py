@@ -55,7 +55,9 @@ def rotation_bound(x, b):
 @pytest.mark.parametrize("M,K,b,dt", [
     (16, 256, 256, "float32"), (5, 4096, 4096, "float16"), (33, 4096, 128, "float16"),
     (9, 14336, 128, "float16"), (3, 14336, 2048, "float16"), (7, 192, 64, "float32"),
-    (4, 1024, 2, "float16"), (2, 512, 512, "float32")])
+    (4, 1024, 2, "float16"), (2, 512, 512, "float32"), (8, 2048, 2048, "float16"),
+    (12, 8192, 4096, "float16"), (64, 4096, 1024, "float32"), (65, 4096, 4096, "float16"),
+    (1, 4096, 4096, "float32")])
 def test_hadamard_rotate_within_bound(M, K, b, dt):
     w = synth.small("r", M, K, 8, x_dtype=dt, n_outlier=2, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
@@ -235,7 +237,8 @@ def test_quantize_weight_fused_rotation(N, K, b, g):
 
 
 @pytest.mark.parametrize("M,K,b,dt", [(16, 256, 256, "float32"), (64, 4096, 4096, "float16"),
-                                      (48, 14336, 128, "float16")])
+                                      (48, 14336, 128, "float16"), (8, 8192, 4096, "float16"),
+                                      (5, 2048, 2048, "float16"), (100, 4096, 4096, "float16")])
 def test_quantize_act_fused_rotation(M, K, b, dt):
     w = synth.small("f", M, K, 8, x_dtype=dt, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
