@@ -89,6 +89,9 @@ int plan_rotq(int64_t M, int64_t K, int64_t had_block, int64_t gsz, int max_lds,
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
+// Weights at most this large are read ahead by decode-sized calls.
+constexpr int64_t kMaxPrefetchBytes = int64_t{64} << 20;
+
 struct WsLayout {
   size_t xq, sx, t, total;
 };
@@ -278,11 +281,31 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
   const bool f16 = x_dtype == W4A4_F16;
 
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  // Decode-sized calls fold the low-rank projection and a read of the
+  // weights (which the skinny GEMM then finds in cache) into the launch of
+  // the rotation kernel, whose few rows leave most of the chip idle.
+  w4a4::RotqExtras ex;
+  const bool fuse_lr = rank > 0 && f16 && M <= 16;
+  if (fuse_lr) {
+    ex.lr_at = At;
+    ex.lr_rank = static_cast<int>(rank);
+    ex.lr_t = t;
+  }
+  const bool skinny = M <= 32 && (w_group == 0 || w_group % 128 == 0);
+  const int64_t units = (N + 15) / 16;
+  const int64_t unit_bytes = 16 * (K / 2);
+  if (skinny && units * unit_bytes <= kMaxPrefetchBytes) {
+    ex.pf = wq;
+    ex.pf_unit = unit_bytes;
+    ex.pf_units = units;
+    ex.pf_last = tiled ? unit_bytes : (N - 16 * (units - 1)) * (K / 2);
+    ex.pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
+  }
   hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b,
                                    tiled ? w4a4::ROTQ_QUANT_I8_TILED : w4a4::ROTQ_QUANT_I8, K, false,
-                                   nullptr, xq, sx, plan, st);
+                                   nullptr, xq, sx, plan, st, &ex);
   if (e != hipSuccess) return hip_fail(e);
-  if (rank > 0) {
+  if (rank > 0 && !fuse_lr) {
     e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
     if (e != hipSuccess) return hip_fail(e);
   }

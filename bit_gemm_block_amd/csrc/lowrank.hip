@@ -12,6 +12,7 @@
 //
 // fp32 inputs: LDS-tiled float32 FMA, T written as float32.
 #include "w4a4_internal.h"
+#include "lowrank_rows.h"
 
 namespace w4a4 {
 namespace {
@@ -97,67 +98,15 @@ __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __
   }
 }
 
-// Few rows (M <= 16), fp16: one workgroup per column j of T.  Lane l of wave
-// w reads the 16 bytes at channel 8 (64 w + l) + 2048 c of X's rows and of
-// row j of At, so that every load instruction is one contiguous 1 KB run,
-// and accumulates x . a with fp16 pair dot products in float32.  Partial sums
-// are reduced across lanes and then across the four waves in a fixed order.
+// Few rows (M <= MR), fp16: one workgroup per column j of T (body in
+// lowrank_rows.h).
 template <int MR>
 __global__ void __launch_bounds__(256) lowrank_rows_kernel(const _Float16* __restrict__ x,
                                                           const _Float16* __restrict__ at,
                                                           int64_t M, int64_t K, int rank,
                                                           void* __restrict__ t, int pair_out) {
-  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-  __shared__ float red[4][MR];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int j = blockIdx.x;
-  const _Float16* arow = at + static_cast<int64_t>(j) * K;
-  float acc[MR];
-#pragma unroll
-  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
-#pragma unroll 2
-  for (int64_t k = 8 * tid; k < K; k += 2048) {
-    const half8 av = *reinterpret_cast<const half8*>(arow + k);
-    half8 xv[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-      xv[m] = m < M ? *reinterpret_cast<const half8*>(x + m * K + k) : half8{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const half2v xa = {xv[m][2 * p], xv[m][2 * p + 1]};
-        const half2v aa = {av[2 * p], av[2 * p + 1]};
-        acc[m] = __builtin_amdgcn_fdot2(xa, aa, acc[m], false);
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < MR; ++m) {
-    float v = acc[m];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    acc[m] = v;
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int m = 0; m < MR; ++m) red[wave][m] = acc[m];
-  }
-  __syncthreads();
-  if (tid < MR && tid < M) {
-    const float sum = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
-    const int64_t m = tid;
-    if (pair_out) {
-      const _Float16 hi = static_cast<_Float16>(sum);
-      const _Float16 lo = static_cast<_Float16>(sum - static_cast<float>(hi));
-      static_cast<_Float16*>(t)[m * rank + j] = hi;
-      static_cast<_Float16*>(t)[M * rank + m * rank + j] = lo;
-    } else {
-      static_cast<float*>(t)[m * rank + j] = sum;
-    }
-  }
+  __shared__ float red[4 * MR];
+  lowrank_rows_body<MR>(x, at, M, K, rank, t, pair_out, blockIdx.x, red);
 }
 
 constexpr int TR = 16;  // rows of X per workgroup (fp32 path)

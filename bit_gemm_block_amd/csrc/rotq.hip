@@ -31,6 +31,7 @@
 // and smaller ones give code 0 whatever their last bits; scales outside that
 // range take the IEEE division.
 #include "w4a4_internal.h"
+#include "lowrank_rows.h"
 
 #include <hip/hip_fp16.h>
 
@@ -109,7 +110,46 @@ struct RotqKArgs {
   int segs_per_row;
   int rows_per_wg;
   int nslots;
+  // Extra block roles after the rotation blocks (all zero/null when unused):
+  int nrot_blocks;        // blocks [0, nrot_blocks) rotate and quantize
+  const void* lr_at;      // then lr_rank blocks: column j of T = X . A (fp16, M <= 16)
+  int lr_rank;
+  void* lr_t;
+  const uint8_t* pf;      // then pf_blocks blocks read pf_units units of pf_unit bytes
+  int64_t pf_unit;        // (unit g is what the GEMM workgroup g will read)
+  int64_t pf_units;
+  int64_t pf_last;        // bytes of the last unit
+  int pf_blocks;
+  uint32_t pf_magic;      // the loaded words are folded and compared with this
 };
+
+// Reads the units g = x + 8 (p / 8 + t * (blocks / 8)) of the prefetch area,
+// where x is the XCD this block is assumed to run on (workgroups are placed
+// on the eight XCDs round-robin by index): the GEMM workgroup g runs on XCD
+// g mod 8, so its operand lands in that XCD's L2 and in the shared
+// last-level cache.  The loaded words are folded into a value that is
+// stored to LDS only if it equals a runtime constant, which keeps the loads.
+__device__ __forceinline__ void prefetch_role(const RotqKArgs& a, int p, int64_t launch_index,
+                                              uint32_t* sink) {
+  const int x = static_cast<int>(launch_index & 7);
+  const int per_xcd = a.pf_blocks / 8;
+  uint32_t fold = 0u;
+  for (int64_t g = x + 8 * static_cast<int64_t>(p / 8); g < a.pf_units; g += 8 * per_xcd) {
+    const int64_t bytes = g == a.pf_units - 1 ? a.pf_last : a.pf_unit;
+    const uint8_t* base = a.pf + g * a.pf_unit;
+    for (int64_t off0 = 0; off0 < bytes; off0 += 4 * 4096) {
+      uint4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t off = off0 + u * 4096 + 16 * threadIdx.x;
+        w[u] = off + 16 <= bytes ? *reinterpret_cast<const uint4*>(base + off) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) fold ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
+    }
+  }
+  if (fold == a.pf_magic) sink[0] = fold;
+}
 
 // Swizzled float offset of element (i, j) of a segment stored as [L][R].
 template <int R>
@@ -129,6 +169,19 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   static_assert(R >= 8 && R <= 64 && (R % V) == 0, "segment shape");
 
   extern __shared__ float lds[];
+  if (static_cast<int>(blockIdx.x) >= a.nrot_blocks) {
+    // Decode prologue roles (whole workgroups, so no barrier is split).
+    const int e = static_cast<int>(blockIdx.x) - a.nrot_blocks;
+    if (e < a.lr_rank) {
+      if constexpr (sizeof(TIn) == 2)
+        lowrank_rows_body<16>(static_cast<const _Float16*>(a.x),
+                              static_cast<const _Float16*>(a.lr_at), a.M, a.K, a.lr_rank, a.lr_t,
+                              1, e, lds);
+    } else {
+      prefetch_role(a, e - a.lr_rank, blockIdx.x, reinterpret_cast<uint32_t*>(lds));
+    }
+    return;
+  }
   const int tid = threadIdx.x;
   const int segs_wg = a.segs_per_row * a.rows_per_wg;
   const int seg_wg = tid / L;
@@ -401,7 +454,7 @@ constexpr int64_t kWideRows = 64;  // at most this many rows use the wide menu
 
 template <typename TIn>
 hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((M + p.rows_per_wg - 1) / p.rows_per_wg));
+  const dim3 grid(static_cast<unsigned>(ka.nrot_blocks + ka.lr_rank + ka.pf_blocks));
   const dim3 block(p.threads);
 #define W4A4_ROTQ_CASE(LL, RR)                                                        \
   if (p.L == LL && p.R == RR) {                                                     \
@@ -463,8 +516,8 @@ bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPl
 
 hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2b, int mode,
                        int64_t gsz, bool scale_f16, float* xrot, uint8_t* q, void* scale,
-                       const RotqPlan& plan, hipStream_t st) {
-  RotqKArgs ka;
+                       const RotqPlan& plan, hipStream_t st, const RotqExtras* ex) {
+  RotqKArgs ka{};
   ka.x = x;
   ka.M = M;
   ka.K = static_cast<int>(K);
@@ -479,6 +532,22 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.segs_per_row = plan.segs_per_row;
   ka.rows_per_wg = plan.rows_per_wg;
   ka.nslots = plan.nslots;
+  ka.nrot_blocks = static_cast<int>((M + plan.rows_per_wg - 1) / plan.rows_per_wg);
+  if (ex) {
+    if (ex->lr_rank > 0 && x_f16 && M <= 16) {
+      ka.lr_at = ex->lr_at;
+      ka.lr_rank = ex->lr_rank;
+      ka.lr_t = ex->lr_t;
+    }
+    if (ex->pf && ex->pf_units > 0 && ex->pf_blocks >= 8) {
+      ka.pf = ex->pf;
+      ka.pf_unit = ex->pf_unit;
+      ka.pf_units = ex->pf_units;
+      ka.pf_last = ex->pf_last;
+      ka.pf_blocks = ex->pf_blocks / 8 * 8;
+      ka.pf_magic = 0x9E3779B9u;
+    }
+  }
   if (x_f16) return launch_typed<_Float16>(ka, plan, M, st);
   return launch_typed<float>(ka, plan, M, st);
 }

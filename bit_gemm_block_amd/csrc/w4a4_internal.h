@@ -38,10 +38,27 @@ enum RotqMode {
 // x: [M, K] (f16 if x_f16 else f32).  mode ROTATE writes xrot [M, K] f32;
 // mode QUANT writes q [M, K/2] (QUANT_I8: q [M, K]) and one scale per group of
 // gsz elements (gsz == K: per row) as f32 or f16 (scale_f16).
+// Optional extra work in the same launch (decode prologue): the low-rank
+// projection t = x . A for M <= 16 and fp16 inputs (lr_rank workgroups,
+// written as the fp16 pair), and a read of the GEMM's weight operand in
+// pf_units units of pf_unit bytes (the last one pf_last bytes) by pf_blocks
+// workgroups (a multiple of 8), so that the GEMM finds it in cache.
+struct RotqExtras {
+  const void* lr_at = nullptr;
+  int lr_rank = 0;
+  void* lr_t = nullptr;
+  const uint8_t* pf = nullptr;
+  int64_t pf_unit = 0;
+  int64_t pf_units = 0;
+  int64_t pf_last = 0;
+  int pf_blocks = 0;
+};
+
 hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K,
                        int log2b, int mode, int64_t gsz, bool scale_f16,
                        float* xrot, uint8_t* q, void* scale,
-                       const RotqPlan& plan, hipStream_t st);
+                       const RotqPlan& plan, hipStream_t st,
+                       const RotqExtras* extras = nullptr);
 
 // ---- int4 GEMM (qgemm.hip) -------------------------------------------------
 // Low-rank epilogue kinds: none; fp16 (t = fp16 pair t_hi [M, r] followed by
