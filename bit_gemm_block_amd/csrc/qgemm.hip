@@ -89,7 +89,7 @@ __device__ __forceinline__ int a8_off(int r, int h, int g) {
 // column lane&15.
 template <int LRMODE>
 __device__ __forceinline__ f32x4 add_lowrank(const GemmArgs& a, f32x4 v, int64_t mblk, int64_t nblk,
-                                             int lane) {
+                                             int lane, int c_begin = 0) {
   if constexpr (LRMODE == LR_F16) {
     const int64_t mr = mblk + (lane & 15);  // operand row (A side)
     const int64_t nr = nblk + (lane & 15);  // operand row of Bt (B side)
@@ -98,7 +98,7 @@ __device__ __forceinline__ f32x4 add_lowrank(const GemmArgs& a, f32x4 v, int64_t
     const _Float16* tl = th + a.M * a.rank;
     const _Float16* bt = static_cast<const _Float16*>(a.B);
     const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = 0; c < a.rank; c += 32) {
+    for (int c = c_begin; c < a.rank; c += 32) {
       const int j = c + koff;
       const bool jok = j < a.rank;
       const half8 hi = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(th + mr * a.rank + j) : z;
@@ -122,6 +122,42 @@ __device__ __forceinline__ f32x4 add_lowrank(const GemmArgs& a, f32x4 v, int64_t
         }
       }
     }
+  }
+  return v;
+}
+
+// The first LR_PRE 32-wide rank chunks of the fp16 low-rank operands of one
+// 16x16 output block, loaded ahead of the main loop by the waves that run
+// the epilogue (so that these loads overlap the weight stream).
+constexpr int LR_PRE = 2;
+struct LowRankPre {
+  half8 hi[LR_PRE], lo[LR_PRE], bb[LR_PRE];
+};
+
+__device__ __forceinline__ void load_lowrank_pre(const GemmArgs& a, int64_t mblk, int64_t nblk,
+                                                 int lane, LowRankPre& p) {
+  const int64_t mr = mblk + (lane & 15);
+  const int64_t nr = nblk + (lane & 15);
+  const int koff = (lane >> 4) * 8;
+  const _Float16* th = static_cast<const _Float16*>(a.t);
+  const _Float16* tl = th + a.M * a.rank;
+  const _Float16* bt = static_cast<const _Float16*>(a.B);
+  const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < LR_PRE; ++q) {
+    const int j = q * 32 + koff;
+    const bool jok = j < a.rank;
+    p.hi[q] = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(th + mr * a.rank + j) : z;
+    p.lo[q] = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(tl + mr * a.rank + j) : z;
+    p.bb[q] = (jok && nr < a.N) ? *reinterpret_cast<const half8*>(bt + nr * a.rank + j) : z;
+  }
+}
+
+__device__ __forceinline__ f32x4 apply_lowrank_pre(const LowRankPre& p, f32x4 v) {
+#pragma unroll
+  for (int q = 0; q < LR_PRE; ++q) {
+    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.lo[q], p.bb[q], v, 0, 0, 0);
+    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.hi[q], p.bb[q], v, 0, 0, 0);
   }
   return v;
 }
@@ -717,6 +753,23 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
   const int64_t p_begin = npairs * wave / KW;
   const int64_t p_end = npairs * (wave + 1) / KW;
 
+  // The epilogue waves load their scales and low-rank operands first, so
+  // that these loads overlap the weight stream instead of following it.
+  float sx_pre[4] = {0.f, 0.f, 0.f, 0.f};
+  float sw_pre = 1.f;
+  LowRankPre lrp;
+  if (wave < MB && want_y) {
+    const int64_t mblk = wave * 16;
+    const int64_t n = n0 + (lane & 15);
+    if (!GROUPED && n < a.N) sw_pre = load_scale(a.sw, n, a.sw_f16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t m = mblk + (lane >> 4) * 4 + r;
+      sx_pre[r] = m < a.M ? a.sx[m] * (AI8 ? kInv16 : kInv256) : 0.f;
+    }
+    if constexpr (LRMODE == LR_F16) load_lowrank_pre(a, mblk, n0, lane, lrp);
+  }
+
   i32x4 acc[MB];
   f32x4 facc[GROUPED ? MB : 1];
   i32x4 full[GROUPED ? MB : 1];
@@ -837,15 +890,15 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int w = 1; w < KW; ++w) fsum += fred[w][b][lane];
       }
-      const int64_t n = n0 + (lane & 15);
-      const float swn = (GROUPED || n >= a.N) ? 1.f : load_scale(a.sw, n, a.sw_f16);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t m = mblk + (lane >> 4) * 4 + r;
-        const float sxm = m < a.M ? a.sx[m] * (AI8 ? kInv16 : kInv256) : 0.f;
-        yv[r] = GROUPED ? fsum[r] * sxm : static_cast<float>(total[r]) * (sxm * swn);
+      for (int r = 0; r < 4; ++r)
+        yv[r] = GROUPED ? fsum[r] * sx_pre[r] : static_cast<float>(total[r]) * (sx_pre[r] * sw_pre);
+      if constexpr (LRMODE == LR_F16) {
+        yv = apply_lowrank_pre(lrp, yv);
+        yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane, 32 * LR_PRE);
+      } else {
+        yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
       }
-      yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
     }
     store_block(a, mblk, n0, lane, total, yv, AI8 ? 4 : 8);
   }
