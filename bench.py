@@ -128,25 +128,11 @@ def time_graph(fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def time_eager(fn, steps: int, warmup: int) -> float:
-    """Seconds per launch of fn(i) issued back to back on the current stream."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    cur = torch.cuda.current_stream()
-    start.record(cur)
-    for i in range(steps):
-        fn(i)
-    end.record(cur)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / steps
-
-
 def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     """Average duration of each kernel of the path, launched alone with the
-    same arguments and code layout as inside qlinear_forward."""
+    same arguments and code layout as inside qlinear_forward: `steps`
+    launches replayed from one HIP graph, timed with events on the stream
+    they run on."""
     wl = layer.wl
     tiled = layer.w_layout == "tiled"
     lay = "i8_tiled" if tiled else "i8"
@@ -155,9 +141,9 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay)
     torch.cuda.synchronize()
     out = {}
-    out["rotq"] = time_eager(
+    out["rotq"] = time_graph(
         lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay), steps, warmup)
-    out["qgemm"] = time_eager(
+    out["qgemm"] = time_graph(
         lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
                                layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
                                layout=lay, w_layout=layer.w_layout),
