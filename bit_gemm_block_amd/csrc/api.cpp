@@ -89,6 +89,11 @@ int plan_rotq(int64_t M, int64_t K, int64_t had_block, int64_t gsz, int max_lds,
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
+// With tiled weights, the layer keeps its activation codes packed (4 bits,
+// the weights' tile layout): half the operand bytes the GEMM moves per step,
+// at the price of widening both operands in registers.
+constexpr bool kPackedTiledCodes = true;
+
 // Weights at most this large are read ahead by decode-sized calls.
 constexpr int64_t kMaxPrefetchBytes = int64_t{64} << 20;
 
@@ -106,7 +111,11 @@ WsLayout ws_layout(int64_t M, int64_t K, int64_t rank) {
 }
 
 bool layout_ok(int l) {
-  return l == W4A4_CODES_PACKED || l == W4A4_CODES_I8 || l == W4A4_CODES_I8_TILED;
+  return l == W4A4_CODES_PACKED || l == W4A4_CODES_I8 || l == W4A4_CODES_I8_TILED ||
+         l == W4A4_CODES_PACKED_TILED;
+}
+bool codes_tiled(int l) { return l == W4A4_CODES_I8_TILED || l == W4A4_CODES_PACKED_TILED; }
+bool codes_i8(int l) { return l == W4A4_CODES_I8 || l == W4A4_CODES_I8_TILED;
 }
 bool wlayout_ok(int l) { return l == W4A4_WEIGHTS_ROWMAJOR || l == W4A4_WEIGHTS_TILED; }
 
@@ -153,7 +162,7 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   if (!dtype_ok(x_dtype) || !layout_ok(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
-  if (codes_layout == W4A4_CODES_I8_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if (codes_tiled(codes_layout) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if (M == 0) return W4A4_OK;
   if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
@@ -162,9 +171,10 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
   w4a4::RotqPlan plan;
   if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  const int mode = codes_layout == W4A4_CODES_I8         ? w4a4::ROTQ_QUANT_I8
-                   : codes_layout == W4A4_CODES_I8_TILED ? w4a4::ROTQ_QUANT_I8_TILED
-                                                         : w4a4::ROTQ_QUANT;
+  const int mode = codes_layout == W4A4_CODES_I8              ? w4a4::ROTQ_QUANT_I8
+                   : codes_layout == W4A4_CODES_I8_TILED     ? w4a4::ROTQ_QUANT_I8_TILED
+                   : codes_layout == W4A4_CODES_PACKED_TILED ? w4a4::ROTQ_QUANT_TILED
+                                                             : w4a4::ROTQ_QUANT;
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, mode, K, false, nullptr, xq,
                                    x_scale, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
@@ -220,7 +230,7 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, c
   int s = check_group(K, w_group, false);
   if (s != W4A4_OK) return s;
   const bool tiled = w_layout == W4A4_WEIGHTS_TILED;
-  if (tiled != (codes_layout == W4A4_CODES_I8_TILED)) return W4A4_ERR_INVALID_ARG;
+  if (tiled != codes_tiled(codes_layout)) return W4A4_ERR_INVALID_ARG;
   if (tiled && (K % 128 != 0 || w_group % 128 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
@@ -236,7 +246,7 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, c
   g.M = M; g.N = N; g.K = K;
   g.y = y; g.acc = acc;
   g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
-  g.a_i8 = codes_layout != W4A4_CODES_PACKED;
+  g.a_i8 = codes_i8(codes_layout);
   g.tiled = tiled;
   hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
@@ -302,8 +312,10 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
     ex.pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
   }
   hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b,
-                                   tiled ? w4a4::ROTQ_QUANT_I8_TILED : w4a4::ROTQ_QUANT_I8, K, false,
-                                   nullptr, xq, sx, plan, st, &ex);
+                                   tiled ? (kPackedTiledCodes ? w4a4::ROTQ_QUANT_TILED
+                                                              : w4a4::ROTQ_QUANT_I8_TILED)
+                                         : w4a4::ROTQ_QUANT_I8,
+                                   K, false, nullptr, xq, sx, plan, st, &ex);
   if (e != hipSuccess) return hip_fail(e);
   if (rank > 0 && !fuse_lr) {
     e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
@@ -319,7 +331,7 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
   g.B = rank > 0 ? Bt : nullptr;
   g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
   g.rank = static_cast<int>(rank);
-  g.a_i8 = 1;
+  g.a_i8 = !(tiled && kPackedTiledCodes);
   g.tiled = tiled;
   e = w4a4::launch_qgemm(g, st);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);

@@ -468,13 +468,18 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED>
+template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
+  // APK: activation codes packed (4 bits) in the weights' tile layout, widened
+  // in registers like the weights; otherwise int8 codes.
+  static_assert(!APK || TILED, "packed activation codes come tiled");
   constexpr int WM = TM * 16, WN = TN * 16;
   constexpr int BM = 2 * WM, BN = 2 * WN;
-  constexpr int A_BYTES = BM * 128, B_BYTES = BN * 64;
+  constexpr int A_BYTES = BM * (APK ? 64 : 128), B_BYTES = BN * 64;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_RUNS = BM / 16 * 2, B_RUNS = BN / 16;
+  constexpr int A_RUNS = APK ? BM / 16 : BM / 16 * 2, B_RUNS = BN / 16;
+  constexpr float kInvA = APK ? kInv256 : kInv16;  // both operands widened: 256 * acc
+  constexpr int kShiftA = APK ? 8 : 4;
   constexpr int RUNS = A_RUNS + B_RUNS;
   static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
   static_assert(STAGES >= 2 && STAGES <= 8, "stages");
@@ -526,7 +531,13 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   for (int q = 0; q < RUNS_PER_WAVE; ++q) {
     const int run = wave + 4 * q;
     const int g = lane >> 4, rr = lane & 15;
-    if (run < A_RUNS) {
+    if (run < A_RUNS && APK) {
+      int64_t mb = m0 / 16 + run;
+      mb = mb < mblocks ? mb : mblocks - 1;
+      src[q] = a.xq + mb * nkt * 1024 + 16 * lane;
+      step[q] = 1024;
+      dst[q] = (run * 4) << 8;
+    } else if (run < A_RUNS) {
       const int blk = run >> 1, h = run & 1;
       if constexpr (TILED) {
         int64_t mb = m0 / 16 + blk;
@@ -585,12 +596,20 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
       fb[j] = *reinterpret_cast<const uint4*>(Bs + ((((wn0 >> 4) + j) * 4 + fg) << 8) + (frow << 4));
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
+    if constexpr (APK) {
+      // packed: fa[0][i] holds both K halves' nibbles of row block i
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        fa[h][i] = *reinterpret_cast<const i32x4*>(
-            As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
+        fa[0][i] = *reinterpret_cast<const i32x4*>(As + ((((wm0 >> 4) + i) * 4 + fg) << 8) +
+                                                   (frow << 4));
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[h][i] = *reinterpret_cast<const i32x4*>(
+              As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
+    }
   };
   auto compute = [&](int kt, const i32x4 (&fa)[2][TM], const uint4 (&fb)[TN]) {
 #pragma unroll
@@ -598,11 +617,19 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       i32x4 opb[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
+      i32x4 opa[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (APK)
+          opa[i] = h ? widen(fa[0][i][2], fa[0][i][3]) : widen(fa[0][i][0], fa[0][i][1]);
+        else
+          opa[i] = fa[h][i];
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[h][i], opb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], acc[i][j], 0, 0, 0);
     }
     if constexpr (GROUPED) {
       if ((kt + 1) % iters_per_group == 0) {
@@ -682,7 +709,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      sxr[i][r] = (want_y && m < a.M) ? a.sx[m] * kInv16 : 0.f;
+      sxr[i][r] = (want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -710,14 +737,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (want_y) yp[r * a.N] = yv[r];
-          if (!GROUPED && a.acc) ap[r * a.N] = acc[i][j][r] >> 4;
+          if (!GROUPED && a.acc) ap[r * a.N] = acc[i][j][r] >> kShiftA;
         }
       } else if (n_ok) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (mb + r < a.M) {
             if (want_y) a.y[(mb + r) * a.N + n] = yv[r];
-            if (!GROUPED && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> 4;
+            if (!GROUPED && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> kShiftA;
           }
         }
       }
@@ -732,7 +759,6 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 // step 1 the last 8, identically on both sides.
 template <int MB, int KW, bool GROUPED, int LRMODE, bool AI8, bool TILED>
 __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
-  static_assert(!TILED || AI8, "tiled weights pair with tiled int8 codes");
   constexpr int CH = 8;  // K pairs loaded per batch
   __shared__ i32x4 ired[KW][MB][64];
   __shared__ f32x4 fred[GROUPED ? KW : 1][GROUPED ? MB : 1][64];
@@ -796,9 +822,14 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int b = 0; b < MB; ++b) {
           const int64_t mb = b < (a.M + 15) / 16 ? b : (a.M + 15) / 16 - 1;
-          const uint8_t* xp = a.xq + (mb * npairs + p) * 2048 + 16 * lane;
-          xv[c][b][0] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
-          xv[c][b][AI8 ? 1 : 0] = ok ? *reinterpret_cast<const uint4*>(xp + 1024) : make_uint4(0, 0, 0, 0);
+          if constexpr (AI8) {  // 2 KB int8 tile
+            const uint8_t* xp = a.xq + (mb * npairs + p) * 2048 + 16 * lane;
+            xv[c][b][0] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
+            xv[c][b][AI8 ? 1 : 0] = ok ? *reinterpret_cast<const uint4*>(xp + 1024) : make_uint4(0, 0, 0, 0);
+          } else {  // 1 KB packed tile, the weights' layout
+            const uint8_t* xp = a.xq + (mb * npairs + p) * 1024 + 16 * lane;
+            xv[c][b][0] = ok ? *reinterpret_cast<const uint4*>(xp) : make_uint4(0, 0, 0, 0);
+          }
         }
       } else {
         const int64_t kb = p * 64 + g * 16;
@@ -930,17 +961,18 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles));
-#define W4A4_PIPE_CASE(G, LR, T)                                                                   \
-  if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T) {                             \
-    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T>), grid, dim3(256), 0, st, a);  \
-    return hipGetLastError();                                                                     \
+#define W4A4_PIPE_CASE(G, LR, T, P)                                                          \
+  if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T && (!a.a_i8) == P) {      \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P>), grid, dim3(256), 0, \
+                       st, a);                                                              \
+    return hipGetLastError();                                                               \
   }
-  W4A4_PIPE_CASE(false, LR_NONE, false) W4A4_PIPE_CASE(false, LR_F16, false)
-  W4A4_PIPE_CASE(false, LR_F32, false) W4A4_PIPE_CASE(true, LR_NONE, false)
-  W4A4_PIPE_CASE(true, LR_F16, false) W4A4_PIPE_CASE(true, LR_F32, false)
-  W4A4_PIPE_CASE(false, LR_NONE, true) W4A4_PIPE_CASE(false, LR_F16, true)
-  W4A4_PIPE_CASE(false, LR_F32, true) W4A4_PIPE_CASE(true, LR_NONE, true)
-  W4A4_PIPE_CASE(true, LR_F16, true) W4A4_PIPE_CASE(true, LR_F32, true)
+#define W4A4_PIPE_CASES(T, P)                                                    \
+  W4A4_PIPE_CASE(false, LR_NONE, T, P) W4A4_PIPE_CASE(false, LR_F16, T, P)       \
+  W4A4_PIPE_CASE(false, LR_F32, T, P) W4A4_PIPE_CASE(true, LR_NONE, T, P)        \
+  W4A4_PIPE_CASE(true, LR_F16, T, P) W4A4_PIPE_CASE(true, LR_F32, T, P)
+  W4A4_PIPE_CASES(false, false) W4A4_PIPE_CASES(true, false) W4A4_PIPE_CASES(true, true)
+#undef W4A4_PIPE_CASES
 #undef W4A4_PIPE_CASE
   return hipErrorInvalidValue;
 }
@@ -963,7 +995,8 @@ hipError_t launch_skinny_a(const GemmArgs& a, hipStream_t st) {
 
 template <int MB>
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
-  if (a.tiled) return launch_skinny_a<MB, true, true>(a, st);
+  if (a.tiled)
+    return a.a_i8 ? launch_skinny_a<MB, true, true>(a, st) : launch_skinny_a<MB, false, true>(a, st);
   return a.a_i8 ? launch_skinny_a<MB, true, false>(a, st) : launch_skinny_a<MB, false, false>(a, st);
 }
 

@@ -21,9 +21,12 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, F16 = 0, 1
-CODES_PACKED, CODES_I8, CODES_I8_TILED = 0, 1, 2
+CODES_PACKED, CODES_I8, CODES_I8_TILED, CODES_PACKED_TILED = 0, 1, 2, 3
 WEIGHTS_ROWMAJOR, WEIGHTS_TILED = 0, 1
-_LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8, "i8_tiled": CODES_I8_TILED}
+_LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8, "i8_tiled": CODES_I8_TILED,
+            "packed_tiled": CODES_PACKED_TILED}
+_TILED_CODES = (CODES_I8_TILED, CODES_PACKED_TILED)
+_PACKED_CODES = (CODES_PACKED, CODES_PACKED_TILED)
 _WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED}
 
 _lib: Optional[ctypes.CDLL] = None
@@ -128,14 +131,15 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
                       x_scale: Optional[torch.Tensor] = None,
                       layout: str = "packed") -> Tuple[torch.Tensor, torch.Tensor]:
     """Codes in layout "packed" ([M, K/2] nibbles), "i8" ([M, K] int8 in
-    the GEMM's K order) or "i8_tiled" ([pad16(M), K] in 2 KB tiles), and one
+    the GEMM's K order), "i8_tiled" ([pad16(M), K] in 2 KB tiles) or
+    "packed_tiled" ([pad16(M), K/2] in the weights' 1 KB tiles), and one
     float32 scale per row."""
     _dev(x, "x")
     M, K = x.shape
     lay = _LAYOUTS[layout]
     if xq is None:
-        rows = pad16(M) if lay == CODES_I8_TILED else M
-        xq = torch.empty((rows, K // 2 if lay == CODES_PACKED else K), dtype=torch.uint8,
+        rows = pad16(M) if lay in _TILED_CODES else M
+        xq = torch.empty((rows, K // 2 if lay in _PACKED_CODES else K), dtype=torch.uint8,
                          device=x.device)
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
@@ -193,9 +197,9 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
     if N is None:
         N = w_scale.shape[0] if w_scale is not None else wq.shape[0]
     K = 2 * wq.shape[1]
-    if xq.shape[1] != (K // 2 if lay == CODES_PACKED else K):
+    if xq.shape[1] != (K // 2 if lay in _PACKED_CODES else K):
         raise ValueError("xq and wq disagree on K")
-    if xq.shape[0] < (pad16(M) if lay == CODES_I8_TILED else M):
+    if xq.shape[0] < (pad16(M) if lay in _TILED_CODES else M):
         raise ValueError("xq has too few rows")
     if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
         raise ValueError("wq has too few rows")

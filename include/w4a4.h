@@ -79,7 +79,8 @@ typedef enum { W4A4_F32 = 0, W4A4_F16 = 1 } w4a4_dtype;
 typedef enum {
   W4A4_CODES_PACKED = 0,
   W4A4_CODES_I8 = 1,
-  W4A4_CODES_I8_TILED = 2
+  W4A4_CODES_I8_TILED = 2,
+  W4A4_CODES_PACKED_TILED = 3
 } w4a4_codes_layout;
 
 /* Tiled layouts (K a multiple of 128).  Rows are taken in blocks of 16 and K
@@ -96,9 +97,11 @@ typedef enum {
  *     1024 bytes at (b*(K/128) + t)*1024; inside it, for g in {0..3},
  *     r in {0..15}, the 16 bytes at (16g + r)*16 are the packed bytes
  *     [64t + 16g, +16) of row 16b + r.
+ *   W4A4_CODES_PACKED_TILED (activations, [ceil(M/16)*16, K/2] bytes): the
+ *     packed codes of W4A4_CODES_PACKED in the W4A4_WEIGHTS_TILED layout.
  * With these layouts every 1 KB of a GEMM operand tile is one contiguous
  * copy, which the strided row-major layouts cannot offer; tiled weights are
- * used with tiled int8 activation codes. */
+ * used with tiled activation codes (int8 or packed). */
 typedef enum { W4A4_WEIGHTS_ROWMAJOR = 0, W4A4_WEIGHTS_TILED = 1 } w4a4_weight_layout;
 
 /* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
@@ -168,8 +171,8 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M,
  * técnico" §3: 4-bit matrix multiplication in the linear layer).
  *   xq in codes_layout, x_scale [M] float32: activation codes and scales.
  *   wq in w_layout, w_scale [N] (w_group 0) or [N, K/w_group] in
- *   w_scale_dtype.  Tiled weights need W4A4_CODES_I8_TILED codes and a
- *   w_group of 0 or a multiple of 128.
+ *   w_scale_dtype.  Tiled weights need tiled codes (W4A4_CODES_I8_TILED or
+ *   W4A4_CODES_PACKED_TILED) and a w_group of 0 or a multiple of 128.
  *   w_group 0 or a multiple of 64 dividing K.
  *   y   [M, N] float32 output, or NULL:
  *         y[m,n] = x_scale[m] * sum_j w_scale[n,j] * acc_j[m,n]

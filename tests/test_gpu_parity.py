@@ -114,6 +114,19 @@ def test_quantize_act_i8_tiled_exact(M, K, b, dt):
     assert np.array_equal(real, untile_codes_i8(got, M))
 
 
+@pytest.mark.parametrize("M,K,b,dt", [(37, 4096, 4096, "float16"), (20, 14336, 128, "float16"),
+                                      (3, 256, 64, "float32"), (100, 1024, 1024, "float16")])
+def test_quantize_act_packed_tiled_exact(M, K, b, dt):
+    w = synth.small("qpt", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xr = O.rotate(X, b)
+    xq, sx = W.quantize_act_int4(dev(xr), 0, layout="packed_tiled")
+    assert tuple(xq.shape) == (W.pad16(M), K // 2)
+    pq, ps, _, _ = O.quantize_activation(xr, 0)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(untile_weights(host(xq), M), pq)
+
+
 def test_quantize_act_exact_unrotated_fp16_and_edge_rows():
     rng = np.random.default_rng(3)
     X = (rng.standard_normal((6, 512)) * 3).astype(np.float16)
@@ -312,7 +325,8 @@ def test_qgemm_dequant(M, N, K, g, sd, layout):
                                      (17, 33, 256, 0), (32, 4096, 4096, 128), (33, 70, 384, 128),
                                      (130, 260, 384, 0), (300, 129, 1024, 256),
                                      (1000, 6500, 256, 128), (2048, 4096, 4096, 0)])
-def test_qgemm_tiled_exact_and_dequant(M, N, K, g):
+@pytest.mark.parametrize("codes", ["i8_tiled", "packed_tiled"])
+def test_qgemm_tiled_exact_and_dequant(M, N, K, g, codes):
     rng = np.random.default_rng(M * 7 + N + K + g)
     qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
     qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
@@ -321,9 +335,10 @@ def test_qgemm_tiled_exact_and_dequant(M, N, K, g):
     sx = rng.uniform(0.01, 2.0, M).astype(np.float32)
     shape = (N,) if g == 0 else (N, K // g)
     sw = rng.uniform(1e-3, 0.05, shape).astype(np.float16)
-    y, acc = W.qgemm_w4a4(dev(tile_codes_i8(i8_from_codes(qx), rng)), dev(sx),
-                          dev(tile_weights(O.pack_int4(qw), rng)), dev(sw), g,
-                          want_y=True, want_acc=True, layout="i8_tiled", w_layout="tiled")
+    xin = (tile_codes_i8(i8_from_codes(qx), rng) if codes == "i8_tiled"
+           else tile_weights(O.pack_int4(qx), rng))
+    y, acc = W.qgemm_w4a4(dev(xin), dev(sx), dev(tile_weights(O.pack_int4(qw), rng)), dev(sw), g,
+                          want_y=True, want_acc=True, layout=codes, w_layout="tiled")
     assert np.array_equal(host(acc), O.int_gemm(qx, qw))
     accs = O.int_gemm(qx, qw) if g == 0 else O.int_gemm_groups(qx, qw, g)
     ref = O.epilogue(accs, sx, sw.astype(np.float32), None).astype(np.float64)
