@@ -588,6 +588,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   }
   const int iters_per_group = GROUPED ? a.group / 128 : 1;
   const int64_t ngroups = GROUPED ? K / a.group : 1;
+  extern __shared__ __attribute__((aligned(16))) uint8_t gsc[];  // grouped scales
 
   const int frow = lane & 15;
   const int fg = lane >> 4;
@@ -636,9 +637,9 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
         const int64_t grp = (kt + 1) / iters_per_group - 1;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          int64_t n = n0 + wn0 + j * 16 + frow;
-          n = n < a.N ? n : a.N - 1;
-          const float sw = load_scale(a.sw, n * ngroups + grp, a.sw_f16);
+          const int col = wn0 + j * 16 + frow;
+          const float sw = a.sw_f16 ? __half2float(reinterpret_cast<const __half*>(gsc)[grp * BN + col])
+                                    : reinterpret_cast<const float*>(gsc)[grp * BN + col];
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -650,6 +651,25 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       }
     }
   };
+
+  // Grouped scales: this tile's columns for every group, staged in LDS as
+  // [group][column] before any copy is in flight.  Read from global memory
+  // inside the loop they would make the compiler wait for every outstanding
+  // vector memory operation, the stage copies included.
+  if constexpr (GROUPED) {
+    const int esz = a.sw_f16 ? 2 : 4;
+    for (int e = tid; e < BN * ngroups; e += 256) {
+      const int col = e % BN;
+      const int64_t grp = e / BN;
+      int64_t n = n0 + col;
+      n = n < a.N ? n : a.N - 1;
+      if (esz == 2)
+        reinterpret_cast<__half*>(gsc)[e] = reinterpret_cast<const __half*>(a.sw)[n * ngroups + grp];
+      else
+        reinterpret_cast<float*>(gsc)[e] = reinterpret_cast<const float*>(a.sw)[n * ngroups + grp];
+    }
+    __syncthreads();
+  }
 
   // Prologue: the first STAGES stages in flight, stage 0 visible, its
   // fragments read.
@@ -961,10 +981,13 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles));
+  // Grouped: the tile's scales for all groups in dynamic LDS.
+  const size_t scale_lds =
+      a.group > 0 ? static_cast<size_t>(BN) * (a.K / a.group) * (a.sw_f16 ? 2 : 4) : 0;
 #define W4A4_PIPE_CASE(G, LR, T, P)                                                          \
   if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T && (!a.a_i8) == P) {      \
-    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P>), grid, dim3(256), 0, \
-                       st, a);                                                              \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P>), grid, dim3(256),    \
+                       scale_lds, st, a);                                                   \
     return hipGetLastError();                                                               \
   }
 #define W4A4_PIPE_CASES(T, P)                                                    \
