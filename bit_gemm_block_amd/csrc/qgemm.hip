@@ -1047,7 +1047,9 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   // int8 codes, whole 128-code iterations: the pipelined direct-to-LDS kernel
   // (the only one that reads tiled operands).
   if (a.tiled || (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0)) {
-    return launch_pipe<4, 4, 3>(ya, st);
+    // Grouped: a 64 x 32 wave tile, so that the float group accumulators fit
+    // beside the integer ones at two waves per SIMD.
+    return ya.group > 0 ? launch_pipe<4, 2, 3>(ya, st) : launch_pipe<4, 4, 3>(ya, st);
   }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
   if (a.group == 0 && a.M >= 256 && big_tiles >= 200) return launch_tiles<8, 4>(ya, st);
