@@ -26,12 +26,16 @@ What is computed, and where the pages fix it
 * Packing: two's-complement nibbles, element 2j in the low nibble of byte j.
 * Integer GEMM: acc[m, n] = sum_k qx[m, k] * qw[n, k], computed as a float64
   matmul of the integer codes, which is exact because every partial sum is an
-  integer of magnitude at most 64*K < 2^53.
+  integer of magnitude at most 127*8*K < 2^53 (8-bit activation codes included).
 * Low-rank term: the single low-rank compensation added to the 4-bit product
   (SERQ page, "Resumen técnico" §2 item 2).  Written as (X @ A) @ B in float64
   on the unrotated input as given.
 * Epilogue: Y = s_x[m] * s_w[n] * acc[m, n] (or the sum over weight groups)
   + low-rank term, in float64, rounded once to float32.
+* W4A8 layers: the layers a phase-aware policy keeps at 8-bit activations
+  while the weights stay 4-bit (DynamicPTQ page, "Metodología" §2).  The
+  same rotation and the same per-token symmetric absmax rule with qmax 127:
+  s = a / 127, q = clamp(rint(x / s), -127, 127).
 
 Parity pins for every function live in ``tests/test_oracle_*.py``.
 """
@@ -110,30 +114,30 @@ def codes_against_scale(v32: np.ndarray, s32) -> np.ndarray:
     return np.clip(np.rint(quot), -QMAX, QMAX).astype(np.int8)
 
 
-def quantize_act(xrot32: np.ndarray):
-    """Per-token symmetric int4 of already-rotated float32 activations.
+def quantize_act(xrot32: np.ndarray, qmax: int = QMAX):
+    """Per-token symmetric quantization of already-rotated float32
+    activations: int4 (qmax 7) or, for W4A8 layers, int8 (qmax 127).
 
-    Returns (codes int8 [M,K] in [-7,7], scales float32 [M])."""
+    Returns (codes int8 [M,K] in [-qmax,qmax], scales float32 [M])."""
     xrot32 = np.asarray(xrot32, dtype=np.float32)
-    M, K = xrot32.shape
-    s = _row_scales(xrot32)
-    return _codes_rows(xrot32, s), s
+    s = _row_scales(xrot32, qmax)
+    return _codes_rows(xrot32, s, qmax), s
 
 
-def _row_scales(v32: np.ndarray) -> np.ndarray:
-    """absmax_scale applied to every row of a 2-D float32 array."""
+def _row_scales(v32: np.ndarray, qmax: int = QMAX) -> np.ndarray:
+    """absmax / qmax in float32 for every row of a 2-D float32 array."""
     if v32.shape[1] == 0:
         return np.zeros(v32.shape[0], np.float32)
     a = np.max(np.abs(v32), axis=1).astype(np.float32)
-    return (a / np.float32(QMAX)).astype(np.float32)
+    return (a / np.float32(qmax)).astype(np.float32)
 
 
-def _codes_rows(v32: np.ndarray, s32: np.ndarray) -> np.ndarray:
+def _codes_rows(v32: np.ndarray, s32: np.ndarray, qmax: int = QMAX) -> np.ndarray:
     """codes_against_scale applied to every row with its own float32 scale."""
     s32 = np.asarray(s32, np.float32)
     safe = np.where(s32 == 0, np.float32(1), s32).astype(np.float32)
     quot = (v32 / safe[:, None]).astype(np.float32)
-    q = np.clip(np.rint(quot), -QMAX, QMAX).astype(np.int8)
+    q = np.clip(np.rint(quot), -qmax, qmax).astype(np.int8)
     q[s32 == 0, :] = 0
     return q
 
@@ -244,19 +248,21 @@ def prepare_weight(W: np.ndarray, had_block: int, group: int, scale_dtype: str):
     return pack_int4(q), s, q
 
 
-def quantize_activation(X: np.ndarray, had_block: int):
+def quantize_activation(X: np.ndarray, had_block: int, qmax: int = QMAX):
     """Rotate (had_block > 1) and quantize per token.
 
-    Returns (packed uint8 [M, K/2], scales float32 [M], codes, rotated fp32)."""
+    Returns (packed uint8 [M, K/2] (None for 8-bit codes), scales float32
+    [M], codes, rotated fp32)."""
     xrot = rotate(X, had_block) if had_block > 1 else np.asarray(X, np.float32)
-    q, s = quantize_act(xrot)
-    return pack_int4(q), s, q, xrot
+    q, s = quantize_act(xrot, qmax)
+    return (pack_int4(q) if qmax <= 7 else None), s, q, xrot
 
 
 def qlinear_forward(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.ndarray,
-                    had_block: int, group: int, A=None, B=None) -> np.ndarray:
-    """The quantized forward Y [M, N] float32."""
-    _, s_x, qx, _ = quantize_activation(X, had_block)
+                    had_block: int, group: int, A=None, B=None, act_bits: int = 4) -> np.ndarray:
+    """The quantized forward Y [M, N] float32; act_bits 8 is the W4A8 layer."""
+    qmax = QMAX if act_bits == 4 else 127
+    _, s_x, qx, _ = quantize_activation(X, had_block, qmax)
     qw = unpack_int4(wq_packed)
     if group == 0:
         acc = int_gemm(qx, qw)
