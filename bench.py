@@ -74,10 +74,10 @@ class Layer:
         self.ws = torch.empty((need,), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
-    def forward(self, i: int = 0):
+    def forward(self, i: int = 0, act_bits: int = 4):
         wq, ws, A, B = self.sets[i % len(self.sets)]
         W.qlinear_forward(self.x, wq, ws, self.wl.had_block, self.wl.w_group, A, B,
-                          y=self.y, workspace=self.ws, w_layout=self.w_layout)
+                          y=self.y, workspace=self.ws, w_layout=self.w_layout, act_bits=act_bits)
 
     def algorithmic_bytes(self) -> int:
         wl = self.wl
@@ -259,6 +259,8 @@ def main() -> int:
     log(f"prefill: {pre.wl.name} timing {args.steps} steps")
     t_step = time_graph(pre.forward, args.steps, args.warmup)
     kt = kernel_times(pre, args.steps, args.warmup)
+    # W4A8 layers (8-bit activations beside the 4-bit weights), same workload.
+    t_step8 = time_graph(lambda i: pre.forward(i, act_bits=8), args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
     rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K + 4 * pre.wl.M  # X in, int8 codes + scales out
@@ -278,11 +280,14 @@ def main() -> int:
         kd = kernel_times(dec, args.steps, args.warmup)
         gbs = dec.algorithmic_bytes() / t_dec / 1e9
         log(f"decode: {t_dec * 1e6:.2f} us/step, {gbs:.0f} GB/s")
+        t_dec8 = time_graph(lambda i: dec.forward(i, act_bits=8), args.steps, args.warmup)
         decode = {
             "metric": "W4A4 qlinear HBM GB/s (M=8)", "value": gbs, "unit": "GB/s",
             "ms_per_step": t_dec * 1e3, "frac_of_hbm": gbs / PEAK_HBM_GBS,
             "bytes_per_step": dec.algorithmic_bytes(), "weight_copies": copies,
             "kernels_us": {k: v * 1e6 for k, v in kd.items()},
+            "w4a8": {"value": dec.algorithmic_bytes() / t_dec8 / 1e9, "unit": "GB/s",
+                     "ms_per_step": t_dec8 * 1e3},
             "config": {"workload": dec.wl.name, "M": dec.wl.M, "N": dec.wl.N, "K": dec.wl.K,
                        "had_block": dec.wl.had_block, "w_group": dec.wl.w_group,
                        "rank": dec.wl.rank},
@@ -319,6 +324,8 @@ def main() -> int:
                      "traffic": read_traffic(gemm_bytes(pre.wl))},
         "kernels_us": {k: v * 1e6 for k, v in kt.items()},
         "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,
+        "w4a8": {"metric": "W4A8 qlinear TOPS (M=2048), K=N=4096", "value": pre.ops() / t_step8 / 1e12,
+                 "unit": "TOP/s", "ms_per_step": t_step8 * 1e3},
         "decode": decode,
         "cpu_baseline": cpu,
     }

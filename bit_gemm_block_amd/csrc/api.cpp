@@ -157,9 +157,12 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot, int64_t M, in
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
-int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
-                           uint8_t* xq, int codes_layout, float* x_scale, void* stream) {
+namespace {
+
+int quantize_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                      uint8_t* xq, int codes_layout, float* x_scale, void* stream, int qmax) {
   if (!dtype_ok(x_dtype) || !layout_ok(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
+  if (qmax != 7 && !codes_i8(codes_layout)) return W4A4_ERR_INVALID_ARG;  // 8-bit codes
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if (codes_tiled(codes_layout) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
@@ -175,9 +178,23 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int
                    : codes_layout == W4A4_CODES_I8_TILED     ? w4a4::ROTQ_QUANT_I8_TILED
                    : codes_layout == W4A4_CODES_PACKED_TILED ? w4a4::ROTQ_QUANT_TILED
                                                              : w4a4::ROTQ_QUANT;
+  w4a4::RotqExtras ex;
+  ex.qmax = qmax;
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, mode, K, false, nullptr, xq,
-                                   x_scale, plan, static_cast<hipStream_t>(stream));
+                                   x_scale, plan, static_cast<hipStream_t>(stream), &ex);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                           uint8_t* xq, int codes_layout, float* x_scale, void* stream) {
+  return quantize_act_impl(x, x_dtype, M, K, had_block, xq, codes_layout, x_scale, stream, 7);
+}
+
+int w4a4_quantize_act_int8(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                           uint8_t* xq, int codes_layout, float* x_scale, void* stream) {
+  return quantize_act_impl(x, x_dtype, M, K, had_block, xq, codes_layout, x_scale, stream, 127);
 }
 
 int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, int64_t had_block,
@@ -257,10 +274,13 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
   return ws_layout(M, K, rank).total;
 }
 
-int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+namespace {
+
+int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
                          int64_t had_block, int64_t w_group, const void* At, const void* Bt,
-                         int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
+                         int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream,
+                  int qmax) {
   if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok(w_layout) || M < 0 || N < 0 ||
       rank < 0)
     return W4A4_ERR_INVALID_ARG;
@@ -295,6 +315,9 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
   // weights (which the skinny GEMM then finds in cache) into the launch of
   // the rotation kernel, whose few rows leave most of the chip idle.
   w4a4::RotqExtras ex;
+  ex.qmax = qmax;
+  // 4-bit codes go packed into the tiled GEMM; 8-bit codes stay int8.
+  const bool packed_codes = tiled && kPackedTiledCodes && qmax == 7;
   const bool fuse_lr = rank > 0 && f16 && M <= 16;
   if (fuse_lr) {
     ex.lr_at = At;
@@ -312,8 +335,8 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
     ex.pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
   }
   hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b,
-                                   tiled ? (kPackedTiledCodes ? w4a4::ROTQ_QUANT_TILED
-                                                              : w4a4::ROTQ_QUANT_I8_TILED)
+                                   tiled ? (packed_codes ? w4a4::ROTQ_QUANT_TILED
+                                                         : w4a4::ROTQ_QUANT_I8_TILED)
                                          : w4a4::ROTQ_QUANT_I8,
                                    K, false, nullptr, xq, sx, plan, st, &ex);
   if (e != hipSuccess) return hip_fail(e);
@@ -331,10 +354,28 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
   g.B = rank > 0 ? Bt : nullptr;
   g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
   g.rank = static_cast<int>(rank);
-  g.a_i8 = !(tiled && kPackedTiledCodes);
+  g.a_i8 = !packed_codes;
   g.tiled = tiled;
   e = w4a4::launch_qgemm(g, st);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+}  // namespace
+
+int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+                         const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
+                         int64_t had_block, int64_t w_group, const void* At, const void* Bt,
+                         int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  return qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
+                      w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 7);
+}
+
+int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+                         const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
+                         int64_t had_block, int64_t w_group, const void* At, const void* Bt,
+                         int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
+  return qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
+                      w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
 }
 
 }  // extern "C"

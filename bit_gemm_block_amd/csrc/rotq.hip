@@ -4,7 +4,9 @@
 // steps 2-3): every contiguous block of b channels of a row is multiplied by
 // the Sylvester Hadamard matrix (first row all ones) scaled by 1/sqrt(b).
 // The quantizer is the per-token (or per weight group) symmetric int4 absmax
-// quantizer of SERQ's 4-bit path (SERQ page, "Resumen técnico" §1-2).
+// quantizer of SERQ's 4-bit path (SERQ page, "Resumen técnico" §1-2), or its
+// 8-bit form (qmax 127) for the activations of W4A8 layers (DynamicPTQ page,
+// "Metodología" §2).
 //
 // Work decomposition.  A row of K elements is cut into segments of S = L*R
 // elements; L consecutive lanes own a segment and every lane keeps R float32
@@ -104,6 +106,7 @@ struct RotqKArgs {
   int mode;          // RotqMode
   int gsz;           // elements per scale group (K = one scale per row)
   int scale_f16;
+  float fqmax;       // largest code: 7 (int4) or 127 (int8 activations)
   float* xrot;
   uint8_t* q;
   void* scale;
@@ -321,7 +324,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 
   // 5. Scale: s = max|x~| / 7 with max|x~| = RN(max|y| * rs).
   const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, 7.0f);
+  const float s = __fdiv_rn(amax, a.fqmax);
   float s_eff = s;
   __half s_h = __float2half_rn(s);
   if (a.scale_f16) s_eff = __half2float(s_h);
@@ -348,14 +351,14 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
       q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
       const float u = q + kMagic;
-      code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - 7.0f, kMagic + 7.0f));
+      code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
     }
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float xt = v[r] * a.rs;
       float qf = rintf(__fdiv_rn(xt, s_eff));
-      qf = fminf(fmaxf(qf, -7.0f), 7.0f);
+      qf = fminf(fmaxf(qf, -a.fqmax), a.fqmax);
       code[r] = static_cast<uint32_t>(static_cast<int>(qf));
     }
   }
@@ -526,6 +529,7 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.mode = mode;
   ka.gsz = static_cast<int>(gsz);
   ka.scale_f16 = scale_f16 ? 1 : 0;
+  ka.fqmax = (ex && ex->qmax == 127) ? 127.0f : 7.0f;
   ka.xrot = xrot;
   ka.q = q;
   ka.scale = scale;

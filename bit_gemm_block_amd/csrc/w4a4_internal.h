@@ -38,12 +38,14 @@ enum RotqMode {
 // x: [M, K] (f16 if x_f16 else f32).  mode ROTATE writes xrot [M, K] f32;
 // mode QUANT writes q [M, K/2] (QUANT_I8: q [M, K]) and one scale per group of
 // gsz elements (gsz == K: per row) as f32 or f16 (scale_f16).
-// Optional extra work in the same launch (decode prologue): the low-rank
+// Options: the code range (qmax), and optional extra work in the same launch
+// (decode prologue): the low-rank
 // projection t = x . A for M <= 16 and fp16 inputs (lr_rank workgroups,
 // written as the fp16 pair), and a read of the GEMM's weight operand in
 // pf_units units of pf_unit bytes (the last one pf_last bytes) by pf_blocks
 // workgroups (a multiple of 8), so that the GEMM finds it in cache.
 struct RotqExtras {
+  int qmax = 7;  // 127: 8-bit activation codes (int8 code modes only)
   const void* lr_at = nullptr;
   int lr_rank = 0;
   void* lr_t = nullptr;

@@ -40,6 +40,7 @@ _SIGS = {
     "w4a4_last_hip_error": (_INT, []),
     "w4a4_hadamard_rotate": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P]),
     "w4a4_quantize_act_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
+    "w4a4_quantize_act_int8": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
     "w4a4_quantize_weight_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _INT,
                                          _P]),
     "w4a4_lowrank_project": (_INT, [_P, _INT, _P, _I64, _I64, _I64, _P, _P]),
@@ -47,6 +48,8 @@ _SIGS = {
                                _P]),
     "w4a4_qlinear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
     "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
+                                    _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "w4a8_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
 }
 
@@ -80,7 +83,7 @@ def header_functions() -> list[str]:
     """Names of the functions include/w4a4.h declares."""
     with open(HEADER) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(w4a4_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(w4a[48]_\w+)\s*\(", text, re.M)))
 
 
 def pad16(n: int) -> int:
@@ -144,6 +147,24 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
     _check("quantize_act_int4", lib().w4a4_quantize_act_int4(
+        _ptr(x), _dt(x), M, K, had_block, _ptr(xq), lay, _ptr(x_scale), _stream(x)))
+    return xq, x_scale
+
+
+def quantize_act_int8(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor] = None,
+                      x_scale: Optional[torch.Tensor] = None,
+                      layout: str = "i8") -> Tuple[torch.Tensor, torch.Tensor]:
+    """8-bit activation codes (|q| <= 127) of a W4A8 layer, in layout "i8"
+    ([M, K]) or "i8_tiled" ([pad16(M), K]), and one float32 scale per row."""
+    _dev(x, "x")
+    M, K = x.shape
+    lay = _LAYOUTS[layout]
+    if xq is None:
+        xq = torch.empty((pad16(M) if lay in _TILED_CODES else M, K), dtype=torch.uint8,
+                         device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
+    _check("quantize_act_int8", lib().w4a4_quantize_act_int8(
         _ptr(x), _dt(x), M, K, had_block, _ptr(xq), lay, _ptr(x_scale), _stream(x)))
     return xq, x_scale
 
@@ -222,10 +243,12 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
                     w_group: int, At: Optional[torch.Tensor] = None,
                     Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None,
-                    w_layout: str = "rowmajor") -> torch.Tensor:
+                    w_layout: str = "rowmajor", act_bits: int = 4) -> torch.Tensor:
     """Y = dequant(int4 GEMM(rotate+quantize(x), wq)) + x . A . B, with the
     low-rank factors given transposed: At [rank, K], Bt [N, rank].  N is
-    w_scale's length."""
+    w_scale's length.  act_bits 8 runs the W4A8 layer."""
+    if act_bits not in (4, 8):
+        raise ValueError("act_bits must be 4 or 8")
     _dev(x, "x")
     _dev(wq, "wq")
     _dev(w_scale, "w_scale")
@@ -247,7 +270,8 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
     need = qlinear_workspace_size(M, N, K, rank)
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
-    _check("qlinear_forward", lib().w4a4_qlinear_forward(
+    fwd = lib().w4a4_qlinear_forward if act_bits == 4 else lib().w4a8_qlinear_forward
+    _check("qlinear_forward", fwd(
         _ptr(x), _dt(x), _ptr(wq), wl, _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
         _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
     return y

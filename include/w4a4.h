@@ -141,6 +141,20 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
                            float* x_scale, void* stream);
 
 /*
+ * 8-bit form of the activation quantizer, for W4A8 layers: the layers a
+ * phase-aware mixed-precision policy keeps at 8-bit activations while the
+ * weights stay 4-bit (DynamicPTQ page, "Metodología" §2).  Same rotation and
+ * rule as w4a4_quantize_act_int4 with the code range [-127, 127]:
+ * s = max|x~| / 127, q = clamp(rint(x~ / s), -127, 127).
+ *   codes_layout must be W4A4_CODES_I8 or W4A4_CODES_I8_TILED (one signed
+ *   code per byte, in those layouts' byte order); other layouts return
+ *   W4A4_ERR_INVALID_ARG.  The codes feed w4a4_qgemm_w4a4 unchanged.
+ */
+int w4a4_quantize_act_int8(const void* x, int x_dtype, int64_t M, int64_t K,
+                           int64_t had_block, uint8_t* xq, int codes_layout,
+                           float* x_scale, void* stream);
+
+/*
  * Offline weight preparation: rotation (had_block > 1) and symmetric
  * round-to-nearest int4 (DynamicPTQ page, "Resultados": RTN weights).
  *   w        [N, K] in dtype w_dtype.
@@ -170,6 +184,8 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M,
  * int4 x int4 GEMM with the dequantizing epilogue (SERQ page, "Resumen
  * técnico" §3: 4-bit matrix multiplication in the linear layer).
  *   xq in codes_layout, x_scale [M] float32: activation codes and scales.
+ *   The int8 layouts also carry the 8-bit codes of w4a4_quantize_act_int8
+ *   (|code| <= 127; exact for K <= 16384).
  *   wq in w_layout, w_scale [N] (w_group 0) or [N, K/w_group] in
  *   w_scale_dtype.  Tiled weights need tiled codes (W4A4_CODES_I8_TILED or
  *   W4A4_CODES_PACKED_TILED) and a w_group of 0 or a multiple of 128.
@@ -208,6 +224,19 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
  *   not matter.
  */
 int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
+                         int w_layout, const void* w_scale, int w_scale_dtype,
+                         int64_t M, int64_t N, int64_t K, int64_t had_block,
+                         int64_t w_group, const void* At, const void* Bt,
+                         int64_t rank, float* y, void* workspace,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * The W4A8 layer (DynamicPTQ page, "Metodología" §2): w4a4_qlinear_forward
+ * with 8-bit per-token activation codes (w4a4_quantize_act_int8's rule) on
+ * the same 4-bit weights, GEMM and epilogue.  Arguments, layouts, workspace
+ * and errors as w4a4_qlinear_forward.
+ */
+int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          int w_layout, const void* w_scale, int w_scale_dtype,
                          int64_t M, int64_t N, int64_t K, int64_t had_block,
                          int64_t w_group, const void* At, const void* Bt,

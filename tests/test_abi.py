@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -54,6 +54,28 @@ def test_quantize_act_argument_errors(lib):
     assert f(Q, W.F16, 4, 256, 0, P, L, P, None) == W.ERR_MISALIGNED
     assert f(P, W.F16, 4, 256, 0, P, L, Q, None) == W.ERR_MISALIGNED
     assert f(None, W.F16, 0, 256, 64, None, L, None, None) == W.OK         # empty: no-op
+
+
+def test_int8_activation_quantizer_argument_errors(lib):
+    f = lib.w4a4_quantize_act_int8
+    assert f(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P, None) == W.ERR_INVALID_ARG         # 4-bit layout
+    assert f(P, W.F16, 4, 256, 0, P, W.CODES_PACKED_TILED, P, None) == W.ERR_INVALID_ARG
+    assert f(P, W.F16, 4, 192, 0, P, W.CODES_I8_TILED, P, None) == W.ERR_UNSUPPORTED       # K % 128
+    assert f(P, W.F16, 4, 256, 3, P, W.CODES_I8, P, None) == W.ERR_UNSUPPORTED             # b
+    assert f(Q, W.F16, 4, 256, 0, P, W.CODES_I8, P, None) == W.ERR_MISALIGNED
+    assert f(None, W.F16, 0, 256, 0, None, W.CODES_I8, None, None) == W.OK
+
+
+def test_w4a8_forward_argument_errors(lib):
+    f = lib.w4a8_qlinear_forward
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 256, 8)
+    args = [P, W.F16, P, 0, P, W.F16, 16, 32, 256, 256, 0, P, P, 8, P, P, need, None]
+    bad = list(args); bad[11] = None
+    assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[16] = need - 1
+    assert f(*bad) == W.ERR_WORKSPACE
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == W.OK
 
 
 def test_rotate_and_weight_argument_errors(lib):

@@ -445,3 +445,106 @@ def test_qlinear_empty_is_noop():
                             torch.ones(16, dtype=torch.float16, device=DEV), 256, 0, y=y,
                             workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert out.shape == (0, 16)
+
+
+# --------------------------------------------------------------------------
+# W4A8 layers: 8-bit activations (qmax 127) beside the 4-bit weights
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("layout", ["i8", "i8_tiled"])
+@pytest.mark.parametrize("M,K,b,dt", [(37, 4096, 4096, "float16"), (20, 14336, 128, "float16"),
+                                      (3, 256, 64, "float32"), (130, 1024, 1024, "float16")])
+def test_quantize_act_int8_exact_on_oracle_rotation(M, K, b, dt, layout):
+    w = synth.small("q8b", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xr = O.rotate(X, b)
+    xq, sx = W.quantize_act_int8(dev(xr), 0, layout=layout)
+    _, ps, pc, _ = O.quantize_activation(xr, 0, qmax=127)
+    assert np.array_equal(host(sx), ps)
+    got = host(xq)
+    if layout == "i8_tiled":
+        got = untile_codes_i8(got, M)
+    assert np.array_equal(codes_from_i8(got), pc)
+
+
+def test_quantize_act_int8_ties_and_extremes():
+    f = np.float32
+    rows = []
+    for a in (127.0, 3.0, 1e-30, 5e30):
+        s = f(f(a) / f(127))
+        row = [f(a)]
+        for n in (0, 1, 2, 61, 62, 125, 126):
+            xv = f((n + 0.5) * float(s))
+            for _ in range(3):
+                row += [xv, -xv]
+                xv = np.nextafter(xv, f(np.inf), dtype=np.float32)
+        rows.append((row + [f(0)] * 256)[:256])
+    X = np.array(rows, np.float32)
+    xq, sx = W.quantize_act_int8(dev(X), 0)
+    _, ps, pc, _ = O.quantize_activation(X, 0, qmax=127)
+    assert np.array_equal(host(sx), ps)
+    assert np.array_equal(codes_from_i8(host(xq)), pc)
+
+
+@pytest.mark.parametrize("M,K,b", [(64, 4096, 4096), (48, 14336, 128), (8, 4096, 4096)])
+def test_quantize_act_int8_fused_rotation(M, K, b):
+    # fp32 FWHT against the float64 rotation: the 8-bit step is 18x finer
+    # than the 4-bit one, so rounding flips are more frequent; every flip is
+    # one step and at most 2% of the codes flip.
+    w = synth.small("f8", M, K, 8, n_outlier=4, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    xq, sx = W.quantize_act_int8(dev(X), b)
+    _, ps, pc, _ = O.quantize_activation(X, b, qmax=127)
+    diff = codes_from_i8(host(xq)).astype(np.int16) - pc
+    print("int8 fused rotation: fraction of codes one step off =", np.count_nonzero(diff) / diff.size)
+    assert np.all(np.abs(diff) <= 1)
+    assert np.count_nonzero(diff) <= 0.02 * diff.size
+    assert np.all(np.abs(host(sx).astype(np.float64) - ps) <= 1e-6 * ps)
+
+
+@pytest.mark.parametrize("layout", ["i8", "i8_tiled"])
+@pytest.mark.parametrize("M,N,K", [(7, 33, 256), (130, 260, 1024), (2048, 4096, 4096), (16, 300, 14336)])
+def test_qgemm_int8_codes_exact(M, N, K, layout):
+    rng = np.random.default_rng(M + N + K + 5)
+    qx = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    qx[0, :] = -127
+    qw[0, :] = -8
+    if layout == "i8":
+        xin, win, wl = i8_from_codes(qx).view(np.uint8), O.pack_int4(qw), "rowmajor"
+    else:
+        xin, win, wl = tile_codes_i8(i8_from_codes(qx), rng), tile_weights(O.pack_int4(qw), rng), "tiled"
+    _, acc = W.qgemm_w4a4(dev(xin), None, dev(win), None, 0, want_y=False, want_acc=True,
+                          layout=layout, w_layout=wl, M=M, N=N)
+    assert np.array_equal(host(acc), O.int_gemm(qx, qw))
+
+
+def run_layer_w4a8(w, w_layout):
+    d = synth.make_inputs(w)
+    X, Wt, A, B = d["X"], d["W"], d["A"], d["B"]
+    wq, ws, _ = O.prepare_weight(Wt, w.had_block, w.w_group, w.w_scale_dtype)
+    Xd = dev(X)
+    wqd = dev(tile_weights(wq) if w_layout == "tiled" else wq)
+    Ad = dev(A.T) if A is not None else None
+    Bd = dev(B.T) if B is not None else None
+    y = host(W.qlinear_forward(Xd, wqd, dev(ws), w.had_block, w.w_group, Ad, Bd,
+                               w_layout=w_layout, act_bits=8))
+    gxq, gsx = W.quantize_act_int8(Xd, w.had_block)
+    gc = codes_from_i8(host(gxq)).astype(np.int16)
+    y_codes = O.qlinear_from_codes(gc, host(gsx), wq, ws, w.w_group, X, A, B)
+    y_or = O.qlinear_forward(X, wq, ws, w.had_block, w.w_group, A, B, act_bits=8)
+    rms = float(np.sqrt(np.mean(y_or.astype(np.float64) ** 2)))
+    return y, y_codes, y_or, rms
+
+
+@pytest.mark.parametrize("wl", ["rowmajor", "tiled"])
+@pytest.mark.parametrize("w", [synth.PREFILL, synth.DECODE, synth.TINY,
+                               synth.small("w8r", 300, 1024, 1030, had_block=256, rank=40),
+                               synth.small("w8g", 65, 14336, 96, had_block=128, w_group=128, rank=32)],
+                         ids=lambda w: w.name)
+def test_w4a8_layer(w, wl):
+    if wl == "tiled" and w.K % 128:
+        pytest.skip("tiled weights need K % 128 == 0")
+    y, y_codes, y_or, rms = run_layer_w4a8(w, wl)
+    err = np.max(np.abs(y.astype(np.float64) - y_codes))
+    assert err <= 1e-3 * rms, (err, rms)
+    print(w.name, wl, "W4A8 max|Y-Y_oracle|/RMS =", float(np.max(np.abs(y - y_or)) / rms))
