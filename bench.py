@@ -92,11 +92,11 @@ class Layer:
 
 
 def gemm_bytes(wl: synth.Workload) -> int:
-    """Bytes the GEMM must move once: int8 codes and scales of X, packed
+    """Bytes the GEMM must move once: packed codes and scales of X, packed
     weights and their scales, float32 Y."""
     sb = 2 if wl.w_scale_dtype == "float16" else 4
     nsc = wl.N if wl.w_group == 0 else wl.N * (wl.K // wl.w_group)
-    return wl.M * wl.K + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N
+    return wl.M * wl.K // 2 + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N
 
 
 def gemm_kernel_name(layer: "Layer") -> str:
@@ -135,8 +135,11 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     they run on."""
     wl = layer.wl
     tiled = layer.w_layout == "tiled"
-    lay = "i8_tiled" if tiled else "i8"
-    xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K), dtype=torch.uint8, device="cuda:0")
+    # the code layout qlinear_forward hands the GEMM: packed tiles with tiled
+    # weights, int8 rows otherwise
+    lay = "packed_tiled" if tiled else "i8"
+    xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K // 2 if tiled else wl.K),
+                     dtype=torch.uint8, device="cuda:0")
     sx = torch.empty((wl.M,), dtype=torch.float32, device="cuda:0")
     W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay)
     torch.cuda.synchronize()
@@ -146,7 +149,7 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     out["qgemm"] = time_graph(
         lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
                                layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
-                               layout=lay, w_layout=layer.w_layout),
+                               layout=lay, w_layout=layer.w_layout, M=wl.M),
         steps, warmup)
     return out
 
@@ -263,7 +266,7 @@ def main() -> int:
     t_step8 = time_graph(lambda i: pre.forward(i, act_bits=8), args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
-    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K + 4 * pre.wl.M  # X in, int8 codes + scales out
+    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M  # X in, packed codes + scales out
     log(f"prefill: {t_step * 1e6:.2f} us/step, {tops:.1f} TOP/s; qgemm {kt['qgemm'] * 1e6:.2f} us "
         f"({gemm_tops:.1f} TOP/s), rotq {kt['rotq'] * 1e6:.2f} us "
         f"({rot_bytes / kt['rotq'] / 1e9:.0f} GB/s)")
