@@ -324,7 +324,8 @@ def test_qgemm_dequant(M, N, K, g, sd, layout):
 @pytest.mark.parametrize("M,N,K,g", [(1, 1, 128, 0), (8, 4096, 4096, 0), (16, 300, 14336, 128),
                                      (17, 33, 256, 0), (32, 4096, 4096, 128), (33, 70, 384, 128),
                                      (130, 260, 384, 0), (300, 129, 1024, 256),
-                                     (1000, 6500, 256, 128), (2048, 4096, 4096, 0)])
+                                     (1000, 6500, 256, 128), (2048, 4096, 4096, 0),
+                                     (2100, 4100, 1024, 0)])
 @pytest.mark.parametrize("codes", ["i8_tiled", "packed_tiled"])
 def test_qgemm_tiled_exact_and_dequant(M, N, K, g, codes):
     rng = np.random.default_rng(M * 7 + N + K + g)
