@@ -32,6 +32,18 @@ What is computed, and where the pages fix it
   on the unrotated input as given.
 * Epilogue: Y = s_x[m] * s_w[n] * acc[m, n] (or the sum over weight groups)
   + low-rank term, in float64, rounded once to float32.
+* Asymmetric group-wise activations (OffQ page, "Metodología" steps 2-3):
+  the all-ones Hadamard row turns a group's outlier into a constant offset,
+  which the zero point of an asymmetric per-group quantizer absorbs.  With
+  the group equal to the Hadamard block, per token and group in float32:
+  s = (max - min) / 15, z = rint(-min / s), q = clamp(rint(x / s) + z, 0, 15),
+  so that x ~ s (q - z).  The zero point is an integer that is not clamped
+  to the code range: an offset larger than the group's spread moves z past
+  0 or 15, and only then is it absorbed whole.  A group with no spread
+  (max = min = c) takes the range spanned by c and 0, so that it is coded
+  as c rather than as 0; s = 0 (c = 0) gives q = z = 0.  The product is
+  Y = sum_g s_x[m,g] s_w[n] (sum_{k in g} q_x q_w - z[m,g] sum_{k in g} q_w[n,k])
+  + the low-rank term; the weight sums are an offline input.
 * W4A8 layers: the layers a phase-aware policy keeps at 8-bit activations
   while the weights stay 4-bit (DynamicPTQ page, "Metodología" §2).  The
   same rotation and the same per-token symmetric absmax rule with qmax 127:
@@ -280,3 +292,67 @@ def qlinear_from_codes(qx: np.ndarray, s_x: np.ndarray, wq_packed: np.ndarray,
     acc = int_gemm(qx, qw) if group == 0 else int_gemm_groups(qx, qw, group)
     lr = lowrank(X, A, B) if X is not None else None
     return epilogue(acc, s_x, np.asarray(w_scale).astype(np.float32), lr)
+
+
+# ----------------------------------------------------------------------------
+# Asymmetric group-wise activations (OffQ page, "Metodología" steps 2-3)
+# ----------------------------------------------------------------------------
+AQMAX = 15
+
+
+def quantize_act_asym(xrot32: np.ndarray, group: int):
+    """Asymmetric uint4 quantization of rotated float32 activations, one
+    (scale, zero point) per token and group of `group` channels.
+
+    Returns (codes uint8 [M, K] in [0, 15], scales float32 [M, K/group],
+    zero points int64 [M, K/group], not clamped)."""
+    x = np.asarray(xrot32, dtype=np.float32)
+    M, K = x.shape
+    G = K // group
+    xg = x.reshape(M, G, group)
+    lo = xg.min(axis=2).astype(np.float32)
+    hi = xg.max(axis=2).astype(np.float32)
+    flat = hi == lo
+    lo = np.where(flat, np.minimum(lo, np.float32(0)), lo).astype(np.float32)
+    hi = np.where(flat, np.maximum(hi, np.float32(0)), hi).astype(np.float32)
+    s = ((hi - lo).astype(np.float32) / np.float32(AQMAX)).astype(np.float32)
+    live = s > 0
+    safe = np.where(live, s, np.float32(1)).astype(np.float32)
+    z = np.rint((-lo / safe).astype(np.float32)).astype(np.int64)
+    quot = (xg / safe[:, :, None]).astype(np.float32)
+    q = np.clip(np.rint(quot).astype(np.int64) + z[:, :, None], 0, AQMAX)
+    q[~live, :] = 0
+    z[~live] = 0
+    return q.reshape(M, K).astype(np.uint8), s, z
+
+
+def weight_group_sums(qw: np.ndarray, group: int) -> np.ndarray:
+    """sum_{k in g} qw[n, k] for every output channel and K-group: [N, K/group]."""
+    N, K = qw.shape
+    return qw.astype(np.int64).reshape(N, K // group, group).sum(axis=2)
+
+
+def asym_from_codes(qx: np.ndarray, s_x: np.ndarray, z_x: np.ndarray, qw: np.ndarray,
+                    s_w: np.ndarray, group: int, X=None, A=None, B=None) -> np.ndarray:
+    """Y = sum_g s_x s_w (acc_g - z_x[m,g] wsum[n,g]) + low-rank, float64 then
+    rounded once to float32; qw are the signed weight codes [N, K]."""
+    acc = int_gemm_groups(qx.astype(np.int64), qw, group)          # [G, M, N]
+    ws = weight_group_sums(qw, group)                              # [N, G]
+    corr = acc - np.asarray(z_x, np.int64).T[:, :, None] * ws.T[:, None, :]
+    y = np.einsum("gmn,mg->mn", corr.astype(np.float64), np.asarray(s_x, np.float64))
+    y = y * np.asarray(s_w, np.float64).reshape(1, -1)
+    lr = lowrank(X, A, B) if X is not None else None
+    if lr is not None:
+        y = y + lr
+    return y.astype(np.float32)
+
+
+def qlinear_forward_asym(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.ndarray,
+                         had_block: int, A=None, B=None) -> np.ndarray:
+    """The forward with asymmetric group-wise activations, the group being the
+    Hadamard block; per-channel weight scales."""
+    xrot = rotate(X, had_block)
+    q, s, z = quantize_act_asym(xrot, had_block)
+    qw = unpack_int4(wq_packed)
+    return asym_from_codes(q, s, z, qw, np.asarray(w_scale).astype(np.float32), had_block, X, A, B)
+
