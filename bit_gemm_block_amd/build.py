@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a4.so")
 
-SOURCES = ["api.cpp", "rotq.hip", "qgemm.hip", "lowrank.hip"]
+SOURCES = ["api.cpp", "rotq.hip", "qgemm.hip", "lowrank.hip", "offq.hip"]
 
 # No fast-math and no denormal flushing: the quantizer's float32 division and
 # rounding must follow IEEE.  Packed-FP32 instructions are disabled.

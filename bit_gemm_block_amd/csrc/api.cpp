@@ -378,4 +378,170 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
                       w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
 }
 
+// ---- asymmetric group-wise activations ------------------------------------
+
+namespace {
+
+// Activation groups of the asymmetric path: a power of two in
+// [128, kMaxHad] dividing K (the GEMM flushes per 128-code iteration).
+int check_agroup(int64_t K, int64_t group) {
+  if (group <= 0) return W4A4_ERR_INVALID_ARG;
+  if (!is_pow2(group) || group < 128 || group > kMaxHad || K % group != 0)
+    return W4A4_ERR_UNSUPPORTED;
+  return W4A4_OK;
+}
+
+int launch_asym_quant(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                      int64_t group, uint8_t* xq, bool tiled, float* x_scale, int32_t* x_zero,
+                      int max_lds, hipStream_t st, w4a4::RotqExtras* ex) {
+  w4a4::RotqPlan plan;
+  int s = plan_rotq(M, K, had_block, group, max_lds, &plan);
+  if (s != W4A4_OK) return s;
+  ex->asym_zero = x_zero;
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b,
+                                   tiled ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT, group, false,
+                                   nullptr, xq, x_scale, plan, st, ex);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+w4a4::GemmArgs asym_gemm_args(const uint8_t* xq, const float* x_scale, const int32_t* x_zero,
+                              int64_t group, const uint8_t* wq, const void* w_scale,
+                              int w_scale_dtype, const int32_t* w_gsum, int64_t M, int64_t N,
+                              int64_t K, float* y) {
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.sx = x_scale; g.wq = wq; g.sw = w_scale;
+  g.sw_f16 = w_scale_dtype == W4A4_F16;
+  g.group = 0;
+  g.M = M; g.N = N; g.K = K;
+  g.y = y; g.acc = nullptr;
+  g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
+  g.a_i8 = 0;
+  g.tiled = 1;
+  g.zx = x_zero;
+  g.wsum = w_gsum;
+  g.agroup = static_cast<int>(group);
+  return g;
+}
+
+}  // namespace
+
+int w4a4_quantize_act_asym_int4(const void* x, int x_dtype, int64_t M, int64_t K,
+                                int64_t had_block, int64_t group, uint8_t* xq, int codes_layout,
+                                float* x_scale, int32_t* x_zero, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0) return W4A4_ERR_INVALID_ARG;
+  if (codes_layout != W4A4_CODES_PACKED && codes_layout != W4A4_CODES_PACKED_TILED)
+    return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if ((s = check_agroup(K, group)) != W4A4_OK) return s;
+  if (had_block > 1 && had_block != group) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0) return W4A4_OK;
+  if (!x || !xq || !x_scale || !x_zero) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale) || !aligned16(x_zero))
+    return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqExtras ex;
+  return launch_asym_quant(x, x_dtype, M, K, had_block, group, xq,
+                           codes_layout == W4A4_CODES_PACKED_TILED, x_scale, x_zero, max_lds,
+                           static_cast<hipStream_t>(stream), &ex);
+}
+
+int w4a4_weight_group_sums(const uint8_t* wq, int w_layout, int64_t N, int64_t K, int64_t group,
+                           int32_t* w_gsum, void* stream) {
+  if (!wlayout_ok(w_layout) || N < 0 || K <= 0 || group <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  int s = check_group(K, group, false);
+  if (s != W4A4_OK) return s;
+  if (w_layout == W4A4_WEIGHTS_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if (N == 0) return W4A4_OK;
+  if (!wq || !w_gsum) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(wq) || !aligned16(w_gsum)) return W4A4_ERR_MISALIGNED;
+  if ((s = device_check(nullptr)) != W4A4_OK) return s;
+  hipError_t e = w4a4::launch_weight_group_sums(wq, w_layout == W4A4_WEIGHTS_TILED, N, K,
+                                                static_cast<int>(group), w_gsum,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qgemm_asym(const uint8_t* xq, const float* x_scale, const int32_t* x_zero, int64_t group,
+                    const uint8_t* wq, const void* w_scale, int w_scale_dtype,
+                    const int32_t* w_gsum, int64_t M, int64_t N, int64_t K, float* y,
+                    void* stream) {
+  if (!dtype_ok(w_scale_dtype) || M < 0 || N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 128 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  int s = check_agroup(K, group);
+  if (s != W4A4_OK) return s;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !x_scale || !x_zero || !wq || !w_scale || !w_gsum || !y) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(x_zero) || !aligned16(wq) ||
+      !aligned16(w_scale) || !aligned16(w_gsum) || !aligned16(y))
+    return W4A4_ERR_MISALIGNED;
+  if ((s = device_check(nullptr)) != W4A4_OK) return s;
+  const w4a4::GemmArgs g = asym_gemm_args(xq, x_scale, x_zero, group, wq, w_scale, w_scale_dtype,
+                                          w_gsum, M, N, K, y);
+  hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qlinear_forward_asym(const void* x, int x_dtype, const uint8_t* wq, const void* w_scale,
+                              int w_scale_dtype, const int32_t* w_gsum, int64_t M, int64_t N,
+                              int64_t K, int64_t had_block, const void* At, const void* Bt,
+                              int64_t rank, float* y, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || M < 0 || N < 0 || rank < 0)
+    return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if ((s = check_agroup(K, had_block)) != W4A4_OK) return s;
+  if (rank > kMaxRank || (x_dtype == W4A4_F16 && rank % 8 != 0)) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !wq || !w_scale || !w_gsum || !y || !workspace) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!At || !Bt)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(w_gsum) ||
+      !aligned16(y) || !aligned16(workspace) || (rank > 0 && (!aligned16(At) || !aligned16(Bt))))
+    return W4A4_ERR_MISALIGNED;
+  const WsLayout L = ws_layout(M, K, rank);
+  if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
+  // The packed codes take half of the int8 code area; the group scales and
+  // zero points (M * K / had_block words each) fit in the other half.
+  const int64_t G = K / had_block;
+  const size_t sx_off = align256(static_cast<size_t>((M + 15) / 16 * 16) * static_cast<size_t>(K / 2));
+  const size_t zx_off = sx_off + align256(static_cast<size_t>(M * G) * 4);
+  if (zx_off + static_cast<size_t>(M * G) * 4 > L.sx) return W4A4_ERR_UNSUPPORTED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws + L.xq;
+  float* sx = reinterpret_cast<float*>(ws + sx_off);
+  int32_t* zx = reinterpret_cast<int32_t*>(ws + zx_off);
+  void* t = ws + L.t;
+  const bool f16 = x_dtype == W4A4_F16;
+  w4a4::RotqExtras ex;
+  const bool fuse_lr = rank > 0 && f16 && M <= 16;
+  if (fuse_lr) {
+    ex.lr_at = At;
+    ex.lr_rank = static_cast<int>(rank);
+    ex.lr_t = t;
+  }
+  if ((s = launch_asym_quant(x, x_dtype, M, K, had_block, had_block, xq, true, sx, zx, max_lds, st,
+                             &ex)) != W4A4_OK)
+    return s;
+  hipError_t e;
+  if (rank > 0 && !fuse_lr) {
+    e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  w4a4::GemmArgs g = asym_gemm_args(xq, sx, zx, had_block, wq, w_scale, w_scale_dtype, w_gsum, M,
+                                    N, K, y);
+  g.t = rank > 0 ? t : nullptr;
+  g.B = rank > 0 ? Bt : nullptr;
+  g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
+  g.rank = static_cast<int>(rank);
+  e = w4a4::launch_qgemm(g, st);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
 }  // extern "C"

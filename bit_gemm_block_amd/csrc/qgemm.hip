@@ -27,6 +27,17 @@
 // split K; every lane streams its weight bytes straight from memory into
 // registers (no LDS staging), the waves' partial tiles are reduced in LDS.
 //
+// Asymmetric activation groups (OffQ page, "Metodología" steps 2-3).  The
+// codes hold q - 8 for uint4 q, with scale s[m, g] and integer zero point
+// z[m, g] per token and group of channels, so that
+//   y[m, n] = sw[n] * (sum_g s[m,g] acc_g[m,n] - sum_g o[m,g] wsum[n,g]),
+//   acc_g = sum_{k in g} (q - 8) qw,  o = s (z - 8),
+// wsum[n, g] being the weight codes summed over group g.  The first sum is
+// the group flush of the main loop with per-row scales; the second, a
+// rank-(K/group) product, runs on fp16 matrix instructions after the loop
+// with both operands split exactly: o scaled by a power of two per row into
+// an fp16 pair (hi + lo, about 22 bits), wsum as 64 a + c.
+//
 // Low-rank term.  fp16 path: T is given as an fp16 pair (t_hi, t_lo) [M, r]
 // and Bt [N, r] is fp16; each 16x16 output block adds t_hi.Bt^T and
 // t_lo.Bt^T with v_mfma_f32_16x16x32_f16, using the dequantized tile as the
@@ -468,11 +479,14 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK>
+template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK,
+          bool ASYM = false>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // APK: activation codes packed (4 bits) in the weights' tile layout, widened
   // in registers like the weights; otherwise int8 codes.
+  // ASYM: asymmetric activation groups (per-row group scales, zero points).
   static_assert(!APK || TILED, "packed activation codes come tiled");
+  static_assert(!ASYM || (APK && !GROUPED), "asymmetric groups: packed codes, per-channel weights");
   constexpr int WM = TM * 16, WN = TN * 16;
   constexpr int BM = 2 * WM, BN = 2 * WN;
   constexpr int A_BYTES = BM * (APK ? 64 : 128), B_BYTES = BN * 64;
@@ -574,20 +588,22 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       dma16(src[q] + static_cast<int64_t>(kt) * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
   };
 
+  constexpr bool FLUSH = GROUPED || ASYM;  // float accumulation per K-group
   i32x4 acc[TM][TN];
-  f32x4 facc[GROUPED ? TM : 1][GROUPED ? TN : 1];
+  f32x4 facc[FLUSH ? TM : 1][FLUSH ? TN : 1];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-  if constexpr (GROUPED) {
+  if constexpr (FLUSH) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int iters_per_group = GROUPED ? a.group / 128 : 1;
-  const int64_t ngroups = GROUPED ? K / a.group : 1;
+  const int gsize = GROUPED ? a.group : ASYM ? a.agroup : 128;
+  const int iters_per_group = gsize / 128;
+  const int64_t ngroups = FLUSH ? K / gsize : 1;
   extern __shared__ __attribute__((aligned(16))) uint8_t gsc[];  // grouped scales
 
   const int frow = lane & 15;
@@ -650,6 +666,23 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
         }
       }
     }
+    if constexpr (ASYM) {
+      if ((kt + 1) % iters_per_group == 0) {
+        const int64_t grp = (kt + 1) / iters_per_group - 1;
+        const float* srow = reinterpret_cast<const float*>(gsc) + grp * BM + wm0 + 4 * fg;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + i * 16);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sv[r], facc[i][j][r]);
+            acc[i][j] = i32x4{0, 0, 0, 0};
+          }
+        }
+      }
+    }
   };
 
   // Grouped scales: this tile's columns for every group, staged in LDS as
@@ -668,6 +701,21 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       else
         reinterpret_cast<float*>(gsc)[e] = reinterpret_cast<const float*>(a.sw)[n * ngroups + grp];
     }
+    __syncthreads();
+  }
+  // Asymmetric groups: this tile's row scales for every group as
+  // [group][row] (times the 1/256 of the widened operands), followed by one
+  // word per row for the epilogue's row maxima.
+  if constexpr (ASYM) {
+    float* sl = reinterpret_cast<float*>(gsc);
+    for (int e = tid; e < BM * ngroups; e += 256) {
+      const int row = e % BM;
+      const int64_t grp = e / BM;
+      int64_t m = m0 + row;
+      m = m < a.M ? m : a.M - 1;
+      sl[e] = a.sx[m * ngroups + grp] * kInvA;
+    }
+    if (tid < BM) reinterpret_cast<uint32_t*>(gsc)[BM * ngroups + tid] = 0u;
     __syncthreads();
   }
 
@@ -718,6 +766,84 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     }
   }
 
+  // Asymmetric groups: corr[i][j] = 2^-e(m) sum_g o[m,g] wsum[n,g] for the
+  // wave's blocks, e(m) the per-row exponent that brings max_g |o[m,g]| into
+  // [2^13, 2^14).  The operands go through the stage buffers (free once every
+  // wave is past its last fragment read) CG groups at a time; MFMA lane
+  // group fg takes hi (fg < 2) or lo (fg >= 2) of o and 64 a (fg even) or c
+  // (fg odd) of wsum, so that one instruction sums (hi + lo)(64 a + c) over
+  // 8 groups.
+  f32x4 corr[ASYM ? TM : 1][ASYM ? TN : 1];
+  int eout[ASYM ? TM : 1][4];
+  if constexpr (ASYM) {
+    constexpr int CG = 16;
+    static_assert(BM * CG * 4 <= STAGE && BN * CG * 4 <= STAGE, "operands fit a stage buffer");
+    const int G = static_cast<int>(ngroups);
+    uint32_t* rmax = reinterpret_cast<uint32_t*>(gsc) + BM * G;
+    stage_barrier();
+    for (int e = tid; e < BM * G; e += 256) {
+      const int row = e / G, g = e % G;
+      const int64_t m = m0 + row;
+      if (m < a.M) {
+        const float o = a.sx[m * G + g] * static_cast<float>(a.zx[m * G + g] - 8);
+        atomicMax(&rmax[row], __float_as_uint(fabsf(o)));
+      }
+    }
+    __syncthreads();
+    auto row_exp = [&](int row) -> int {
+      const uint32_t u = rmax[row];
+      return u ? static_cast<int>((u >> 23) & 0xFF) - 140 : 0;
+    };
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) corr[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    _Float16* ao = reinterpret_cast<_Float16*>(st0);
+    _Float16* bo = reinterpret_cast<_Float16*>(st1);
+    for (int g0 = 0; g0 < G; g0 += CG) {
+      for (int e = tid; e < BM * CG; e += 256) {
+        const int row = e / CG, t = e % CG, g = g0 + t;
+        const int64_t m = m0 + row;
+        float o = 0.f;
+        if (m < a.M && g < G) o = a.sx[m * G + g] * static_cast<float>(a.zx[m * G + g] - 8);
+        const float oh = ldexpf(o, -row_exp(row));
+        const _Float16 h = static_cast<_Float16>(oh);
+        ao[row * 2 * CG + t] = h;
+        ao[row * 2 * CG + CG + t] = static_cast<_Float16>(oh - static_cast<float>(h));
+      }
+      for (int e = tid; e < BN * CG; e += 256) {
+        const int col = e / CG, t = e % CG, g = g0 + t;
+        const int64_t n = n0 + col;
+        const int w = (n < a.N && g < G) ? a.wsum[n * G + g] : 0;
+        const int w64 = ((w + 32) >> 6) * 64;
+        bo[col * 2 * CG + t] = static_cast<_Float16>(static_cast<float>(w64));
+        bo[col * 2 * CG + CG + t] = static_cast<_Float16>(static_cast<float>(w - w64));
+      }
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < CG / 8; ++h) {
+        half8 bv[TN];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bv[j] = *reinterpret_cast<const half8*>(bo + (wn0 + 16 * j + frow) * 2 * CG +
+                                                  ((fg & 1) ? CG : 0) + 8 * h);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const half8 av = *reinterpret_cast<const half8*>(ao + (wm0 + 16 * i + frow) * 2 * CG +
+                                                           (fg >= 2 ? CG : 0) + 8 * h);
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            corr[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv[j], corr[i][j], 0, 0, 0);
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) eout[i][r] = row_exp(wm0 + 16 * i + 4 * fg + r);
+  }
+
   // Epilogue (accumulators hold 16 * acc: only the weights carry the factor).
   const bool want_y = a.y != nullptr;
   const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
@@ -729,7 +855,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      sxr[i][r] = (want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
+      sxr[i][r] = (!ASYM && want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -741,7 +867,9 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       f32x4 yv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (GROUPED)
+        if constexpr (ASYM)
+          yv[r] = (facc[i][j][r] - ldexpf(corr[i][j][r], eout[i][r])) * swn;
+        else if constexpr (GROUPED)
           yv[r] = facc[i][j][r] * sxr[i][r];
         else
           yv[r] = static_cast<float>(acc[i][j][r]) * (sxr[i][r] * swn);
@@ -757,14 +885,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (want_y) yp[r * a.N] = yv[r];
-          if (!GROUPED && a.acc) ap[r * a.N] = acc[i][j][r] >> kShiftA;
+          if (!FLUSH && a.acc) ap[r * a.N] = acc[i][j][r] >> kShiftA;
         }
       } else if (n_ok) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (mb + r < a.M) {
             if (want_y) a.y[(mb + r) * a.N + n] = yv[r];
-            if (!GROUPED && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> kShiftA;
+            if (!FLUSH && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> kShiftA;
           }
         }
       }
@@ -1000,6 +1128,25 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Asymmetric activation groups: packed tiled codes, tiled weights.  Dynamic
+// LDS: the row scales of every group and the row maxima.
+template <int TM, int TN, int STAGES>
+hipError_t launch_pipe_asym(const GemmArgs& a, hipStream_t st) {
+  constexpr int BM = 32 * TM, BN = 32 * TN;
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const dim3 grid(static_cast<unsigned>(tiles));
+  const size_t lds = static_cast<size_t>(BM) * (a.K / a.agroup) * 4 + BM * 4;
+#define W4A4_ASYM_CASE(LR)                                                                     \
+  if (a.lr_mode == LR) {                                                                       \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR, true, true, true>), grid, \
+                       dim3(256), lds, st, a);                                                 \
+    return hipGetLastError();                                                                  \
+  }
+  W4A4_ASYM_CASE(LR_NONE) W4A4_ASYM_CASE(LR_F16) W4A4_ASYM_CASE(LR_F32)
+#undef W4A4_ASYM_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int MB, bool AI8, bool TILED>
 hipError_t launch_skinny_a(const GemmArgs& a, hipStream_t st) {
   constexpr int KW = 4;
@@ -1026,6 +1173,9 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
+  // Asymmetric groups: a 32 x 64 wave tile, so that the row scales of every
+  // group fit in LDS beside two workgroups per CU.
+  if (a.zx) return launch_pipe_asym<2, 4, 3>(a, st);
   // The skinny kernel flushes weight groups at 128-code granularity.
   const bool skinny_ok = a.group == 0 || a.group % 128 == 0;
   if (a.M <= 16 && skinny_ok) return launch_skinny<1>(a, st);

@@ -24,6 +24,14 @@
 // granularity so that row reads (ds_read_b128) and column reads (ds_read_b32)
 // are free of bank conflicts for R = 64.
 //
+// Asymmetric mode (OffQ page, "Metodología" steps 2-3): one scale and zero
+// point per token and Hadamard block, s = (max - min) / 15,
+// z = rint(-min / s) (an integer, not clamped), q = clamp(rint(x~ / s) + z,
+// 0, 15), with a group of equal values c taking the range spanned by c and
+// 0.  The stored nibble is q - 8 in two's complement (q with its top bit
+// flipped), so that the codes feed the same signed int8 widening as the
+// symmetric ones.
+//
 // Quantization is exact with respect to the float32 rule
 // q = clamp(rint(fl(x~ / s)), -7, 7) with x~ = RN(y * rs): the quotient is
 // formed as x~ * RN(1/s) and refined twice by Markstein's step (residual
@@ -107,6 +115,8 @@ struct RotqKArgs {
   int gsz;           // elements per scale group (K = one scale per row)
   int scale_f16;
   float fqmax;       // largest code: 7 (int4) or 127 (int8 activations)
+  int asym;          // asymmetric uint4 codes with zero points (packed modes)
+  int32_t* zero;     // asym: zero points, laid out like the scales
   float* xrot;
   uint8_t* q;
   void* scale;
@@ -152,6 +162,16 @@ __device__ __forceinline__ void prefetch_role(const RotqKArgs& a, int p, int64_t
     }
   }
   if (fold == a.pf_magic) sink[0] = fold;
+}
+
+// Order-preserving map of float32 onto uint32 (unsigned compare = float
+// compare), for LDS atomic max of signed values, and its inverse.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_val(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // Swizzled float offset of element (i, j) of a segment stored as [L][R].
@@ -305,61 +325,127 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
     return;
   }
 
-  // 4. absmax of the scale group (max |y|; the rotated value is y * rs).
-  float m = 0.f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) m = fmaxf(m, fabsf(v[r]));
   const int gsz = a.gsz;
   // Lanes sharing one scale: shuffles inside a wave, then an LDS atomic max
   // when the group spans several waves or segments.
   const int span_lanes = (gsz < S ? gsz : S) / R;
   const int span_wave = span_lanes < 64 ? span_lanes : 64;
-  for (int o = 1; o < span_wave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (gsz > S || span_lanes > 64) {
-    const int slot = row_wg * (a.K / gsz) + kfirst / gsz;
-    if (valid && (lam & (span_wave - 1)) == 0) atomicMax(&slots[slot], __float_as_uint(m));
-    __syncthreads();
-    if (on) m = __uint_as_float(slots[slot]);
-  }
-
-  // 5. Scale: s = max|x~| / 7 with max|x~| = RN(max|y| * rs).
-  const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, a.fqmax);
-  float s_eff = s;
-  __half s_h = __float2half_rn(s);
-  if (a.scale_f16) s_eff = __half2float(s_h);
-  if (valid && (kfirst % gsz) == 0) {
-    const int64_t si = row * (a.K / gsz) + kfirst / gsz;
-    if (a.scale_f16)
-      reinterpret_cast<__half*>(a.scale)[si] = s_h;
-    else
-      reinterpret_cast<float*>(a.scale)[si] = s;
-  }
-
-  // 6. Codes.  code[r] holds the code of element r in its low bits (two's
-  // complement: low nibble = q & 0xF, low byte = q & 0xFF).
-  // A zero scale (an all-zero group) takes the reciprocal 0, so every
-  // quotient and code is 0.  The rint is the magic-number addition: the low
-  // mantissa bits of q + 1.5 * 2^23 are rint(q) in two's complement.
+  const bool cross = gsz > S || span_lanes > 64;
+  const int slot = row_wg * (a.K / gsz) + kfirst / gsz;
+  const bool leader = valid && (kfirst % gsz) == 0;
+  const int64_t si = row * (a.K / gsz) + kfirst / gsz;
+  // code[r] holds the code of element r in its low bits (two's complement:
+  // low nibble = q & 0xF, low byte = q & 0xFF).
   uint32_t code[R];
-  if (s_eff == 0.f || (s_eff >= 0x1p-100f && s_eff <= 0x1p100f)) {
-    const float rc = s_eff == 0.f ? 0.f : __frcp_rn(s_eff);
+  if (a.asym) {
+    // 4a. min and max of the group (of y; x~ = RN(y * rs) is monotone in y).
+    float ymax = v[0], ymin = v[0];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float xt = v[r] * a.rs;
-      float q = xt * rc;
-      q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
-      q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
-      const float u = q + kMagic;
-      code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
+    for (int r = 1; r < R; ++r) {
+      ymax = fmaxf(ymax, v[r]);
+      ymin = fminf(ymin, v[r]);
+    }
+    for (int o = 1; o < span_wave; o <<= 1) {
+      ymax = fmaxf(ymax, __shfl_xor(ymax, o));
+      ymin = fminf(ymin, __shfl_xor(ymin, o));
+    }
+    if (cross) {
+      const int half = a.nslots / 2;
+      if (valid && (lam & (span_wave - 1)) == 0) {
+        atomicMax(&slots[slot], order_key(ymax));
+        atomicMax(&slots[half + slot], order_key(-ymin));
+      }
+      __syncthreads();
+      if (on) {
+        ymax = order_val(slots[slot]);
+        ymin = -order_val(slots[half + slot]);
+      }
+    }
+    // 5a. Scale and zero point; a group without spread spans [min(c,0), max(c,0)].
+    float lo = ymin * a.rs, hi = ymax * a.rs;
+    if (hi == lo) {
+      lo = fminf(lo, 0.f);
+      hi = fmaxf(hi, 0.f);
+    }
+    const float s = __fdiv_rn(hi - lo, 15.f);
+    const bool live = s > 0.f;
+    const int zi = live ? static_cast<int>(rintf(__fdiv_rn(-lo, s))) : 0;
+    if (leader) {
+      reinterpret_cast<float*>(a.scale)[si] = s;
+      a.zero[si] = zi;
+    }
+    // 6a. Codes q = clamp(rint(x~ / s) + z, 0, 15), stored as q - 8.  Zero
+    // scale: q = 0.  Quotients here can exceed the magic-number range, so
+    // rint is the rounding instruction.
+    if (!live) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) code[r] = 8u;
+    } else if (s >= 0x1p-100f && s <= 0x1p100f) {
+      const float rc = __frcp_rn(s);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xt = v[r] * a.rs;
+        float q = xt * rc;
+        q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+        q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+        const int qi = static_cast<int>(rintf(q)) + zi;
+        code[r] = static_cast<uint32_t>(min(max(qi, 0), 15)) ^ 8u;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xt = v[r] * a.rs;
+        const int qi = static_cast<int>(rintf(__fdiv_rn(xt, s))) + zi;
+        code[r] = static_cast<uint32_t>(min(max(qi, 0), 15)) ^ 8u;
+      }
     }
   } else {
+    // 4. absmax of the scale group (max |y|; the rotated value is y * rs).
+    float m = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float xt = v[r] * a.rs;
-      float qf = rintf(__fdiv_rn(xt, s_eff));
-      qf = fminf(fmaxf(qf, -a.fqmax), a.fqmax);
-      code[r] = static_cast<uint32_t>(static_cast<int>(qf));
+    for (int r = 0; r < R; ++r) m = fmaxf(m, fabsf(v[r]));
+    for (int o = 1; o < span_wave; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    if (cross) {
+      if (valid && (lam & (span_wave - 1)) == 0) atomicMax(&slots[slot], __float_as_uint(m));
+      __syncthreads();
+      if (on) m = __uint_as_float(slots[slot]);
+    }
+
+    // 5. Scale: s = max|x~| / 7 with max|x~| = RN(max|y| * rs).
+    const float amax = m * a.rs;
+    const float s = __fdiv_rn(amax, a.fqmax);
+    float s_eff = s;
+    __half s_h = __float2half_rn(s);
+    if (a.scale_f16) s_eff = __half2float(s_h);
+    if (leader) {
+      if (a.scale_f16)
+        reinterpret_cast<__half*>(a.scale)[si] = s_h;
+      else
+        reinterpret_cast<float*>(a.scale)[si] = s;
+    }
+
+    // 6. Codes.  A zero scale (an all-zero group) takes the reciprocal 0, so every
+    // quotient and code is 0.  The rint is the magic-number addition: the low
+    // mantissa bits of q + 1.5 * 2^23 are rint(q) in two's complement.
+    if (s_eff == 0.f || (s_eff >= 0x1p-100f && s_eff <= 0x1p100f)) {
+      const float rc = s_eff == 0.f ? 0.f : __frcp_rn(s_eff);
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xt = v[r] * a.rs;
+        float q = xt * rc;
+        q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
+        q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
+        const float u = q + kMagic;
+        code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xt = v[r] * a.rs;
+        float qf = rintf(__fdiv_rn(xt, s_eff));
+        qf = fminf(fmaxf(qf, -a.fqmax), a.fqmax);
+        code[r] = static_cast<uint32_t>(static_cast<int>(qf));
+      }
     }
   }
   if (!valid) return;
@@ -488,20 +574,22 @@ bool try_shape(const Shape& sh, bool wide, int64_t K, int log2b, int64_t gsz, in
   if (segs_per_row * sh.L > 256) return false;
   const int64_t span_lanes = (gsz < S ? gsz : S) / sh.R;
   const int64_t slots_per_row = (gsz > S || span_lanes > 64) ? K / gsz : 0;
-  const int64_t row_bytes = K * 4 + slots_per_row * 4;
+  // Two slot arrays: the maxima, and the negated minima of the asymmetric
+  // mode.
+  const int64_t row_bytes = K * 4 + slots_per_row * 8;
   int64_t rows = 256 / (segs_per_row * sh.L);
   if (rows < 1) rows = 1;
   while (rows > 1 && rows * row_bytes > max_lds) --rows;
   if (rows * row_bytes > max_lds) return false;
   const int64_t threads = ((rows * segs_per_row * sh.L + 63) / 64) * 64;
-  if (threads > 256) return false;
+  if (threads > 256 || 2 * rows * slots_per_row > threads) return false;
   plan->L = sh.L;
   plan->R = sh.R;
   plan->segs_per_row = static_cast<int>(segs_per_row);
   plan->rows_per_wg = static_cast<int>(rows);
   plan->threads = static_cast<int>(threads);
   plan->lds_bytes = static_cast<int>(rows * row_bytes);
-  plan->nslots = static_cast<int>(rows * slots_per_row);
+  plan->nslots = static_cast<int>(2 * rows * slots_per_row);
   return true;
 }
 
@@ -530,6 +618,8 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.gsz = static_cast<int>(gsz);
   ka.scale_f16 = scale_f16 ? 1 : 0;
   ka.fqmax = (ex && ex->qmax == 127) ? 127.0f : 7.0f;
+  ka.asym = (ex && ex->asym_zero) ? 1 : 0;
+  ka.zero = ex ? ex->asym_zero : nullptr;
   ka.xrot = xrot;
   ka.q = q;
   ka.scale = scale;

@@ -46,6 +46,10 @@ enum RotqMode {
 // workgroups (a multiple of 8), so that the GEMM finds it in cache.
 struct RotqExtras {
   int qmax = 7;  // 127: 8-bit activation codes (int8 code modes only)
+  // Asymmetric uint4 codes (packed modes, float32 scales): one scale and one
+  // int32 zero point per group of gsz elements, zero points written here;
+  // the nibbles hold q - 8.
+  int32_t* asym_zero = nullptr;
   const void* lr_at = nullptr;
   int lr_rank = 0;
   void* lr_t = nullptr;
@@ -83,9 +87,22 @@ struct GemmArgs {
   int rank;
   int a_i8;              // activation codes as int8 (ROTQ_QUANT_I8 layout)
   int tiled;             // int8 codes and weights both in the 16 x 128 tiled layouts
+  // Asymmetric activation groups (zx non-null; packed tiled codes holding
+  // q - 8, tiled weights, per-channel weight scales, no acc): sx is
+  // [M, K/agroup], zx [M, K/agroup] the zero points, wsum [N, K/agroup] the
+  // weight codes summed over each group.
+  const int32_t* zx;
+  const int32_t* wsum;
+  int agroup;
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
+
+// ---- weight group sums (offq.hip) ------------------------------------------
+// out[n, g] = sum of the signed weight codes of row n over K-group g
+// (group a multiple of 8 dividing K); wq row-major [N, K/2] or tiled.
+hipError_t launch_weight_group_sums(const uint8_t* wq, bool tiled, int64_t N, int64_t K,
+                                    int group, int32_t* out, hipStream_t st);
 
 // ---- low-rank projection (lowrank.hip) -------------------------------------
 // t = x [M, K] . At[rank, K]^T.  fp16 inputs: pair_out writes the fp16 pair

@@ -51,6 +51,12 @@ _SIGS = {
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "w4a8_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "w4a4_quantize_act_asym_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _P,
+                                           _P]),
+    "w4a4_weight_group_sums": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P]),
+    "w4a4_qgemm_asym": (_INT, [_P, _P, _P, _I64, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _P]),
+    "w4a4_qlinear_forward_asym": (_INT, [_P, _INT, _P, _P, _INT, _P, _I64, _I64, _I64, _I64, _P,
+                                         _P, _I64, _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -274,4 +280,100 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
     _check("qlinear_forward", fwd(
         _ptr(x), _dt(x), _ptr(wq), wl, _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
         _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
+    return y
+
+
+# ---- asymmetric group-wise activations -------------------------------------
+def quantize_act_asym_int4(x: torch.Tensor, had_block: int, group: Optional[int] = None,
+                           layout: str = "packed"):
+    """uint4 codes with one float32 scale and one int32 zero point per token
+    and group (default: the Hadamard block).  The nibbles hold q - 8; layout
+    "packed" ([M, K/2]) or "packed_tiled" ([pad16(M), K/2]).  Returns
+    (xq, x_scale [M, K/group], x_zero [M, K/group])."""
+    _dev(x, "x")
+    M, K = x.shape
+    group = had_block if group is None else group
+    lay = _LAYOUTS[layout]
+    xq = torch.empty((pad16(M) if lay in _TILED_CODES else M, K // 2), dtype=torch.uint8,
+                     device=x.device)
+    G = K // group if group > 0 else 0
+    sx = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    zx = torch.empty((M, G), dtype=torch.int32, device=x.device)
+    _check("quantize_act_asym_int4", lib().w4a4_quantize_act_asym_int4(
+        _ptr(x), _dt(x), M, K, had_block, group, _ptr(xq), lay, _ptr(sx), _ptr(zx), _stream(x)))
+    return xq, sx, zx
+
+
+def weight_group_sums(wq: torch.Tensor, group: int, N: Optional[int] = None,
+                      w_layout: str = "rowmajor") -> torch.Tensor:
+    """int32 [N, K/group]: the signed weight codes summed over each group."""
+    _dev(wq, "wq")
+    wl = _WLAYOUTS[w_layout]
+    K = 2 * wq.shape[1]
+    N = wq.shape[0] if N is None else N
+    if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
+        raise ValueError("wq has too few rows")
+    out = torch.empty((N, K // group if group > 0 else 0), dtype=torch.int32, device=wq.device)
+    _check("weight_group_sums", lib().w4a4_weight_group_sums(
+        _ptr(wq), wl, N, K, group, _ptr(out), _stream(wq)))
+    return out
+
+
+def qgemm_asym(xq: torch.Tensor, x_scale: torch.Tensor, x_zero: torch.Tensor, group: int,
+               wq: torch.Tensor, w_scale: torch.Tensor, w_gsum: torch.Tensor,
+               y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Asymmetric activation codes (packed tiled) times tiled int4 weights
+    with per-channel scales; M from x_scale, N from w_scale."""
+    for t, n in ((xq, "xq"), (x_scale, "x_scale"), (x_zero, "x_zero"), (wq, "wq"),
+                 (w_scale, "w_scale"), (w_gsum, "w_gsum")):
+        _dev(t, n)
+    M, N, K = x_scale.shape[0], w_scale.shape[0], 2 * wq.shape[1]
+    G = K // group if group > 0 else 0
+    if xq.shape[1] != K // 2 or xq.shape[0] < pad16(M) or wq.shape[0] < pad16(N):
+        raise ValueError("xq / wq do not match the tiled layouts of M, N, K")
+    if tuple(x_scale.shape) != (M, G) or tuple(x_zero.shape) != (M, G) or \
+            tuple(w_gsum.shape) != (N, G):
+        raise ValueError("scales, zero points and weight sums must be [rows, K/group]")
+    if x_zero.dtype != torch.int32 or w_gsum.dtype != torch.int32:
+        raise TypeError("zero points and weight sums are int32")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check("qgemm_asym", lib().w4a4_qgemm_asym(
+        _ptr(xq), _ptr(x_scale), _ptr(x_zero), group, _ptr(wq), _ptr(w_scale), _dt(w_scale),
+        _ptr(w_gsum), M, N, K, _ptr(y), _stream(xq)))
+    return y
+
+
+def qlinear_forward_asym(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                         w_gsum: torch.Tensor, had_block: int,
+                         At: Optional[torch.Tensor] = None, Bt: Optional[torch.Tensor] = None,
+                         y: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer with asymmetric group-wise activations (group = had_block)
+    on tiled weights with per-channel scales."""
+    _dev(x, "x")
+    _dev(wq, "wq")
+    _dev(w_scale, "w_scale")
+    _dev(w_gsum, "w_gsum")
+    M, K = x.shape
+    N = w_scale.shape[0]
+    if wq.shape[0] < pad16(N) or wq.shape[1] != K // 2:
+        raise ValueError("wq does not match w_scale and x")
+    rank = 0 if At is None else At.shape[0]
+    if rank:
+        if Bt is None or At.dtype != x.dtype or Bt.dtype != x.dtype:
+            raise ValueError("At and Bt must both be given in x's dtype")
+        if tuple(At.shape) != (rank, K) or tuple(Bt.shape) != (N, rank):
+            raise ValueError("At must be [rank, K] and Bt [N, rank]")
+        _dev(At, "At")
+        _dev(Bt, "Bt")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = qlinear_workspace_size(M, N, K, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check("qlinear_forward_asym", lib().w4a4_qlinear_forward_asym(
+        _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), _ptr(w_gsum), M, N, K,
+        had_block, _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(),
+        _stream(x)))
     return y

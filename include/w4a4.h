@@ -243,6 +243,77 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          int64_t rank, float* y, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/*
+ * Asymmetric group-wise activations (OffQ page, "Metodología" steps 2-3):
+ * the all-ones first row of the Hadamard block turns a channel's outlier
+ * into a constant offset over its group, which the zero point of a
+ * per-group asymmetric quantizer absorbs.
+ *
+ * Activation quantizer, per token and group of `group` channels (the
+ * Hadamard block), in float32:
+ *   s = (max - min) / 15,  z = rint(-min / s),
+ *   q = clamp(rint(x~ / s) + z, 0, 15),  so that x~ ~ s (q - z).
+ * The zero point z is an int32 that is not clamped to [0, 15]: an offset
+ * larger than the group's spread moves it past the code range.  A group of
+ * equal values c takes the range spanned by c and 0; s = 0 gives q = z = 0.
+ * Codes are stored as the signed nibble q - 8 (q with its top bit flipped),
+ * in the W4A4_CODES_PACKED or W4A4_CODES_PACKED_TILED layout.
+ *   x        [M, K] in x_dtype.
+ *   group    a power of two in [128, 4096] dividing K.
+ *   had_block 0/1: x is already rotated; otherwise equal to group.
+ *   x_scale  [M, K/group] float32 output, x_zero [M, K/group] int32 output.
+ */
+int w4a4_quantize_act_asym_int4(const void* x, int x_dtype, int64_t M, int64_t K,
+                                int64_t had_block, int64_t group, uint8_t* xq,
+                                int codes_layout, float* x_scale, int32_t* x_zero,
+                                void* stream);
+
+/*
+ * Offline weight group sums for the asymmetric product (OffQ page,
+ * "Metodología" step 3: per-group zero points):
+ *   w_gsum[n, g] = sum of the signed weight codes of row n over channels
+ *   [g*group, (g+1)*group), int32 [N, K/group].
+ *   wq packed in w_layout; group a multiple of 64 dividing K.
+ */
+int w4a4_weight_group_sums(const uint8_t* wq, int w_layout, int64_t N, int64_t K,
+                           int64_t group, int32_t* w_gsum, void* stream);
+
+/*
+ * GEMM of asymmetric activation codes with int4 weights (OffQ page,
+ * "Metodología" steps 2-3; SERQ page, "Resumen técnico" §3):
+ *   y[m,n] = w_scale[n] * sum_g x_scale[m,g] * (sum_{k in g} q[m,k] qw[n,k]
+ *                                               - x_zero[m,g] * w_gsum[n,g])
+ * with q the uint4 codes (stored as q - 8) of w4a4_quantize_act_asym_int4.
+ *   xq       W4A4_CODES_PACKED_TILED codes; x_scale, x_zero [M, K/group].
+ *   wq       W4A4_WEIGHTS_TILED codes, w_scale [N] (per channel) in
+ *            w_scale_dtype, w_gsum [N, K/group] from w4a4_weight_group_sums.
+ *   group    a power of two in [128, 4096] dividing K; K a multiple of 128.
+ *   y        [M, N] float32 output.  The integer sums are exact; the
+ *            zero-point term is formed with about 22 significant bits.
+ */
+int w4a4_qgemm_asym(const uint8_t* xq, const float* x_scale, const int32_t* x_zero,
+                    int64_t group, const uint8_t* wq, const void* w_scale,
+                    int w_scale_dtype, const int32_t* w_gsum, int64_t M, int64_t N,
+                    int64_t K, float* y, void* stream);
+
+/*
+ * The layer with asymmetric group-wise activations: rotate by Hadamard
+ * blocks of had_block (a power of two in [128, 4096]), quantize each
+ * (token, block) with w4a4_quantize_act_asym_int4's rule, w4a4_qgemm_asym,
+ * plus the optional rank-r term as in w4a4_qlinear_forward.
+ *   wq W4A4_WEIGHTS_TILED with per-channel scales (w_group 0) from
+ *   w4a4_quantize_weight_int4 with the same had_block; w_gsum from
+ *   w4a4_weight_group_sums with group = had_block.
+ *   workspace: at least w4a4_qlinear_workspace_size(M, N, K, rank) bytes.
+ *   Other arguments and errors as w4a4_qlinear_forward.
+ */
+int w4a4_qlinear_forward_asym(const void* x, int x_dtype, const uint8_t* wq,
+                              const void* w_scale, int w_scale_dtype,
+                              const int32_t* w_gsum, int64_t M, int64_t N, int64_t K,
+                              int64_t had_block, const void* At, const void* Bt,
+                              int64_t rank, float* y, void* workspace,
+                              size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 12
+    assert len(names) == 16
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -138,6 +138,47 @@ def test_qlinear_argument_errors(lib):
     assert f(*bad) == W.ERR_INVALID_ARG
     bad = list(args); bad[3] = W.WEIGHTS_TILED; bad[10] = 64          # tiled needs group % 128
     assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == W.OK
+
+
+def test_asymmetric_argument_errors(lib):
+    q = lib.w4a4_quantize_act_asym_int4
+    L, LT = W.CODES_PACKED, W.CODES_PACKED_TILED
+    assert q(P, W.F16, 4, 512, 0, 128, P, W.CODES_I8, P, P, None) == W.ERR_INVALID_ARG   # layout
+    assert q(P, W.F16, 4, 512, 0, 128, P, L, P, None, None) == W.ERR_INVALID_ARG         # no zeros
+    assert q(P, W.F16, 4, 512, 0, 0, P, L, P, P, None) == W.ERR_INVALID_ARG              # group 0
+    assert q(P, W.F16, 4, 512, 0, 64, P, L, P, P, None) == W.ERR_UNSUPPORTED             # group < 128
+    assert q(P, W.F16, 4, 384, 0, 256, P, L, P, P, None) == W.ERR_UNSUPPORTED            # group | K
+    assert q(P, W.F16, 4, 512, 256, 128, P, L, P, P, None) == W.ERR_UNSUPPORTED          # b != group
+    assert q(P, W.F16, 4, 512, 0, 128, P, L, P, Q, None) == W.ERR_MISALIGNED
+    assert q(None, W.F16, 0, 512, 128, 128, None, LT, None, None, None) == W.OK
+    s = lib.w4a4_weight_group_sums
+    assert s(P, 3, 8, 256, 128, P, None) == W.ERR_INVALID_ARG                           # layout
+    assert s(P, 0, 8, 256, 96, P, None) == W.ERR_UNSUPPORTED                            # group % 64
+    assert s(P, 0, 8, 256, 128, None, None) == W.ERR_INVALID_ARG
+    assert s(None, 0, 0, 256, 128, None, None) == W.OK
+    g = lib.w4a4_qgemm_asym
+    args = [P, P, P, 128, P, P, W.F16, P, 4, 8, 512, P, None]
+    bad = list(args); bad[2] = None
+    assert g(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[3] = 64
+    assert g(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[10] = 448                                                     # K % 128
+    assert g(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[7] = Q
+    assert g(*bad) == W.ERR_MISALIGNED
+    bad = list(args); bad[9] = 0
+    assert g(*bad) == W.OK
+    f = lib.w4a4_qlinear_forward_asym
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 512, 8)
+    args = [P, W.F16, P, P, W.F16, P, 16, 32, 512, 128, P, P, 8, P, P, need, None]
+    bad = list(args); bad[5] = None
+    assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[9] = 64
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[15] = need - 1
+    assert f(*bad) == W.ERR_WORKSPACE
     bad = list(args); bad[6] = 0
     assert f(*bad) == W.OK
 
