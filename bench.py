@@ -14,6 +14,11 @@ resident in device memory before the timed region.  The timed region is a
 captured HIP graph of exactly --steps calls, bracketed by device
 synchronisation and timed with events on the stream the kernels run on.
 
+A third leg runs the layer with asymmetric group-wise activations (per
+token and 128-channel group: scale and zero point) on the Llama-3-8B o-proj
+shape (4096 x 4096 x 4096, rank-32 term), beside the symmetric layer on the
+same workload.
+
 The roofline object is the GEMM kernel alone (the dominant kernel): its
 average launch duration from events around --steps back-to-back launches,
 against the chip's dense int8 matrix peak.  cpu_baseline is the float64 CPU
@@ -78,6 +83,18 @@ class Layer:
         wq, ws, A, B = self.sets[i % len(self.sets)]
         W.qlinear_forward(self.x, wq, ws, self.wl.had_block, self.wl.w_group, A, B,
                           y=self.y, workspace=self.ws, w_layout=self.w_layout, act_bits=act_bits)
+
+    def forward_asym(self, i: int = 0):
+        """The layer with asymmetric group-wise activations (tiled weights,
+        per-channel scales, group = the Hadamard block)."""
+        wq, ws, A, B = self.sets[i % len(self.sets)]
+        W.qlinear_forward_asym(self.x, wq, ws, self.gsum, self.wl.had_block, A, B, y=self.y,
+                               workspace=self.ws)
+
+    def prepare_asym(self):
+        self.gsum = W.weight_group_sums(self.sets[0][0], self.wl.had_block, self.wl.N,
+                                        w_layout="tiled")
+        torch.cuda.synchronize()
 
     def algorithmic_bytes(self) -> int:
         wl = self.wl
@@ -151,6 +168,25 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
                                layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
                                layout=lay, w_layout=layer.w_layout, M=wl.M),
         steps, warmup)
+    return out
+
+
+def asym_kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
+    """Kernel durations of the asymmetric path, launched alone with the
+    arguments of qlinear_forward_asym (packed tiled codes)."""
+    wl = layer.wl
+    G = wl.K // wl.had_block
+    xq = torch.empty((W.pad16(wl.M), wl.K // 2), dtype=torch.uint8, device="cuda:0")
+    sx = torch.empty((wl.M, G), dtype=torch.float32, device="cuda:0")
+    zx = torch.empty((wl.M, G), dtype=torch.int32, device="cuda:0")
+    q = lambda i: W.quantize_act_asym_int4(layer.x, wl.had_block, wl.had_block, "packed_tiled",
+                                           xq, sx, zx)
+    q(0)
+    torch.cuda.synchronize()
+    out = {"rotq_asym": time_graph(q, steps, warmup)}
+    out["qgemm_asym"] = time_graph(
+        lambda i: W.qgemm_asym(xq, sx, zx, wl.had_block, layer.sets[0][0], layer.sets[0][1],
+                               layer.gsum, y=layer.y), steps, warmup)
     return out
 
 
@@ -242,6 +278,7 @@ def main() -> int:
     ap.add_argument("--w-layout", choices=["tiled", "rowmajor"], default="tiled")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-offq", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the prefill kernels and a calibration copy (for counters)")
     args = ap.parse_args()
@@ -297,6 +334,36 @@ def main() -> int:
         }
         del dec
 
+    # ---- asymmetric group-wise activations (OffQ), Llama-3-8B o-proj shape ------
+    offq = None
+    if not args.no_offq:
+        ow = synth.by_name("llama3_8b_o_4096x4096x4096")
+        lay = Layer(ow, w_layout="tiled")
+        lay.prepare_asym()
+        log(f"offq: {ow.name} timing {args.steps} steps (asymmetric and symmetric)")
+        t_asym = time_graph(lay.forward_asym, args.steps, args.warmup)
+        t_sym = time_graph(lay.forward, args.steps, args.warmup)
+        ka = asym_kernel_times(lay, args.steps, args.warmup)
+        ks = kernel_times(lay, args.steps, args.warmup)
+        gemm_tops_a = lay.ops() / ka["qgemm_asym"] / 1e12
+        log(f"offq: asym {t_asym * 1e6:.2f} us/step ({lay.ops() / t_asym / 1e12:.1f} TOP/s), "
+            f"sym {t_sym * 1e6:.2f} us/step; qgemm_asym {ka['qgemm_asym'] * 1e6:.2f} us, "
+            f"rotq_asym {ka['rotq_asym'] * 1e6:.2f} us")
+        offq = {
+            "metric": "W4A4 qlinear TOPS, asymmetric group-wise activations",
+            "value": lay.ops() / t_asym / 1e12, "unit": "TOP/s", "ms_per_step": t_asym * 1e3,
+            "symmetric_same_workload": {"value": lay.ops() / t_sym / 1e12, "unit": "TOP/s",
+                                        "ms_per_step": t_sym * 1e3},
+            "gemm": {"kernel": "qgemm_pipe_kernel (asymmetric groups)", "achieved": gemm_tops_a,
+                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": gemm_tops_a / PEAK_INT8_TOPS},
+            "kernels_us": {**{k: v * 1e6 for k, v in ka.items()},
+                           **{k + "_sym": v * 1e6 for k, v in ks.items()}},
+            "config": {"workload": ow.name, "M": ow.M, "N": ow.N, "K": ow.K,
+                       "had_block": ow.had_block, "group": ow.had_block, "rank": ow.rank},
+        }
+        del lay
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
@@ -330,6 +397,7 @@ def main() -> int:
         "w4a8": {"metric": "W4A8 qlinear TOPS (M=2048), K=N=4096", "value": pre.ops() / t_step8 / 1e12,
                  "unit": "TOP/s", "ms_per_step": t_step8 * 1e3},
         "decode": decode,
+        "offq": offq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -285,7 +285,8 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
 
 # ---- asymmetric group-wise activations -------------------------------------
 def quantize_act_asym_int4(x: torch.Tensor, had_block: int, group: Optional[int] = None,
-                           layout: str = "packed"):
+                           layout: str = "packed", xq: Optional[torch.Tensor] = None,
+                           sx: Optional[torch.Tensor] = None, zx: Optional[torch.Tensor] = None):
     """uint4 codes with one float32 scale and one int32 zero point per token
     and group (default: the Hadamard block).  The nibbles hold q - 8; layout
     "packed" ([M, K/2]) or "packed_tiled" ([pad16(M), K/2]).  Returns
@@ -294,11 +295,16 @@ def quantize_act_asym_int4(x: torch.Tensor, had_block: int, group: Optional[int]
     M, K = x.shape
     group = had_block if group is None else group
     lay = _LAYOUTS[layout]
-    xq = torch.empty((pad16(M) if lay in _TILED_CODES else M, K // 2), dtype=torch.uint8,
-                     device=x.device)
+    if xq is None:
+        xq = torch.empty((pad16(M) if lay in _TILED_CODES else M, K // 2), dtype=torch.uint8,
+                         device=x.device)
     G = K // group if group > 0 else 0
-    sx = torch.empty((M, G), dtype=torch.float32, device=x.device)
-    zx = torch.empty((M, G), dtype=torch.int32, device=x.device)
+    if sx is None:
+        sx = torch.empty((M, G), dtype=torch.float32, device=x.device)
+    if zx is None:
+        zx = torch.empty((M, G), dtype=torch.int32, device=x.device)
+    for t, n in ((xq, "xq"), (sx, "x_scale"), (zx, "x_zero")):
+        _dev(t, n)
     _check("quantize_act_asym_int4", lib().w4a4_quantize_act_asym_int4(
         _ptr(x), _dt(x), M, K, had_block, group, _ptr(xq), lay, _ptr(sx), _ptr(zx), _stream(x)))
     return xq, sx, zx
