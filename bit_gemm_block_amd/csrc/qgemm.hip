@@ -480,13 +480,20 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK,
-          bool ASYM = false>
+          bool ASYM = false, bool G128 = false, bool AG1 = false>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // APK: activation codes packed (4 bits) in the weights' tile layout, widened
   // in registers like the weights; otherwise int8 codes.
   // ASYM: asymmetric activation groups (per-row group scales, zero points).
   static_assert(!APK || TILED, "packed activation codes come tiled");
   static_assert(!ASYM || (APK && !GROUPED), "asymmetric groups: packed codes, per-channel weights");
+  // G128: groups of exactly one 128-code iteration.  The integer
+  // accumulators are then double-buffered: iteration kt issues its matrix
+  // instructions into one set and flushes the other (group kt - 1), so the
+  // flush does not wait for the instructions just issued.
+  // AG1: asymmetric codes with a single group per row (group = K): the
+  // integer product runs over all of K like the symmetric one, and the row
+  // scale and zero-point term enter in the epilogue only.
   constexpr int WM = TM * 16, WN = TN * 16;
   constexpr int BM = 2 * WM, BN = 2 * WN;
   constexpr int A_BYTES = BM * (APK ? 64 : 128), B_BYTES = BN * 64;
@@ -588,13 +595,22 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       dma16(src[q] + static_cast<int64_t>(kt) * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
   };
 
-  constexpr bool FLUSH = GROUPED || ASYM;  // float accumulation per K-group
+  static_assert(!AG1 || ASYM, "single-group mode is asymmetric");
+  constexpr bool FLUSH = GROUPED || (ASYM && !AG1);  // float accumulation per K-group
+  static_assert(!G128 || FLUSH, "double-buffered flush needs groups");
   i32x4 acc[TM][TN];
+  i32x4 acc2[G128 ? TM : 1][G128 ? TN : 1];
   f32x4 facc[FLUSH ? TM : 1][FLUSH ? TN : 1];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+  if constexpr (G128) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc2[i][j] = i32x4{0, 0, 0, 0};
+  }
   if constexpr (FLUSH) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -628,7 +644,42 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
               As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
     }
   };
-  auto compute = [&](int kt, const i32x4 (&fa)[2][TM], const uint4 (&fb)[TN]) {
+  // Adds the float value of one set of group accumulators, scaled, to facc
+  // and clears the set.
+  auto flush = [&](i32x4 (&ac)[TM][TN], int64_t grp) {
+    if constexpr (GROUPED) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = wn0 + j * 16 + frow;
+        const float sw = a.sw_f16 ? __half2float(reinterpret_cast<const __half*>(gsc)[grp * BN + col])
+                                  : reinterpret_cast<const float*>(gsc)[grp * BN + col];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            facc[i][j][r] = fmaf(static_cast<float>(ac[i][j][r]), sw, facc[i][j][r]);
+          ac[i][j] = i32x4{0, 0, 0, 0};
+        }
+      }
+    }
+    if constexpr (ASYM && !AG1) {
+      const float* srow = reinterpret_cast<const float*>(gsc) + grp * BM + wm0 + 4 * fg;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + i * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            facc[i][j][r] = fmaf(static_cast<float>(ac[i][j][r]), sv[r], facc[i][j][r]);
+          ac[i][j] = i32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  };
+  // cur: the accumulators of this iteration; prev: the other set (G128).
+  auto compute = [&](int kt, const i32x4 (&fa)[2][TM], const uint4 (&fb)[TN],
+                     i32x4 (&cur)[TM][TN], i32x4 (&prev)[TM][TN]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       i32x4 opb[TN];
@@ -646,42 +697,13 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], acc[i][j], 0, 0, 0);
+          cur[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], cur[i][j], 0, 0, 0);
     }
-    if constexpr (GROUPED) {
-      if ((kt + 1) % iters_per_group == 0) {
-        const int64_t grp = (kt + 1) / iters_per_group - 1;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = wn0 + j * 16 + frow;
-          const float sw = a.sw_f16 ? __half2float(reinterpret_cast<const __half*>(gsc)[grp * BN + col])
-                                    : reinterpret_cast<const float*>(gsc)[grp * BN + col];
-#pragma unroll
-          for (int i = 0; i < TM; ++i) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sw, facc[i][j][r]);
-            acc[i][j] = i32x4{0, 0, 0, 0};
-          }
-        }
-      }
-    }
-    if constexpr (ASYM) {
-      if ((kt + 1) % iters_per_group == 0) {
-        const int64_t grp = (kt + 1) / iters_per_group - 1;
-        const float* srow = reinterpret_cast<const float*>(gsc) + grp * BM + wm0 + 4 * fg;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + i * 16);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              facc[i][j][r] = fmaf(static_cast<float>(acc[i][j][r]), sv[r], facc[i][j][r]);
-            acc[i][j] = i32x4{0, 0, 0, 0};
-          }
-        }
-      }
+    if constexpr (G128) {
+      // group kt - 1 (at kt = 0 the set is all zero and any scale adds 0)
+      flush(prev, kt > 0 ? kt - 1 : 0);
+    } else if constexpr (FLUSH) {
+      if ((kt + 1) % iters_per_group == 0) flush(cur, (kt + 1) / iters_per_group - 1);
     }
   };
 
@@ -707,15 +729,16 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // [group][row] (times the 1/256 of the widened operands), followed by one
   // word per row for the epilogue's row maxima.
   if constexpr (ASYM) {
+    const int64_t nstaged = AG1 ? 0 : ngroups;  // single group: scale applied in the epilogue
     float* sl = reinterpret_cast<float*>(gsc);
-    for (int e = tid; e < BM * ngroups; e += 256) {
+    for (int e = tid; e < BM * nstaged; e += 256) {
       const int row = e % BM;
       const int64_t grp = e / BM;
       int64_t m = m0 + row;
       m = m < a.M ? m : a.M - 1;
       sl[e] = a.sx[m * ngroups + grp] * kInvA;
     }
-    if (tid < BM) reinterpret_cast<uint32_t*>(gsc)[BM * ngroups + tid] = 0u;
+    if (tid < BM) reinterpret_cast<uint32_t*>(gsc)[BM * nstaged + tid] = 0u;
     __syncthreads();
   }
 
@@ -739,7 +762,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // fragments are read into the other register set; stage kt's matrix
   // instructions then run while those reads are in flight.
   auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[2][TM], uint4 (&fbc)[TN], i32x4 (&fan)[2][TM],
-                     uint4 (&fbn)[TN]) {
+                     uint4 (&fbn)[TN], int odd) {
     // The reads are unconditional (on the last iteration they read a stale,
     // in-bounds buffer) so that no branch joins between them and the matrix
     // instructions, where the compiler would wait for them.
@@ -751,19 +774,35 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
     read_frags(stage((sbuf + 1) % STAGES), fan, fbn);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
-    compute(kt, fac, fbc);
+    if constexpr (G128) {
+      if (odd)
+        compute(kt, fac, fbc, acc2, acc);
+      else
+        compute(kt, fac, fbc, acc, acc2);
+    } else {
+      compute(kt, fac, fbc, acc, acc);
+    }
   };
+  // kt0 is a multiple of 2 * STAGES, so the parity of kt is that of u, a
+  // compile-time constant in every unrolled iteration.
   for (int kt0 = 0; kt0 < nkt; kt0 += 2 * STAGES) {
 #pragma unroll
     for (int u = 0; u < 2 * STAGES; ++u) {
       const int kt = kt0 + u;
       if (kt < nkt) {
         if (u & 1)
-          iterate(kt, u % STAGES, fa1, fb1, fa0, fb0);
+          iterate(kt, u % STAGES, fa1, fb1, fa0, fb0, 1);
         else
-          iterate(kt, u % STAGES, fa0, fb0, fa1, fb1);
+          iterate(kt, u % STAGES, fa0, fb0, fa1, fb1, 0);
       }
     }
+  }
+  if constexpr (G128) {
+    // the last group sits in the set of parity (nkt - 1) & 1; the other set
+    // was flushed and is zero
+    const int last = nkt - 1;
+    flush(acc, (last & 1) ? 0 : last);
+    flush(acc2, (last & 1) ? last : 0);
   }
 
   // Asymmetric groups: corr[i][j] = 2^-e(m) sum_g o[m,g] wsum[n,g] for the
@@ -778,8 +817,8 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   if constexpr (ASYM) {
     constexpr int CG = 16;
     static_assert(BM * CG * 4 <= STAGE && BN * CG * 4 <= STAGE, "operands fit a stage buffer");
-    const int G = static_cast<int>(ngroups);
-    uint32_t* rmax = reinterpret_cast<uint32_t*>(gsc) + BM * G;
+    const int G = AG1 ? 1 : static_cast<int>(ngroups);
+    uint32_t* rmax = reinterpret_cast<uint32_t*>(gsc) + (AG1 ? 0 : BM * G);
     stage_barrier();
     for (int e = tid; e < BM * G; e += 256) {
       const int row = e / G, g = e % G;
@@ -855,7 +894,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      sxr[i][r] = (!ASYM && want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
+      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -867,7 +906,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       f32x4 yv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if constexpr (ASYM)
+        if constexpr (AG1)
+          yv[r] = (static_cast<float>(acc[i][j][r]) * sxr[i][r] -
+                   ldexpf(corr[i][j][r], eout[i][r])) * swn;
+        else if constexpr (ASYM)
           yv[r] = (facc[i][j][r] - ldexpf(corr[i][j][r], eout[i][r])) * swn;
         else if constexpr (GROUPED)
           yv[r] = facc[i][j][r] * sxr[i][r];
@@ -885,14 +927,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (want_y) yp[r * a.N] = yv[r];
-          if (!FLUSH && a.acc) ap[r * a.N] = acc[i][j][r] >> kShiftA;
+          if (!FLUSH && !ASYM && a.acc) ap[r * a.N] = acc[i][j][r] >> kShiftA;
         }
       } else if (n_ok) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           if (mb + r < a.M) {
             if (want_y) a.y[(mb + r) * a.N + n] = yv[r];
-            if (!FLUSH && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> kShiftA;
+            if (!FLUSH && !ASYM && a.acc) a.acc[(mb + r) * a.N + n] = acc[i][j][r] >> kShiftA;
           }
         }
       }
@@ -1114,8 +1156,12 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
       a.group > 0 ? static_cast<size_t>(BN) * (a.K / a.group) * (a.sw_f16 ? 2 : 4) : 0;
 #define W4A4_PIPE_CASE(G, LR, T, P)                                                          \
   if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T && (!a.a_i8) == P) {      \
-    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P>), grid, dim3(256),    \
-                       scale_lds, st, a);                                                   \
+    if (G && P && a.group == 128)                                                           \
+      hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P, false, G && P>),   \
+                         grid, dim3(256), scale_lds, st, a);                                \
+    else                                                                                    \
+      hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, G, LR, T, P>), grid, dim3(256), \
+                         scale_lds, st, a);                                                 \
     return hipGetLastError();                                                               \
   }
 #define W4A4_PIPE_CASES(T, P)                                                    \
@@ -1135,14 +1181,24 @@ hipError_t launch_pipe_asym(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const dim3 grid(static_cast<unsigned>(tiles));
-  const size_t lds = static_cast<size_t>(BM) * (a.K / a.agroup) * 4 + BM * 4;
-#define W4A4_ASYM_CASE(LR)                                                                     \
-  if (a.lr_mode == LR) {                                                                       \
-    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR, true, true, true>), grid, \
-                       dim3(256), lds, st, a);                                                 \
-    return hipGetLastError();                                                                  \
+  if (a.agroup == a.K && a.lr_mode == LR_NONE) {
+    // One group per row: the symmetric kernel's 128 x 128 tile, no flush.
+    // (With a low-rank term this tile would drop to one wave per SIMD.)
+    constexpr int BM1 = 128, BN1 = 128;
+    const dim3 grid1(static_cast<unsigned>(((a.M + BM1 - 1) / BM1) * ((a.N + BN1 - 1) / BN1)));
+    hipLaunchKernelGGL((qgemm_pipe_kernel<4, 4, STAGES, false, LR_NONE, true, true, true, false,
+                                          true>), grid1, dim3(256), BM1 * 4, st, a);
+    return hipGetLastError();
   }
-  W4A4_ASYM_CASE(LR_NONE) W4A4_ASYM_CASE(LR_F16) W4A4_ASYM_CASE(LR_F32)
+  const size_t lds = static_cast<size_t>(BM) * (a.K / a.agroup) * 4 + BM * 4;
+#define W4A4_ASYM_CASE(LR, G1)                                                               \
+  if (a.lr_mode == LR && (a.agroup == 128) == G1) {                                          \
+    hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR, true, true, true, G1>), \
+                       grid, dim3(256), lds, st, a);                                         \
+    return hipGetLastError();                                                                \
+  }
+  W4A4_ASYM_CASE(LR_NONE, true) W4A4_ASYM_CASE(LR_F16, true) W4A4_ASYM_CASE(LR_F32, true)
+  W4A4_ASYM_CASE(LR_NONE, false) W4A4_ASYM_CASE(LR_F16, false) W4A4_ASYM_CASE(LR_F32, false)
 #undef W4A4_ASYM_CASE
   return hipErrorInvalidValue;
 }

@@ -153,7 +153,8 @@ def asym_bound(q, s, z, qw, sw, g, rows):
 @pytest.mark.parametrize("M,N,K,g", [
     (1, 1, 128, 128), (7, 33, 256, 128), (130, 260, 1024, 256), (64, 128, 4096, 4096),
     (300, 129, 14336, 128), (2100, 4100, 1024, 128), (2048, 4096, 4096, 128),
-    (16, 300, 2048, 512), (65, 70, 16384, 128)])
+    (16, 300, 2048, 512), (65, 70, 16384, 128), (2048, 4096, 4096, 4096), (130, 260, 1024, 1024),
+    (300, 129, 2048, 2048)])
 def test_qgemm_asym(M, N, K, g):
     rng = np.random.default_rng(M + 3 * N + K + g)
     G = K // g
@@ -218,14 +219,16 @@ def run_asym_layer(w, sample_rows=None):
     (1, 256, 64, 128, 0, "float16"), (130, 1024, 260, 128, 16, "float16"),
     (33, 4096, 100, 4096, 64, "float16"), (65, 14336, 96, 128, 32, "float16"),
     (20, 4096, 520, 256, 24, "float16"), (300, 1024, 1030, 512, 40, "float16"),
-    (40, 384, 100, 128, 0, "float32"), (16, 512, 48, 128, 8, "float32")])
+    (40, 384, 100, 128, 0, "float32"), (16, 512, 48, 128, 8, "float32"),
+    (33, 4096, 100, 4096, 0, "float16"), (130, 1024, 260, 1024, 0, "float32")])
 def test_qlinear_asym_ragged(M, K, N, b, r, dt):
     w = synth.small("asl", M, K, N, x_dtype=dt, had_block=b, rank=r,
                     w_scale_dtype="float16" if dt == "float16" else "float32")
     run_asym_layer(w)
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_o_4096x4096x4096", "llama3_8b_down_4096x14336x4096"])
+@pytest.mark.parametrize("name", ["llama3_8b_o_4096x4096x4096", "llama3_8b_down_4096x14336x4096",
+                                  "prefill_2048x4096x4096"])
 def test_qlinear_asym_full_size(name):
     w = synth.by_name(name)
     rows = np.unique(np.r_[0, 1, np.random.default_rng(5).integers(0, w.M, 40), w.M - 1])
