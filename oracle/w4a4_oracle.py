@@ -44,6 +44,16 @@ What is computed, and where the pages fix it
   as c rather than as 0; s = 0 (c = 0) gives q = z = 0.  The product is
   Y = sum_g s_x[m,g] s_w[n] (sum_{k in g} q_x q_w - z[m,g] sum_{k in g} q_w[n,k])
   + the low-rank term; the weight sums are an offline input.
+* In-GEMM 4-bit residual of salient channels (SERQ page, "Metodología"
+  items 2-3): the weight rows that collect the most error (input channels,
+  permuted offline to the front, so that they are the first r channels) are
+  reconstructed by one 4-bit matrix R, the quantization error of those
+  channels, and the layer adds X_s . R^T, X_s being the same 4-bit
+  activation codes of those channels.  With per-channel weight scale s:
+  e = x~ - s q (float32), q_r = clamp(rint(e / (s/8)), -8, 7) for k < r, and
+  Y = s_x s_w (sum_k q_x q_w + (1/8) sum_{k<r} q_x q_r).  The step s/8 lets
+  R cover the whole rounding error (|e| <= s/2 gives |q_r| <= 4) and keeps
+  both sums in one integer: 8 sum_k q_x q_w + sum_{k<r} q_x q_r.
 * W4A8 layers: the layers a phase-aware policy keeps at 8-bit activations
   while the weights stay 4-bit (DynamicPTQ page, "Metodología" §2).  The
   same rotation and the same per-token symmetric absmax rule with qmax 127:
@@ -356,3 +366,63 @@ def qlinear_forward_asym(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.ndarr
     qw = unpack_int4(wq_packed)
     return asym_from_codes(q, s, z, qw, np.asarray(w_scale).astype(np.float32), had_block, X, A, B)
 
+
+
+# ----------------------------------------------------------------------------
+# In-GEMM residual of salient channels (SERQ page, "Metodología" items 2-3)
+# ----------------------------------------------------------------------------
+RES_STEPS = 8   # residual step = weight scale / RES_STEPS
+
+
+def quantize_weight_residual(wrot32: np.ndarray, r: int, scale_dtype: str):
+    """Per-channel RTN int4 weights (quantize_weight with group 0) plus the
+    4-bit residual of the first r channels, taken against the stored scale:
+    e = RN(x~ - RN(s q)), q_r = clamp(rint(RN(e / RN(s / 8))), -8, 7).
+
+    Returns (codes int8 [N, K], scales [N] in scale_dtype, residual codes
+    int8 [N, r])."""
+    wrot32 = np.asarray(wrot32, dtype=np.float32)
+    q, s = quantize_weight(wrot32, 0, scale_dtype)
+    s32 = np.asarray(s).astype(np.float32)
+    recon = (s32[:, None] * q[:, :r].astype(np.float32)).astype(np.float32)
+    e = (wrot32[:, :r] - recon).astype(np.float32)
+    t = (s32 / np.float32(RES_STEPS)).astype(np.float32)
+    live = t > 0
+    safe = np.where(live, t, np.float32(1)).astype(np.float32)
+    qr = np.clip(np.rint((e / safe[:, None]).astype(np.float32)), -8, 7)
+    qr[~live, :] = 0
+    return q, s, qr.astype(np.int8)
+
+
+def prepare_weight_residual(W: np.ndarray, had_block: int, r: int, scale_dtype: str):
+    """Offline preparation with the residual: rotate, quantize, pack.
+
+    Returns (packed uint8 [N, K/2], scales [N], codes int8 [N, K], residual
+    codes int8 [N, r])."""
+    wrot = rotate(W, had_block) if had_block > 1 else np.asarray(W, np.float32)
+    q, s, qr = quantize_weight_residual(wrot, r, scale_dtype)
+    return pack_int4(q), s, q, qr
+
+
+def residual_int_gemm(qx: np.ndarray, qw: np.ndarray, qr: np.ndarray) -> np.ndarray:
+    """The one integer of the residual product, exact int64:
+    8 sum_k qx qw + sum_{k<r} qx qr."""
+    r = qr.shape[1]
+    return RES_STEPS * int_gemm(qx, qw) + int_gemm(qx[:, :r], qr)
+
+
+def residual_from_codes(qx: np.ndarray, s_x: np.ndarray, qw: np.ndarray, s_w: np.ndarray,
+                        qr: np.ndarray) -> np.ndarray:
+    """Y = s_x s_w (sum_k qx qw + (1/8) sum_{k<r} qx qr), float64 then rounded
+    once to float32."""
+    acc = residual_int_gemm(qx, qw, qr).astype(np.float64)
+    y = np.asarray(s_x, np.float64)[:, None] * np.asarray(s_w, np.float64)[None, :] * acc
+    return (y / RES_STEPS).astype(np.float32)
+
+
+def qlinear_forward_residual(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.ndarray,
+                             qr: np.ndarray, had_block: int) -> np.ndarray:
+    """The forward with the in-GEMM residual of the first r channels."""
+    _, s_x, qx, _ = quantize_activation(X, had_block)
+    qw = unpack_int4(wq_packed)
+    return residual_from_codes(qx, s_x, qw, np.asarray(w_scale).astype(np.float32), qr)
