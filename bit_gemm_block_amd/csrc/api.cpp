@@ -378,6 +378,117 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
                       w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
 }
 
+// ---- in-GEMM residual of salient channels ---------------------------------
+
+namespace {
+
+// Residual rank r: 0 <= r <= K; the int32 accumulator holds
+// 256 (8 sum_K + sum_r) of 4-bit products exactly while 8 K + r_pad < 2^17.
+int check_res(int64_t K, int64_t r) {
+  if (r < 0) return W4A4_ERR_INVALID_ARG;
+  const int64_t rpad = (r + 127) / 128 * 128;
+  if (r > K || 8 * K + rpad >= (int64_t{1} << 17)) return W4A4_ERR_UNSUPPORTED;
+  return W4A4_OK;
+}
+
+w4a4::GemmArgs res_gemm_args(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                             const void* w_scale, int w_scale_dtype, int64_t r, int64_t M,
+                             int64_t N, int64_t K, float* y, int32_t* acc) {
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.sx = x_scale; g.wq = wq; g.sw = w_scale;
+  g.sw_f16 = w_scale_dtype == W4A4_F16;
+  g.group = 0;
+  g.M = M; g.N = N; g.K = K;
+  g.y = y; g.acc = acc;
+  g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
+  g.a_i8 = 0;
+  g.tiled = 1;
+  g.res = 1;
+  g.res_iters = static_cast<int>((r + 127) / 128);
+  return g;
+}
+
+}  // namespace
+
+int w4a4_quantize_weight_residual_int4(const void* w, int w_dtype, int64_t N, int64_t K,
+                                       int64_t had_block, int64_t res_rank, uint8_t* wq,
+                                       void* w_scale, int scale_dtype, void* stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || N < 0) return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if (K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if ((s = check_res(K, res_rank)) != W4A4_OK) return s;
+  if (N == 0) return W4A4_OK;
+  if (!w || !wq || !w_scale) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(w) || !aligned16(wq) || !aligned16(w_scale)) return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(N, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  w4a4::RotqExtras ex;
+  ex.res_r = static_cast<int>(res_rank);
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, w4a4::ROTQ_QUANT_TILED, K,
+                                   scale_dtype == W4A4_F16, nullptr, wq, w_scale, plan,
+                                   static_cast<hipStream_t>(stream), &ex);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qgemm_residual(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                        const void* w_scale, int w_scale_dtype, int64_t res_rank, int64_t M,
+                        int64_t N, int64_t K, float* y, int32_t* acc, void* stream) {
+  if (!dtype_ok(w_scale_dtype) || M < 0 || N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 128 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  int s = check_res(K, res_rank);
+  if (s != W4A4_OK) return s;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
+  if (y && (!x_scale || !w_scale)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(wq) || (x_scale && !aligned16(x_scale)) ||
+      (w_scale && !aligned16(w_scale)) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
+    return W4A4_ERR_MISALIGNED;
+  if ((s = device_check(nullptr)) != W4A4_OK) return s;
+  const w4a4::GemmArgs g =
+      res_gemm_args(xq, x_scale, wq, w_scale, w_scale_dtype, res_rank, M, N, K, y, acc);
+  hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qlinear_forward_residual(const void* x, int x_dtype, const uint8_t* wq,
+                                  const void* w_scale, int w_scale_dtype, int64_t res_rank,
+                                  int64_t M, int64_t N, int64_t K, int64_t had_block, float* y,
+                                  void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || M < 0 || N < 0)
+    return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if (K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if ((s = check_res(K, res_rank)) != W4A4_OK) return s;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !wq || !w_scale || !y || !workspace) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace))
+    return W4A4_ERR_MISALIGNED;
+  const WsLayout L = ws_layout(M, K, 0);
+  if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws + L.xq;
+  float* sx = reinterpret_cast<float*>(ws + L.sx);
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT_TILED, K,
+                                   false, nullptr, xq, sx, plan, st);
+  if (e != hipSuccess) return hip_fail(e);
+  const w4a4::GemmArgs g =
+      res_gemm_args(xq, sx, wq, w_scale, w_scale_dtype, res_rank, M, N, K, y, nullptr);
+  e = w4a4::launch_qgemm(g, st);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
 // ---- asymmetric group-wise activations ------------------------------------
 
 namespace {

@@ -480,7 +480,7 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK,
-          bool ASYM = false, bool G128 = false, bool AG1 = false>
+          bool ASYM = false, bool G128 = false, bool AG1 = false, bool RES = false>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // APK: activation codes packed (4 bits) in the weights' tile layout, widened
   // in registers like the weights; otherwise int8 codes.
@@ -491,6 +491,11 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // accumulators are then double-buffered: iteration kt issues its matrix
   // instructions into one set and flushes the other (group kt - 1), so the
   // flush does not wait for the instructions just issued.
+  // RES: in-GEMM residual (SERQ page, "Metodología" items 2-3).  After the
+  // K / 128 main iterations, res_iters more iterations multiply code columns
+  // [0, 128 res_iters) again, by the weights' residual tiles.  The main
+  // accumulator is multiplied by 8 once at the switch, so that one int32
+  // holds 256 (8 sum_k qx qw + sum_{k<r} qx qr); the epilogue scales by 1/8.
   // AG1: asymmetric codes with a single group per row (group = K): the
   // integer product runs over all of K like the symmetric one, and the row
   // scale and zero-point term enter in the epilogue only.
@@ -539,7 +544,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   const int64_t m0 = tmi * BM;
   const int64_t n0 = tni * BN;
   const int64_t K = a.K;
-  const int nkt = static_cast<int>(K / 128);
+  static_assert(!RES || (APK && !GROUPED && !ASYM && LRMODE == LR_NONE),
+                "residual: packed codes, per-channel weights");
+  const int nkt_a = static_cast<int>(K / 128);               // code tiles per row block
+  const int nkt = nkt_a + (RES ? a.res_iters : 0);           // iterations (weight tiles)
 
   // Source pointer (at iteration 0) and LDS offset of each run this wave
   // copies.  Row-major operands: a run is 16 rows x 64 bytes.  Tiled
@@ -555,7 +563,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     if (run < A_RUNS && APK) {
       int64_t mb = m0 / 16 + run;
       mb = mb < mblocks ? mb : mblocks - 1;
-      src[q] = a.xq + mb * nkt * 1024 + 16 * lane;
+      src[q] = a.xq + mb * nkt_a * 1024 + 16 * lane;
       step[q] = 1024;
       dst[q] = (run * 4) << 8;
     } else if (run < A_RUNS) {
@@ -563,7 +571,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       if constexpr (TILED) {
         int64_t mb = m0 / 16 + blk;
         mb = mb < mblocks ? mb : mblocks - 1;
-        src[q] = a.xq + (mb * nkt * 2 + h) * 1024 + 16 * lane;
+        src[q] = a.xq + (mb * nkt_a * 2 + h) * 1024 + 16 * lane;
         step[q] = 2048;
       } else {
         int64_t m = m0 + blk * 16 + rr;
@@ -591,8 +599,12 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   auto issue = [&](int kt, uint8_t* base) {
     const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
 #pragma unroll
-    for (int q = 0; q < RUNS_PER_WAVE; ++q)
-      dma16(src[q] + static_cast<int64_t>(kt) * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
+    for (int q = 0; q < RUNS_PER_WAVE; ++q) {
+      int64_t t = kt;
+      // residual iterations read the code columns from the start again
+      if (RES && kt >= nkt_a && wave + 4 * q < A_RUNS) t -= nkt_a;
+      dma16(src[q] + t * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
+    }
   };
 
   static_assert(!AG1 || ASYM, "single-group mode is asymmetric");
@@ -698,6 +710,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
           cur[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], cur[i][j], 0, 0, 0);
+    }
+    if constexpr (RES) {
+      if (kt == nkt_a - 1) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) cur[i][j] = cur[i][j] << 3;
+      }
     }
     if constexpr (G128) {
       // group kt - 1 (at kt = 0 the set is all zero and any scale adds 0)
@@ -894,7 +914,8 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? a.sx[m] * kInvA : 0.f;
+      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? a.sx[m] * (RES ? kInvA * 0.125f : kInvA)
+                                                          : 0.f;
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -1228,7 +1249,16 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// In-GEMM residual: the 128 x 128 tile, packed tiled codes.
+static hipError_t launch_pipe_res(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(((a.M + 127) / 128) * ((a.N + 127) / 128)));
+  hipLaunchKernelGGL((qgemm_pipe_kernel<4, 4, 3, false, LR_NONE, true, true, false, false, false,
+                                        true>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
+  if (a.res) return launch_pipe_res(a, st);
   // Asymmetric groups: a 32 x 64 wave tile, so that the row scales of every
   // group fit in LDS beside two workgroups per CU.
   if (a.zx) return launch_pipe_asym<2, 4, 3>(a, st);

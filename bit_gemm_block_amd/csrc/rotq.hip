@@ -24,6 +24,12 @@
 // granularity so that row reads (ds_read_b128) and column reads (ds_read_b32)
 // are free of bank conflicts for R = 64.
 //
+// Residual (weights, tiled; SERQ page, "Metodología" items 2-3): for the
+// first r channels (the salient ones, permuted to the front offline) the
+// kernel also writes the 4-bit residual q_r = clamp(rint(e / (s/8)), -8, 7),
+// e = RN(x~ - RN(s q)), taken against the stored scale, into res_pad / 128
+// extra tiles that follow each row block's K / 128 code tiles.
+//
 // Asymmetric mode (OffQ page, "Metodología" steps 2-3): one scale and zero
 // point per token and Hadamard block, s = (max - min) / 15,
 // z = rint(-min / s) (an integer, not clamped), q = clamp(rint(x~ / s) + z,
@@ -117,6 +123,9 @@ struct RotqKArgs {
   float fqmax;       // largest code: 7 (int4) or 127 (int8 activations)
   int asym;          // asymmetric uint4 codes with zero points (packed modes)
   int32_t* zero;     // asym: zero points, laid out like the scales
+  int res_r;         // residual codes for channels [0, res_r) (tiled weights)
+  int res_pad;       // res_r rounded up to 128 (0: no residual)
+  int64_t tile_stride;  // 128-code tiles per 16-row block of the tiled output
   float* xrot;
   uint8_t* q;
   void* scale;
@@ -337,6 +346,8 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   // code[r] holds the code of element r in its low bits (two's complement:
   // low nibble = q & 0xF, low byte = q & 0xFF).
   uint32_t code[R];
+  uint32_t rpk[R / 8];  // packed residual codes (weights with a residual)
+  const bool res_lane = kfirst < a.res_pad;
   if (a.asym) {
     // 4a. min and max of the group (of y; x~ = RN(y * rs) is monotone in y).
     float ymax = v[0], ymin = v[0];
@@ -447,10 +458,33 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         code[r] = static_cast<uint32_t>(static_cast<int>(qf));
       }
     }
+    // 7. Residual codes of the first res_r channels, packed like the codes.
+    if (res_lane) {
+      const float t = s_eff * 0.125f;  // the residual step s / 8
+#pragma unroll
+      for (int d = 0; d < R / 8; ++d) {
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int r = 8 * d + u;
+          int qr = 0;
+          if (kfirst + r < a.res_r && t > 0.f) {
+            const int q = static_cast<int>(code[r] << 28) >> 28;
+            const float xt = v[r] * a.rs;
+            const float e = xt - s_eff * static_cast<float>(q);
+            qr = static_cast<int>(rintf(__fdiv_rn(e, t)));
+            qr = min(max(qr, -8), 7);
+          }
+          acc = __builtin_amdgcn_alignbit(static_cast<uint32_t>(qr), acc, 4);
+        }
+        rpk[d] = acc;
+      }
+    }
   }
   if (!valid) return;
   const bool tiled = a.mode == ROTQ_QUANT_TILED || a.mode == ROTQ_QUANT_I8_TILED;
   const int64_t nkit = a.K / 128;               // 128-code K iterations per row
+  const int64_t tstride = a.tile_stride;        // tiles per row block of the output
   const int64_t rblk = row >> 4, rin = row & 15;  // 16-row block, row inside it
   if (a.mode == ROTQ_QUANT || a.mode == ROTQ_QUANT_TILED) {
     // Packed nibbles: element 8d+t in nibble t of dword d.
@@ -479,7 +513,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 #pragma unroll
       for (int c = 0; c < (R >= 32 ? R / 32 : 1); ++c) {
         const int64_t j = (kfirst >> 1) + c * 16;
-        uint8_t* dst = a.q + (rblk * nkit + (j >> 6)) * 1024 + ((((j & 63) >> 4) * 16 + rin) << 4) +
+        uint8_t* dst = a.q + (rblk * tstride + (j >> 6)) * 1024 + ((((j & 63) >> 4) * 16 + rin) << 4) +
                        (j & 15);
         if constexpr (R == 8) {
           *reinterpret_cast<uint32_t*>(dst) = pk[0];
@@ -487,6 +521,23 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
         } else {
           *reinterpret_cast<uint4*>(dst) = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
+        }
+      }
+    }
+    if (tiled && res_lane) {
+      // Residual: packed byte jj of the residual region sits in tile
+      // (rblk, nkit + jj / 64) at the same in-tile place as a code byte.
+#pragma unroll
+      for (int c = 0; c < (R >= 32 ? R / 32 : 1); ++c) {
+        const int64_t jj = (kfirst >> 1) + c * 16;
+        uint8_t* dst = a.q + (rblk * tstride + nkit + (jj >> 6)) * 1024 +
+                       ((((jj & 63) >> 4) * 16 + rin) << 4) + (jj & 15);
+        if constexpr (R == 8) {
+          *reinterpret_cast<uint32_t*>(dst) = rpk[0];
+        } else if constexpr (R == 16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(rpk[0], rpk[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(rpk[4 * c], rpk[4 * c + 1], rpk[4 * c + 2], rpk[4 * c + 3]);
         }
       }
     }
@@ -520,7 +571,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
 #pragma unroll
       for (int c = 0; c < (R >= 16 ? R / 16 : 1); ++c) {
         const int64_t k = kfirst + c * 16;
-        uint8_t* dst = a.q + (rblk * nkit + (k >> 7)) * 2048 +
+        uint8_t* dst = a.q + (rblk * tstride + (k >> 7)) * 2048 +
                        ((((((k & 31) >> 4) << 2) + ((k & 127) >> 5)) * 16 + rin) << 4) + (k & 15);
         if constexpr (R == 8) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
@@ -620,6 +671,9 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.fqmax = (ex && ex->qmax == 127) ? 127.0f : 7.0f;
   ka.asym = (ex && ex->asym_zero) ? 1 : 0;
   ka.zero = ex ? ex->asym_zero : nullptr;
+  ka.res_r = ex ? ex->res_r : 0;
+  ka.res_pad = (ka.res_r + 127) / 128 * 128;
+  ka.tile_stride = K / 128 + ka.res_pad / 128;
   ka.xrot = xrot;
   ka.q = q;
   ka.scale = scale;

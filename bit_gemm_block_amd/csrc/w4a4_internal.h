@@ -50,6 +50,9 @@ struct RotqExtras {
   // int32 zero point per group of gsz elements, zero points written here;
   // the nibbles hold q - 8.
   int32_t* asym_zero = nullptr;
+  // Tiled weights only: residual codes of channels [0, res_r) in
+  // ceil(res_r / 128) extra tiles after each row block's K / 128 tiles.
+  int res_r = 0;
   const void* lr_at = nullptr;
   int lr_rank = 0;
   void* lr_t = nullptr;
@@ -94,6 +97,13 @@ struct GemmArgs {
   const int32_t* zx;
   const int32_t* wsum;
   int agroup;
+  // In-GEMM residual (res non-zero; packed tiled codes, tiled weights whose
+  // row blocks hold K / 128 + res_iters tiles, no groups, no low-rank term):
+  // the last res_iters (>= 0) iterations multiply the first 128 * res_iters
+  // code columns again, by the residual tiles, at 1/8 the weight of the main
+  // sum; acc holds 8 sum_k + sum_{k<r}.
+  int res;
+  int res_iters;
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);

@@ -53,6 +53,11 @@ _SIGS = {
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "w4a4_quantize_act_asym_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _P,
                                            _P]),
+    "w4a4_quantize_weight_residual_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT,
+                                                  _P]),
+    "w4a4_qgemm_residual": (_INT, [_P, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_qlinear_forward_residual": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
+                                             _P, _P, ctypes.c_size_t, _P]),
     "w4a4_weight_group_sums": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P]),
     "w4a4_qgemm_asym": (_INT, [_P, _P, _P, _I64, _P, _P, _INT, _P, _I64, _I64, _I64, _P, _P]),
     "w4a4_qlinear_forward_asym": (_INT, [_P, _INT, _P, _P, _INT, _P, _I64, _I64, _I64, _I64, _P,
@@ -382,4 +387,68 @@ def qlinear_forward_asym(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tenso
         _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), _ptr(w_gsum), M, N, K,
         had_block, _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(),
         _stream(x)))
+    return y
+
+
+# ---- in-GEMM residual of salient channels ----------------------------------
+def res_pad(r: int) -> int:
+    """Residual rank rounded up to whole 128-channel tiles."""
+    return (r + 127) // 128 * 128
+
+
+def quantize_weight_residual_int4(w: torch.Tensor, had_block: int, res_rank: int,
+                                  scale_dtype: torch.dtype = torch.float16):
+    """Tiled packed codes with the residual tiles of channels [0, res_rank)
+    after each row block's code tiles ([pad16(N), (K + res_pad)/2]), and the
+    per-channel scales [N]."""
+    _dev(w, "w")
+    N, K = w.shape
+    wq = torch.empty((pad16(N), (K + res_pad(res_rank)) // 2), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((N,), dtype=scale_dtype, device=w.device)
+    _check("quantize_weight_residual_int4", lib().w4a4_quantize_weight_residual_int4(
+        _ptr(w), _dt(w), N, K, had_block, res_rank, _ptr(wq), _ptr(ws), _dt(ws), _stream(w)))
+    return wq, ws
+
+
+def qgemm_residual(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tensor,
+                   w_scale: Optional[torch.Tensor], res_rank: int, M: int, N: int, K: int,
+                   want_y: bool = True, want_acc: bool = False,
+                   y: Optional[torch.Tensor] = None, acc: Optional[torch.Tensor] = None):
+    """Packed tiled codes times residual-extended tiled weights."""
+    _dev(xq, "xq")
+    _dev(wq, "wq")
+    if xq.shape[1] != K // 2 or xq.shape[0] < pad16(M):
+        raise ValueError("xq does not match M and K")
+    if wq.shape[1] != (K + res_pad(res_rank)) // 2 or wq.shape[0] < pad16(N):
+        raise ValueError("wq does not match N, K and the residual rank")
+    if want_y and y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if want_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    wst = _dt(w_scale) if w_scale is not None else F32
+    _check("qgemm_residual", lib().w4a4_qgemm_residual(
+        _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), wst, res_rank, M, N, K, _ptr(y),
+        _ptr(acc), _stream(xq)))
+    return y, acc
+
+
+def qlinear_forward_residual(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                             res_rank: int, had_block: int, y: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer with the in-GEMM residual of the first res_rank channels."""
+    _dev(x, "x")
+    _dev(wq, "wq")
+    _dev(w_scale, "w_scale")
+    M, K = x.shape
+    N = w_scale.shape[0]
+    if wq.shape[0] < pad16(N) or wq.shape[1] != (K + res_pad(res_rank)) // 2:
+        raise ValueError("wq does not match w_scale, x and the residual rank")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = qlinear_workspace_size(M, N, K, 0)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check("qlinear_forward_residual", lib().w4a4_qlinear_forward_residual(
+        _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), res_rank, M, N, K, had_block,
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
     return y

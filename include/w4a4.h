@@ -244,6 +244,59 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          size_t ws_bytes, void* stream);
 
 /*
+ * In-GEMM 4-bit residual of salient channels (SERQ page, "Metodología"
+ * items 2-3): the weight rows that collect the most quantization error
+ * (input channels, permuted offline so that they are the first r channels,
+ * with the activations reordered by the previous layer) are reconstructed
+ * by one 4-bit matrix R, and the layer adds X_s . R^T with X_s the same
+ * 4-bit activation codes of those channels.  Here R is the rounding error of
+ * those channels' weights on the step s_w / 8:
+ *   e = RN(w~ - RN(s_w q)),  q_r = clamp(rint(RN(e / RN(s_w / 8))), -8, 7),
+ *   y[m,n] = s_x[m] s_w[n] (sum_k q_x qw + (1/8) sum_{k<r} q_x q_r),
+ * computed as one int32 sum 8 sum_k q_x qw + sum_{k<r} q_x q_r in the same
+ * int8 matrix loop (r extra K columns, rounded up to 128).
+ * Limits: K a multiple of 128, 0 <= r <= K and 8 K + r_pad < 131072
+ * (r_pad = r rounded up to a multiple of 128), which keeps the int32 sum
+ * exact for 4-bit codes.
+ */
+
+/*
+ * Offline weight preparation with the residual: as w4a4_quantize_weight_int4
+ * with per-channel scales (w_group 0) and W4A4_WEIGHTS_TILED output, plus
+ * the residual codes of channels [0, res_rank).
+ *   wq  [ceil(N/16)*16, (K + r_pad)/2] bytes: every 16-row block holds its
+ *       K/128 code tiles followed by r_pad/128 residual tiles in the same
+ *       1 KB tile layout (residual tile t' holds channels 128 t' ...; codes
+ *       of channels r .. r_pad - 1 are 0).
+ *   w_scale [N] in scale_dtype.
+ */
+int w4a4_quantize_weight_residual_int4(const void* w, int w_dtype, int64_t N, int64_t K,
+                                       int64_t had_block, int64_t res_rank, uint8_t* wq,
+                                       void* w_scale, int scale_dtype, void* stream);
+
+/*
+ * GEMM with the in-GEMM residual: xq W4A4_CODES_PACKED_TILED codes and
+ * x_scale [M]; wq, w_scale from w4a4_quantize_weight_residual_int4 with the
+ * same res_rank.
+ *   y   [M, N] float32: s_x[m] s_w[n] (acc[m,n] / 8), or NULL;
+ *   acc [M, N] int32: the exact 8 sum_k q_x qw + sum_{k<r} q_x q_r, or NULL.
+ */
+int w4a4_qgemm_residual(const uint8_t* xq, const float* x_scale, const uint8_t* wq,
+                        const void* w_scale, int w_scale_dtype, int64_t res_rank, int64_t M,
+                        int64_t N, int64_t K, float* y, int32_t* acc, void* stream);
+
+/*
+ * The layer with the in-GEMM residual: rotate + quantize X per token
+ * (w4a4_quantize_act_int4's rule), then w4a4_qgemm_residual.
+ *   workspace: at least w4a4_qlinear_workspace_size(M, N, K, 0) bytes.
+ *   Other arguments and errors as w4a4_qlinear_forward.
+ */
+int w4a4_qlinear_forward_residual(const void* x, int x_dtype, const uint8_t* wq,
+                                  const void* w_scale, int w_scale_dtype, int64_t res_rank,
+                                  int64_t M, int64_t N, int64_t K, int64_t had_block, float* y,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Asymmetric group-wise activations (OffQ page, "Metodología" steps 2-3):
  * the all-ones first row of the Hadamard block turns a channel's outlier
  * into a constant offset over its group, which the zero point of a

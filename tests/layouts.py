@@ -60,3 +60,25 @@ def untile_weights(tiled, N):
     Np, H = tiled.shape
     t = tiled.reshape(Np // 16, H // 64, 4, 16, 16).transpose(0, 3, 1, 2, 4)
     return np.ascontiguousarray(t).reshape(Np, H)[:N]
+
+
+def tile_weights_residual(packed, packed_res, rng=None):
+    """Residual-extended tiled weights: every 16-row block holds the K/128
+    tiles of packed [N, K/2] followed by the r_pad/128 tiles of packed_res
+    [N, r_pad/2], each in the W4A4_WEIGHTS_TILED tile layout."""
+    main = tile_weights(packed, rng)
+    res = tile_weights(packed_res, rng)
+    Np = main.shape[0]
+    m = main.reshape(Np // 16, -1, 1024)
+    r = res.reshape(Np // 16, -1, 1024)
+    return np.ascontiguousarray(np.concatenate([m, r], axis=1)).reshape(Np, -1)
+
+
+def untile_weights_residual(ext, N, K):
+    """Inverse of tile_weights_residual: (packed [N, K/2], packed_res [N, r_pad/2])."""
+    Np, H = ext.shape
+    t = ext.reshape(Np // 16, H // 64, 1024)
+    nk = K // 128
+    main = np.ascontiguousarray(t[:, :nk]).reshape(Np, K // 2)
+    res = np.ascontiguousarray(t[:, nk:]).reshape(Np, H - K // 2)
+    return untile_weights(main, N), untile_weights(res, N)

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 16
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -138,6 +138,34 @@ def test_qlinear_argument_errors(lib):
     assert f(*bad) == W.ERR_INVALID_ARG
     bad = list(args); bad[3] = W.WEIGHTS_TILED; bad[10] = 64          # tiled needs group % 128
     assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[6] = 0
+    assert f(*bad) == W.OK
+
+
+def test_residual_argument_errors(lib):
+    w = lib.w4a4_quantize_weight_residual_int4
+    assert w(P, W.F32, 8, 256, 0, -1, P, P, W.F16, None) == W.ERR_INVALID_ARG      # r < 0
+    assert w(P, W.F32, 8, 256, 0, 300, P, P, W.F16, None) == W.ERR_UNSUPPORTED     # r > K
+    assert w(P, W.F32, 8, 192, 0, 32, P, P, W.F16, None) == W.ERR_UNSUPPORTED      # K % 128
+    assert w(P, W.F32, 8, 16384, 0, 32, P, P, W.F16, None) == W.ERR_UNSUPPORTED    # int32 bound
+    assert w(P, W.F32, 8, 256, 0, 32, None, P, W.F16, None) == W.ERR_INVALID_ARG
+    assert w(P, W.F32, 8, 256, 0, 32, P, Q, W.F16, None) == W.ERR_MISALIGNED
+    assert w(None, W.F32, 0, 256, 0, 32, None, None, W.F16, None) == W.OK
+    g = lib.w4a4_qgemm_residual
+    assert g(P, P, P, P, W.F16, 32, 4, 8, 256, None, None, None) == W.ERR_INVALID_ARG  # no output
+    assert g(P, None, P, P, W.F16, 32, 4, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # y needs scales
+    assert g(P, P, P, P, W.F16, 32, 4, 8, 320, P, None, None) == W.ERR_UNSUPPORTED     # K % 128
+    assert g(P, P, Q, P, W.F16, 32, 4, 8, 256, P, None, None) == W.ERR_MISALIGNED
+    assert g(None, None, None, None, W.F16, 32, 0, 8, 256, None, None, None) == W.OK
+    f = lib.w4a4_qlinear_forward_residual
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 512, 0)
+    args = [P, W.F16, P, P, W.F16, 64, 16, 32, 512, 128, P, P, need, None]
+    bad = list(args); bad[5] = 600
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[12] = need - 1
+    assert f(*bad) == W.ERR_WORKSPACE
+    bad = list(args); bad[2] = None
+    assert f(*bad) == W.ERR_INVALID_ARG
     bad = list(args); bad[6] = 0
     assert f(*bad) == W.OK
 

@@ -3,6 +3,7 @@ put bytes where include/w4a4.h says they go."""
 import numpy as np
 
 from layouts import (codes_from_i8, i8_from_codes, tile_codes_i8, tile_weights, untile_codes_i8,
+                     tile_weights_residual, untile_weights_residual,
                      untile_weights)
 
 
@@ -33,3 +34,22 @@ def test_tiling_helpers_are_inverse_permutations():
         for j in range(H):
             off = ((n // 16) * (H // 64) + j // 64) * 1024 + (16 * ((j % 64) // 16) + n % 16) * 16 + j % 16
             assert tw[off] == wq[n, j]
+
+
+def test_residual_extended_tiling():
+    # every row block holds its K/128 code tiles, then its residual tiles
+    rng = np.random.default_rng(6)
+    N, K, rp = 21, 384, 256
+    main = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    res = rng.integers(0, 256, (N, rp // 2), dtype=np.uint8)
+    ext = tile_weights_residual(main, res)
+    assert ext.shape == (32, (K + rp) // 2)
+    m2, r2 = untile_weights_residual(ext, N, K)
+    assert np.array_equal(m2, main) and np.array_equal(r2, res)
+    flat = ext.reshape(-1)
+    nt = (K + rp) // 128
+    for n in range(N):
+        for jj in range(rp // 2):
+            t = K // 128 + jj // 64
+            off = ((n // 16) * nt + t) * 1024 + (16 * ((jj % 64) // 16) + n % 16) * 16 + jj % 16
+            assert flat[off] == res[n, jj]
