@@ -17,7 +17,8 @@ synchronisation and timed with events on the stream the kernels run on.
 A third leg runs the layer with asymmetric group-wise activations (per
 token and 128-channel group: scale and zero point) on the Llama-3-8B o-proj
 shape (4096 x 4096 x 4096, rank-32 term), beside the symmetric layer on the
-same workload.
+same workload.  A fourth runs the same shape with the in-GEMM 4-bit residual
+of 32 salient channels in place of the rank-32 term.
 
 The roofline object is the GEMM kernel alone (the dominant kernel): its
 average launch duration from events around --steps back-to-back launches,
@@ -279,6 +280,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offq", action="store_true")
+    ap.add_argument("--no-serq", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the prefill kernels and a calibration copy (for counters)")
     args = ap.parse_args()
@@ -364,6 +366,43 @@ def main() -> int:
         }
         del lay
 
+    # ---- in-GEMM 4-bit residual of salient channels, same o-proj shape -------
+    serq = None
+    if not args.no_serq:
+        rw = synth.by_name("llama3_8b_o_4096x4096x4096")
+        r, b = rw.rank, rw.had_block       # the residual takes the rank-32 term's place
+        d = synth.make_inputs(rw)
+        dev = "cuda:0"
+        x = torch.from_numpy(d["X"]).to(dev)
+        Wd = torch.from_numpy(d["W"]).to(dev)
+        wq, ws = W.quantize_weight_residual_int4(Wd, b, r, torch.float16)
+        del Wd, d
+        y = torch.empty((rw.M, rw.N), dtype=torch.float32, device=dev)
+        wsb = torch.empty((W.qlinear_workspace_size(rw.M, rw.N, rw.K, 0),), dtype=torch.uint8,
+                          device=dev)
+        log(f"serq: {rw.name} with an in-GEMM residual of {r} channels, timing {args.steps} steps")
+        t_res = time_graph(lambda i: W.qlinear_forward_residual(x, wq, ws, r, b, y=y, workspace=wsb),
+                           args.steps, args.warmup)
+        xq, sx = W.quantize_act_int4(x, b, layout="packed_tiled")
+        torch.cuda.synchronize()
+        t_g = time_graph(lambda i: W.qgemm_residual(xq, sx, wq, ws, r, rw.M, rw.N, rw.K, y=y),
+                         args.steps, args.warmup)
+        ops = 2 * rw.M * rw.N * rw.K
+        log(f"serq: {t_res * 1e6:.2f} us/step ({ops / t_res / 1e12:.1f} TOP/s); qgemm_residual "
+            f"{t_g * 1e6:.2f} us ({ops / t_g / 1e12:.1f} TOP/s)")
+        serq = {
+            "metric": "W4A4 qlinear TOPS with the in-GEMM 4-bit residual",
+            "value": ops / t_res / 1e12, "unit": "TOP/s", "ms_per_step": t_res * 1e3,
+            "gemm": {"kernel": "qgemm_pipe_kernel (residual)", "achieved": ops / t_g / 1e12,
+                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": ops / t_g / 1e12 / PEAK_INT8_TOPS, "us_per_launch": t_g * 1e6,
+                     "ops_per_launch": ops},
+            "dense_lowrank_same_workload": (offq or {}).get("symmetric_same_workload"),
+            "config": {"workload": rw.name, "M": rw.M, "N": rw.N, "K": rw.K, "had_block": b,
+                       "residual_channels": r},
+        }
+        del x, wq, ws, y, wsb, xq, sx
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
@@ -398,6 +437,7 @@ def main() -> int:
                  "unit": "TOP/s", "ms_per_step": t_step8 * 1e3},
         "decode": decode,
         "offq": offq,
+        "serq": serq,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
