@@ -54,6 +54,16 @@ What is computed, and where the pages fix it
   Y = s_x s_w (sum_k q_x q_w + (1/8) sum_{k<r} q_x q_r).  The step s/8 lets
   R cover the whole rounding error (|e| <= s/2 gives |q_r| <= 4) and keeps
   both sums in one integer: 8 sum_k q_x q_w + sum_{k<r} q_x q_r.
+* MXFP4 (SERQ page, "Metodología" item 2 and "Contribuciones Clave": the
+  4-bit path may be INT4 or MXFP4, the microscaling format): read as the
+  OCP microscaling definition.  Every 32 consecutive elements along K share
+  a power-of-two scale 2^e (an E8M0 byte e + 127) with
+  e = max(floor(log2(max|v|)) - 2, -127) (e = -127 for an all-zero block);
+  each element is v / 2^e rounded to the nearest FP4 E2M1 value
+  {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even encoding, saturating at 6),
+  with the sign in bit 3 (set only for negative quotients).  Rotation as
+  above; Y = sum_blocks 2^(e_x + e_w) sum_k fp4_x fp4_w, exact in float64,
+  rounded once to float32, + the low-rank term.
 * W4A8 layers: the layers a phase-aware policy keeps at 8-bit activations
   while the weights stay 4-bit (DynamicPTQ page, "Metodología" §2).  The
   same rotation and the same per-token symmetric absmax rule with qmax 127:
@@ -426,3 +436,84 @@ def qlinear_forward_residual(X: np.ndarray, wq_packed: np.ndarray, w_scale: np.n
     _, s_x, qx, _ = quantize_activation(X, had_block)
     qw = unpack_int4(wq_packed)
     return residual_from_codes(qx, s_x, qw, np.asarray(w_scale).astype(np.float32), qr)
+
+
+# ----------------------------------------------------------------------------
+# MXFP4 (SERQ page, "Metodología" item 2; the OCP microscaling format)
+# ----------------------------------------------------------------------------
+MX_BLOCK = 32
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_code(p: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 encoding of float values p: magnitude bits from the nearest
+    of E2M1 (ties to the even encoding, |p| > 6 saturates to 6), sign bit 8
+    for p < 0."""
+    p = np.asarray(p, dtype=np.float64)
+    a = np.abs(p)
+    # upper bounds of each magnitude code; '<=' where the tie goes down
+    # (to the even code), '<' where it goes up
+    mag = np.full(p.shape, 7, dtype=np.int16)
+    for code, bound, inclusive in ((6, 5.0, True), (5, 3.5, False), (4, 2.5, True),
+                                   (3, 1.75, False), (2, 1.25, True), (1, 0.75, False),
+                                   (0, 0.25, True)):
+        hit = (a <= bound) if inclusive else (a < bound)
+        mag = np.where(hit, code, mag)
+    return (mag | np.where(p < 0, 8, 0)).astype(np.uint8)
+
+
+def e2m1_value(code: np.ndarray) -> np.ndarray:
+    """Value of FP4 E2M1 codes (0..15)."""
+    c = np.asarray(code).astype(np.int64)
+    v = E2M1[c & 7]
+    return np.where(c & 8, -v, v)
+
+
+def mx_block_exponent(amax: np.ndarray) -> np.ndarray:
+    """e = max(floor(log2(amax)) - 2, -127), with -127 for amax = 0."""
+    amax = np.asarray(amax, dtype=np.float64)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    pos = amax > 0
+    e[pos] = np.maximum(np.floor(np.log2(amax[pos])).astype(np.int64) - 2, -127)
+    return e
+
+
+def quantize_mxfp4(v32: np.ndarray):
+    """MXFP4 of float32 rows [R, K] (K a multiple of 32).
+
+    Returns (codes uint8 [R, K] in 0..15, block exponents int [R, K/32]);
+    the E8M0 byte of a block is exponent + 127."""
+    v = np.asarray(v32, dtype=np.float32).astype(np.float64)
+    R, K = v.shape
+    blocks = v.reshape(R, K // MX_BLOCK, MX_BLOCK)
+    e = mx_block_exponent(np.abs(blocks).max(axis=2))
+    p = blocks / np.exp2(e)[:, :, None]           # exact: a power-of-two scaling
+    return e2m1_code(p).reshape(R, K), e
+
+
+def mxfp4_values(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """Dequantized values fp4(code) 2^e, float64 [R, K]."""
+    R, K = codes.shape
+    v = e2m1_value(codes).reshape(R, K // MX_BLOCK, MX_BLOCK) * np.exp2(e)[:, :, None]
+    return v.reshape(R, K)
+
+
+def mxfp4_gemm(cx: np.ndarray, ex: np.ndarray, cw: np.ndarray, ew: np.ndarray) -> np.ndarray:
+    """sum_blocks 2^(ex + ew) sum_k fp4_x fp4_w as float64 [M, N] (exact:
+    every product of two E2M1 values is a multiple of 1/4 and the partial
+    sums stay far below 2^53 times the smallest scale)."""
+    return mxfp4_values(cx, ex) @ mxfp4_values(cw, ew).T
+
+
+def qlinear_forward_mxfp4(X: np.ndarray, W: np.ndarray, had_block: int, A=None, B=None) -> np.ndarray:
+    """The MXFP4 layer: rotate X and W, quantize both to MXFP4, multiply,
+    add the low-rank term; float64 then rounded once to float32."""
+    xr = rotate(X, had_block) if had_block > 1 else np.asarray(X, np.float32)
+    wr = rotate(W, had_block) if had_block > 1 else np.asarray(W, np.float32)
+    cx, ex = quantize_mxfp4(xr)
+    cw, ew = quantize_mxfp4(wr)
+    y = mxfp4_gemm(cx, ex, cw, ew)
+    lr = lowrank(X, A, B)
+    if lr is not None:
+        y = y + lr
+    return y.astype(np.float32)
