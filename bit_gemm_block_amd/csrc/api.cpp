@@ -378,6 +378,119 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_la
                       w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
 }
 
+// ---- MXFP4 -----------------------------------------------------------------
+
+int w4a4_quantize_mxfp4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                        uint8_t* xq, int codes_layout, uint8_t* x_scale, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0) return W4A4_ERR_INVALID_ARG;
+  if (codes_layout != W4A4_CODES_PACKED && codes_layout != W4A4_CODES_PACKED_TILED)
+    return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if (codes_layout == W4A4_CODES_PACKED_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0) return W4A4_OK;
+  if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  w4a4::RotqExtras ex;
+  ex.mx_scale = x_scale;
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(
+      x, x_dtype == W4A4_F16, M, K, log2b,
+      codes_layout == W4A4_CODES_PACKED_TILED ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT, K, false,
+      nullptr, xq, nullptr, plan, static_cast<hipStream_t>(stream), &ex);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qgemm_mxfp4(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* wq,
+                     const uint8_t* w_scale, int64_t M, int64_t N, int64_t K, float* y,
+                     void* stream) {
+  if (M < 0 || N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 128 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!xq || !x_scale || !wq || !w_scale || !y) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(xq) || !aligned16(x_scale) || !aligned16(wq) || !aligned16(w_scale) ||
+      !aligned16(y))
+    return W4A4_ERR_MISALIGNED;
+  int s = device_check(nullptr);
+  if (s != W4A4_OK) return s;
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.wq = wq;
+  g.M = M; g.N = N; g.K = K;
+  g.y = y;
+  g.lr_mode = w4a4::LR_NONE;
+  g.tiled = 1;
+  g.mx_xs = x_scale;
+  g.mx_ws = w_scale;
+  hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_qlinear_forward_mxfp4(const void* x, int x_dtype, const uint8_t* wq,
+                               const uint8_t* w_scale, int64_t M, int64_t N, int64_t K,
+                               int64_t had_block, const void* At, const void* Bt, int64_t rank,
+                               float* y, void* workspace, size_t ws_bytes, void* stream) {
+  if (!dtype_ok(x_dtype) || M < 0 || N < 0 || rank < 0) return W4A4_ERR_INVALID_ARG;
+  int s = check_k_had(K, had_block, false);
+  if (s != W4A4_OK) return s;
+  if (K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if (rank > kMaxRank || (x_dtype == W4A4_F16 && rank % 8 != 0)) return W4A4_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return W4A4_OK;
+  if (!x || !wq || !w_scale || !y || !workspace) return W4A4_ERR_INVALID_ARG;
+  if (rank > 0 && (!At || !Bt)) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wq) || !aligned16(w_scale) || !aligned16(y) ||
+      !aligned16(workspace) || (rank > 0 && (!aligned16(At) || !aligned16(Bt))))
+    return W4A4_ERR_MISALIGNED;
+  const WsLayout L = ws_layout(M, K, rank);
+  if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
+  // Codes take half of the int8 code area, their scale tiles 1/16 of it.
+  const size_t rows = static_cast<size_t>((M + 15) / 16 * 16);
+  const size_t xs_off = align256(rows * static_cast<size_t>(K / 2));
+  if (xs_off + rows * static_cast<size_t>(K / 32) > L.sx) return W4A4_ERR_UNSUPPORTED;
+  int max_lds = 0;
+  if ((s = device_check(&max_lds)) != W4A4_OK) return s;
+  w4a4::RotqPlan plan;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* xq = ws + L.xq;
+  uint8_t* xs = ws + xs_off;
+  void* t = ws + L.t;
+  const bool f16 = x_dtype == W4A4_F16;
+  w4a4::RotqExtras ex;
+  ex.mx_scale = xs;
+  const bool fuse_lr = rank > 0 && f16 && M <= 16;
+  if (fuse_lr) {
+    ex.lr_at = At;
+    ex.lr_rank = static_cast<int>(rank);
+    ex.lr_t = t;
+  }
+  const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b, w4a4::ROTQ_QUANT_TILED, K, false, nullptr,
+                                   xq, nullptr, plan, st, &ex);
+  if (e != hipSuccess) return hip_fail(e);
+  if (rank > 0 && !fuse_lr) {
+    e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  w4a4::GemmArgs g{};
+  g.xq = xq; g.wq = wq;
+  g.M = M; g.N = N; g.K = K;
+  g.y = y;
+  g.t = rank > 0 ? t : nullptr;
+  g.B = rank > 0 ? Bt : nullptr;
+  g.lr_mode = rank == 0 ? w4a4::LR_NONE : (f16 ? w4a4::LR_F16 : w4a4::LR_F32);
+  g.rank = static_cast<int>(rank);
+  g.tiled = 1;
+  g.mx_xs = xs;
+  g.mx_ws = w_scale;
+  e = w4a4::launch_qgemm(g, st);
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
 // ---- in-GEMM residual of salient channels ---------------------------------
 
 namespace {

@@ -963,6 +963,197 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   }
 }
 
+// MXFP4 GEMM (SERQ page, "Metodología" item 2: the 4-bit path in MXFP4).
+// Codes are FP4 E2M1 in the packed tiled layout, with one E8M0 scale byte
+// per 32 elements in 64-byte tiles.  The tile layout is already the operand
+// layout of v_mfma_scale_f32_16x16x128_f8f6f4 (lane 16 g + r: row r,
+// elements 32 g .. 32 g + 31 of the 128-element step, low nibble first; the
+// lane's scale byte covers exactly those 32), so one instruction per 16x16
+// block and 128-element step takes the fragments as they are, with no
+// widening.  Per stage each wave also copies one 256-byte run of scales:
+// waves 0-1 the A row blocks, waves 2-3 the B column blocks.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+template <int TM, int TN, int STAGES, int LRMODE>
+__global__ void __launch_bounds__(256) qgemm_mx_kernel(GemmArgs a) {
+  constexpr int WM = TM * 16, WN = TN * 16;
+  constexpr int BM = 2 * WM, BN = 2 * WN;
+  constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+  constexpr int SA_BYTES = BM / 16 * 64, SB_BYTES = BN / 16 * 64;
+  static_assert(SA_BYTES == 512 && SB_BYTES == 512, "two scale runs per side");
+  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  constexpr int A_RUNS = BM / 16, B_RUNS = BN / 16;
+  constexpr int RUNS = A_RUNS + B_RUNS;
+  static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
+  constexpr int RUNS_PER_WAVE = RUNS / 4 + 1;  // + the scale run
+  static_assert((STAGES - 1) * RUNS_PER_WAVE < 64, "in-flight copies exceed vmcnt");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGES > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t st3[STAGES > 3 ? STAGE : 16];
+  auto stage = [&](int sidx) -> uint8_t* {
+    switch (sidx) {
+      case 0: return st0;
+      case 1: return st1;
+      case 2: return st2;
+      default: return st3;
+    }
+  };
+  static_assert(STAGES >= 2 && STAGES <= 4, "stages");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm0 = (wave >> 1) * WM;
+  const int wn0 = (wave & 1) * WN;
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (a.N + BN - 1) / BN;
+  int64_t tmi, tni;
+  tile_of(blockIdx.x, tiles_m, tiles_n, &tmi, &tni);
+  const int64_t m0 = tmi * BM;
+  const int64_t n0 = tni * BN;
+  const int nkt = static_cast<int>(a.K / 128);
+  const int64_t mblocks = (a.M + 15) / 16, nblocks = (a.N + 15) / 16;
+
+  // Code runs: one contiguous 1 KB tile each.  Scale run: 16 lanes x 16 B,
+  // lane l copying bytes 16 (l & 3) .. of the scale tile of block l / 4.
+  const uint8_t* src[RUNS_PER_WAVE];
+  int dst[RUNS_PER_WAVE];
+#pragma unroll
+  for (int q = 0; q < RUNS_PER_WAVE - 1; ++q) {
+    const int run = wave + 4 * q;
+    if (run < A_RUNS) {
+      int64_t mb = m0 / 16 + run;
+      mb = mb < mblocks ? mb : mblocks - 1;
+      src[q] = a.xq + mb * nkt * 1024 + 16 * lane;
+      dst[q] = (run * 4) << 8;
+    } else {
+      const int blk = run - A_RUNS;
+      int64_t nb = n0 / 16 + blk;
+      nb = nb < nblocks ? nb : nblocks - 1;
+      src[q] = a.wq + nb * nkt * 1024 + 16 * lane;
+      dst[q] = A_BYTES + ((blk * 4) << 8);
+    }
+  }
+  {
+    const int side = wave >> 1;                      // 0: A scales, 1: B scales
+    const int blk = (wave & 1) * 4 + ((lane & 15) >> 2);
+    int64_t b = (side ? n0 : m0) / 16 + blk;
+    const int64_t nbl = side ? nblocks : mblocks;
+    b = b < nbl ? b : nbl - 1;
+    src[RUNS_PER_WAVE - 1] = (side ? a.mx_ws : a.mx_xs) + b * nkt * 64 + 16 * (lane & 3);
+    dst[RUNS_PER_WAVE - 1] = A_BYTES + B_BYTES + side * SA_BYTES + (wave & 1) * 256;
+  }
+  auto issue = [&](int kt, uint8_t* base) {
+    const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
+#pragma unroll
+    for (int q = 0; q < RUNS_PER_WAVE - 1; ++q)
+      dma16(src[q] + static_cast<int64_t>(kt) * 1024, __builtin_amdgcn_readfirstlane(b + dst[q]));
+    if (lane < 16)
+      dma16(src[RUNS_PER_WAVE - 1] + static_cast<int64_t>(kt) * 64,
+            __builtin_amdgcn_readfirstlane(b + dst[RUNS_PER_WAVE - 1]));
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fg = lane >> 4;
+  auto read_frags = [&](const uint8_t* As, i32x4 (&fa)[TM], i32x4 (&fb)[TN], int (&sa)[TM],
+                        int (&sb)[TN]) {
+    const uint8_t* Bs = As + A_BYTES;
+    const uint8_t* Ss = As + A_BYTES + B_BYTES;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      fa[i] = *reinterpret_cast<const i32x4*>(As + ((((wm0 >> 4) + i) * 4 + fg) << 8) + (frow << 4));
+      sa[i] = Ss[((wm0 >> 4) + i) * 64 + fg * 16 + frow];
+    }
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      fb[j] = *reinterpret_cast<const i32x4*>(Bs + ((((wn0 >> 4) + j) * 4 + fg) << 8) + (frow << 4));
+      sb[j] = Ss[SA_BYTES + ((wn0 >> 4) + j) * 64 + fg * 16 + frow];
+    }
+  };
+  auto compute = [&](const i32x4 (&fa)[TM], const i32x4 (&fb)[TN], const int (&sa)[TM],
+                     const int (&sb)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const i32x8 av = {fa[i][0], fa[i][1], fa[i][2], fa[i][3], 0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const i32x8 bv = {fb[j][0], fb[j][1], fb[j][2], fb[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0,
+                                                                     sa[i], 0, sb[j]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int sidx = 0; sidx < STAGES; ++sidx)
+    if (sidx < nkt) issue(sidx, stage(sidx));
+  if (nkt >= STAGES)
+    wait_vmcnt<(STAGES - 1) * RUNS_PER_WAVE>();
+  else
+    wait_vmcnt<0>();
+  stage_barrier();
+  i32x4 fa0[TM], fa1[TM], fb0[TN], fb1[TN];
+  int sa0[TM], sa1[TM], sb0[TN], sb1[TN];
+  read_frags(stage(0), fa0, fb0, sa0, sb0);
+
+  auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[TM], i32x4 (&fbc)[TN], int (&sac)[TM],
+                     int (&sbc)[TN], i32x4 (&fan)[TM], i32x4 (&fbn)[TN], int (&san)[TM],
+                     int (&sbn)[TN]) {
+    if (kt + STAGES <= nkt)
+      wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
+    read_frags(stage((sbuf + 1) % STAGES), fan, fbn, san, sbn);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
+    compute(fac, fbc, sac, sbc);
+  };
+  for (int kt0 = 0; kt0 < nkt; kt0 += 2 * STAGES) {
+#pragma unroll
+    for (int u = 0; u < 2 * STAGES; ++u) {
+      const int kt = kt0 + u;
+      if (kt < nkt) {
+        if (u & 1)
+          iterate(kt, u % STAGES, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
+        else
+          iterate(kt, u % STAGES, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+      }
+    }
+  }
+
+  const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
+  const int64_t nlane = n0 + wn0 + (lane & 15);
+  const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t n = nlane + j * 16;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      f32x4 yv = acc[i][j];
+      if constexpr (LRMODE != LR_NONE)
+        yv = add_lowrank<LRMODE>(a, yv, m0 + wm0 + i * 16, n0 + wn0 + j * 16, lane);
+      const int64_t mb = mlane + i * 16;
+      if (interior) {
+        float* yp = a.y + mb * a.N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yp[r * a.N] = yv[r];
+      } else if (n < a.N) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mb + r < a.M) a.y[(mb + r) * a.N + n] = yv[r];
+      }
+    }
+  }
+}
+
 // Small M: 16 output columns per workgroup, KW waves split K.  MB row blocks
 // of 16 cover M <= 16 * MB.  Every lane loads, per 128-code K pair t, the 16
 // bytes [64t + 16g, 64t + 16g + 16) of its weight row (g = lane >> 4) and of
@@ -1257,7 +1448,20 @@ static hipError_t launch_pipe_res(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+static hipError_t launch_qgemm_mx(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(((a.M + 127) / 128) * ((a.N + 127) / 128)));
+#define W4A4_MX_CASE(LR)                                                               \
+  if (a.lr_mode == LR) {                                                               \
+    hipLaunchKernelGGL((qgemm_mx_kernel<4, 4, 3, LR>), grid, dim3(256), 0, st, a);     \
+    return hipGetLastError();                                                          \
+  }
+  W4A4_MX_CASE(LR_NONE) W4A4_MX_CASE(LR_F16) W4A4_MX_CASE(LR_F32)
+#undef W4A4_MX_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
+  if (a.mx_xs) return launch_qgemm_mx(a, st);
   if (a.res) return launch_pipe_res(a, st);
   // Asymmetric groups: a 32 x 64 wave tile, so that the row scales of every
   // group fit in LDS beside two workgroups per CU.

@@ -30,6 +30,13 @@
 // e = RN(x~ - RN(s q)), taken against the stored scale, into res_pad / 128
 // extra tiles that follow each row block's K / 128 code tiles.
 //
+// MXFP4 mode (SERQ page, "Metodología" item 2, read as the OCP
+// microscaling format): every 32 consecutive elements share the scale 2^e,
+// e = max(floor(log2(max|x~|)) - 2, -127), stored as the byte e + 127; each
+// element is x~ 2^-e (exact) rounded to the nearest E2M1 value
+// {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even encoding and saturation
+// at 6, sign in bit 3 for negative quotients.
+//
 // Asymmetric mode (OffQ page, "Metodología" steps 2-3): one scale and zero
 // point per token and Hadamard block, s = (max - min) / 15,
 // z = rint(-min / s) (an integer, not clamped), q = clamp(rint(x~ / s) + z,
@@ -123,9 +130,11 @@ struct RotqKArgs {
   float fqmax;       // largest code: 7 (int4) or 127 (int8 activations)
   int asym;          // asymmetric uint4 codes with zero points (packed modes)
   int32_t* zero;     // asym: zero points, laid out like the scales
+  int mx;            // MXFP4: E2M1 codes, one E8M0 scale byte per 32 elements
   int res_r;         // residual codes for channels [0, res_r) (tiled weights)
   int res_pad;       // res_r rounded up to 128 (0: no residual)
   int64_t tile_stride;  // 128-code tiles per 16-row block of the tiled output
+  uint8_t* mx_scale;    // MXFP4 scale bytes: [M, K/32], or tiled (64 B per 16 x 128 tile)
   float* xrot;
   uint8_t* q;
   void* scale;
@@ -348,7 +357,49 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   uint32_t code[R];
   uint32_t rpk[R / 8];  // packed residual codes (weights with a residual)
   const bool res_lane = kfirst < a.res_pad;
-  if (a.asym) {
+  if (a.mx) {
+    // 4m. block maxima over 32 elements: in-lane for R >= 32, else over the
+    // 32 / R lanes that hold one block.
+    constexpr int NB = R >= 32 ? R / 32 : 1;   // blocks per lane
+    constexpr int BL = R >= 32 ? 32 : R;        // elements of a block in this lane
+    float bm[NB];
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      float m = 0.f;
+#pragma unroll
+      for (int u = 0; u < BL; ++u) m = fmaxf(m, fabsf(v[c * BL + u]));
+      if constexpr (R < 32) {
+#pragma unroll
+        for (int o = 1; o < 32 / R; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      }
+      bm[c] = m;
+    }
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+      // e from the exponent field of RN(max|y| rs) = max|x~|: floor(log2)
+      // for normals; subnormals and 0 land on the clamp.
+      const float amax = bm[c] * a.rs;
+      const int e = max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 129, -127);
+      const int kb = kfirst + c * BL;           // first element of this lane's part
+      if (valid && (kb & 31) == 0) {
+        uint8_t* sp;
+        if (a.mode == ROTQ_QUANT_TILED)
+          sp = a.mx_scale + ((row >> 4) * (a.K / 128) + (kb >> 7)) * 64 + ((kb & 127) >> 5) * 16 +
+               (row & 15);
+        else
+          sp = a.mx_scale + row * (a.K / 32) + (kb >> 5);
+        *sp = static_cast<uint8_t>(e + 127);
+      }
+#pragma unroll
+      for (int u = 0; u < BL; ++u) {
+        const float p = ldexpf(v[c * BL + u] * a.rs, -e);
+        const float q = fabsf(p);
+        const uint32_t mag = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
+                             (q > 2.5f) + (q >= 3.5f) + (q > 5.f);
+        code[c * BL + u] = mag | (p < 0.f ? 8u : 0u);
+      }
+    }
+  } else if (a.asym) {
     // 4a. min and max of the group (of y; x~ = RN(y * rs) is monotone in y).
     float ymax = v[0], ymin = v[0];
 #pragma unroll
@@ -671,6 +722,8 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.fqmax = (ex && ex->qmax == 127) ? 127.0f : 7.0f;
   ka.asym = (ex && ex->asym_zero) ? 1 : 0;
   ka.zero = ex ? ex->asym_zero : nullptr;
+  ka.mx = (ex && ex->mx_scale) ? 1 : 0;
+  ka.mx_scale = ex ? ex->mx_scale : nullptr;
   ka.res_r = ex ? ex->res_r : 0;
   ka.res_pad = (ka.res_r + 127) / 128 * 128;
   ka.tile_stride = K / 128 + ka.res_pad / 128;

@@ -53,6 +53,10 @@ struct RotqExtras {
   // Tiled weights only: residual codes of channels [0, res_r) in
   // ceil(res_r / 128) extra tiles after each row block's K / 128 tiles.
   int res_r = 0;
+  // MXFP4 (packed modes): E2M1 codes and one E8M0 byte per 32 elements,
+  // written here ([M, K/32] row-major, or in 64-byte tiles with the tiled
+  // codes: byte (g * 16 + r) of tile (row block, t) is block 4 t + g of row r).
+  uint8_t* mx_scale = nullptr;
   const void* lr_at = nullptr;
   int lr_rank = 0;
   void* lr_t = nullptr;
@@ -104,6 +108,10 @@ struct GemmArgs {
   // sum; acc holds 8 sum_k + sum_{k<r}.
   int res;
   int res_iters;
+  // MXFP4 (mx_xs non-null): xq and wq hold E2M1 codes in the packed tiled
+  // layout, mx_xs and mx_ws their E8M0 scales in 64-byte tiles; sx, sw unused.
+  const uint8_t* mx_xs;
+  const uint8_t* mx_ws;
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);

@@ -56,6 +56,10 @@ _SIGS = {
     "w4a4_quantize_weight_residual_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT,
                                                   _P]),
     "w4a4_qgemm_residual": (_INT, [_P, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "w4a4_quantize_mxfp4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
+    "w4a4_qgemm_mxfp4": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "w4a4_qlinear_forward_mxfp4": (_INT, [_P, _INT, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64,
+                                          _P, _P, ctypes.c_size_t, _P]),
     "w4a4_qlinear_forward_residual": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                              _P, _P, ctypes.c_size_t, _P]),
     "w4a4_weight_group_sums": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P]),
@@ -450,5 +454,80 @@ def qlinear_forward_residual(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.T
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check("qlinear_forward_residual", lib().w4a4_qlinear_forward_residual(
         _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), res_rank, M, N, K, had_block,
+        _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
+    return y
+
+
+# ---- MXFP4 ------------------------------------------------------------------
+def mx_scale_bytes(rows: int, K: int, layout: str) -> int:
+    """Bytes of the E8M0 scales of [rows, K] MXFP4 codes in a layout."""
+    return pad16(rows) * K // 32 if layout == "packed_tiled" else rows * K // 32
+
+
+def quantize_mxfp4(x: torch.Tensor, had_block: int, layout: str = "packed",
+                   xq: Optional[torch.Tensor] = None, xs: Optional[torch.Tensor] = None):
+    """E2M1 codes (packed, [M, K/2] or tiled [pad16(M), K/2]) and E8M0 scale
+    bytes ([M, K/32], or the tiled scale array of w4a4_quantize_mxfp4)."""
+    _dev(x, "x")
+    M, K = x.shape
+    lay = _LAYOUTS[layout]
+    if lay not in _PACKED_CODES:
+        raise ValueError("MXFP4 codes are packed")
+    if xq is None:
+        xq = torch.empty((pad16(M) if lay in _TILED_CODES else M, K // 2), dtype=torch.uint8,
+                         device=x.device)
+    if xs is None:
+        xs = (torch.empty((M, K // 32), dtype=torch.uint8, device=x.device) if layout == "packed"
+              else torch.empty((mx_scale_bytes(M, K, layout),), dtype=torch.uint8, device=x.device))
+    _dev(xq, "xq")
+    _dev(xs, "xs")
+    _check("quantize_mxfp4", lib().w4a4_quantize_mxfp4(
+        _ptr(x), _dt(x), M, K, had_block, _ptr(xq), lay, _ptr(xs), _stream(x)))
+    return xq, xs
+
+
+def qgemm_mxfp4(xq: torch.Tensor, xs: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor,
+                M: int, N: int, K: int, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MXFP4 GEMM on tiled codes and scales."""
+    for t, n in ((xq, "xq"), (xs, "xs"), (wq, "wq"), (ws, "ws")):
+        _dev(t, n)
+    if xq.shape[1] != K // 2 or wq.shape[1] != K // 2 or xq.shape[0] < pad16(M) or \
+            wq.shape[0] < pad16(N):
+        raise ValueError("codes do not match the tiled layouts of M, N, K")
+    if xs.numel() < mx_scale_bytes(M, K, "packed_tiled") or ws.numel() < mx_scale_bytes(N, K, "packed_tiled"):
+        raise ValueError("scale arrays too small")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    _check("qgemm_mxfp4", lib().w4a4_qgemm_mxfp4(
+        _ptr(xq), _ptr(xs), _ptr(wq), _ptr(ws), M, N, K, _ptr(y), _stream(xq)))
+    return y
+
+
+def qlinear_forward_mxfp4(x: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor, N: int,
+                          had_block: int, At: Optional[torch.Tensor] = None,
+                          Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The MXFP4 layer on tiled MXFP4 weights (codes wq, scales ws)."""
+    _dev(x, "x")
+    _dev(wq, "wq")
+    _dev(ws, "ws")
+    M, K = x.shape
+    if wq.shape[0] < pad16(N) or wq.shape[1] != K // 2 or ws.numel() < mx_scale_bytes(N, K, "packed_tiled"):
+        raise ValueError("wq / ws do not match N and K")
+    rank = 0 if At is None else At.shape[0]
+    if rank:
+        if Bt is None or At.dtype != x.dtype or Bt.dtype != x.dtype:
+            raise ValueError("At and Bt must both be given in x's dtype")
+        if tuple(At.shape) != (rank, K) or tuple(Bt.shape) != (N, rank):
+            raise ValueError("At must be [rank, K] and Bt [N, rank]")
+        _dev(At, "At")
+        _dev(Bt, "Bt")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    need = qlinear_workspace_size(M, N, K, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    _check("qlinear_forward_mxfp4", lib().w4a4_qlinear_forward_mxfp4(
+        _ptr(x), _dt(x), _ptr(wq), _ptr(ws), M, N, K, had_block, _ptr(At), _ptr(Bt), rank,
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
     return y

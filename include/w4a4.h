@@ -244,6 +244,51 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          size_t ws_bytes, void* stream);
 
 /*
+ * MXFP4 form of the 4-bit path (SERQ page, "Metodología" item 2 and
+ * "Contribuciones Clave": the path may be INT4 or MXFP4), following the OCP
+ * microscaling format: every 32 consecutive elements along K share the
+ * scale 2^e, stored as the E8M0 byte e + 127, with
+ *   e = max(floor(log2(max|v|)) - 2, -127)   (-127 for an all-zero block);
+ * each element is the FP4 E2M1 code of v / 2^e: the nearest of
+ * {0, 0.5, 1, 1.5, 2, 3, 4, 6} with ties to the even encoding, saturating at
+ * 6, sign in bit 3 (set only for negative quotients).  Codes are packed two
+ * per byte like the int4 codes.
+ */
+
+/*
+ * MXFP4 quantization with the block Hadamard rotation in front (had_block
+ * 0/1: none), for activations and, offline, for weights.
+ *   codes_layout W4A4_CODES_PACKED: xq [M, K/2], x_scale [M, K/32] bytes;
+ *   W4A4_CODES_PACKED_TILED (K a multiple of 128): xq in the 1 KB tile
+ *   layout, x_scale [ceil(M/16) * (K/128) * 64] bytes, where byte
+ *   (g * 16 + r) of the 64-byte tile (b, t), at (b * (K/128) + t) * 64, is
+ *   the scale of elements [128 t + 32 g, +32) of row 16 b + r.
+ */
+int w4a4_quantize_mxfp4(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
+                        uint8_t* xq, int codes_layout, uint8_t* x_scale, void* stream);
+
+/*
+ * MXFP4 GEMM on the CDNA4 scaled FP4 matrix instruction:
+ *   y[m,n] = sum_blocks 2^(e_x + e_w) sum_k fp4_x[m,k] fp4_w[n,k]
+ * with float32 accumulation.  xq/x_scale and wq/w_scale in the tiled
+ * layouts of w4a4_quantize_mxfp4; K a multiple of 128; y [M, N] float32.
+ */
+int w4a4_qgemm_mxfp4(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* wq,
+                     const uint8_t* w_scale, int64_t M, int64_t N, int64_t K, float* y,
+                     void* stream);
+
+/*
+ * The MXFP4 layer: rotate + MXFP4-quantize X, MXFP4 GEMM with weights from
+ * w4a4_quantize_mxfp4 (same had_block, tiled), plus the optional rank-r term
+ * as in w4a4_qlinear_forward.
+ *   workspace: at least w4a4_qlinear_workspace_size(M, N, K, rank) bytes.
+ */
+int w4a4_qlinear_forward_mxfp4(const void* x, int x_dtype, const uint8_t* wq,
+                               const uint8_t* w_scale, int64_t M, int64_t N, int64_t K,
+                               int64_t had_block, const void* At, const void* Bt, int64_t rank,
+                               float* y, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * In-GEMM 4-bit residual of salient channels (SERQ page, "Metodología"
  * items 2-3): the weight rows that collect the most quantization error
  * (input channels, permuted offline so that they are the first r channels,

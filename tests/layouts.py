@@ -82,3 +82,22 @@ def untile_weights_residual(ext, N, K):
     main = np.ascontiguousarray(t[:, :nk]).reshape(Np, K // 2)
     res = np.ascontiguousarray(t[:, nk:]).reshape(Np, H - K // 2)
     return untile_weights(main, N), untile_weights(res, N)
+
+
+def tile_mx_scales(s, rng=None):
+    """[M, K/32] E8M0 bytes -> the tiled scale array: byte (g 16 + r) of the
+    64-byte tile (b, t) is the scale of block 4 t + g of row 16 b + r.
+    Padding rows get random bytes."""
+    M, KB = s.shape
+    Mp = pad16(M)
+    full = np.empty((Mp, KB), np.uint8)
+    full[:M] = s
+    full[M:] = (rng or np.random.default_rng(2)).integers(0, 256, (Mp - M, KB), dtype=np.uint8)
+    t = full.reshape(Mp // 16, 16, KB // 4, 4).transpose(0, 2, 3, 1)
+    return np.ascontiguousarray(t).reshape(-1)
+
+
+def untile_mx_scales(flat, M, K):
+    Mp = pad16(M)
+    t = np.asarray(flat)[:Mp * K // 32].reshape(Mp // 16, K // 128, 4, 16).transpose(0, 3, 1, 2)
+    return np.ascontiguousarray(t).reshape(Mp, K // 32)[:M]

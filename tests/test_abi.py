@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 19
+    assert len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -139,6 +139,31 @@ def test_qlinear_argument_errors(lib):
     bad = list(args); bad[3] = W.WEIGHTS_TILED; bad[10] = 64          # tiled needs group % 128
     assert f(*bad) == W.ERR_UNSUPPORTED
     bad = list(args); bad[6] = 0
+    assert f(*bad) == W.OK
+
+
+def test_mxfp4_argument_errors(lib):
+    q = lib.w4a4_quantize_mxfp4
+    assert q(P, W.F16, 4, 256, 0, P, W.CODES_I8, P, None) == W.ERR_INVALID_ARG          # layout
+    assert q(P, W.F16, 4, 192, 0, P, W.CODES_PACKED_TILED, P, None) == W.ERR_UNSUPPORTED  # K % 128
+    assert q(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, None, None) == W.ERR_INVALID_ARG
+    assert q(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, Q, None) == W.ERR_MISALIGNED
+    assert q(None, W.F16, 0, 256, 0, None, W.CODES_PACKED, None, None) == W.OK
+    g = lib.w4a4_qgemm_mxfp4
+    assert g(P, P, P, None, 4, 8, 256, P, None) == W.ERR_INVALID_ARG
+    assert g(P, P, P, P, 4, 8, 192, P, None) == W.ERR_UNSUPPORTED
+    assert g(P, Q, P, P, 4, 8, 256, P, None) == W.ERR_MISALIGNED
+    assert g(None, None, None, None, 4, 0, 256, None, None) == W.OK
+    f = lib.w4a4_qlinear_forward_mxfp4
+    need = lib.w4a4_qlinear_workspace_size(16, 32, 512, 8)
+    args = [P, W.F16, P, P, 16, 32, 512, 128, P, P, 8, P, P, need, None]
+    bad = list(args); bad[8] = None
+    assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[13] = need - 1
+    assert f(*bad) == W.ERR_WORKSPACE
+    bad = list(args); bad[6] = 448
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[4] = 0
     assert f(*bad) == W.OK
 
 

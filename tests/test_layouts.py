@@ -3,7 +3,8 @@ put bytes where include/w4a4.h says they go."""
 import numpy as np
 
 from layouts import (codes_from_i8, i8_from_codes, tile_codes_i8, tile_weights, untile_codes_i8,
-                     tile_weights_residual, untile_weights_residual,
+                     tile_weights_residual, untile_weights_residual, tile_mx_scales,
+                     untile_mx_scales,
                      untile_weights)
 
 
@@ -53,3 +54,16 @@ def test_residual_extended_tiling():
             t = K // 128 + jj // 64
             off = ((n // 16) * nt + t) * 1024 + (16 * ((jj % 64) // 16) + n % 16) * 16 + jj % 16
             assert flat[off] == res[n, jj]
+
+
+def test_mx_scale_tiling():
+    rng = np.random.default_rng(7)
+    M, K = 21, 384
+    s = rng.integers(0, 256, (M, K // 32), dtype=np.uint8)
+    flat = tile_mx_scales(s)
+    assert flat.size == 32 * K // 32
+    assert np.array_equal(untile_mx_scales(flat, M, K), s)
+    for m in range(M):
+        for blk in range(K // 32):
+            t, g = blk // 4, blk % 4
+            assert flat[((m // 16) * (K // 128) + t) * 64 + g * 16 + m % 16] == s[m, blk]
