@@ -18,7 +18,9 @@ A third leg runs the layer with asymmetric group-wise activations (per
 token and 128-channel group: scale and zero point) on the Llama-3-8B o-proj
 shape (4096 x 4096 x 4096, rank-32 term), beside the symmetric layer on the
 same workload.  A fourth runs the same shape with the in-GEMM 4-bit residual
-of 32 salient channels in place of the rank-32 term.
+of 32 salient channels in place of the rank-32 term.  A fifth runs the
+prefill workload in MXFP4 (E2M1 elements, one E8M0 scale per 32) on the
+scaled FP4 matrix instruction, against the dense FP4 peak.
 
 The roofline object is the GEMM kernel alone (the dominant kernel): its
 average launch duration from events around --steps back-to-back launches,
@@ -44,6 +46,7 @@ from bit_gemm_block_amd import synth  # noqa: E402
 from bit_gemm_block_amd import w4a4 as W  # noqa: E402
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 matrix peak, TOP/s
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 (MXFP4) matrix peak, TFLOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 LLC_BYTES = 256 << 20     # MI355X Infinity Cache
 
@@ -281,6 +284,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offq", action="store_true")
     ap.add_argument("--no-serq", action="store_true")
+    ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the prefill kernels and a calibration copy (for counters)")
     args = ap.parse_args()
@@ -403,6 +407,45 @@ def main() -> int:
         }
         del x, wq, ws, y, wsb, xq, sx
 
+    # ---- MXFP4 form of the layer, prefill workload ---------------------------
+    mxfp4 = None
+    if not args.no_mxfp4:
+        mw = synth.PREFILL
+        d = synth.make_inputs(mw)
+        dev = "cuda:0"
+        x = torch.from_numpy(d["X"]).to(dev)
+        Wd = torch.from_numpy(d["W"]).to(dev)
+        wq, ws = W.quantize_mxfp4(Wd, mw.had_block, "packed_tiled")
+        del Wd, d
+        y = torch.empty((mw.M, mw.N), dtype=torch.float32, device=dev)
+        wsb = torch.empty((W.qlinear_workspace_size(mw.M, mw.N, mw.K, 0),), dtype=torch.uint8,
+                          device=dev)
+        log(f"mxfp4: {mw.name} timing {args.steps} steps")
+        t_mx = time_graph(lambda i: W.qlinear_forward_mxfp4(x, wq, ws, mw.N, mw.had_block, y=y,
+                                                            workspace=wsb),
+                          args.steps, args.warmup)
+        xq, xs = W.quantize_mxfp4(x, mw.had_block, "packed_tiled")
+        torch.cuda.synchronize()
+        t_q = time_graph(lambda i: W.quantize_mxfp4(x, mw.had_block, "packed_tiled", xq, xs),
+                         args.steps, args.warmup)
+        t_g = time_graph(lambda i: W.qgemm_mxfp4(xq, xs, wq, ws, mw.M, mw.N, mw.K, y=y),
+                         args.steps, args.warmup)
+        ops = 2 * mw.M * mw.N * mw.K
+        log(f"mxfp4: {t_mx * 1e6:.2f} us/step ({ops / t_mx / 1e12:.1f} TFLOP/s); qgemm_mxfp4 "
+            f"{t_g * 1e6:.2f} us ({ops / t_g / 1e12:.1f} TFLOP/s), quantize {t_q * 1e6:.2f} us")
+        mxfp4 = {
+            "metric": "MXFP4 qlinear TFLOP/s (M=2048), K=N=4096",
+            "value": ops / t_mx / 1e12, "unit": "TFLOP/s", "ms_per_step": t_mx * 1e3,
+            "gemm": {"kernel": "qgemm_mx_kernel", "achieved": ops / t_g / 1e12,
+                     "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ops / t_g / 1e12 / PEAK_FP4_TFLOPS, "us_per_launch": t_g * 1e6,
+                     "ops_per_launch": ops},
+            "kernels_us": {"quantize_mxfp4": t_q * 1e6, "qgemm_mxfp4": t_g * 1e6},
+            "config": {"workload": mw.name, "M": mw.M, "N": mw.N, "K": mw.K,
+                       "had_block": mw.had_block, "block": 32},
+        }
+        del x, wq, ws, y, wsb, xq, xs
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
@@ -438,6 +481,7 @@ def main() -> int:
         "decode": decode,
         "offq": offq,
         "serq": serq,
+        "mxfp4": mxfp4,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
