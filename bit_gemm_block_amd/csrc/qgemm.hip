@@ -18,8 +18,9 @@
 //
 // Large M: a 256-thread workgroup owns a (32 TM) x (32 TN) output tile; its
 // four waves form a 2 x 2 grid of (16 TM) x (16 TN) wave tiles.  K advances
-// 128 codes (64 bytes per row, two MFMA K steps) per iteration through
-// double-buffered LDS tiles.  Tiles are handed to workgroups so that the
+// 128 codes (64 bytes per row, two MFMA K steps) per iteration through a
+// ring of LDS tiles (four stages for the tiled operands: the copies in
+// flight per CU set the L2-to-LDS rate).  Tiles are handed to workgroups so that the
 // workgroups resident on one XCD (each XCD has its own L2) cover a compact
 // block of output tiles and share their A and B panels in that L2.
 //
@@ -1452,7 +1453,7 @@ static hipError_t launch_qgemm_mx(const GemmArgs& a, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(((a.M + 127) / 128) * ((a.N + 127) / 128)));
 #define W4A4_MX_CASE(LR)                                                               \
   if (a.lr_mode == LR) {                                                               \
-    hipLaunchKernelGGL((qgemm_mx_kernel<4, 4, 3, LR>), grid, dim3(256), 0, st, a);     \
+    hipLaunchKernelGGL((qgemm_mx_kernel<4, 4, 4, LR>), grid, dim3(256), 0, st, a);     \
     return hipGetLastError();                                                          \
   }
   W4A4_MX_CASE(LR_NONE) W4A4_MX_CASE(LR_F16) W4A4_MX_CASE(LR_F32)
@@ -1478,7 +1479,7 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
     ia.group = 0;
     ia.y = nullptr;
     ia.lr_mode = LR_NONE;
-    hipError_t e = a.tiled ? launch_pipe<4, 4, 3>(ia, st) : launch_tiles<4, 4>(ia, st);
+    hipError_t e = a.tiled ? launch_pipe<4, 4, 4>(ia, st) : launch_tiles<4, 4>(ia, st);
     if (e != hipSuccess) return e;
     if (!a.y) return hipSuccess;
   }
@@ -1489,7 +1490,7 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   if (a.tiled || (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0)) {
     // Grouped: a 64 x 32 wave tile, so that the float group accumulators fit
     // beside the integer ones at two waves per SIMD.
-    return ya.group > 0 ? launch_pipe<4, 2, 3>(ya, st) : launch_pipe<4, 4, 3>(ya, st);
+    return ya.group > 0 ? launch_pipe<4, 2, 3>(ya, st) : launch_pipe<4, 4, 4>(ya, st);
   }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
   if (a.group == 0 && a.M >= 256 && big_tiles >= 200) return launch_tiles<8, 4>(ya, st);
