@@ -975,18 +975,25 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 // waves 0-1 the A row blocks, waves 2-3 the B column blocks.
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
-template <int TM, int TN, int STAGES, int LRMODE>
-__global__ void __launch_bounds__(256) qgemm_mx_kernel(GemmArgs a) {
+template <int TM, int TN, int STAGES, int LRMODE, int WGM = 2>
+__global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
+  // WGM x 2 waves, each a (16 TM) x (16 TN) wave tile.
+  constexpr int NW = 2 * WGM;
   constexpr int WM = TM * 16, WN = TN * 16;
-  constexpr int BM = 2 * WM, BN = 2 * WN;
+  constexpr int BM = WGM * WM, BN = 2 * WN;
   constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
   constexpr int SA_BYTES = BM / 16 * 64, SB_BYTES = BN / 16 * 64;
-  static_assert(SA_BYTES == 512 && SB_BYTES == 512, "two scale runs per side");
-  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+  // Scale runs: 256 bytes (4 blocks) per wave; waves past the A and B scale
+  // runs repeat a B run into a spare slot, so every wave issues the same
+  // number of copies.
+  constexpr int SA_WAVES = SA_BYTES / 256, SB_WAVES = SB_BYTES / 256;
+  static_assert(SA_WAVES + SB_WAVES <= NW, "scale runs fit the waves");
+  constexpr int SPARE = 256;
+  constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES + SPARE;
   constexpr int A_RUNS = BM / 16, B_RUNS = BN / 16;
   constexpr int RUNS = A_RUNS + B_RUNS;
-  static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
-  constexpr int RUNS_PER_WAVE = RUNS / 4 + 1;  // + the scale run
+  static_assert(RUNS % NW == 0, "runs split evenly over the waves");
+  constexpr int RUNS_PER_WAVE = RUNS / NW + 1;  // + the scale run
   static_assert((STAGES - 1) * RUNS_PER_WAVE < 64, "in-flight copies exceed vmcnt");
   __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
@@ -1022,7 +1029,7 @@ __global__ void __launch_bounds__(256) qgemm_mx_kernel(GemmArgs a) {
   int dst[RUNS_PER_WAVE];
 #pragma unroll
   for (int q = 0; q < RUNS_PER_WAVE - 1; ++q) {
-    const int run = wave + 4 * q;
+    const int run = wave + NW * q;
     if (run < A_RUNS) {
       int64_t mb = m0 / 16 + run;
       mb = mb < mblocks ? mb : mblocks - 1;
@@ -1037,13 +1044,16 @@ __global__ void __launch_bounds__(256) qgemm_mx_kernel(GemmArgs a) {
     }
   }
   {
-    const int side = wave >> 1;                      // 0: A scales, 1: B scales
-    const int blk = (wave & 1) * 4 + ((lane & 15) >> 2);
+    const int side = wave < SA_WAVES ? 0 : 1;        // 0: A scales, 1: B scales
+    const int part = side ? (wave - SA_WAVES) % SB_WAVES : wave;
+    const int blk = part * 4 + ((lane & 15) >> 2);
     int64_t b = (side ? n0 : m0) / 16 + blk;
     const int64_t nbl = side ? nblocks : mblocks;
     b = b < nbl ? b : nbl - 1;
     src[RUNS_PER_WAVE - 1] = (side ? a.mx_ws : a.mx_xs) + b * nkt * 64 + 16 * (lane & 3);
-    dst[RUNS_PER_WAVE - 1] = A_BYTES + B_BYTES + side * SA_BYTES + (wave & 1) * 256;
+    dst[RUNS_PER_WAVE - 1] = wave >= SA_WAVES + SB_WAVES
+                                 ? A_BYTES + B_BYTES + SA_BYTES + SB_BYTES
+                                 : A_BYTES + B_BYTES + side * SA_BYTES + part * 256;
   }
   auto issue = [&](int kt, uint8_t* base) {
     const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
@@ -1338,6 +1348,228 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
   }
 }
 
+// Small M for the other 4-bit forms (tiled operands, packed codes): the
+// skinny kernel's decomposition (16 output columns per workgroup, KW waves
+// over contiguous 128-code steps, partials reduced through LDS) with
+//   XRES:  the residual steps after the K / 128 main ones, into their own
+//          accumulator; total = 8 main + residual;
+//   XMX:   MXFP4 codes on the scaled FP4 instruction, scale bytes read per
+//          lane beside the code bytes;
+//   XASYM: asymmetric activation groups, flushed with per-row scales; the
+//          zero-point term sum_g s (z - 8) wsum is a float32 loop in the
+//          epilogue (K / group terms per output).
+enum SkinnyMode { XRES = 1, XMX = 2, XASYM = 3 };
+
+template <int MB, int KW, int XM, int LRMODE>
+__global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
+  constexpr int CH = 8;  // steps loaded per batch
+  constexpr bool FL = XM == XMX || XM == XASYM;  // float partials
+  __shared__ i32x4 ired[KW][MB][64];
+  __shared__ f32x4 fred[FL ? KW : 1][FL ? MB : 1][64];
+  const int lane = threadIdx.x & 63;
+  // Wave-uniform by construction: the branches on the step index below
+  // (main or residual accumulator) must be scalar branches, because a
+  // matrix instruction on the untaken side of an EXEC-masked branch would
+  // still execute.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nkt = static_cast<int>(a.K / 128);                  // code steps
+  const int nsteps = nkt + (XM == XRES ? a.res_iters : 0);       // weight steps
+  const int64_t nrow = n0 + (lane & 15);
+  const bool n_ok = nrow < a.N;
+  const bool want_y = a.y != nullptr;
+  const int64_t mlast = (a.M + 15) / 16 - 1;
+  const int ipg = XM == XASYM ? a.agroup / 128 : 1;              // steps per group
+  const int G = XM == XASYM ? nkt / ipg : 1;
+
+  const int p_begin = static_cast<int>(static_cast<int64_t>(nsteps) * wave / KW);
+  const int p_end = static_cast<int>(static_cast<int64_t>(nsteps) * (wave + 1) / KW);
+
+  i32x4 acc[MB], accr[XM == XRES ? MB : 1];
+  f32x4 facc[FL ? MB : 1];
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    acc[b] = i32x4{0, 0, 0, 0};
+    if constexpr (XM == XRES) accr[b] = i32x4{0, 0, 0, 0};
+    if constexpr (FL) facc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Asymmetric groups: the rows' scales (times 1/256) and offsets
+  // s (z - 8), and the columns' weight sums, staged in LDS as [group][row]
+  // and [group][column] before the loop (dynamic LDS of 4 (2 * 16 MB + 16) G
+  // bytes), so that neither the flushes nor the epilogue wait on memory.
+  extern __shared__ __attribute__((aligned(16))) float xsh[];
+  float* s_st = xsh;                         // [G][16 MB]
+  float* o_st = xsh + G * 16 * MB;           // [G][16 MB]
+  float* w_st = xsh + 2 * G * 16 * MB;       // [G][16]
+  if constexpr (XM == XASYM) {
+    for (int e = threadIdx.x; e < G * 16 * MB; e += 64 * KW) {
+      const int row = e % (16 * MB), gg = e / (16 * MB);
+      const bool ok = row < a.M;
+      const float sv = ok ? a.sx[row * G + gg] : 0.f;
+      s_st[e] = sv * kInv256;
+      o_st[e] = ok ? sv * static_cast<float>(a.zx[row * G + gg] - 8) : 0.f;
+    }
+    for (int e = threadIdx.x; e < G * 16; e += 64 * KW) {
+      const int col = e % 16, gg = e / 16;
+      const int64_t n = n0 + col;
+      w_st[e] = n < a.N ? static_cast<float>(a.wsum[n * G + gg]) : 0.f;
+    }
+    __syncthreads();
+  }
+  // asymmetric groups: adds acc * s[m, grp] to facc and clears acc
+  auto flush = [&](int grp) {
+#pragma unroll
+    for (int b = 0; b < MB; ++b) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sv = s_st[grp * 16 * MB + b * 16 + (lane >> 4) * 4 + r];
+        facc[b][r] = fmaf(static_cast<float>(acc[b][r]), sv, facc[b][r]);
+      }
+      acc[b] = i32x4{0, 0, 0, 0};
+    }
+  };
+
+  for (int p0 = p_begin; p0 < p_end; p0 += CH) {
+    uint4 wv[CH], xv[CH][MB];
+    int ws_[XM == XMX ? CH : 1], xs_[XM == XMX ? CH : 1][MB];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int p = p0 + c;
+      const bool ok = p < p_end;
+      const int pa = (XM == XRES && p >= nkt) ? p - nkt : p;     // code step
+      wv[c] = ok ? *reinterpret_cast<const uint4*>(a.wq + (n0 / 16 * nsteps + p) * 1024 + 16 * lane)
+                 : make_uint4(0, 0, 0, 0);
+      if constexpr (XM == XMX)
+        ws_[c] = ok ? a.mx_ws[(n0 / 16 * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int64_t mb = b < mlast ? b : mlast;
+        xv[c][b] = ok ? *reinterpret_cast<const uint4*>(a.xq + (mb * nkt + pa) * 1024 + 16 * lane)
+                      : make_uint4(0, 0, 0, 0);
+        if constexpr (XM == XMX)
+          xs_[c][b] = ok ? a.mx_xs[(mb * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int p = p0 + c;
+      if constexpr (XM == XMX) {
+        const i32x8 bv = {static_cast<int>(wv[c].x), static_cast<int>(wv[c].y),
+                          static_cast<int>(wv[c].z), static_cast<int>(wv[c].w), 0, 0, 0, 0};
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const i32x8 av = {static_cast<int>(xv[c][b].x), static_cast<int>(xv[c][b].y),
+                            static_cast<int>(xv[c][b].z), static_cast<int>(xv[c][b].w), 0, 0, 0, 0};
+          facc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, facc[b], 4, 4, 0,
+                                                                     xs_[c][b], 0, ws_[c]);
+        }
+      } else {
+        const i32x4 w0 = widen(wv[c].x, wv[c].y);
+        const i32x4 w1 = widen(wv[c].z, wv[c].w);
+        const bool res_step = XM == XRES && p >= nkt;
+#pragma unroll
+        for (int b = 0; b < MB; ++b) {
+          const i32x4 x0 = widen(xv[c][b].x, xv[c][b].y);
+          const i32x4 x1 = widen(xv[c][b].z, xv[c][b].w);
+          if (res_step) {
+            if constexpr (XM == XRES) {
+              accr[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, w0, accr[b], 0, 0, 0);
+              accr[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, w1, accr[b], 0, 0, 0);
+            }
+          } else {
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, w0, acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, w1, acc[b], 0, 0, 0);
+          }
+        }
+        if constexpr (XM == XASYM) {
+          if (p < p_end && (p + 1) % ipg == 0) flush(p / ipg);
+        }
+      }
+    }
+  }
+  if constexpr (XM == XASYM) {
+    // a group straddling this wave's last step and the next wave's first is
+    // flushed by both waves, each with its part of the sum
+    if (p_end > p_begin && p_end % ipg != 0) flush((p_end - 1) / ipg);
+  }
+#pragma unroll
+  for (int b = 0; b < MB; ++b) {
+    if constexpr (XM == XRES)
+      ired[wave][b][lane] = (acc[b] << 3) + accr[b];
+    else
+      ired[wave][b][lane] = acc[b];
+    if constexpr (FL) fred[wave][b][lane] = facc[b];
+  }
+  __syncthreads();
+  if (wave < MB) {
+    const int b = wave;
+    const int64_t mblk = b * 16;
+    i32x4 total = ired[0][b][lane];
+#pragma unroll
+    for (int w = 1; w < KW; ++w) total += ired[w][b][lane];
+    f32x4 fsum = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (FL) {
+      fsum = fred[0][b][lane];
+#pragma unroll
+      for (int w = 1; w < KW; ++w) fsum += fred[w][b][lane];
+    }
+    f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (want_y) {
+      const float swn = (XM != XMX && n_ok) ? load_scale(a.sw, nrow, a.sw_f16) : 1.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mblk + (lane >> 4) * 4 + r;
+        if constexpr (XM == XRES) {
+          const float sx = m < a.M ? a.sx[m] * (kInv256 * 0.125f) : 0.f;
+          yv[r] = static_cast<float>(total[r]) * (sx * swn);
+        } else if constexpr (XM == XMX) {
+          yv[r] = fsum[r];
+        } else {
+          const int row = b * 16 + (lane >> 4) * 4 + r;
+          float corr = 0.f;
+          for (int gg = 0; gg < G; ++gg)
+            corr = fmaf(o_st[gg * 16 * MB + row], w_st[gg * 16 + (lane & 15)], corr);
+          yv[r] = (fsum[r] - corr) * swn;
+        }
+      }
+      yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
+    }
+    const int64_t n = n0 + (lane & 15);
+    if (n < a.N) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mblk + (lane >> 4) * 4 + r;
+        if (m < a.M) {
+          if (want_y) a.y[m * a.N + n] = yv[r];
+          if (XM == XRES && a.acc) a.acc[m * a.N + n] = total[r] >> 8;
+        }
+      }
+    }
+  }
+}
+
+template <int MB, int XM>
+hipError_t launch_skinny_x(const GemmArgs& a, hipStream_t st) {
+  constexpr int KW = 4;
+  const dim3 grid(static_cast<unsigned>((a.N + 15) / 16));
+  const size_t lds =
+      XM == XASYM ? static_cast<size_t>(a.K / a.agroup) * (2 * 16 * MB + 16) * 4 : 0;
+#define W4A4_SKX_CASE(LR)                                                                  \
+  if (a.lr_mode == LR) {                                                                   \
+    hipLaunchKernelGGL((qgemm_skinny_x_kernel<MB, KW, XM, LR>), grid, dim3(64 * KW), lds, \
+                       st, a);                                                             \
+    return hipGetLastError();                                                              \
+  }
+  W4A4_SKX_CASE(LR_NONE) W4A4_SKX_CASE(LR_F16) W4A4_SKX_CASE(LR_F32)
+#undef W4A4_SKX_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int XM>
+hipError_t launch_skinny_x_m(const GemmArgs& a, hipStream_t st) {
+  return a.M <= 16 ? launch_skinny_x<1, XM>(a, st) : launch_skinny_x<2, XM>(a, st);
+}
+
 template <int TM, int TN, bool AI8>
 hipError_t launch_tiles_a(const GemmArgs& a, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
@@ -1450,11 +1682,12 @@ static hipError_t launch_pipe_res(const GemmArgs& a, hipStream_t st) {
 }
 
 static hipError_t launch_qgemm_mx(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(((a.M + 127) / 128) * ((a.N + 127) / 128)));
-#define W4A4_MX_CASE(LR)                                                               \
-  if (a.lr_mode == LR) {                                                               \
-    hipLaunchKernelGGL((qgemm_mx_kernel<4, 4, 4, LR>), grid, dim3(256), 0, st, a);     \
-    return hipGetLastError();                                                          \
+  constexpr int WGM = 2;  // 8 waves (256 x 128) read less but ran no faster on square shapes
+  const dim3 grid(static_cast<unsigned>(((a.M + 64 * WGM - 1) / (64 * WGM)) * ((a.N + 127) / 128)));
+#define W4A4_MX_CASE(LR)                                                                      \
+  if (a.lr_mode == LR) {                                                                      \
+    hipLaunchKernelGGL((qgemm_mx_kernel<4, 4, 4, LR, WGM>), grid, dim3(128 * WGM), 0, st, a); \
+    return hipGetLastError();                                                                 \
   }
   W4A4_MX_CASE(LR_NONE) W4A4_MX_CASE(LR_F16) W4A4_MX_CASE(LR_F32)
 #undef W4A4_MX_CASE
@@ -1462,6 +1695,12 @@ static hipError_t launch_qgemm_mx(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
+  // Decode-sized calls of the other 4-bit forms take the skinny decomposition.
+  if (a.M <= 32) {
+    if (a.mx_xs) return launch_skinny_x_m<XMX>(a, st);
+    if (a.res) return launch_skinny_x_m<XRES>(a, st);
+    if (a.zx) return launch_skinny_x_m<XASYM>(a, st);
+  }
   if (a.mx_xs) return launch_qgemm_mx(a, st);
   if (a.res) return launch_pipe_res(a, st);
   // Asymmetric groups: a 32 x 64 wave tile, so that the row scales of every

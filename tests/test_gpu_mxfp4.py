@@ -110,7 +110,8 @@ def test_quantize_mxfp4_fused_rotation(M, K, b):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (7, 33, 256), (130, 260, 1024), (2048, 4096, 4096),
-                                   (300, 129, 14336), (2100, 4100, 1024), (16, 300, 16384)])
+                                   (300, 129, 14336), (2100, 4100, 1024), (16, 300, 16384),
+                                   (25, 77, 1024), (8, 4096, 4096), (32, 48, 2048)])
 def test_qgemm_mxfp4(M, N, K):
     rng = np.random.default_rng(M + N + K)
     cx = rng.integers(0, 16, (M, K)).astype(np.uint8)

@@ -154,7 +154,7 @@ def asym_bound(q, s, z, qw, sw, g, rows):
     (1, 1, 128, 128), (7, 33, 256, 128), (130, 260, 1024, 256), (64, 128, 4096, 4096),
     (300, 129, 14336, 128), (2100, 4100, 1024, 128), (2048, 4096, 4096, 128),
     (16, 300, 2048, 512), (65, 70, 16384, 128), (2048, 4096, 4096, 4096), (130, 260, 1024, 1024),
-    (300, 129, 2048, 2048)])
+    (300, 129, 2048, 2048), (32, 100, 1024, 256), (17, 40, 4096, 128), (8, 4096, 4096, 4096)])
 def test_qgemm_asym(M, N, K, g):
     rng = np.random.default_rng(M + 3 * N + K + g)
     G = K // g

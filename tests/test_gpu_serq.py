@@ -91,7 +91,8 @@ def test_quantize_weight_residual_fused_rotation(N, K, b, r):
 @pytest.mark.parametrize("M,N,K,r", [(1, 1, 128, 1), (7, 33, 256, 32), (130, 260, 1024, 128),
                                      (2048, 4096, 4096, 32), (300, 129, 14336, 200),
                                      (2100, 4100, 1024, 256), (16, 300, 4096, 4096),
-                                     (65, 70, 2048, 0)])
+                                     (65, 70, 2048, 0), (30, 70, 2048, 100), (8, 4096, 4096, 64),
+                                     (17, 33, 1024, 0)])
 def test_qgemm_residual_exact_and_dequant(M, N, K, r):
     rng = np.random.default_rng(M + N + K + r)
     qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
