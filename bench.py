@@ -194,6 +194,52 @@ def asym_kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     return out
 
 
+def decode_forms(wl: synth.Workload, copies: int, steps: int, warmup: int) -> dict:
+    """The decode workload in the other 4-bit forms, each with `copies`
+    distinct weight sets so that the weights stream from HBM: MXFP4 and the
+    asymmetric layer with the workload's low-rank term, the in-GEMM residual
+    (its rank as residual channels) in its place.  Algorithmic bytes: X, the
+    form's weight codes and per-weight side data, A and B when used, Y."""
+    dev = "cuda:0"
+    d = synth.make_inputs(wl)
+    x = torch.from_numpy(d["X"]).to(dev)
+    Wd = torch.from_numpy(d["W"]).to(dev)
+    At = torch.from_numpy(d["A"].T.copy()).to(dev)
+    Bt = torch.from_numpy(d["B"].T.copy()).to(dev)
+    M, N, K, r, b = wl.M, wl.N, wl.K, wl.rank, wl.had_block
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    wsb = torch.empty((W.qlinear_workspace_size(M, N, K, r),), dtype=torch.uint8, device=dev)
+    base = 2 * M * K + 4 * M * N
+    lr = 2 * (K * r + r * N)
+    out = {}
+
+    def run(name, prep, fwd, side_bytes, uses_lr):
+        sets = [prep()]
+        for _ in range(copies - 1):
+            sets.append(tuple(t.clone() for t in sets[0]))
+        t = time_graph(lambda i: fwd(*sets[i % copies]), steps, warmup)
+        nbytes = base + N * K // 2 + side_bytes + (lr if uses_lr else 0)
+        out[name] = {"us_per_step": t * 1e6, "GB/s": nbytes / t / 1e9, "bytes_per_step": nbytes}
+        log(f"decode {name}: {t * 1e6:.2f} us/step, {nbytes / t / 1e9:.0f} GB/s")
+        del sets
+
+    run("mxfp4", lambda: W.quantize_mxfp4(Wd, b, "packed_tiled"),
+        lambda wq, ws: W.qlinear_forward_mxfp4(x, wq, ws, N, b, At, Bt, y=y, workspace=wsb),
+        N * K // 32, True)
+
+    def prep_asym():
+        wq, ws = W.quantize_weight_int4(Wd, b, 0, torch.float16, layout="tiled")
+        return wq, ws, W.weight_group_sums(wq, b, N, w_layout="tiled")
+    run("asymmetric", prep_asym,
+        lambda wq, ws, gs: W.qlinear_forward_asym(x, wq, ws, gs, b, At, Bt, y=y, workspace=wsb),
+        2 * N + 4 * N * (K // b), True)
+    run("residual", lambda: W.quantize_weight_residual_int4(Wd, b, r, torch.float16),
+        lambda wq, ws: W.qlinear_forward_residual(x, wq, ws, r, b, y=y, workspace=wsb),
+        2 * N + N * W.res_pad(r) // 2, False)
+    del x, Wd, At, Bt, y, wsb
+    return out
+
+
 CALIB_BYTES = 256 << 20   # the calibration copy reads and writes this much
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_prefill_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "bit_gemm_block_amd", "csrc", f)
@@ -327,6 +373,7 @@ def main() -> int:
         gbs = dec.algorithmic_bytes() / t_dec / 1e9
         log(f"decode: {t_dec * 1e6:.2f} us/step, {gbs:.0f} GB/s")
         t_dec8 = time_graph(lambda i: dec.forward(i, act_bits=8), args.steps, args.warmup)
+        forms = decode_forms(probe, copies, args.steps, args.warmup)
         decode = {
             "metric": "W4A4 qlinear HBM GB/s (M=8)", "value": gbs, "unit": "GB/s",
             "ms_per_step": t_dec * 1e3, "frac_of_hbm": gbs / PEAK_HBM_GBS,
@@ -334,6 +381,7 @@ def main() -> int:
             "kernels_us": {k: v * 1e6 for k, v in kd.items()},
             "w4a8": {"value": dec.algorithmic_bytes() / t_dec8 / 1e9, "unit": "GB/s",
                      "ms_per_step": t_dec8 * 1e3},
+            "other_forms": forms,
             "config": {"workload": dec.wl.name, "M": dec.wl.M, "N": dec.wl.N, "K": dec.wl.K,
                        "had_block": dec.wl.had_block, "w_group": dec.wl.w_group,
                        "rank": dec.wl.rank},
