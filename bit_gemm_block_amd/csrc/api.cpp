@@ -97,6 +97,21 @@ constexpr bool kPackedTiledCodes = true;
 // Weights at most this large are read ahead by decode-sized calls.
 constexpr int64_t kMaxPrefetchBytes = int64_t{64} << 20;
 
+// Decode-sized calls: the rotation launch also reads the tiled weights that
+// the skinny GEMM's workgroups will stream (one 16-row block of row_bytes
+// per workgroup), so that the GEMM finds them in cache.
+void set_prefetch(w4a4::RotqExtras* ex, const uint8_t* wq, int64_t M, int64_t N,
+                  int64_t row_bytes) {
+  const int64_t units = (N + 15) / 16;
+  const int64_t unit_bytes = 16 * row_bytes;
+  if (M > 32 || units * unit_bytes > kMaxPrefetchBytes) return;
+  ex->pf = wq;
+  ex->pf_unit = unit_bytes;
+  ex->pf_units = units;
+  ex->pf_last = unit_bytes;
+  ex->pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
+}
+
 struct WsLayout {
   size_t xq, sx, t, total;
 };
@@ -462,6 +477,7 @@ int w4a4_qlinear_forward_mxfp4(const void* x, int x_dtype, const uint8_t* wq,
   const bool f16 = x_dtype == W4A4_F16;
   w4a4::RotqExtras ex;
   ex.mx_scale = xs;
+  set_prefetch(&ex, wq, M, N, K / 2);
   const bool fuse_lr = rank > 0 && f16 && M <= 16;
   if (fuse_lr) {
     ex.lr_at = At;
@@ -593,8 +609,10 @@ int w4a4_qlinear_forward_residual(const void* x, int x_dtype, const uint8_t* wq,
   uint8_t* xq = ws + L.xq;
   float* sx = reinterpret_cast<float*>(ws + L.sx);
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
+  w4a4::RotqExtras ex;
+  set_prefetch(&ex, wq, M, N, (K + (res_rank + 127) / 128 * 128) / 2);
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, w4a4::ROTQ_QUANT_TILED, K,
-                                   false, nullptr, xq, sx, plan, st);
+                                   false, nullptr, xq, sx, plan, st, &ex);
   if (e != hipSuccess) return hip_fail(e);
   const w4a4::GemmArgs g =
       res_gemm_args(xq, sx, wq, w_scale, w_scale_dtype, res_rank, M, N, K, y, nullptr);
@@ -744,6 +762,7 @@ int w4a4_qlinear_forward_asym(const void* x, int x_dtype, const uint8_t* wq, con
   void* t = ws + L.t;
   const bool f16 = x_dtype == W4A4_F16;
   w4a4::RotqExtras ex;
+  set_prefetch(&ex, wq, M, N, K / 2);
   const bool fuse_lr = rank > 0 && f16 && M <= 16;
   if (fuse_lr) {
     ex.lr_at = At;
