@@ -61,7 +61,9 @@ What is computed, and where the pages fix it
   e = max(floor(log2(max|v|)) - 2, -127) (e = -127 for an all-zero block);
   each element is v / 2^e rounded to the nearest FP4 E2M1 value
   {0, 0.5, 1, 1.5, 2, 3, 4, 6} (ties to the even encoding, saturating at 6),
-  with the sign in bit 3 (set only for negative quotients).  Rotation as
+  with the sign of the quotient in bit 3 (as an IEEE conversion keeps it,
+  so a negative zero, and a negative quotient that rounds to zero, encode
+  as -0).  Rotation as
   above; Y = sum_blocks 2^(e_x + e_w) sum_k fp4_x fp4_w, exact in float64,
   rounded once to float32, + the low-rank term.
 * W4A8 layers: the layers a phase-aware policy keeps at 8-bit activations
@@ -448,7 +450,7 @@ E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 def e2m1_code(p: np.ndarray) -> np.ndarray:
     """FP4 E2M1 encoding of float values p: magnitude bits from the nearest
     of E2M1 (ties to the even encoding, |p| > 6 saturates to 6), sign bit 8
-    for p < 0."""
+    from the sign of p (negative zero included)."""
     p = np.asarray(p, dtype=np.float64)
     a = np.abs(p)
     # upper bounds of each magnitude code; '<=' where the tie goes down
@@ -459,7 +461,7 @@ def e2m1_code(p: np.ndarray) -> np.ndarray:
                                    (0, 0.25, True)):
         hit = (a <= bound) if inclusive else (a < bound)
         mag = np.where(hit, code, mag)
-    return (mag | np.where(p < 0, 8, 0)).astype(np.uint8)
+    return (mag | np.where(np.signbit(p), 8, 0)).astype(np.uint8)
 
 
 def e2m1_value(code: np.ndarray) -> np.ndarray:

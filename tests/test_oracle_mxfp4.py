@@ -16,7 +16,8 @@ def test_e2m1_rounding_table():
            (3.4999999, 5), (5.0000001, 7), (6.5, 7), (7.99, 7), (0.1, 0)]
     for v, code in pts:
         assert O.e2m1_code(np.array([v]))[0] == code, v
-        assert O.e2m1_code(np.array([-v]))[0] == (code | 8 if v > 0 else 0), -v
+        assert O.e2m1_code(np.array([-v]))[0] == code | 8, -v      # the sign is kept, -0 included
+    assert O.e2m1_code(np.array([0.0]))[0] == 0
     assert np.array_equal(O.e2m1_value(np.arange(16)),
                           [0, .5, 1, 1.5, 2, 3, 4, 6, 0, -.5, -1, -1.5, -2, -3, -4, -6])
 
