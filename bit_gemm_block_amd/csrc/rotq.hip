@@ -35,7 +35,9 @@
 // e = max(floor(log2(max|x~|)) - 2, -127), stored as the byte e + 127; each
 // element is x~ 2^-e (exact) rounded to the nearest E2M1 value
 // {0, .5, 1, 1.5, 2, 3, 4, 6} with ties to the even encoding and saturation
-// at 6, sign in bit 3 for negative quotients.
+// at 6, the quotient's sign (negative zero included) in bit 3.  The
+// rounding is the hardware's packed conversion (two quotients per
+// instruction, scale 1), which follows exactly this rule.
 //
 // Asymmetric mode (OffQ page, "Metodología" steps 2-3): one scale and zero
 // point per token and Hadamard block, s = (max - min) / 15,
@@ -391,12 +393,12 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         *sp = static_cast<uint8_t>(e + 127);
       }
 #pragma unroll
-      for (int u = 0; u < BL; ++u) {
-        const float p = ldexpf(v[c * BL + u] * a.rs, -e);
-        const float q = fabsf(p);
-        const uint32_t mag = (q > 0.25f) + (q >= 0.75f) + (q > 1.25f) + (q >= 1.75f) +
-                             (q > 2.5f) + (q >= 3.5f) + (q > 5.f);
-        code[c * BL + u] = mag | (p < 0.f ? 8u : 0u);
+      for (int u = 0; u < BL; u += 2) {
+        const float p0 = ldexpf(v[c * BL + u] * a.rs, -e);
+        const float p1 = ldexpf(v[c * BL + u + 1] * a.rs, -e);
+        const uint32_t pr = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p0, p1, 1.0f, 0);
+        code[c * BL + u] = pr & 0xFu;
+        code[c * BL + u + 1] = (pr >> 4) & 0xFu;
       }
     }
   } else if (a.asym) {

@@ -251,8 +251,8 @@ int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
  *   e = max(floor(log2(max|v|)) - 2, -127)   (-127 for an all-zero block);
  * each element is the FP4 E2M1 code of v / 2^e: the nearest of
  * {0, 0.5, 1, 1.5, 2, 3, 4, 6} with ties to the even encoding, saturating at
- * 6, sign in bit 3 (set only for negative quotients).  Codes are packed two
- * per byte like the int4 codes.
+ * 6, sign of the quotient in bit 3 (negative zero included, as an IEEE
+ * conversion keeps it).  Codes are packed two per byte like the int4 codes.
  */
 
 /*
