@@ -657,8 +657,13 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
               As + (((((wm0 >> 4) + i) * 2 + h) * 4 + fg) << 8) + (frow << 4));
     }
   };
+  // ZC: with G128 and no low-rank epilogue, each group's first matrix
+  // instruction starts from a zero accumulator input, so a flush need not
+  // clear its set (with the low-rank epilogue this would cost the kernel its
+  // second wave per SIMD).
+  constexpr bool ZC = G128 && LRMODE == LR_NONE;
   // Adds the float value of one set of group accumulators, scaled, to facc
-  // and clears the set.
+  // and clears the set (unless ZC).
   auto flush = [&](i32x4 (&ac)[TM][TN], int64_t grp) {
     if constexpr (GROUPED) {
 #pragma unroll
@@ -671,7 +676,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             facc[i][j][r] = fmaf(static_cast<float>(ac[i][j][r]), sw, facc[i][j][r]);
-          ac[i][j] = i32x4{0, 0, 0, 0};
+          if constexpr (!ZC) ac[i][j] = i32x4{0, 0, 0, 0};
         }
       }
     }
@@ -685,7 +690,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             facc[i][j][r] = fmaf(static_cast<float>(ac[i][j][r]), sv[r], facc[i][j][r]);
-          ac[i][j] = i32x4{0, 0, 0, 0};
+          if constexpr (!ZC) ac[i][j] = i32x4{0, 0, 0, 0};
         }
       }
     }
@@ -710,7 +715,8 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          cur[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(opa[i], opb[j], cur[i][j], 0, 0, 0);
+          cur[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+              opa[i], opb[j], (ZC && h == 0) ? i32x4{0, 0, 0, 0} : cur[i][j], 0, 0, 0);
     }
     if constexpr (RES) {
       if (kt == nkt_a - 1) {
@@ -820,10 +826,12 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   }
   if constexpr (G128) {
     // the last group sits in the set of parity (nkt - 1) & 1; the other set
-    // was flushed and is zero
+    // was flushed already (and, unless ZC, cleared)
     const int last = nkt - 1;
-    flush(acc, (last & 1) ? 0 : last);
-    flush(acc2, (last & 1) ? last : 0);
+    if (last & 1)
+      flush(acc2, last);
+    else
+      flush(acc, last);
   }
 
   // Asymmetric groups: corr[i][j] = 2^-e(m) sum_g o[m,g] wsum[n,g] for the
