@@ -1726,7 +1726,9 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
     ia.group = 0;
     ia.y = nullptr;
     ia.lr_mode = LR_NONE;
-    hipError_t e = a.tiled ? launch_pipe<4, 4, 4>(ia, st) : launch_tiles<4, 4>(ia, st);
+    hipError_t e = !a.tiled ? launch_tiles<4, 4>(ia, st)
+                   : ia.a_i8 ? launch_pipe<4, 4, 3>(ia, st)
+                             : launch_pipe<4, 4, 4>(ia, st);
     if (e != hipSuccess) return e;
     if (!a.y) return hipSuccess;
   }
@@ -1737,7 +1739,11 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   if (a.tiled || (a.a_i8 && a.K % 128 == 0 && a.group % 128 == 0)) {
     // Grouped: a 64 x 32 wave tile, so that the float group accumulators fit
     // beside the integer ones at two waves per SIMD.
-    return ya.group > 0 ? launch_pipe<4, 2, 3>(ya, st) : launch_pipe<4, 4, 4>(ya, st);
+    // Four stages for packed codes (2 x 64 KB of LDS per CU); int8 codes
+    // double the activation tile, and four of their stages would leave one
+    // workgroup per CU.
+    if (ya.group > 0) return launch_pipe<4, 2, 3>(ya, st);
+    return ya.a_i8 ? launch_pipe<4, 4, 3>(ya, st) : launch_pipe<4, 4, 4>(ya, st);
   }
   const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
   if (a.group == 0 && a.M >= 256 && big_tiles >= 200) return launch_tiles<8, 4>(ya, st);
