@@ -137,7 +137,8 @@ def time_graph(fn, steps: int, warmup: int) -> float:
             for i in range(steps):
                 fn(i)
     torch.cuda.synchronize()
-    g.replay()                      # untimed replay: first-launch costs
+    for _ in range(3):              # untimed replays: first-launch costs, clocks settle
+        g.replay()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -147,6 +148,69 @@ def time_graph(fn, steps: int, warmup: int) -> float:
     end.record(cur)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / 1e3 / steps
+
+
+def replay_stats(fn, steps: int, warmup: int, reps: int = 7) -> dict:
+    """Spread of the per-step time over `reps` further replays of one graph of
+    `steps` calls (each replay timed alone with events): median, p10, p90."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for i in range(steps):
+                fn(i)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    t = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b) / steps)
+    q = np.percentile(np.array(t), [10, 50, 90])
+    return {"median_ms_per_step": float(q[1]), "p10_ms_per_step": float(q[0]),
+            "p90_ms_per_step": float(q[2]), "replays": reps, "steps_per_replay": steps}
+
+
+def environment() -> dict:
+    """ROCm and device identification, and the clocks rocm-smi reports."""
+    import subprocess
+    prop = torch.cuda.get_device_properties(0)
+    env = {"rocm": torch.version.hip, "torch": torch.__version__, "device": prop.name,
+           "compute_units": prop.multi_processor_count,
+           "arch": getattr(prop, "gcnArchName", None)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15)
+        env["clocks"] = [l.strip() for l in r.stdout.splitlines() if "clk" in l.lower()][:8]
+    except Exception as e:  # pragma: no cover - informational only
+        env["clocks"] = f"unavailable: {type(e).__name__}"
+    return env
+
+
+def prefill_shapes(steps: int, warmup: int) -> dict:
+    """qlinear_forward TOP/s on the other prefill shapes: the grouped
+    down-projection and the Llama-3-8B decoder linears (4096 tokens)."""
+    out = {}
+    for wl in [synth.DOWN_PROJ] + synth.LLAMA3_8B:
+        layer = Layer(wl, w_layout="tiled")
+        t = time_graph(layer.forward, steps, warmup)
+        tops = layer.ops() / t / 1e12
+        out[wl.name] = {"TOP/s": tops, "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
+                        "ms_per_step": t * 1e3, "had_block": wl.had_block,
+                        "w_group": wl.w_group, "rank": wl.rank}
+        log(f"shape {wl.name}: {t * 1e6:.1f} us/step, {tops:.0f} TOP/s")
+        del layer
+        torch.cuda.empty_cache()
+    return out
 
 
 def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
@@ -295,9 +359,12 @@ def cpu_baseline(wl: synth.Workload, seconds: float) -> dict:
     """The float64 oracle on the whole workload, repeated until `seconds` of
     CPU time have passed (at least once)."""
     from oracle import w4a4_oracle as O
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        info = threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in info), default=1)
+        blas = ", ".join(sorted({str(p.get("internal_api")) for p in info if p.get("user_api") == "blas"}))
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     d = synth.make_inputs(wl)
@@ -314,7 +381,8 @@ def cpu_baseline(wl: synth.Workload, seconds: float) -> dict:
         if t >= seconds:
             break
     return {"value": calls * 2 * wl.M * wl.N * wl.K / t / 1e12, "unit": "TOP/s",
-            "cores": int(threads), "kind": "oracle", "seconds": t,
+            "cores": int(threads), "kind": "oracle", "seconds": t, "blas": blas,
+            "ms_per_call": t / calls * 1e3,
             "sample": f"{calls} oracle calls on the whole {wl.M}-row {wl.name} workload "
                       f"(weights prepared untimed)"}
 
@@ -331,6 +399,7 @@ def main() -> int:
     ap.add_argument("--no-offq", action="store_true")
     ap.add_argument("--no-serq", action="store_true")
     ap.add_argument("--no-mxfp4", action="store_true")
+    ap.add_argument("--no-shapes", action="store_true")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="only launch the prefill kernels and a calibration copy (for counters)")
     args = ap.parse_args()
@@ -353,6 +422,7 @@ def main() -> int:
     kt = kernel_times(pre, args.steps, args.warmup)
     # W4A8 layers (8-bit activations beside the 4-bit weights), same workload.
     t_step8 = time_graph(lambda i: pre.forward(i, act_bits=8), args.steps, args.warmup)
+    pre_stats = replay_stats(pre.forward, args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
     rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M  # X in, packed codes + scales out
@@ -369,6 +439,7 @@ def main() -> int:
         dec = Layer(probe, copies=copies, w_layout=args.w_layout)
         log(f"decode: {dec.wl.name} with {copies} weight copies, timing {args.steps} steps")
         t_dec = time_graph(dec.forward, args.steps, args.warmup)
+        dec_stats = replay_stats(dec.forward, args.steps, args.warmup)
         kd = kernel_times(dec, args.steps, args.warmup)
         gbs = dec.algorithmic_bytes() / t_dec / 1e9
         log(f"decode: {t_dec * 1e6:.2f} us/step, {gbs:.0f} GB/s")
@@ -377,6 +448,7 @@ def main() -> int:
         decode = {
             "metric": "W4A4 qlinear HBM GB/s (M=8)", "value": gbs, "unit": "GB/s",
             "ms_per_step": t_dec * 1e3, "frac_of_hbm": gbs / PEAK_HBM_GBS,
+            "spread": dec_stats,
             "bytes_per_step": dec.algorithmic_bytes(), "weight_copies": copies,
             "kernels_us": {k: v * 1e6 for k, v in kd.items()},
             "w4a8": {"value": dec.algorithmic_bytes() / t_dec8 / 1e9, "unit": "GB/s",
@@ -494,6 +566,8 @@ def main() -> int:
         }
         del x, wq, ws, y, wsb, xq, xs
 
+    shapes = None if args.no_shapes else prefill_shapes(min(args.steps, 50), args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle for {args.cpu_seconds:.0f} s")
@@ -522,6 +596,7 @@ def main() -> int:
                      "ops_per_launch": pre.ops(), "us_per_launch": kt["qgemm"] * 1e6,
                      "algorithmic_bytes_per_launch": gemm_bytes(pre.wl),
                      "traffic": read_traffic(gemm_bytes(pre.wl))},
+        "spread": pre_stats,
         "kernels_us": {k: v * 1e6 for k, v in kt.items()},
         "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,
         "w4a8": {"metric": "W4A8 qlinear TOPS (M=2048), K=N=4096", "value": pre.ops() / t_step8 / 1e12,
@@ -530,7 +605,9 @@ def main() -> int:
         "offq": offq,
         "serq": serq,
         "mxfp4": mxfp4,
+        "prefill_shapes": shapes,
         "cpu_baseline": cpu,
+        "environment": environment(),
     }
     print(json.dumps(out), flush=True)
     return 0
