@@ -470,6 +470,15 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same copy from a wave-uniform base address (SGPR pair) plus a 32-bit
+// per-lane offset: the per-iteration address arithmetic stays scalar.
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // Workgroup barrier that also waits for this wave's own LDS reads: no wave
 // passes it while another may still read a stage that is about to be
 // refilled.  Written as asm with a memory clobber so that the compiler keeps
@@ -535,7 +544,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar run addresses
   const int wm0 = (wave >> 1) * WM;
   const int wn0 = (wave & 1) * WN;
   const int64_t tiles_m = (a.M + BM - 1) / BM;
@@ -551,8 +560,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   const int nkt = nkt_a + (RES ? a.res_iters : 0);           // iterations (weight tiles)
 
   // Source pointer (at iteration 0) and LDS offset of each run this wave
-  // copies.  Row-major operands: a run is 16 rows x 64 bytes.  Tiled
-  // operands: a run is one contiguous 1 KB block already in fragment order.
+  // copies.  Row-major operands: a run is 16 rows x 64 bytes, and the pointer
+  // is the lane's own.  Tiled operands: a run is one contiguous 1 KB block
+  // already in fragment order, and the pointer is the block's (wave-uniform)
+  // start.
   const uint8_t* src[RUNS_PER_WAVE];
   int dst[RUNS_PER_WAVE];
   int step[RUNS_PER_WAVE];
@@ -564,7 +575,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     if (run < A_RUNS && APK) {
       int64_t mb = m0 / 16 + run;
       mb = mb < mblocks ? mb : mblocks - 1;
-      src[q] = a.xq + mb * nkt_a * 1024 + 16 * lane;
+      src[q] = a.xq + mb * nkt_a * 1024;
       step[q] = 1024;
       dst[q] = (run * 4) << 8;
     } else if (run < A_RUNS) {
@@ -572,7 +583,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       if constexpr (TILED) {
         int64_t mb = m0 / 16 + blk;
         mb = mb < mblocks ? mb : mblocks - 1;
-        src[q] = a.xq + (mb * nkt_a * 2 + h) * 1024 + 16 * lane;
+        src[q] = a.xq + (mb * nkt_a * 2 + h) * 1024;
         step[q] = 2048;
       } else {
         int64_t m = m0 + blk * 16 + rr;
@@ -586,7 +597,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       if constexpr (TILED) {
         int64_t nb = n0 / 16 + blk;
         nb = nb < nblocks ? nb : nblocks - 1;
-        src[q] = a.wq + nb * nkt * 1024 + 16 * lane;
+        src[q] = a.wq + nb * nkt * 1024;
         step[q] = 1024;
       } else {
         int64_t n = n0 + blk * 16 + rr;
@@ -604,7 +615,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       int64_t t = kt;
       // residual iterations read the code columns from the start again
       if (RES && kt >= nkt_a && wave + 4 * q < A_RUNS) t -= nkt_a;
-      dma16(src[q] + t * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
+      if constexpr (TILED)  // src[q] is the run's uniform base; lane l copies bytes [16 l, 16 l + 16)
+        dma16s(src[q] + t * step[q], 16 * lane, b + dst[q]);
+      else
+        dma16(src[q] + t * step[q], __builtin_amdgcn_readfirstlane(b + dst[q]));
     }
   };
 
@@ -788,17 +802,18 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // of stage kt is refilled with stage kt + STAGES and stage kt + 1's
   // fragments are read into the other register set; stage kt's matrix
   // instructions then run while those reads are in flight.
+  // steady: kt + STAGES < nkt is known to hold (no branch on it).
   auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[2][TM], uint4 (&fbc)[TN], i32x4 (&fan)[2][TM],
-                     uint4 (&fbn)[TN], int odd) {
+                     uint4 (&fbn)[TN], int odd, bool steady) {
     // The reads are unconditional (on the last iteration they read a stale,
     // in-bounds buffer) so that no branch joins between them and the matrix
     // instructions, where the compiler would wait for them.
-    if (kt + STAGES <= nkt)
+    if (steady || kt + STAGES <= nkt)
       wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
     else
       wait_vmcnt<0>();
     stage_barrier();
-    if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
+    if (steady || kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
     read_frags(stage((sbuf + 1) % STAGES), fan, fbn);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
     if constexpr (G128) {
@@ -811,16 +826,46 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     }
   };
   // kt0 is a multiple of 2 * STAGES, so the parity of kt is that of u, a
-  // compile-time constant in every unrolled iteration.
-  for (int kt0 = 0; kt0 < nkt; kt0 += 2 * STAGES) {
+  // compile-time constant in every unrolled iteration.  The loop runs the
+  // blocks of 2 * STAGES iterations that all refill a stage, with no
+  // per-iteration branch; it leaves fewer than 3 * STAGES iterations, which
+  // run unrolled after it.
+  // (Kernels with group flushes, and the row-major ones, keep the single
+  // loop: with two copies of the iteration their registers no longer fit two
+  // waves per SIMD.)
+  constexpr bool SPLIT = !FLUSH && TILED;
+  int kt0 = 0;
+  for (; SPLIT && kt0 + 3 * STAGES <= nkt; kt0 += 2 * STAGES) {
 #pragma unroll
     for (int u = 0; u < 2 * STAGES; ++u) {
+      if (u & 1)
+        iterate(kt0 + u, u % STAGES, fa1, fb1, fa0, fb0, 1, true);
+      else
+        iterate(kt0 + u, u % STAGES, fa0, fb0, fa1, fb1, 0, true);
+    }
+  }
+  if constexpr (!SPLIT) {
+    for (; kt0 < nkt; kt0 += 2 * STAGES) {
+#pragma unroll
+      for (int u = 0; u < 2 * STAGES; ++u) {
+        const int kt = kt0 + u;
+        if (kt < nkt) {
+          if (u & 1)
+            iterate(kt, u % STAGES, fa1, fb1, fa0, fb0, 1, false);
+          else
+            iterate(kt, u % STAGES, fa0, fb0, fa1, fb1, 0, false);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 3 * STAGES; ++u) {
       const int kt = kt0 + u;
       if (kt < nkt) {
         if (u & 1)
-          iterate(kt, u % STAGES, fa1, fb1, fa0, fb0, 1);
+          iterate(kt, u % STAGES, fa1, fb1, fa0, fb0, 1, false);
         else
-          iterate(kt, u % STAGES, fa0, fb0, fa1, fb1, 0);
+          iterate(kt, u % STAGES, fa0, fb0, fa1, fb1, 0, false);
       }
     }
   }
@@ -913,11 +958,11 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   }
 
   // Epilogue (accumulators hold 16 * acc: only the weights carry the factor).
+  const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
   const bool want_y = a.y != nullptr;
   const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
   const int64_t nlane = n0 + wn0 + (lane & 15);
-  const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
-  float sxr[TM][4];
+  float sxr[TM][4], swr[TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -929,8 +974,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t n = nlane + j * 16;
+    swr[j] = (GROUPED || !want_y || n >= a.N) ? 1.f : load_scale(a.sw, n, a.sw_f16);
+  }
+
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t n = nlane + j * 16;
     const bool n_ok = n < a.N;
-    const float swn = (GROUPED || !want_y || !n_ok) ? 1.f : load_scale(a.sw, n, a.sw_f16);
+    const float swn = swr[j];
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       f32x4 yv;
