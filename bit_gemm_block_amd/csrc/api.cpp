@@ -133,6 +133,13 @@ bool codes_tiled(int l) { return l == W4A4_CODES_I8_TILED || l == W4A4_CODES_PAC
 bool codes_i8(int l) { return l == W4A4_CODES_I8 || l == W4A4_CODES_I8_TILED;
 }
 bool wlayout_ok(int l) { return l == W4A4_WEIGHTS_ROWMAJOR || l == W4A4_WEIGHTS_TILED; }
+// Entry points that also take the offset-binary layouts check with these.
+bool layout_ok_ob(int l) { return layout_ok(l) || l == W4A4_CODES_PACKED_TILED_OB; }
+bool wlayout_ok_ob(int l) { return wlayout_ok(l) || l == W4A4_WEIGHTS_TILED_OB; }
+// Offset-binary buffers: the row sums follow the ceil(rows/16)*16 tiled rows.
+const int32_t* ob_sums(const uint8_t* q, int64_t rows, int64_t K) {
+  return reinterpret_cast<const int32_t*>(q + (rows + 15) / 16 * 16 * (K / 2));
+}
 
 }  // namespace
 
@@ -176,11 +183,12 @@ namespace {
 
 int quantize_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
                       uint8_t* xq, int codes_layout, float* x_scale, void* stream, int qmax) {
-  if (!dtype_ok(x_dtype) || !layout_ok(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
+  if (!dtype_ok(x_dtype) || !layout_ok_ob(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
   if (qmax != 7 && !codes_i8(codes_layout)) return W4A4_ERR_INVALID_ARG;  // 8-bit codes
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
-  if (codes_tiled(codes_layout) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  const bool ob = codes_layout == W4A4_CODES_PACKED_TILED_OB;
+  if ((codes_tiled(codes_layout) || ob) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if (M == 0) return W4A4_OK;
   if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
@@ -192,9 +200,11 @@ int quantize_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
   const int mode = codes_layout == W4A4_CODES_I8              ? w4a4::ROTQ_QUANT_I8
                    : codes_layout == W4A4_CODES_I8_TILED     ? w4a4::ROTQ_QUANT_I8_TILED
                    : codes_layout == W4A4_CODES_PACKED_TILED ? w4a4::ROTQ_QUANT_TILED
+                   : ob                                      ? w4a4::ROTQ_QUANT_TILED
                                                              : w4a4::ROTQ_QUANT;
   w4a4::RotqExtras ex;
   ex.qmax = qmax;
+  if (ob) ex.ob_sum = const_cast<int32_t*>(ob_sums(xq, M, K));
   hipError_t e = w4a4::launch_rotq(x, x_dtype == W4A4_F16, M, K, log2b, mode, K, false, nullptr, xq,
                                    x_scale, plan, static_cast<hipStream_t>(stream), &ex);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
@@ -255,14 +265,21 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M, 
 int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, const uint8_t* wq,
                     int w_layout, const void* w_scale, int w_scale_dtype, int64_t w_group,
                     int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, void* stream) {
-  if (!dtype_ok(w_scale_dtype) || !layout_ok(codes_layout) || !wlayout_ok(w_layout) || M < 0 ||
-      N < 0 || K <= 0)
+  if (!dtype_ok(w_scale_dtype) || !layout_ok_ob(codes_layout) || !wlayout_ok_ob(w_layout) ||
+      M < 0 || N < 0 || K <= 0)
     return W4A4_ERR_INVALID_ARG;
   if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
   int s = check_group(K, w_group, false);
   if (s != W4A4_OK) return s;
-  const bool tiled = w_layout == W4A4_WEIGHTS_TILED;
-  if (tiled != codes_tiled(codes_layout)) return W4A4_ERR_INVALID_ARG;
+  const bool w_ob = w_layout == W4A4_WEIGHTS_TILED_OB;
+  const bool a_ob = codes_layout == W4A4_CODES_PACKED_TILED_OB;
+  const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
+  if (tiled != (codes_tiled(codes_layout) || a_ob)) return W4A4_ERR_INVALID_ARG;
+  // offset-binary codes need offset-binary weights; the weights take them,
+  // or packed tiled codes in the decode kernel, with per-channel scales
+  if (a_ob && !w_ob) return W4A4_ERR_INVALID_ARG;
+  if (w_ob && (w_group != 0 || (!a_ob && (codes_layout != W4A4_CODES_PACKED_TILED || M > 32))))
+    return W4A4_ERR_UNSUPPORTED;
   if (tiled && (K % 128 != 0 || w_group % 128 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
   if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
@@ -280,7 +297,26 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, c
   g.t = nullptr; g.B = nullptr; g.lr_mode = w4a4::LR_NONE; g.rank = 0;
   g.a_i8 = codes_i8(codes_layout);
   g.tiled = tiled;
+  g.w_ob = w_ob;
+  if (a_ob) {
+    g.ob_sa = ob_sums(xq, M, K);
+    g.ob_sb = ob_sums(wq, N, K);
+  }
   hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? W4A4_OK : hip_fail(e);
+}
+
+int w4a4_weights_tiled_to_ob(const uint8_t* wq, int64_t N, int64_t K, uint8_t* out,
+                             void* stream) {
+  if (N < 0 || K <= 0) return W4A4_ERR_INVALID_ARG;
+  if (K % 128 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
+  if (N == 0) return W4A4_OK;
+  if (!wq || !out) return W4A4_ERR_INVALID_ARG;
+  if (!aligned16(wq) || !aligned16(out)) return W4A4_ERR_MISALIGNED;
+  int s = device_check(nullptr);
+  if (s != W4A4_OK) return s;
+  hipError_t e = w4a4::launch_weights_to_ob(wq, (N + 15) / 16 * 16, K, out,
+                                            static_cast<hipStream_t>(stream));
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
@@ -296,13 +332,15 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          int64_t had_block, int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream,
                   int qmax) {
-  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok(w_layout) || M < 0 || N < 0 ||
-      rank < 0)
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok_ob(w_layout) || M < 0 ||
+      N < 0 || rank < 0)
     return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if ((s = check_group(K, w_group, false)) != W4A4_OK) return s;
-  const bool tiled = w_layout == W4A4_WEIGHTS_TILED;
+  const bool w_ob = w_layout == W4A4_WEIGHTS_TILED_OB;
+  if (w_ob && (w_group != 0 || qmax != 7)) return W4A4_ERR_UNSUPPORTED;
+  const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
   if (tiled && (K % 128 != 0 || w_group % 128 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (rank > kMaxRank || (x_dtype == W4A4_F16 && rank % 8 != 0)) return W4A4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return W4A4_OK;
@@ -340,6 +378,10 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
     ex.lr_t = t;
   }
   const bool skinny = M <= 32 && (w_group == 0 || w_group % 128 == 0);
+  // Offset-binary weights: offset-binary codes (and their row sums) for the
+  // tiled GEMM; the decode kernel converts the weights and takes plain codes.
+  const bool a_ob = w_ob && !skinny;
+  if (a_ob) ex.ob_sum = const_cast<int32_t*>(ob_sums(xq, M, K));
   const int64_t units = (N + 15) / 16;
   const int64_t unit_bytes = 16 * (K / 2);
   if (skinny && units * unit_bytes <= kMaxPrefetchBytes) {
@@ -371,6 +413,11 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
   g.rank = static_cast<int>(rank);
   g.a_i8 = !packed_codes;
   g.tiled = tiled;
+  g.w_ob = w_ob;
+  if (a_ob) {
+    g.ob_sa = ob_sums(xq, M, K);
+    g.ob_sb = ob_sums(wq, N, K);
+  }
   e = w4a4::launch_qgemm(g, st);
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }

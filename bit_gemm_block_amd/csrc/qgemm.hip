@@ -70,6 +70,15 @@ __device__ __forceinline__ i32x4 widen(uint32_t p0, uint32_t p1) {
                static_cast<int32_t>((p1 << 4) & 0xF0F0F0F0u), static_cast<int32_t>(p1 & 0xF0F0F0F0u)};
 }
 
+// The same 16 values 16*q from offset-binary weight bytes (high nibble: the
+// even channel's signed code; low nibble: the odd channel's code + 8).
+__device__ __forceinline__ i32x4 widen_ob(uint32_t p0, uint32_t p1) {
+  return i32x4{static_cast<int32_t>(p0 & 0xF0F0F0F0u),
+               static_cast<int32_t>(((p0 ^ 0x08080808u) << 4) & 0xF0F0F0F0u),
+               static_cast<int32_t>(p1 & 0xF0F0F0F0u),
+               static_cast<int32_t>(((p1 ^ 0x08080808u) << 4) & 0xF0F0F0F0u)};
+}
+
 // LDS tile layout ("fragment-major").  A K iteration covers 128 codes
 // (64 bytes) of each tile row.  The 16-byte piece lane group g
 // (lanes 16g..16g+15) of an MFMA reads holds codes [16g, 16g+16) of K step 0
@@ -490,7 +499,8 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <int TM, int TN, int STAGES, bool GROUPED, int LRMODE, bool TILED, bool APK,
-          bool ASYM = false, bool G128 = false, bool AG1 = false, bool RES = false>
+          bool ASYM = false, bool G128 = false, bool AG1 = false, bool RES = false,
+          bool OB = false>
 __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // APK: activation codes packed (4 bits) in the weights' tile layout, widened
   // in registers like the weights; otherwise int8 codes.
@@ -509,13 +519,20 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   // AG1: asymmetric codes with a single group per row (group = K): the
   // integer product runs over all of K like the symmetric one, and the row
   // scale and zero-point term enter in the epilogue only.
+  // OB: offset-binary codes and weights (each byte: one signed nibble on top,
+  // one offset nibble q + 8 below, paired crosswise between the operands).
+  // Per 16 packed bytes the first K step takes the activations' high nibbles
+  // with the weights' low ones and the second step the reverse, one AND per
+  // dword; the accumulator holds 16 sum qx qw + 128 (row sum + column sum).
+  static_assert(!OB || (APK && TILED && !GROUPED && !ASYM && !RES), "offset-binary: plain packed");
   constexpr int WM = TM * 16, WN = TN * 16;
   constexpr int BM = 2 * WM, BN = 2 * WN;
   constexpr int A_BYTES = BM * (APK ? 64 : 128), B_BYTES = BN * 64;
   constexpr int STAGE = A_BYTES + B_BYTES;
   constexpr int A_RUNS = APK ? BM / 16 : BM / 16 * 2, B_RUNS = BN / 16;
-  constexpr float kInvA = APK ? kInv256 : kInv16;  // both operands widened: 256 * acc
-  constexpr int kShiftA = APK ? 8 : 4;
+  // both operands widened: 256 * acc (offset-binary: 16 * acc after the correction)
+  constexpr float kInvA = (APK && !OB) ? kInv256 : kInv16;
+  constexpr int kShiftA = (APK && !OB) ? 8 : 4;
   constexpr int RUNS = A_RUNS + B_RUNS;
   static_assert(RUNS % 4 == 0, "runs split evenly over 4 waves");
   static_assert(STAGES >= 2 && STAGES <= 8, "stages");
@@ -715,15 +732,26 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       i32x4 opb[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
       i32x4 opa[TM];
+      if constexpr (OB) {
+        // step 0: activation high x weight low nibbles; step 1: the reverse
+        const uint32_t ma = h ? 0x0F0F0F0Fu : 0xF0F0F0F0u, mb = ~ma;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        if constexpr (APK)
-          opa[i] = h ? widen(fa[0][i][2], fa[0][i][3]) : widen(fa[0][i][0], fa[0][i][1]);
-        else
-          opa[i] = fa[h][i];
+        for (int j = 0; j < TN; ++j)
+          opb[j] = i32x4{static_cast<int32_t>(fb[j].x & mb), static_cast<int32_t>(fb[j].y & mb),
+                         static_cast<int32_t>(fb[j].z & mb), static_cast<int32_t>(fb[j].w & mb)};
+#pragma unroll
+        for (int i = 0; i < TM; ++i) opa[i] = fa[0][i] & static_cast<int32_t>(ma);
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) opb[j] = h ? widen(fb[j].z, fb[j].w) : widen(fb[j].x, fb[j].y);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          if constexpr (APK)
+            opa[i] = h ? widen(fa[0][i][2], fa[0][i][3]) : widen(fa[0][i][0], fa[0][i][1]);
+          else
+            opa[i] = fa[h][i];
+        }
       }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -963,6 +991,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   const int64_t mlane = m0 + wm0 + (lane >> 4) * 4;
   const int64_t nlane = n0 + wn0 + (lane & 15);
   float sxr[TM][4], swr[TN];
+  int32_t sar[OB ? TM : 1][4];  // offset-binary: 128 * (row sum) of each lane row
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -970,6 +999,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       const int64_t m = mlane + i * 16 + r;
       sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? a.sx[m] * (RES ? kInvA * 0.125f : kInvA)
                                                           : 0.f;
+      if constexpr (OB) sar[i][r] = m < a.M ? 128 * a.ob_sa[m] : 0;
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -982,8 +1012,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     const int64_t n = nlane + j * 16;
     const bool n_ok = n < a.N;
     const float swn = swr[j];
+    const int32_t sbn = (OB && n_ok) ? 128 * a.ob_sb[n] : 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
+      if constexpr (OB) {
+        // exact: the accumulator less 128 (row sum + column sum) is 16 sum qx qw
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] -= sar[i][r] + sbn;
+      }
       f32x4 yv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1325,8 +1361,8 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const i32x4 w0 = widen(wv[c].x, wv[c].y);
-      const i32x4 w1 = widen(wv[c].z, wv[c].w);
+      const i32x4 w0 = (TILED && a.w_ob) ? widen_ob(wv[c].x, wv[c].y) : widen(wv[c].x, wv[c].y);
+      const i32x4 w1 = (TILED && a.w_ob) ? widen_ob(wv[c].z, wv[c].w) : widen(wv[c].z, wv[c].w);
 #pragma unroll
       for (int b = 0; b < MB; ++b) {
         i32x4 x0, x1;
@@ -1658,6 +1694,22 @@ hipError_t launch_pipe(const GemmArgs& a, hipStream_t st) {
   // Grouped: the tile's scales for all groups in dynamic LDS.
   const size_t scale_lds =
       a.group > 0 ? static_cast<size_t>(BN) * (a.K / a.group) * (a.sw_f16 ? 2 : 4) : 0;
+  if (a.ob_sa) {  // offset-binary packed codes and weights, per-channel scales
+    if constexpr (TM == 4 && TN == 4 && STAGES == 4) {
+      if (a.lr_mode == LR_F16)
+        hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR_F16, true, true, false,
+                                              false, false, false, true>), grid, dim3(256), 0, st, a);
+      else if (a.lr_mode == LR_F32)
+        hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR_F32, true, true, false,
+                                              false, false, false, true>), grid, dim3(256), 0, st, a);
+      else
+        hipLaunchKernelGGL((qgemm_pipe_kernel<TM, TN, STAGES, false, LR_NONE, true, true, false,
+                                              false, false, false, true>), grid, dim3(256), 0, st, a);
+      return hipGetLastError();
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
 #define W4A4_PIPE_CASE(G, LR, T, P)                                                          \
   if ((a.group > 0) == G && a.lr_mode == LR && (a.tiled != 0) == T && (!a.a_i8) == P) {      \
     if (G && P && a.group == 128)                                                           \
@@ -1766,7 +1818,8 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st) {
   // group fit in LDS beside two workgroups per CU.
   if (a.zx) return launch_pipe_asym<2, 4, 3>(a, st);
   // The skinny kernel flushes weight groups at 128-code granularity.
-  const bool skinny_ok = a.group == 0 || a.group % 128 == 0;
+  // (offset-binary codes take the tiled kernel at any M)
+  const bool skinny_ok = (a.group == 0 || a.group % 128 == 0) && !a.ob_sa;
   if (a.M <= 16 && skinny_ok) return launch_skinny<1>(a, st);
   if (a.M <= 32 && skinny_ok) return launch_skinny<2>(a, st);
   // The tiled kernels write the int32 product only when ungrouped: a grouped

@@ -137,6 +137,7 @@ struct RotqKArgs {
   int res_pad;       // res_r rounded up to 128 (0: no residual)
   int64_t tile_stride;  // 128-code tiles per 16-row block of the tiled output
   uint8_t* mx_scale;    // MXFP4 scale bytes: [M, K/32], or tiled (64 B per 16 x 128 tile)
+  int32_t* ob_sum;      // offset-binary packed codes: per-row sums of the odd channels' codes
   float* xrot;
   uint8_t* q;
   void* scale;
@@ -533,6 +534,22 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         rpk[d] = acc;
       }
     }
+    // 8. Offset-binary codes: the sum of the row's codes at odd channels
+    // (elements kfirst + r with r odd, kfirst being even), reduced like the
+    // absmax.
+    if (a.ob_sum) {
+      int os = 0;
+#pragma unroll
+      for (int r = 1; r < R; r += 2) os += static_cast<int32_t>(code[r] << 28) >> 28;
+      for (int o = 1; o < span_wave; o <<= 1) os += __shfl_xor(os, o);
+      if (cross) {
+        uint32_t* ssum = slots + a.nslots / 2;
+        if (valid && (lam & (span_wave - 1)) == 0) atomicAdd(&ssum[slot], static_cast<uint32_t>(os));
+        __syncthreads();
+        if (on) os = static_cast<int>(ssum[slot]);
+      }
+      if (leader) a.ob_sum[row] = os;
+    }
   }
   if (!valid) return;
   const bool tiled = a.mode == ROTQ_QUANT_TILED || a.mode == ROTQ_QUANT_I8_TILED;
@@ -542,12 +559,13 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   if (a.mode == ROTQ_QUANT || a.mode == ROTQ_QUANT_TILED) {
     // Packed nibbles: element 8d+t in nibble t of dword d.
     uint32_t pk[R / 8];
+    const uint32_t obx = a.ob_sum ? 0x08080808u : 0u;  // offset-binary low nibbles
 #pragma unroll
     for (int d = 0; d < R / 8; ++d) {
       uint32_t acc = 0u;
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_alignbit(code[8 * d + t], acc, 4);
-      pk[d] = acc;
+      pk[d] = acc ^ obx;
     }
     if (!tiled) {
       uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
@@ -726,6 +744,7 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   ka.zero = ex ? ex->asym_zero : nullptr;
   ka.mx = (ex && ex->mx_scale) ? 1 : 0;
   ka.mx_scale = ex ? ex->mx_scale : nullptr;
+  ka.ob_sum = ex ? ex->ob_sum : nullptr;
   ka.res_r = ex ? ex->res_r : 0;
   ka.res_pad = (ka.res_r + 127) / 128 * 128;
   ka.tile_stride = K / 128 + ka.res_pad / 128;

@@ -57,6 +57,9 @@ struct RotqExtras {
   // written here ([M, K/32] row-major, or in 64-byte tiles with the tiled
   // codes: byte (g * 16 + r) of tile (row block, t) is block 4 t + g of row r).
   uint8_t* mx_scale = nullptr;
+  // Offset-binary packed codes (packed tiled mode): every byte XOR 0x08, and
+  // the sum of each row's codes at odd channels written here ([rows] int32).
+  int32_t* ob_sum = nullptr;
   const void* lr_at = nullptr;
   int lr_rank = 0;
   void* lr_t = nullptr;
@@ -112,6 +115,14 @@ struct GemmArgs {
   // layout, mx_xs and mx_ws their E8M0 scales in 64-byte tiles; sx, sw unused.
   const uint8_t* mx_xs;
   const uint8_t* mx_ws;
+  // Offset-binary operands.  w_ob: the tiled weights are in the offset-binary
+  // layout.  ob_sa non-null: the packed tiled codes are too (every byte XOR
+  // 0x08), ob_sa [M] and ob_sb [N] being the sums of the activation codes at
+  // odd and of the weight codes at even channels; the accumulator then holds
+  // 16 sum_k qx qw + 128 (ob_sa[m] + ob_sb[n]).
+  int w_ob;
+  const int32_t* ob_sa;
+  const int32_t* ob_sb;
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
@@ -121,6 +132,11 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
 // (group a multiple of 8 dividing K); wq row-major [N, K/2] or tiled.
 hipError_t launch_weight_group_sums(const uint8_t* wq, bool tiled, int64_t N, int64_t K,
                                     int group, int32_t* out, hipStream_t st);
+
+// Tiled int4 weights -> offset-binary tiled weights followed by the per-row
+// sums of the codes at even channels (rows a multiple of 16, K of 128).
+hipError_t launch_weights_to_ob(const uint8_t* wq, int64_t rows, int64_t K, uint8_t* out,
+                                hipStream_t st);
 
 // ---- low-rank projection (lowrank.hip) -------------------------------------
 // t = x [M, K] . At[rank, K]^T.  fp16 inputs: pair_out writes the fp16 pair

@@ -21,13 +21,13 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, F16 = 0, 1
-CODES_PACKED, CODES_I8, CODES_I8_TILED, CODES_PACKED_TILED = 0, 1, 2, 3
-WEIGHTS_ROWMAJOR, WEIGHTS_TILED = 0, 1
+CODES_PACKED, CODES_I8, CODES_I8_TILED, CODES_PACKED_TILED, CODES_PACKED_TILED_OB = range(5)
+WEIGHTS_ROWMAJOR, WEIGHTS_TILED, WEIGHTS_TILED_OB = 0, 1, 2
 _LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8, "i8_tiled": CODES_I8_TILED,
-            "packed_tiled": CODES_PACKED_TILED}
+            "packed_tiled": CODES_PACKED_TILED, "packed_tiled_ob": CODES_PACKED_TILED_OB}
 _TILED_CODES = (CODES_I8_TILED, CODES_PACKED_TILED)
 _PACKED_CODES = (CODES_PACKED, CODES_PACKED_TILED)
-_WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED}
+_WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED, "tiled_ob": WEIGHTS_TILED_OB}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -58,6 +58,7 @@ _SIGS = {
     "w4a4_qgemm_residual": (_INT, [_P, _P, _P, _P, _INT, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "w4a4_quantize_mxfp4": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _INT, _P, _P]),
     "w4a4_qgemm_mxfp4": (_INT, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "w4a4_weights_tiled_to_ob": (_INT, [_P, _I64, _I64, _P, _P]),
     "w4a4_qlinear_forward_mxfp4": (_INT, [_P, _INT, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _I64,
                                           _P, _P, ctypes.c_size_t, _P]),
     "w4a4_qlinear_forward_residual": (_INT, [_P, _INT, _P, _P, _INT, _I64, _I64, _I64, _I64, _I64,
@@ -106,6 +107,18 @@ def pad16(n: int) -> int:
     return (n + 15) // 16 * 16
 
 
+def ob_bytes(rows: int, K: int) -> int:
+    """Bytes of an offset-binary tiled buffer (flat uint8): the tiles of
+    pad16(rows) rows, then one int32 sum per padded row."""
+    return pad16(rows) * (K // 2 + 4)
+
+
+def ob_sums(buf: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """The int32 row sums that follow the tiles of an offset-binary buffer."""
+    off = pad16(rows) * (K // 2)
+    return buf[off:off + 4 * pad16(rows)].view(torch.int32)[:rows]
+
+
 def _check(fn: str, status: int) -> None:
     if status != OK:
         raise W4A4Error(fn, status)
@@ -150,12 +163,15 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
                       layout: str = "packed") -> Tuple[torch.Tensor, torch.Tensor]:
     """Codes in layout "packed" ([M, K/2] nibbles), "i8" ([M, K] int8 in
     the GEMM's K order), "i8_tiled" ([pad16(M), K] in 2 KB tiles) or
-    "packed_tiled" ([pad16(M), K/2] in the weights' 1 KB tiles), and one
-    float32 scale per row."""
+    "packed_tiled" ([pad16(M), K/2] in the weights' 1 KB tiles) or
+    "packed_tiled_ob" (flat, ob_bytes(M, K): offset-binary tiles and the row
+    sums of the odd channels' codes), and one float32 scale per row."""
     _dev(x, "x")
     M, K = x.shape
     lay = _LAYOUTS[layout]
-    if xq is None:
+    if xq is None and lay == CODES_PACKED_TILED_OB:
+        xq = torch.empty((ob_bytes(M, K),), dtype=torch.uint8, device=x.device)
+    elif xq is None:
         rows = pad16(M) if lay in _TILED_CODES else M
         xq = torch.empty((rows, K // 2 if lay in _PACKED_CODES else K), dtype=torch.uint8,
                          device=x.device)
@@ -232,13 +248,22 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
         M = x_scale.shape[0] if x_scale is not None else xq.shape[0]
     if N is None:
         N = w_scale.shape[0] if w_scale is not None else wq.shape[0]
-    K = 2 * wq.shape[1]
-    if xq.shape[1] != (K // 2 if lay in _PACKED_CODES else K):
-        raise ValueError("xq and wq disagree on K")
-    if xq.shape[0] < (pad16(M) if lay in _TILED_CODES else M):
-        raise ValueError("xq has too few rows")
-    if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
-        raise ValueError("wq has too few rows")
+    if wl == WEIGHTS_TILED_OB:  # flat buffers: K from the weights' size
+        K = 2 * (wq.numel() // pad16(N) - 4)
+        if wq.numel() != ob_bytes(N, K):
+            raise ValueError("wq is not an offset-binary buffer of N rows")
+    else:
+        K = 2 * wq.shape[1]
+        if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
+            raise ValueError("wq has too few rows")
+    if lay == CODES_PACKED_TILED_OB:
+        if xq.numel() != ob_bytes(M, K):
+            raise ValueError("xq is not an offset-binary buffer of M rows and K channels")
+    else:
+        if xq.shape[1] != (K // 2 if lay in _PACKED_CODES else K):
+            raise ValueError("xq and wq disagree on K")
+        if xq.shape[0] < (pad16(M) if lay in _TILED_CODES else M):
+            raise ValueError("xq has too few rows")
     if want_y and y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     if want_acc and acc is None:
@@ -248,6 +273,21 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
         _ptr(xq), lay, _ptr(x_scale), _ptr(wq), wl, _ptr(w_scale), wst, w_group, M, N, K,
         _ptr(y), _ptr(acc), _stream(xq)))
     return y, acc
+
+
+def weights_tiled_to_ob(wq: torch.Tensor, N: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Offset-binary form (flat, ob_bytes(N, K)) of tiled weights [pad16(N), K/2]."""
+    _dev(wq, "wq")
+    K = 2 * wq.shape[1]
+    if wq.shape[0] != pad16(N):
+        raise ValueError("wq must be tiled weights of pad16(N) rows")
+    if out is None:
+        out = torch.empty((ob_bytes(N, K),), dtype=torch.uint8, device=wq.device)
+    if out.numel() != ob_bytes(N, K):
+        raise ValueError("out must hold ob_bytes(N, K) bytes")
+    _check("weights_tiled_to_ob", lib().w4a4_weights_tiled_to_ob(
+        _ptr(wq), N, K, _ptr(out), _stream(wq)))
+    return out
 
 
 def qlinear_workspace_size(M: int, N: int, K: int, rank: int) -> int:
@@ -270,7 +310,10 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
     wl = _WLAYOUTS[w_layout]
     M, K = x.shape
     N = w_scale.shape[0]
-    if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N) or wq.shape[1] != K // 2:
+    if wl == WEIGHTS_TILED_OB:
+        if wq.numel() != ob_bytes(N, K):
+            raise ValueError("wq is not an offset-binary buffer matching w_scale and x")
+    elif wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N) or wq.shape[1] != K // 2:
         raise ValueError("wq does not match w_scale and x")
     rank = 0 if At is None else At.shape[0]
     if rank:

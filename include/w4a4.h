@@ -80,7 +80,8 @@ typedef enum {
   W4A4_CODES_PACKED = 0,
   W4A4_CODES_I8 = 1,
   W4A4_CODES_I8_TILED = 2,
-  W4A4_CODES_PACKED_TILED = 3
+  W4A4_CODES_PACKED_TILED = 3,
+  W4A4_CODES_PACKED_TILED_OB = 4
 } w4a4_codes_layout;
 
 /* Tiled layouts (K a multiple of 128).  Rows are taken in blocks of 16 and K
@@ -102,7 +103,32 @@ typedef enum {
  * With these layouts every 1 KB of a GEMM operand tile is one contiguous
  * copy, which the strided row-major layouts cannot offer; tiled weights are
  * used with tiled activation codes (int8 or packed). */
-typedef enum { W4A4_WEIGHTS_ROWMAJOR = 0, W4A4_WEIGHTS_TILED = 1 } w4a4_weight_layout;
+typedef enum {
+  W4A4_WEIGHTS_ROWMAJOR = 0,
+  W4A4_WEIGHTS_TILED = 1,
+  W4A4_WEIGHTS_TILED_OB = 2
+} w4a4_weight_layout;
+
+/* Offset-binary tiled layouts: the same 16-row x 128-code tiles, with one
+ * code of every byte stored as q + 8 (0..15) so that the GEMM isolates each
+ * nibble with a single AND per dword instead of a shift and an AND.  Each
+ * buffer is followed by one int32 per padded row.
+ *   W4A4_CODES_PACKED_TILED_OB (activations, [ceil(M/16)*16, K/2] bytes and
+ *     then ceil(M/16)*16 int32): every W4A4_CODES_PACKED_TILED byte XOR 0x08
+ *     (low nibble: the even channel's code + 8; high nibble: the odd
+ *     channel's signed code); int32 m after the tiles: the sum of row m's
+ *     codes at odd channels.
+ *   W4A4_WEIGHTS_TILED_OB (weights, [ceil(N/16)*16, K/2] bytes and then
+ *     ceil(N/16)*16 int32): every W4A4_WEIGHTS_TILED byte with its nibbles
+ *     swapped and the new low nibble XOR 8 (low nibble: the odd channel's
+ *     code + 8; high nibble: the even channel's signed code); int32 n after
+ *     the tiles: the sum of row n's codes at even channels.
+ * In a product of the two, the GEMM pairs each high (signed, times 16) nibble
+ * with the other operand's low (offset) nibble of the same channel, so its
+ * int32 accumulator holds 16 sum_k qx qw + 128 (row sum + column sum), which
+ * the epilogue corrects exactly.  Offset-binary weights are produced from
+ * tiled ones by w4a4_weights_tiled_to_ob and serve per-channel weight scales
+ * (w_group 0) of the int4 layer and GEMM. */
 
 /* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
 int w4a4_abi_version(void);
@@ -139,6 +165,9 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot,
 int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
                            int64_t had_block, uint8_t* xq, int codes_layout,
                            float* x_scale, void* stream);
+/*   With W4A4_CODES_PACKED_TILED_OB, xq holds ceil(M/16)*16 * (K/2 + 4)
+ *   bytes: the offset-binary tiles and then the per-row sums of the codes at
+ *   odd channels. */
 
 /*
  * 8-bit form of the activation quantizer, for W4A8 layers: the layers a
@@ -201,6 +230,24 @@ int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale,
                     const uint8_t* wq, int w_layout, const void* w_scale,
                     int w_scale_dtype, int64_t w_group, int64_t M, int64_t N,
                     int64_t K, float* y, int32_t* acc, void* stream);
+/*   Offset-binary weights (W4A4_WEIGHTS_TILED_OB, w_group 0) pair with
+ *   W4A4_CODES_PACKED_TILED_OB codes at any M, or with W4A4_CODES_PACKED_TILED
+ *   codes for M <= 32; W4A4_CODES_PACKED_TILED_OB codes need such weights.
+ *   Other combinations return W4A4_ERR_INVALID_ARG or W4A4_ERR_UNSUPPORTED. */
+
+/*
+ * Converts tiled int4 weights to the offset-binary tiled layout (a storage
+ * encoding of the same codes; see W4A4_WEIGHTS_TILED_OB).
+ *   wq   [ceil(N/16)*16, K/2] bytes in W4A4_WEIGHTS_TILED (K a multiple of
+ *        128), as written by w4a4_quantize_weight_int4.
+ *   out  ceil(N/16)*16 * (K/2 + 4) bytes: the converted tiles, then the
+ *        per-row sums of the codes at even channels.  out may equal wq when
+ *        that buffer has room for the sums.  Padding rows are converted like
+ *        the others; their sums are unspecified.
+ * Meant for weight preparation; the weight scales are unchanged.
+ */
+int w4a4_weights_tiled_to_ob(const uint8_t* wq, int64_t N, int64_t K, uint8_t* out,
+                             void* stream);
 
 /* Bytes of workspace qlinear_forward needs for these sizes (0 if M or N is
  * 0). */

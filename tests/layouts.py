@@ -101,3 +101,34 @@ def untile_mx_scales(flat, M, K):
     Mp = pad16(M)
     t = np.asarray(flat)[:Mp * K // 32].reshape(Mp // 16, K // 128, 4, 16).transpose(0, 3, 1, 2)
     return np.ascontiguousarray(t).reshape(Mp, K // 32)[:M]
+
+
+def ob_weights(tiled, N, K):
+    """W4A4_WEIGHTS_TILED bytes [pad16(N), K/2] -> the flat
+    W4A4_WEIGHTS_TILED_OB buffer: every byte with its nibbles swapped and the
+    new low nibble XOR 8, then one int32 per padded row, the sum of the row's
+    codes at even channels (0 for padding rows here)."""
+    t = np.asarray(tiled, np.uint8)
+    conv = (((t & 0x0F) << 4) | (((t >> 4) & 0x0F) ^ 0x08)).astype(np.uint8)
+    lo = (untile_weights(t, N) & 0x0F).astype(np.int32)
+    sums = np.zeros(pad16(N), np.int32)
+    sums[:N] = np.where(lo >= 8, lo - 16, lo).sum(axis=1)
+    return np.concatenate([conv.reshape(-1), sums.view(np.uint8)])
+
+
+def ob_codes(tiled, M, K):
+    """W4A4_CODES_PACKED_TILED bytes [pad16(M), K/2] -> the flat
+    W4A4_CODES_PACKED_TILED_OB buffer: every byte XOR 0x08, then one int32
+    per padded row, the sum of the row's codes at odd channels."""
+    t = np.asarray(tiled, np.uint8)
+    hi = (untile_weights(t, M) >> 4).astype(np.int32)
+    sums = np.zeros(pad16(M), np.int32)
+    sums[:M] = np.where(hi >= 8, hi - 16, hi).sum(axis=1)
+    return np.concatenate([(t ^ 0x08).reshape(-1), sums.view(np.uint8)])
+
+
+def split_ob(flat, rows, K):
+    """Flat offset-binary buffer -> (tile bytes [pad16(rows), K/2], int32 sums [rows])."""
+    Rp = pad16(rows)
+    nb = Rp * (K // 2)
+    return flat[:nb].reshape(Rp, K // 2), flat[nb:nb + 4 * Rp].view(np.int32)[:rows]

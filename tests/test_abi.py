@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 22
+    assert len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -134,12 +134,38 @@ def test_qlinear_argument_errors(lib):
     assert f(*bad) == W.ERR_MISALIGNED
     bad = list(args); bad[10] = 100
     assert f(*bad) == W.ERR_UNSUPPORTED
-    bad = list(args); bad[3] = 2                                      # weight layout
+    bad = list(args); bad[3] = 3                                      # weight layout
     assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[3] = W.WEIGHTS_TILED_OB; bad[10] = 128      # offset-binary: no groups
+    assert f(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[3] = W.WEIGHTS_TILED_OB                     # offset-binary: no W4A8
+    assert lib.w4a8_qlinear_forward(*bad) == W.ERR_UNSUPPORTED
     bad = list(args); bad[3] = W.WEIGHTS_TILED; bad[10] = 64          # tiled needs group % 128
     assert f(*bad) == W.ERR_UNSUPPORTED
     bad = list(args); bad[6] = 0
     assert f(*bad) == W.OK
+
+
+def test_offset_binary_argument_errors(lib):
+    g = lib.w4a4_qgemm_w4a4
+    OB, WOB = W.CODES_PACKED_TILED_OB, W.WEIGHTS_TILED_OB
+    PT, WT = W.CODES_PACKED_TILED, W.WEIGHTS_TILED
+    assert g(P, OB, P, P, WT, P, W.F16, 0, 64, 8, 256, P, None, None) == W.ERR_INVALID_ARG  # codes need OB weights
+    assert g(P, OB, P, P, 0, P, W.F16, 0, 64, 8, 256, P, None, None) == W.ERR_INVALID_ARG   # row-major weights
+    assert g(P, OB, P, P, WOB, P, W.F16, 128, 64, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, PT, P, P, WOB, P, W.F16, 0, 33, 8, 256, P, None, None) == W.ERR_UNSUPPORTED  # M > 32
+    assert g(P, W.CODES_I8_TILED, P, P, WOB, P, W.F16, 0, 8, 8, 256, P, None, None) == W.ERR_UNSUPPORTED
+    assert g(P, OB, P, P, WOB, P, W.F16, 0, 64, 8, 192, P, None, None) == W.ERR_UNSUPPORTED  # K % 128
+    assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 192, 0, P, OB, P, None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_quantize_act_int8(P, W.F16, 4, 256, 0, P, OB, P, None) == W.ERR_INVALID_ARG
+    assert lib.w4a4_quantize_weight_int4(P, W.F32, 8, 256, 0, 0, P, WOB, P, W.F16,
+                                         None) == W.ERR_INVALID_ARG
+    c = lib.w4a4_weights_tiled_to_ob
+    assert c(P, 8, 192, P, None) == W.ERR_UNSUPPORTED
+    assert c(P, -1, 256, P, None) == W.ERR_INVALID_ARG
+    assert c(None, 8, 256, P, None) == W.ERR_INVALID_ARG
+    assert c(P, 8, 256, Q, None) == W.ERR_MISALIGNED
+    assert c(None, 0, 256, None, None) == W.OK
 
 
 def test_mxfp4_argument_errors(lib):
@@ -243,3 +269,4 @@ def test_valid_call_without_device_reports_unsupported(lib):
                                     P, need, None) == W.ERR_UNSUPPORTED
     assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P,
                                       None) == W.ERR_UNSUPPORTED
+    assert lib.w4a4_weights_tiled_to_ob(P, 8, 256, P, None) == W.ERR_UNSUPPORTED

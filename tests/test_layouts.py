@@ -4,8 +4,9 @@ import numpy as np
 
 from layouts import (codes_from_i8, i8_from_codes, tile_codes_i8, tile_weights, untile_codes_i8,
                      tile_weights_residual, untile_weights_residual, tile_mx_scales,
-                     untile_mx_scales,
+                     untile_mx_scales, ob_codes, ob_weights, split_ob,
                      untile_weights)
+from oracle import w4a4_oracle as O
 
 
 def test_i8_order_is_even_then_odd_channels():
@@ -67,3 +68,31 @@ def test_mx_scale_tiling():
         for blk in range(K // 32):
             t, g = blk // 4, blk % 4
             assert flat[((m // 16) * (K // 128) + t) * 64 + g * 16 + m % 16] == s[m, blk]
+
+
+def test_offset_binary_pairing_gives_the_corrected_integer_product():
+    # The nibble pairing the offset-binary GEMM uses, emulated byte by byte on
+    # the encoded operands: signed high nibble (times 16) of one side with the
+    # offset low nibble of the other, both ways, summed over the bytes of a
+    # row pair, equals 16 qx.qw + 128 (row sum + column sum).
+    rng = np.random.default_rng(11)
+    M, N, K = 19, 23, 256
+    qx = rng.integers(-8, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    qx[0] = -8
+    qw[0] = 7
+    ta, sa = split_ob(ob_codes(tile_weights(O.pack_int4(qx)), M, K), M, K)
+    tb, sb = split_ob(ob_weights(tile_weights(O.pack_int4(qw)), N, K), N, K)
+    A = untile_weights(ta, M).astype(np.int64)
+    B = untile_weights(tb, N).astype(np.int64)
+
+    def hi(v):
+        h = v >> 4
+        return np.where(h >= 8, h - 16, h)
+
+    acc = 16 * (hi(A) @ (B & 15).T + (A & 15) @ hi(B).T)
+    ref = O.int_gemm(qx, qw).astype(np.int64)
+    assert np.array_equal(acc, 16 * ref + 128 * (sa[:, None].astype(np.int64) + sb[None, :]))
+    # the sums are those of the odd (activations) and even (weights) channels
+    assert np.array_equal(sa, qx[:, 1::2].sum(axis=1))
+    assert np.array_equal(sb, qw[:, 0::2].sum(axis=1))
