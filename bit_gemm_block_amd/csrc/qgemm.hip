@@ -479,6 +479,14 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane straight into LDS: lane l writes [lds_base + 4 l, +4).
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // The same copy from a wave-uniform base address (SGPR pair) plus a 32-bit
 // per-lane offset: the per-iteration address arithmetic stays scalar.
 __device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
@@ -811,6 +819,39 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     __syncthreads();
   }
 
+  // EPL (offset-binary kernels): the epilogue's row scales, row sums and
+  // column sums are copied into LDS before the first stage, so that the
+  // epilogue reads them from LDS instead of waiting for global loads after
+  // the loop: [0, BM) the row scales, [BM, 2 BM) the row sums and
+  // [2 BM, 2 BM + BN) the column sums.  Rows and columns past the ends copy
+  // the last valid element (never used).  The copies precede the stage
+  // copies, so the prologue's wait covers them.  (Measured on the plain
+  // kernel, the same staging made the 4096 x 28672 x 4096 product slower.)
+  constexpr bool EPL = OB;
+  __shared__ __attribute__((aligned(16))) uint32_t epl[EPL ? 2 * BM + BN : 1];
+  if constexpr (EPL) {
+    const uint32_t eb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(epl));
+    if (a.y && a.sx) {
+      for (int c = wave; c < BM / 64; c += 4) {
+        int64_t m = m0 + c * 64 + lane;
+        m = m < a.M ? m : a.M - 1;
+        dma4(a.sx + m, eb + c * 256);
+      }
+    }
+    if constexpr (OB) {
+      for (int c = wave; c < BM / 64; c += 4) {
+        int64_t m = m0 + c * 64 + lane;
+        m = m < a.M ? m : a.M - 1;
+        dma4(a.ob_sa + m, eb + 4 * BM + c * 256);
+      }
+      for (int c = wave; c < BN / 64; c += 4) {
+        int64_t n = n0 + c * 64 + lane;
+        n = n < a.N ? n : a.N - 1;
+        dma4(a.ob_sb + n, eb + 8 * BM + c * 256);
+      }
+    }
+  }
+
   // Prologue: the first STAGES stages in flight, stage 0 visible, its
   // fragments read.
 #pragma unroll
@@ -997,9 +1038,11 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? a.sx[m] * (RES ? kInvA * 0.125f : kInvA)
+      const int lr = wm0 + (lane >> 4) * 4 + i * 16 + r;  // row in the tile
+      const float sxm = EPL ? __uint_as_float(epl[lr]) : a.sx[m];
+      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? sxm * (RES ? kInvA * 0.125f : kInvA)
                                                           : 0.f;
-      if constexpr (OB) sar[i][r] = m < a.M ? 128 * a.ob_sa[m] : 0;
+      if constexpr (OB) sar[i][r] = 128 * static_cast<int32_t>(epl[BM + lr]);
     }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
@@ -1012,7 +1055,7 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     const int64_t n = nlane + j * 16;
     const bool n_ok = n < a.N;
     const float swn = swr[j];
-    const int32_t sbn = (OB && n_ok) ? 128 * a.ob_sb[n] : 0;
+    const int32_t sbn = OB ? 128 * static_cast<int32_t>(epl[2 * BM + wn0 + (lane & 15) + j * 16]) : 0;
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       if constexpr (OB) {
