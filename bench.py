@@ -58,7 +58,7 @@ def log(*a):
 class Layer:
     """Device-resident inputs of one workload with weights quantized on GPU."""
 
-    def __init__(self, wl: synth.Workload, copies: int = 1, w_layout: str = "tiled"):
+    def __init__(self, wl: synth.Workload, copies: int = 1, w_layout: str = "tiled_ob"):
         self.wl = wl
         self.w_layout = w_layout
         d = synth.make_inputs(wl)
@@ -69,24 +69,38 @@ class Layer:
         self.B = torch.from_numpy(d["B"].T.copy()).to(dev) if d["B"] is not None else None
         Wd = torch.from_numpy(d["W"]).to(dev)
         sdt = torch.float16 if wl.w_scale_dtype == "float16" else torch.float32
-        wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt, layout=w_layout)
+        ob = w_layout == "tiled_ob"
+        wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt,
+                                        layout="tiled" if ob else w_layout)
         del Wd
+        # Offset-binary weights are converted from the tiled ones; the W4A8
+        # layer keeps the tiled form (the offset-binary form serves 4-bit codes).
+        wq8 = wq
+        if ob:
+            wq = W.weights_tiled_to_ob(wq, wl.N)
         # Distinct copies of the weights (and low-rank factors) so a decode
         # loop streams them from HBM rather than from the last-level cache.
         self.sets = [(wq, ws, self.A, self.B)]
+        self.sets8 = [(wq8, ws, self.A, self.B)]
         for _ in range(copies - 1):
-            self.sets.append((wq.clone(), ws.clone(),
-                              self.A.clone() if self.A is not None else None,
-                              self.B.clone() if self.B is not None else None))
+            c = (wq.clone(), ws.clone(), self.A.clone() if self.A is not None else None,
+                 self.B.clone() if self.B is not None else None)
+            self.sets.append(c)
+            self.sets8.append((wq8.clone() if ob else c[0],) + c[1:])
         self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         need = W.qlinear_workspace_size(wl.M, wl.N, wl.K, wl.rank)
         self.ws = torch.empty((need,), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def forward(self, i: int = 0, act_bits: int = 4):
-        wq, ws, A, B = self.sets[i % len(self.sets)]
+        if act_bits == 8:
+            wq, ws, A, B = self.sets8[i % len(self.sets8)]
+            wl = "tiled" if self.w_layout == "tiled_ob" else self.w_layout
+        else:
+            wq, ws, A, B = self.sets[i % len(self.sets)]
+            wl = self.w_layout
         W.qlinear_forward(self.x, wq, ws, self.wl.had_block, self.wl.w_group, A, B,
-                          y=self.y, workspace=self.ws, w_layout=self.w_layout, act_bits=act_bits)
+                          y=self.y, workspace=self.ws, w_layout=wl, act_bits=act_bits)
 
     def forward_asym(self, i: int = 0):
         """The layer with asymmetric group-wise activations (tiled weights,
@@ -96,7 +110,7 @@ class Layer:
                                workspace=self.ws)
 
     def prepare_asym(self):
-        self.gsum = W.weight_group_sums(self.sets[0][0], self.wl.had_block, self.wl.N,
+        self.gsum = W.weight_group_sums(self.sets8[0][0], self.wl.had_block, self.wl.N,
                                         w_layout="tiled")
         torch.cuda.synchronize()
 
@@ -112,16 +126,20 @@ class Layer:
         return 2 * self.wl.M * self.wl.N * self.wl.K
 
 
-def gemm_bytes(wl: synth.Workload) -> int:
+def gemm_bytes(wl: synth.Workload, ob: bool = False) -> int:
     """Bytes the GEMM must move once: packed codes and scales of X, packed
-    weights and their scales, float32 Y."""
+    weights and their scales, float32 Y (offset-binary operands: plus one
+    int32 sum per row of X and of the weights)."""
     sb = 2 if wl.w_scale_dtype == "float16" else 4
     nsc = wl.N if wl.w_group == 0 else wl.N * (wl.K // wl.w_group)
-    return wl.M * wl.K // 2 + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N
+    sums = 4 * (wl.M + wl.N) if ob else 0
+    return wl.M * wl.K // 2 + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N + sums
 
 
 def gemm_kernel_name(layer: "Layer") -> str:
-    return "qgemm_pipe_kernel" if layer.w_layout == "tiled" or layer.wl.M > 32 else "qgemm_skinny_kernel"
+    if layer.wl.M <= 32:
+        return "qgemm_skinny_kernel"
+    return "qgemm_pipe_kernel" + (" (offset-binary)" if layer.w_layout == "tiled_ob" else "")
 
 
 def time_graph(fn, steps: int, warmup: int) -> float:
@@ -201,12 +219,13 @@ def prefill_shapes(steps: int, warmup: int) -> dict:
     down-projection and the Llama-3-8B decoder linears (4096 tokens)."""
     out = {}
     for wl in [synth.DOWN_PROJ] + synth.LLAMA3_8B:
-        layer = Layer(wl, w_layout="tiled")
+        # offset-binary weights serve per-channel scales; grouped ones stay tiled
+        layer = Layer(wl, w_layout="tiled_ob" if wl.w_group == 0 else "tiled")
         t = time_graph(layer.forward, steps, warmup)
         tops = layer.ops() / t / 1e12
         out[wl.name] = {"TOP/s": tops, "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
                         "ms_per_step": t * 1e3, "had_block": wl.had_block,
-                        "w_group": wl.w_group, "rank": wl.rank}
+                        "w_group": wl.w_group, "rank": wl.rank, "w_layout": layer.w_layout}
         log(f"shape {wl.name}: {t * 1e6:.1f} us/step, {tops:.0f} TOP/s")
         del layer
         torch.cuda.empty_cache()
@@ -219,12 +238,17 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     launches replayed from one HIP graph, timed with events on the stream
     they run on."""
     wl = layer.wl
-    tiled = layer.w_layout == "tiled"
+    tiled = layer.w_layout in ("tiled", "tiled_ob")
     # the code layout qlinear_forward hands the GEMM: packed tiles with tiled
-    # weights, int8 rows otherwise
-    lay = "packed_tiled" if tiled else "i8"
-    xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K // 2 if tiled else wl.K),
-                     dtype=torch.uint8, device="cuda:0")
+    # weights (offset-binary ones above 32 rows with offset-binary weights),
+    # int8 rows otherwise
+    ob = layer.w_layout == "tiled_ob" and wl.M > 32
+    lay = "packed_tiled_ob" if ob else "packed_tiled" if tiled else "i8"
+    if ob:
+        xq = torch.empty((W.ob_bytes(wl.M, wl.K),), dtype=torch.uint8, device="cuda:0")
+    else:
+        xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K // 2 if tiled else wl.K),
+                         dtype=torch.uint8, device="cuda:0")
     sx = torch.empty((wl.M,), dtype=torch.float32, device="cuda:0")
     W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay)
     torch.cuda.synchronize()
@@ -234,7 +258,7 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     out["qgemm"] = time_graph(
         lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
                                layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
-                               layout=lay, w_layout=layer.w_layout, M=wl.M),
+                               layout=lay, w_layout=layer.w_layout, M=wl.M, N=wl.N),
         steps, warmup)
     return out
 
@@ -393,7 +417,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--w-layout", choices=["tiled", "rowmajor"], default="tiled")
+    ap.add_argument("--w-layout", choices=["tiled_ob", "tiled", "rowmajor"], default="tiled_ob")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offq", action="store_true")
@@ -417,7 +441,8 @@ def main() -> int:
 
     # ---- prefill: the headline ------------------------------------------------
     pre = Layer(synth.PREFILL, w_layout=args.w_layout)
-    log(f"prefill: {pre.wl.name} timing {args.steps} steps")
+    ob_pre = args.w_layout == "tiled_ob"
+    log(f"prefill: {pre.wl.name} ({args.w_layout} weights) timing {args.steps} steps")
     t_step = time_graph(pre.forward, args.steps, args.warmup)
     kt = kernel_times(pre, args.steps, args.warmup)
     # W4A8 layers (8-bit activations beside the 4-bit weights), same workload.
@@ -594,8 +619,8 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(pre), "achieved": gemm_tops,
                      "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
                      "ops_per_launch": pre.ops(), "us_per_launch": kt["qgemm"] * 1e6,
-                     "algorithmic_bytes_per_launch": gemm_bytes(pre.wl),
-                     "traffic": read_traffic(gemm_bytes(pre.wl))},
+                     "algorithmic_bytes_per_launch": gemm_bytes(pre.wl, ob_pre),
+                     "traffic": read_traffic(gemm_bytes(pre.wl, ob_pre))},
         "spread": pre_stats,
         "kernels_us": {k: v * 1e6 for k, v in kt.items()},
         "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,

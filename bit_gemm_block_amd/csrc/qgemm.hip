@@ -1039,9 +1039,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
       const int lr = wm0 + (lane >> 4) * 4 + i * 16 + r;  // row in the tile
-      const float sxm = EPL ? __uint_as_float(epl[lr]) : a.sx[m];
-      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M) ? sxm * (RES ? kInvA * 0.125f : kInvA)
-                                                          : 0.f;
+      // (global reads only for rows that exist)
+      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M)
+                      ? (EPL ? __uint_as_float(epl[lr]) : a.sx[m]) * (RES ? kInvA * 0.125f : kInvA)
+                      : 0.f;
       if constexpr (OB) sar[i][r] = 128 * static_cast<int32_t>(epl[BM + lr]);
     }
 #pragma unroll

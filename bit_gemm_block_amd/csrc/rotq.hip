@@ -534,39 +534,46 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         rpk[d] = acc;
       }
     }
-    // 8. Offset-binary codes: the sum of the row's codes at odd channels
-    // (elements kfirst + r with r odd, kfirst being even), reduced like the
-    // absmax.
-    if (a.ob_sum) {
-      int os = 0;
+  }
+  // Packed nibbles (packed modes): element 8d+t in nibble t of dword d.
+  const bool packed_mode = a.mode == ROTQ_QUANT || a.mode == ROTQ_QUANT_TILED;
+  uint32_t pk[R / 8];
+  if (packed_mode) {
 #pragma unroll
-      for (int r = 1; r < R; r += 2) os += static_cast<int32_t>(code[r] << 28) >> 28;
-      for (int o = 1; o < span_wave; o <<= 1) os += __shfl_xor(os, o);
-      if (cross) {
-        uint32_t* ssum = slots + a.nslots / 2;
-        if (valid && (lam & (span_wave - 1)) == 0) atomicAdd(&ssum[slot], static_cast<uint32_t>(os));
-        __syncthreads();
-        if (on) os = static_cast<int>(ssum[slot]);
-      }
-      if (leader) a.ob_sum[row] = os;
+    for (int d = 0; d < R / 8; ++d) {
+      uint32_t acc = 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_alignbit(code[8 * d + t], acc, 4);
+      pk[d] = acc;
     }
+  }
+  // 8. Offset-binary codes: the sum of the row's codes at odd channels (the
+  // high nibbles of the packed bytes, kfirst being even), reduced like the
+  // absmax.  Each dword's high nibbles are 4 int8 values 16 q.
+  if (a.ob_sum) {
+    int os16 = 0;
+#pragma unroll
+    for (int d = 0; d < R / 8; ++d)
+      os16 = __builtin_amdgcn_sdot4(static_cast<int>(pk[d] & 0xF0F0F0F0u), 0x01010101, os16, false);
+    int os = os16 >> 4;
+    for (int o = 1; o < span_wave; o <<= 1) os += __shfl_xor(os, o);
+    if (cross) {
+      uint32_t* ssum = slots + a.nslots / 2;
+      if (valid && (lam & (span_wave - 1)) == 0) atomicAdd(&ssum[slot], static_cast<uint32_t>(os));
+      __syncthreads();
+      if (on) os = static_cast<int>(ssum[slot]);
+    }
+    if (leader) a.ob_sum[row] = os;
   }
   if (!valid) return;
   const bool tiled = a.mode == ROTQ_QUANT_TILED || a.mode == ROTQ_QUANT_I8_TILED;
   const int64_t nkit = a.K / 128;               // 128-code K iterations per row
   const int64_t tstride = a.tile_stride;        // tiles per row block of the output
   const int64_t rblk = row >> 4, rin = row & 15;  // 16-row block, row inside it
-  if (a.mode == ROTQ_QUANT || a.mode == ROTQ_QUANT_TILED) {
-    // Packed nibbles: element 8d+t in nibble t of dword d.
-    uint32_t pk[R / 8];
+  if (packed_mode) {
     const uint32_t obx = a.ob_sum ? 0x08080808u : 0u;  // offset-binary low nibbles
 #pragma unroll
-    for (int d = 0; d < R / 8; ++d) {
-      uint32_t acc = 0u;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) acc = __builtin_amdgcn_alignbit(code[8 * d + t], acc, 4);
-      pk[d] = acc ^ obx;
-    }
+    for (int d = 0; d < R / 8; ++d) pk[d] ^= obx;
     if (!tiled) {
       uint8_t* dst = a.q + ((row * a.K + kfirst) >> 1);
       if constexpr (R == 8) {
