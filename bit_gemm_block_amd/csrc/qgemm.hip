@@ -1150,7 +1150,7 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar run addresses
   const int wm0 = (wave >> 1) * WM;
   const int wn0 = (wave & 1) * WN;
   const int64_t tiles_m = (a.M + BM - 1) / BM;
@@ -1162,8 +1162,10 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
   const int nkt = static_cast<int>(a.K / 128);
   const int64_t mblocks = (a.M + 15) / 16, nblocks = (a.N + 15) / 16;
 
-  // Code runs: one contiguous 1 KB tile each.  Scale run: 16 lanes x 16 B,
-  // lane l copying bytes 16 (l & 3) .. of the scale tile of block l / 4.
+  // Code runs: one contiguous 1 KB tile each, from the run's uniform base
+  // (lane l copies bytes [16 l, 16 l + 16)).  Scale run: 16 lanes x 16 B,
+  // lane l copying bytes 16 (l & 3) .. of the scale tile of block l / 4
+  // (a per-lane address).
   const uint8_t* src[RUNS_PER_WAVE];
   int dst[RUNS_PER_WAVE];
 #pragma unroll
@@ -1172,13 +1174,13 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
     if (run < A_RUNS) {
       int64_t mb = m0 / 16 + run;
       mb = mb < mblocks ? mb : mblocks - 1;
-      src[q] = a.xq + mb * nkt * 1024 + 16 * lane;
+      src[q] = a.xq + mb * nkt * 1024;
       dst[q] = (run * 4) << 8;
     } else {
       const int blk = run - A_RUNS;
       int64_t nb = n0 / 16 + blk;
       nb = nb < nblocks ? nb : nblocks - 1;
-      src[q] = a.wq + nb * nkt * 1024 + 16 * lane;
+      src[q] = a.wq + nb * nkt * 1024;
       dst[q] = A_BYTES + ((blk * 4) << 8);
     }
   }
@@ -1198,7 +1200,7 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
     const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(base));
 #pragma unroll
     for (int q = 0; q < RUNS_PER_WAVE - 1; ++q)
-      dma16(src[q] + static_cast<int64_t>(kt) * 1024, __builtin_amdgcn_readfirstlane(b + dst[q]));
+      dma16s(src[q] + static_cast<int64_t>(kt) * 1024, 16 * lane, b + dst[q]);
     if (lane < 16)
       dma16(src[RUNS_PER_WAVE - 1] + static_cast<int64_t>(kt) * 64,
             __builtin_amdgcn_readfirstlane(b + dst[RUNS_PER_WAVE - 1]));
@@ -1255,26 +1257,28 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
 
   auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[TM], i32x4 (&fbc)[TN], int (&sac)[TM],
                      int (&sbc)[TN], i32x4 (&fan)[TM], i32x4 (&fbn)[TN], int (&san)[TM],
-                     int (&sbn)[TN]) {
-    if (kt + STAGES <= nkt)
+                     int (&sbn)[TN], bool steady) {
+    if (steady || kt + STAGES <= nkt)
       wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
     else
       wait_vmcnt<0>();
     stage_barrier();
-    if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
+    if (steady || kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
     read_frags(stage((sbuf + 1) % STAGES), fan, fbn, san, sbn);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
     compute(fac, fbc, sac, sbc);
   };
+  // (A branch-free copy of the steady iterations, as in the int4 kernel,
+  // does not fit this kernel's registers at two waves per SIMD.)
   for (int kt0 = 0; kt0 < nkt; kt0 += 2 * STAGES) {
 #pragma unroll
     for (int u = 0; u < 2 * STAGES; ++u) {
       const int kt = kt0 + u;
       if (kt < nkt) {
         if (u & 1)
-          iterate(kt, u % STAGES, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
+          iterate(kt, u % STAGES, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0, false);
         else
-          iterate(kt, u % STAGES, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
+          iterate(kt, u % STAGES, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1, false);
       }
     }
   }
