@@ -1034,17 +1034,28 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   float sxr[TM][4], swr[TN];
   int32_t sar[OB ? TM : 1][4];  // offset-binary: 128 * (row sum) of each lane row
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    const int lr0 = wm0 + (lane >> 4) * 4 + i * 16;  // the lane's first row of block i, in the tile
+    // The staged rows are read unconditionally (one 16-byte LDS read per block,
+    // every row of the tile is staged) and masked after; global reads only
+    // for rows that exist.
+    f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 av = i32x4{0, 0, 0, 0};
+    if constexpr (EPL) {
+      sv = *reinterpret_cast<const f32x4*>(&epl[lr0]);
+      av = *reinterpret_cast<const i32x4*>(&epl[BM + lr0]);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mlane + i * 16 + r;
-      const int lr = wm0 + (lane >> 4) * 4 + i * 16 + r;  // row in the tile
-      // (global reads only for rows that exist)
-      sxr[i][r] = ((!ASYM || AG1) && want_y && m < a.M)
-                      ? (EPL ? __uint_as_float(epl[lr]) : a.sx[m]) * (RES ? kInvA * 0.125f : kInvA)
-                      : 0.f;
-      if constexpr (OB) sar[i][r] = 128 * static_cast<int32_t>(epl[BM + lr]);
+      const bool live = (!ASYM || AG1) && want_y && m < a.M;
+      if constexpr (EPL)
+        sxr[i][r] = live ? sv[r] * (RES ? kInvA * 0.125f : kInvA) : 0.f;
+      else
+        sxr[i][r] = live ? a.sx[m] * (RES ? kInvA * 0.125f : kInvA) : 0.f;
+      if constexpr (OB) sar[i][r] = 128 * av[r];
     }
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t n = nlane + j * 16;
