@@ -47,6 +47,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 namespace w4a4 {
 namespace {
 
@@ -1062,6 +1064,10 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     swr[j] = (GROUPED || !want_y || n >= a.N) ? 1.f : load_scale(a.sw, n, a.sw_f16);
   }
 
+  // The common case (interior tile, Y only) runs a copy of the store loop
+  // with no per-store checks.
+  auto emit = [&](auto fast) {
+    constexpr bool FAST = decltype(fast)::value;
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t n = nlane + j * 16;
@@ -1093,7 +1099,11 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
           yv = add_lowrank<LRMODE>(a, yv, m0 + wm0 + i * 16, n0 + wn0 + j * 16, lane);
       }
       const int64_t mb = mlane + i * 16;
-      if (interior) {
+      if constexpr (FAST) {
+        float* yp = a.y + mb * a.N + n;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yp[r * a.N] = yv[r];
+      } else if (interior) {
         float* yp = a.y + mb * a.N + n;
         int32_t* ap = a.acc + mb * a.N + n;
 #pragma unroll
@@ -1112,6 +1122,11 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
       }
     }
   }
+  };
+  if (interior && want_y && (FLUSH || ASYM || !a.acc))
+    emit(std::true_type{});
+  else
+    emit(std::false_type{});
 }
 
 // MXFP4 GEMM (SERQ page, "Metodología" item 2: the 4-bit path in MXFP4).
