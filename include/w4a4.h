@@ -167,7 +167,7 @@ int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
                            float* x_scale, void* stream);
 /*   With W4A4_CODES_PACKED_TILED_OB, xq holds ceil(M/16)*16 * (K/2 + 4)
  *   bytes: the offset-binary tiles and then the per-row sums of the codes at
- *   odd channels. */
+ *   odd channels (rows M and above: unspecified). */
 
 /*
  * 8-bit form of the activation quantizer, for W4A8 layers: the layers a
