@@ -1039,22 +1039,27 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
   for (int i = 0; i < TM; ++i) {
     const int lr0 = wm0 + (lane >> 4) * 4 + i * 16;  // the lane's first row of block i, in the tile
     // The staged rows are read unconditionally (one 16-byte LDS read per block,
-    // every row of the tile is staged) and masked after; global reads only
-    // for rows that exist.
+    // every row of the tile is staged) and masked after.  Unstaged: one
+    // 16-byte global read when the block's four rows exist, else per row.
     f32x4 sv = f32x4{0.f, 0.f, 0.f, 0.f};
     i32x4 av = i32x4{0, 0, 0, 0};
+    const int64_t mf = mlane + i * 16;  // a multiple of 4: x_scale + mf is 16-byte aligned
     if constexpr (EPL) {
       sv = *reinterpret_cast<const f32x4*>(&epl[lr0]);
       av = *reinterpret_cast<const i32x4*>(&epl[BM + lr0]);
+    } else if ((!ASYM || AG1) && want_y) {
+      if (mf + 3 < a.M) {
+        sv = *reinterpret_cast<const f32x4*>(a.sx + mf);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (mf + r < a.M) sv[r] = a.sx[mf + r];
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t m = mlane + i * 16 + r;
-      const bool live = (!ASYM || AG1) && want_y && m < a.M;
-      if constexpr (EPL)
-        sxr[i][r] = live ? sv[r] * (RES ? kInvA * 0.125f : kInvA) : 0.f;
-      else
-        sxr[i][r] = live ? a.sx[m] * (RES ? kInvA * 0.125f : kInvA) : 0.f;
+      const bool live = (!ASYM || AG1) && want_y && mf + r < a.M;
+      sxr[i][r] = live ? sv[r] * (RES ? kInvA * 0.125f : kInvA) : 0.f;
       if constexpr (OB) sar[i][r] = 128 * av[r];
     }
   }
