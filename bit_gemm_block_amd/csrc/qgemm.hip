@@ -1288,13 +1288,13 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
 
   auto iterate = [&](int kt, int sbuf, i32x4 (&fac)[TM], i32x4 (&fbc)[TN], int (&sac)[TM],
                      int (&sbc)[TN], i32x4 (&fan)[TM], i32x4 (&fbn)[TN], int (&san)[TM],
-                     int (&sbn)[TN], bool steady) {
-    if (steady || kt + STAGES <= nkt)
+                     int (&sbn)[TN]) {
+    if (kt + STAGES <= nkt)
       wait_vmcnt<(STAGES - 2) * RUNS_PER_WAVE>();
     else
       wait_vmcnt<0>();
     stage_barrier();
-    if (steady || kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
+    if (kt + STAGES < nkt) issue(kt + STAGES, stage(sbuf));
     read_frags(stage((sbuf + 1) % STAGES), fan, fbn, san, sbn);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMAs
     compute(fac, fbc, sac, sbc);
@@ -1307,9 +1307,9 @@ __global__ void __launch_bounds__(128 * WGM) qgemm_mx_kernel(GemmArgs a) {
       const int kt = kt0 + u;
       if (kt < nkt) {
         if (u & 1)
-          iterate(kt, u % STAGES, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0, false);
+          iterate(kt, u % STAGES, fa1, fb1, sa1, sb1, fa0, fb0, sa0, sb0);
         else
-          iterate(kt, u % STAGES, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1, false);
+          iterate(kt, u % STAGES, fa0, fb0, sa0, sb0, fa1, fb1, sa1, sb1);
       }
     }
   }

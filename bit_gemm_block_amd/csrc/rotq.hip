@@ -622,7 +622,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   } else {
     // One int8 code per byte, each group of 8 elements stored in the order
     // 0,2,4,6,1,3,5,7: the K order in which the GEMM widens packed weights.
-    uint32_t pk[R / 4];
+    uint32_t pb[R / 4];
 #pragma unroll
     for (int d = 0; d < R / 8; ++d) {
       uint32_t e = 0u, o = 0u;
@@ -631,17 +631,17 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         e = __builtin_amdgcn_alignbit(code[8 * d + 2 * t], e, 8);
         o = __builtin_amdgcn_alignbit(code[8 * d + 2 * t + 1], o, 8);
       }
-      pk[2 * d] = e;
-      pk[2 * d + 1] = o;
+      pb[2 * d] = e;
+      pb[2 * d + 1] = o;
     }
     if (!tiled) {
       uint8_t* dst = a.q + row * a.K + kfirst;
       if constexpr (R == 8) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+        *reinterpret_cast<uint2*>(dst) = make_uint2(pb[0], pb[1]);
       } else {
 #pragma unroll
         for (int d = 0; d < R / 4; d += 4)
-          *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pk[d], pk[d + 1], pk[d + 2], pk[d + 3]);
+          *reinterpret_cast<uint4*>(dst + 4 * d) = make_uint4(pb[d], pb[d + 1], pb[d + 2], pb[d + 3]);
       }
     } else {
       // Code k of the row sits in the 2 KB block (rblk, k / 128) at
@@ -652,9 +652,9 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         uint8_t* dst = a.q + (rblk * tstride + (k >> 7)) * 2048 +
                        ((((((k & 31) >> 4) << 2) + ((k & 127) >> 5)) * 16 + rin) << 4) + (k & 15);
         if constexpr (R == 8) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[1]);
+          *reinterpret_cast<uint2*>(dst) = make_uint2(pb[0], pb[1]);
         } else {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
+          *reinterpret_cast<uint4*>(dst) = make_uint4(pb[4 * c], pb[4 * c + 1], pb[4 * c + 2], pb[4 * c + 3]);
         }
       }
     }
