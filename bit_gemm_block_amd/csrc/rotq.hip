@@ -59,6 +59,7 @@
 #include "lowrank_rows.h"
 
 #include <hip/hip_fp16.h>
+#include <type_traits>
 
 #pragma clang fp contract(off)
 
@@ -87,6 +88,21 @@ template <> struct Piece<_Float16> {
     for (int i = 0; i < 8; ++i) out[i] = static_cast<float>(h[i]);
   }
 };
+
+// First butterfly stage straight from a pair of fp16 values packed in one
+// dword (element 2i in the low half, 2i + 1 in the high half): v_fma_mix_f32
+// widens its fp16 operands exactly and rounds once, so lo * 1 + hi and
+// hi * (-1) + lo equal the float32 sum and difference of the widened values.
+__device__ __forceinline__ float mix_sum(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
+__device__ __forceinline__ float mix_dif(uint32_t w) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %1 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(w));
+  return r;
+}
 
 // Butterflies on register-index bits [LO, HI) of v: for every pair
 // (r, r | 2^st) with bit st of r clear, (a, b) -> (a + b, a - b).  The stage
@@ -243,15 +259,33 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   float v[R];
 
   // 1. Coalesced load and the in-piece butterflies.
+  // fp16 input with b >= 2: the first stage is fused into the widening.
+  const bool mix0 = sizeof(TIn) == 2 && a.log2b >= 1;
   if (valid) {
     const TIn* src = reinterpret_cast<const TIn*>(a.x) + row * a.K + k0;
+    if (mix0) {
 #pragma unroll
-    for (int j = 0; j < PPL; ++j) Piece<TIn>::load(src + (j * L + lam) * V, &v[j * V]);
+      for (int j = 0; j < PPL; ++j) {
+        const uint4 w = *reinterpret_cast<const uint4*>(src + (j * L + lam) * V);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int u = 0; u < V / 2; ++u) {
+          v[j * V + 2 * u] = mix_sum(wd[u]);
+          v[j * V + 2 * u + 1] = mix_dif(wd[u]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) Piece<TIn>::load(src + (j * L + lam) * V, &v[j * V]);
+    }
   } else {
 #pragma unroll
     for (int r = 0; r < R; ++r) v[r] = 0.f;
   }
-  fwht_bits_upto<0, LOGV>(v, a.log2b);
+  if (mix0)
+    fwht_bits_upto<1, LOGV>(v, a.log2b);
+  else
+    fwht_bits_upto<0, LOGV>(v, a.log2b);
   if (on) {
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
@@ -493,16 +527,28 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
     // quotient and code is 0.  The rint is the magic-number addition: the low
     // mantissa bits of q + 1.5 * 2^23 are rint(q) in two's complement.
     if (s_eff == 0.f || (s_eff >= 0x1p-100f && s_eff <= 0x1p100f)) {
-      const float rc = s_eff == 0.f ? 0.f : __frcp_rn(s_eff);
+      // When rs is a power of two (b = 4^k) the product y * rs is exact, so the
+      // quotient x~ / s is the same real number as y / (s / rs), with s / rs
+      // exact too, and both round alike.  An x~ that would underflow gives a
+      // quotient below 2^-26 in magnitude either way, that is code 0.
+      const bool fold = (__float_as_uint(a.rs) & 0x807FFFFFu) == 0u;
+      const float sd = fold ? s_eff * __fdiv_rn(1.f, a.rs) : s_eff;
+      const float rc = s_eff == 0.f ? 0.f : __frcp_rn(sd);
+      auto quantize = [&](auto folded) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float xt = v[r] * a.rs;
-        float q = xt * rc;
-        q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
-        q = __builtin_fmaf(__builtin_fmaf(-q, s_eff, xt), rc, q);
-        const float u = q + kMagic;
-        code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
-      }
+        for (int r = 0; r < R; ++r) {
+          const float xt = decltype(folded)::value ? v[r] : v[r] * a.rs;
+          float q = xt * rc;
+          q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
+          q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
+          const float u = q + kMagic;
+          code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
+        }
+      };
+      if (fold)
+        quantize(std::true_type{});
+      else
+        quantize(std::false_type{});
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
