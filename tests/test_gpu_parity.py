@@ -264,6 +264,22 @@ def test_quantize_act_fused_rotation(M, K, b, dt):
     assert np.all(np.abs(host(sx).astype(np.float64) - ps) <= 1e-6 * ps)
 
 
+@pytest.mark.parametrize("M,K,b,dt", [(64, 4096, 4096, "float16"), (33, 4096, 1024, "float16"),
+                                      (20, 4096, 2048, "float16"), (16, 512, 256, "float32"),
+                                      (9, 1024, 128, "float32"), (300, 4096, 4096, "float16")])
+def test_quantize_act_fused_equals_rotate_then_quantize(M, K, b, dt):
+    # The fused kernel quantizes x~ = RN(y / sqrt(b)) from the same butterflies
+    # as the rotation kernel; when 1 / sqrt(b) is a power of two it divides y by
+    # s sqrt(b) instead.  Either way its codes and scales equal those of the
+    # exact quantizer applied to the rotation kernel's output.
+    w = synth.small("fr", M, K, 8, x_dtype=dt, n_outlier=4, bos_factor=500.0)
+    X = dev(synth.make_inputs(w)["X"])
+    xq, sx = W.quantize_act_int4(X, b)
+    rq, rs = W.quantize_act_int4(W.hadamard_rotate(X, b), 0)
+    assert np.array_equal(host(sx), host(rs))
+    assert np.array_equal(host(xq), host(rq))
+
+
 # --------------------------------------------------------------------------
 # Integer GEMM
 # --------------------------------------------------------------------------
