@@ -531,10 +531,16 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       // quotient x~ / s is the same real number as y / (s / rs), with s / rs
       // exact too, and both round alike.  An x~ that would underflow gives a
       // quotient below 2^-26 in magnitude either way, that is code 0.
-      const bool fold = (__float_as_uint(a.rs) & 0x807FFFFFu) == 0u;
+      // The clamp to [-qmax, qmax] is needed only for a float16 scale below
+      // 2^-14: otherwise |x~| <= RN(max|y| rs) and s_eff is that maximum over
+      // qmax rounded to float32 or to a normal float16, so |q| <= qmax (1 + 2^-11),
+      // below qmax + 1/2, for every finite input.  (The clamped form keeps
+      // the multiply by rs.)
+      const bool clamp = a.scale_f16 && s_eff < 0x1p-14f;
+      const bool fold = !clamp && (__float_as_uint(a.rs) & 0x807FFFFFu) == 0u;
       const float sd = fold ? s_eff * __fdiv_rn(1.f, a.rs) : s_eff;
       const float rc = s_eff == 0.f ? 0.f : __frcp_rn(sd);
-      auto quantize = [&](auto folded) {
+      auto quantize = [&](auto folded, auto clamped) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float xt = decltype(folded)::value ? v[r] : v[r] * a.rs;
@@ -542,13 +548,17 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
           q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
           q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
           const float u = q + kMagic;
-          code[r] = __float_as_uint(__builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax));
+          code[r] = __float_as_uint(decltype(clamped)::value
+                                        ? __builtin_amdgcn_fmed3f(u, kMagic - a.fqmax, kMagic + a.fqmax)
+                                        : u);
         }
       };
-      if (fold)
-        quantize(std::true_type{});
+      if (clamp)
+        quantize(std::false_type{}, std::true_type{});
+      else if (fold)
+        quantize(std::true_type{}, std::false_type{});
       else
-        quantize(std::false_type{});
+        quantize(std::false_type{}, std::false_type{});
     } else {
 #pragma unroll
       for (int r = 0; r < R; ++r) {

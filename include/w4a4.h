@@ -161,6 +161,8 @@ int w4a4_hadamard_rotate(const void* x, int x_dtype, float* x_rot,
  *   xq       output codes in codes_layout ([M, K/2] packed, [M, K] int8 or
  *            tiled int8).
  *   x_scale  [M] float32 output, one scale per row.
+ *   The input must be finite: a row holding a NaN or an infinity gets
+ *   unspecified codes and scale.
  */
 int w4a4_quantize_act_int4(const void* x, int x_dtype, int64_t M, int64_t K,
                            int64_t had_block, uint8_t* xq, int codes_layout,

@@ -220,6 +220,23 @@ def test_quantize_weight_exact_on_oracle_rotation(N, K, g, sd):
     assert np.array_equal(host(wq), O.pack_int4(oq))
 
 
+@pytest.mark.parametrize("g", [0, 64])
+def test_quantize_weight_exact_float16_scales_normal_subnormal_zero(g):
+    # Row n is scaled by 2^-n, so the float16 scales run from normal through
+    # subnormal (where rounding the scale can push a quotient past 7.5 and
+    # the clamp decides the code) down to zero.
+    rng = np.random.default_rng(77 + g)
+    N, K = 48, 512
+    Wt = (0.5 * rng.standard_normal((N, K))).astype(np.float32)
+    Wt *= (2.0 ** -np.arange(N, dtype=np.float64))[:, None].astype(np.float32)
+    wq, ws = W.quantize_weight_int4(dev(Wt), 0, g, torch.float16)
+    oq, os_ = O.quantize_weight(Wt, g, "float16")
+    assert np.array_equal(host(ws), os_)
+    assert np.array_equal(host(wq), O.pack_int4(oq))
+    s = os_.astype(np.float32).reshape(-1)
+    assert np.any((s > 0) & (s < 2.0 ** -14)) and np.any(s == 0) and np.any(s >= 2.0 ** -14)
+
+
 @pytest.mark.parametrize("N,K,g,sd", [(64, 256, 0, "float32"), (100, 4096, 0, "float16"),
                                       (40, 14336, 128, "float16"), (8, 4096, 4096, "float32")])
 def test_quantize_weight_tiled_exact(N, K, g, sd):
