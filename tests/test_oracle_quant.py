@@ -94,6 +94,28 @@ def test_weight_codes_taken_against_stored_scale(scale_dtype):
         assert np.array_equal(q[n], np.clip(np.rint(quot), -7, 7).astype(np.int8))
 
 
+@pytest.mark.parametrize("scale_dtype", ["float16", "float32"])
+def test_clamp_only_acts_on_subnormal_float16_scales(scale_dtype):
+    # With s = RN(max|x| / 7) stored in float32 or as a normal float16, every
+    # quotient x / s rounds into [-7, 7] without the clamp; only a float16
+    # scale below 2^-14 can leave a quotient at or past 7.5.
+    rng = np.random.default_rng(21)
+    n = 400
+    w = rng.standard_normal((n, 64)) * rng.uniform(0.5, 2.0, (n, 1))
+    w = (w * 2.0 ** rng.integers(-40, 12, (n, 1))).astype(np.float32)
+    q, s = O.quantize_weight(w, 0, scale_dtype)
+    s32 = s.astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        raw = np.rint((w / s32[:, None]).astype(np.float32))
+    normal = s32 >= np.float32(2.0 ** -14) if scale_dtype == "float16" else s32 > 0
+    assert np.count_nonzero(normal) > 100
+    assert np.all(np.abs(raw[normal]) <= 7)
+    assert np.array_equal(q[normal], raw[normal].astype(np.int8))
+    if scale_dtype == "float16":
+        sub = (s32 > 0) & ~normal
+        assert np.any(np.abs(raw[sub]) > 7)  # the clamp does decide codes there
+
+
 def test_weight_groups_equal_per_segment_quantization():
     rng = np.random.default_rng(5)
     w = (0.02 * rng.standard_normal((6, 512))).astype(np.float32)
