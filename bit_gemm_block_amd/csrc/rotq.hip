@@ -13,7 +13,8 @@
 // values in registers.  The fast Walsh-Hadamard transform runs in three
 // passes, each on register-resident data with compile-time butterfly pairs:
 //   1. load pass: the row is read with coalesced 16-byte loads (V = 8 fp16 or
-//      4 fp32 elements per load); element bits [0, log2 V) are in registers;
+//      4 fp32 elements per load); element bits [0, log2 V) are in registers
+//      (fp16: bit 0 is transformed while widening, one v_fma_mix_f32 per value);
 //   2. column pass: after a trip through LDS a lane holds, for a few fixed
 //      columns of the [L][R] view of the segment, all values of the row
 //      bits the block spans; element bits [log2 R, log2 b) are transformed;
@@ -54,7 +55,10 @@
 // of x~ / s, the refined value is the correctly rounded quotient.  Quotients
 // of magnitude >= 1/4 keep every intermediate normal for 2^-100 <= s <= 2^100,
 // and smaller ones give code 0 whatever their last bits; scales outside that
-// range take the IEEE division.
+// range take the IEEE division.  The clamp is applied only where it can act,
+// under float16 scales below 2^-14; with a float32 or normal float16 scale
+// every rounded quotient already lies in [-qmax, qmax].  When rs is a power
+// of two the quotient is formed as y / (s / rs), the same real number.
 #include "w4a4_internal.h"
 #include "lowrank_rows.h"
 
