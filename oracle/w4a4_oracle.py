@@ -132,22 +132,6 @@ def rotate(x: np.ndarray, b: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Quantization (SERQ page, "Resumen técnico" §1-2)
 # ----------------------------------------------------------------------------
-def absmax_scale(v32: np.ndarray) -> np.float32:
-    """s = max|v| / 7 in float32 (IEEE division, round to nearest even)."""
-    a = np.float32(np.max(np.abs(v32))) if v32.size else np.float32(0.0)
-    return np.float32(a / np.float32(QMAX))
-
-
-def codes_against_scale(v32: np.ndarray, s32) -> np.ndarray:
-    """q = clamp(rint(v / s), -7, 7) with the quotient rounded to float32 and
-    rint rounding half to even.  A zero scale gives all-zero codes."""
-    s32 = np.float32(s32)
-    if s32 == 0:
-        return np.zeros(v32.shape, dtype=np.int8)
-    quot = (v32.astype(np.float32) / s32).astype(np.float32)
-    return np.clip(np.rint(quot), -QMAX, QMAX).astype(np.int8)
-
-
 def quantize_act(xrot32: np.ndarray, qmax: int = QMAX):
     """Per-token symmetric quantization of already-rotated float32
     activations: int4 (qmax 7) or, for W4A8 layers, int8 (qmax 127).
@@ -167,7 +151,9 @@ def _row_scales(v32: np.ndarray, qmax: int = QMAX) -> np.ndarray:
 
 
 def _codes_rows(v32: np.ndarray, s32: np.ndarray, qmax: int = QMAX) -> np.ndarray:
-    """codes_against_scale applied to every row with its own float32 scale."""
+    """q = clamp(rint(v / s), -qmax, qmax) for every row with its own float32
+    scale: the quotient rounded to float32 (IEEE division), rint rounding half
+    to even.  A zero scale gives all-zero codes."""
     s32 = np.asarray(s32, np.float32)
     safe = np.where(s32 == 0, np.float32(1), s32).astype(np.float32)
     quot = (v32 / safe[:, None]).astype(np.float32)

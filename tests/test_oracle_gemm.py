@@ -162,3 +162,68 @@ def test_rotation_reduces_error_on_outlier_inputs():
 
     assert rel_err(128) < 0.9 * rel_err(1)
     assert rel_err(1024) < 0.9 * rel_err(1)
+
+
+def literal_layer(qx, sx, qw, sw, group, X=None, A=None, B=None):
+    """The layer's output written out element by element from its definition
+    (SERQ page, "Resumen técnico" §2-3): for every output, the activation
+    scale times the sum over K-groups of the group's weight scale times the
+    group's integer dot product, plus the low-rank term sum_r (X A)[m,r] B[r,n];
+    float64 sums, rounded once to float32."""
+    M, K = qx.shape
+    N = qw.shape[0]
+    g = K if group == 0 else group
+    sw2 = np.asarray(sw, np.float64).reshape(N, -1)
+    y = np.zeros((M, N), np.float32)
+    for m in range(M):
+        t = None
+        if A is not None:
+            t = [sum(float(X[m, k]) * float(A[k, r]) for k in range(K)) for r in range(A.shape[1])]
+        for n in range(N):
+            acc = 0.0
+            for j in range(K // g):
+                dot = sum(int(qx[m, k]) * int(qw[n, k]) for k in range(j * g, (j + 1) * g))
+                acc += float(sx[m]) * float(sw2[n, j]) * dot
+            if t is not None:
+                acc += sum(t[r] * float(B[r, n]) for r in range(len(t)))
+            y[m, n] = np.float32(acc)
+    return y
+
+
+@pytest.mark.parametrize("g,rank", [(0, 0), (0, 4), (64, 0), (128, 4), (64, 4)])
+def test_qlinear_from_codes_matches_a_literal_loop(g, rank):
+    # Brute force on tiny shapes, with scales that differ from group to group
+    # so that a dropped group index, a single scale per row or a missing
+    # low-rank term cannot pass.
+    rng = np.random.default_rng(20 + g + rank)
+    M, N, K = 3, 5, 256
+    qx = rng.integers(-7, 8, (M, K)).astype(np.int8)
+    qw = rng.integers(-8, 8, (N, K)).astype(np.int8)
+    sx = rng.uniform(0.5, 2.0, M).astype(np.float32)
+    G = 1 if g == 0 else K // g
+    sw = rng.uniform(0.01, 0.05, (N, G)).astype(np.float16)
+    sw = sw[:, 0] if g == 0 else sw
+    X = A = B = None
+    if rank:
+        X = rng.standard_normal((M, K)).astype(np.float16)
+        A = (0.1 * rng.standard_normal((K, rank))).astype(np.float16)
+        B = (0.1 * rng.standard_normal((rank, N))).astype(np.float16)
+    got = O.qlinear_from_codes(qx, sx, O.pack_int4(qw), sw, g, X, A, B)
+    want = literal_layer(qx, sx, qw, sw, g, X, A, B)
+    # float64 sums in another order: equal up to the final rounding to float32
+    assert np.all(np.abs(got.astype(np.float64) - want) <= 2.0 ** -23 * np.abs(want))
+
+
+@pytest.mark.parametrize("b,g,rank,dt", [(64, 0, 0, "float32"), (128, 64, 8, "float16"),
+                                        (256, 128, 8, "float16"), (128, 128, 0, "float16"),
+                                        (256, 0, 16, "float16")])
+def test_qlinear_from_codes_on_the_oracle_codes_is_the_forward(b, g, rank, dt):
+    # Fed the oracle's own codes and scales, the epilogue the GPU results are
+    # judged by is the oracle's forward, bit for bit.
+    w = synth.small("fc", 9, 512, 40, x_dtype=dt, had_block=b, w_group=g, rank=rank,
+                    w_scale_dtype="float16" if dt == "float16" else "float32")
+    d = synth.make_inputs(w)
+    wq, ws, _ = O.prepare_weight(d["W"], b, g, w.w_scale_dtype)
+    _, sx, qx, _ = O.quantize_activation(d["X"], b)
+    got = O.qlinear_from_codes(qx, sx, wq, ws, g, d["X"], d["A"], d["B"])
+    assert np.array_equal(got, O.qlinear_forward(d["X"], wq, ws, b, g, d["A"], d["B"]))

@@ -98,3 +98,22 @@ def test_mxfp4_lossless_grid_gives_exact_product(b):
     assert np.array_equal(O.rotate64(X, b), xt)
     y = O.qlinear_forward_mxfp4(X, Wm, b)
     assert np.array_equal(y, (xt @ wt.T).astype(np.float32))
+
+
+def test_sign_of_zero_leaves_the_product_unchanged():
+    # A negative quotient that rounds to zero keeps its sign bit (code 8, an
+    # IEEE-style -0); -0 and +0 both have the value 0, so the product and the
+    # layer's output do not depend on which of the two encodings is chosen.
+    v = np.array([[-1e-9, 1e-9, -0.0, 0.0] + [6.0] * 28], np.float32)
+    codes, e = O.quantize_mxfp4(v)
+    assert codes[0, :4].tolist() == [8, 0, 8, 0]
+    rng = np.random.default_rng(6)
+    M, N, K = 4, 5, 128
+    cx = rng.integers(0, 16, (M, K)).astype(np.uint8)
+    cw = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    ex = rng.integers(-6, 6, (M, K // 32))
+    ew = rng.integers(-6, 6, (N, K // 32))
+    flip = lambda c: np.where((c & 7) == 0, c ^ 8, c).astype(np.uint8)   # +0 <-> -0
+    y = O.mxfp4_gemm(cx, ex, cw, ew)
+    assert np.array_equal(O.mxfp4_gemm(flip(cx), ex, cw, ew), y)
+    assert np.array_equal(O.mxfp4_gemm(cx, ex, flip(cw), ew), y)
