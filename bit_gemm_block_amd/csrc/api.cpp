@@ -112,13 +112,14 @@ void set_prefetch(w4a4::RotqExtras* ex, const uint8_t* wq, int64_t M, int64_t N,
   ex->pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
 }
 
+// Workspace of the layer: the activation codes (room for int8 codes of rows
+// padded to a multiple of 16), the scales and X.A.
 struct WsLayout {
   size_t xq, sx, t, total;
 };
 WsLayout ws_layout(int64_t M, int64_t K, int64_t rank) {
   WsLayout w;
   w.xq = 0;
-  // int8 codes, rows padded to a multiple of 16 for the tiled layout
   w.sx = align256(static_cast<size_t>((M + 15) / 16 * 16) * static_cast<size_t>(K));
   w.t = w.sx + align256(static_cast<size_t>(M) * 4);
   w.total = w.t + align256(static_cast<size_t>(M) * static_cast<size_t>(rank) * 4);
@@ -325,6 +326,30 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
   return ws_layout(M, K, rank).total;
 }
 
+int w4a4_qlinear_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int w_layout,
+                                  int64_t w_group, int act_bits, size_t* codes_offset,
+                                  int* codes_layout, size_t* scale_offset) {
+  if (M <= 0 || N <= 0 || K <= 0 || rank < 0 || w_group < 0 || !wlayout_ok_ob(w_layout) ||
+      (act_bits != 4 && act_bits != 8) || !codes_offset || !codes_layout || !scale_offset)
+    return W4A4_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(M, K, rank);
+  const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
+  const bool skinny = M <= 32 && (w_group == 0 || w_group % 128 == 0);
+  int lay;
+  if (act_bits == 8)
+    lay = tiled ? W4A4_CODES_I8_TILED : W4A4_CODES_I8;
+  else if (!tiled)
+    lay = W4A4_CODES_I8;
+  else if (w_layout == W4A4_WEIGHTS_TILED_OB && !skinny)
+    lay = W4A4_CODES_PACKED_TILED_OB;
+  else
+    lay = W4A4_CODES_PACKED_TILED;
+  *codes_offset = L.xq;
+  *codes_layout = lay;
+  *scale_offset = L.sx;
+  return W4A4_OK;
+}
+
 namespace {
 
 int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
@@ -510,7 +535,7 @@ int w4a4_qlinear_forward_mxfp4(const void* x, int x_dtype, const uint8_t* wq,
   if (ws_bytes < L.total) return W4A4_ERR_WORKSPACE;
   // Codes take half of the int8 code area, their scale tiles 1/16 of it.
   const size_t rows = static_cast<size_t>((M + 15) / 16 * 16);
-  const size_t xs_off = align256(rows * static_cast<size_t>(K / 2));
+  const size_t xs_off = L.xq + align256(rows * static_cast<size_t>(K / 2));
   if (xs_off + rows * static_cast<size_t>(K / 32) > L.sx) return W4A4_ERR_UNSUPPORTED;
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
@@ -796,7 +821,8 @@ int w4a4_qlinear_forward_asym(const void* x, int x_dtype, const uint8_t* wq, con
   // The packed codes take half of the int8 code area; the group scales and
   // zero points (M * K / had_block words each) fit in the other half.
   const int64_t G = K / had_block;
-  const size_t sx_off = align256(static_cast<size_t>((M + 15) / 16 * 16) * static_cast<size_t>(K / 2));
+  const size_t sx_off =
+      L.xq + align256(static_cast<size_t>((M + 15) / 16 * 16) * static_cast<size_t>(K / 2));
   const size_t zx_off = sx_off + align256(static_cast<size_t>(M * G) * 4);
   if (zx_off + static_cast<size_t>(M * G) * 4 > L.sx) return W4A4_ERR_UNSUPPORTED;
   int max_lds = 0;

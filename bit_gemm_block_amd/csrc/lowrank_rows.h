@@ -3,8 +3,8 @@
 // of the rotation kernel.  First factor of the single low-rank compensation
 // term of SERQ (SERQ page, "Resumen técnico" §2 item 2), on the unrotated X.
 //
-// The 256 threads of a workgroup read, at channel 8 (64 w + l) + 2048 c, the
-// 16 bytes of every row of X and of row j of At ([rank, K]), so that every
+// Needs exactly 256 threads (four waves).  They read, at channel
+// 8 (64 w + l) + 2048 c, the 16 bytes of every row of X and of row j of At ([rank, K]), so that every
 // load instruction is one contiguous 1 KB run, and accumulate x . a with fp16
 // pair dot products in float32.  Partial sums are reduced across lanes, then
 // across the four waves in a fixed order.  T is written as float32 [M, rank]

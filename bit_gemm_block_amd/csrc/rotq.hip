@@ -733,7 +733,10 @@ constexpr int64_t kWideRows = 64;  // at most this many rows use the wide menu
 template <typename TIn>
 hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(ka.nrot_blocks + ka.lr_rank + ka.pf_blocks));
-  const dim3 block(p.threads);
+  // The low-rank and read-ahead roles are written for 256 threads (their K
+  // and byte strides, and the four-wave reduction); the rotation blocks leave
+  // threads past the plan's count idle.
+  const dim3 block((ka.lr_rank > 0 || ka.pf_blocks > 0) ? 256 : p.threads);
 #define W4A4_ROTQ_CASE(LL, RR)                                                        \
   if (p.L == LL && p.R == RR) {                                                     \
     hipLaunchKernelGGL((rotq_kernel<TIn, LL, RR>), grid, block, p.lds_bytes, st, ka); \

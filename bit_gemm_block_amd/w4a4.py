@@ -47,6 +47,10 @@ _SIGS = {
     "w4a4_qgemm_w4a4": (_INT, [_P, _INT, _P, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _P, _P,
                                _P]),
     "w4a4_qlinear_workspace_size": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "w4a4_qlinear_workspace_layout": (_INT, [_I64, _I64, _I64, _I64, _INT, _I64, _INT,
+                                             ctypes.POINTER(ctypes.c_size_t),
+                                             ctypes.POINTER(_INT),
+                                             ctypes.POINTER(ctypes.c_size_t)]),
     "w4a4_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "w4a8_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
@@ -294,6 +298,26 @@ def qlinear_workspace_size(M: int, N: int, K: int, rank: int) -> int:
     return int(lib().w4a4_qlinear_workspace_size(M, N, K, rank))
 
 
+def qlinear_workspace(M: int, N: int, K: int, rank: int, device) -> torch.Tensor:
+    """A workspace for qlinear_forward calls up to these sizes (device memory,
+    contents unspecified)."""
+    return torch.empty((max(qlinear_workspace_size(M, N, K, rank), 1),), dtype=torch.uint8,
+                       device=device)
+
+
+def qlinear_workspace_layout(M: int, N: int, K: int, rank: int, w_layout: str = "rowmajor",
+                             w_group: int = 0, act_bits: int = 4) -> Tuple[int, str, int]:
+    """(codes byte offset, codes layout name, scales byte offset) of what
+    qlinear_forward leaves in its workspace for a call of these sizes."""
+    co, so = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    cl = _INT(0)
+    _check("qlinear_workspace_layout", lib().w4a4_qlinear_workspace_layout(
+        M, N, K, rank, _WLAYOUTS[w_layout], w_group, act_bits, ctypes.byref(co),
+        ctypes.byref(cl), ctypes.byref(so)))
+    name = {v: k for k, v in _LAYOUTS.items()}[cl.value]
+    return int(co.value), name, int(so.value)
+
+
 def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, had_block: int,
                     w_group: int, At: Optional[torch.Tensor] = None,
                     Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
@@ -325,9 +349,8 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
         _dev(Bt, "Bt")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = qlinear_workspace_size(M, N, K, rank)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        workspace = qlinear_workspace(M, N, K, rank, x.device)
     fwd = lib().w4a4_qlinear_forward if act_bits == 4 else lib().w4a8_qlinear_forward
     _check("qlinear_forward", fwd(
         _ptr(x), _dt(x), _ptr(wq), wl, _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
@@ -427,9 +450,8 @@ def qlinear_forward_asym(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tenso
         _dev(Bt, "Bt")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = qlinear_workspace_size(M, N, K, rank)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        workspace = qlinear_workspace(M, N, K, rank, x.device)
     _check("qlinear_forward_asym", lib().w4a4_qlinear_forward_asym(
         _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), _ptr(w_gsum), M, N, K,
         had_block, _ptr(At), _ptr(Bt), rank, _ptr(y), _ptr(workspace), workspace.numel(),
@@ -492,9 +514,8 @@ def qlinear_forward_residual(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.T
         raise ValueError("wq does not match w_scale, x and the residual rank")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = qlinear_workspace_size(M, N, K, 0)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        workspace = qlinear_workspace(M, N, K, 0, x.device)
     _check("qlinear_forward_residual", lib().w4a4_qlinear_forward_residual(
         _ptr(x), _dt(x), _ptr(wq), _ptr(w_scale), _dt(w_scale), res_rank, M, N, K, had_block,
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))
@@ -567,9 +588,8 @@ def qlinear_forward_mxfp4(x: torch.Tensor, wq: torch.Tensor, ws: torch.Tensor, N
         _dev(Bt, "Bt")
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=x.device)
-    need = qlinear_workspace_size(M, N, K, rank)
     if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+        workspace = qlinear_workspace(M, N, K, rank, x.device)
     _check("qlinear_forward_mxfp4", lib().w4a4_qlinear_forward_mxfp4(
         _ptr(x), _dt(x), _ptr(wq), _ptr(ws), M, N, K, had_block, _ptr(At), _ptr(Bt), rank,
         _ptr(y), _ptr(workspace), workspace.numel(), _stream(x)))

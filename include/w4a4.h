@@ -252,8 +252,24 @@ int w4a4_weights_tiled_to_ob(const uint8_t* wq, int64_t N, int64_t K, uint8_t* o
                              void* stream);
 
 /* Bytes of workspace qlinear_forward needs for these sizes (0 if M or N is
- * 0). */
+ * 0).  Calls that share one workspace must not overlap in time (the codes
+ * and scales live there). */
 size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank);
+
+/*
+ * Where w4a4_qlinear_forward (act_bits 4) or w4a8_qlinear_forward
+ * (act_bits 8) leaves the activation codes and scales in its workspace, for
+ * a call with the same M, N, K, rank, weight layout and w_group (for
+ * inspection and testing):
+ *   codes_offset  byte offset of the codes, stored in *codes_layout (a
+ *                 w4a4_codes_layout: the layout the GEMM reads);
+ *   scale_offset  byte offset of the float32 per-token scales [M].
+ * Returns W4A4_ERR_INVALID_ARG for sizes <= 0, a bad layout or act_bits, or
+ * a NULL output pointer.
+ */
+int w4a4_qlinear_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int w_layout,
+                                  int64_t w_group, int act_bits, size_t* codes_offset,
+                                  int* codes_layout, size_t* scale_offset);
 
 /*
  * The whole layer: rotate + quantize X, int4 GEMM, dequant, + X.A.B.

@@ -132,3 +132,23 @@ def split_ob(flat, rows, K):
     Rp = pad16(rows)
     nb = Rp * (K // 2)
     return flat[:nb].reshape(Rp, K // 2), flat[nb:nb + 4 * Rp].view(np.int32)[:rows]
+
+
+def workspace_codes(ws, off, M, K, layout):
+    """The activation codes a layer call left in its workspace (flat uint8
+    bytes, codes at byte offset `off`, stored in `layout`), rearranged row-major:
+    ("packed", [M, K/2] uint8 packed bytes) or ("i8", [M, K] int8 codes)."""
+    ws = np.asarray(ws, np.uint8)
+    Mp = pad16(M)
+    if layout in ("packed_tiled", "packed_tiled_ob"):
+        t = ws[off:off + Mp * (K // 2)].reshape(Mp, K // 2)
+        if layout == "packed_tiled_ob":
+            t = t ^ 0x08
+        return "packed", untile_weights(t, M)
+    if layout == "packed":
+        return "packed", ws[off:off + M * (K // 2)].reshape(M, K // 2)
+    if layout == "i8":
+        return "i8", codes_from_i8(ws[off:off + M * K].reshape(M, K))
+    if layout == "i8_tiled":
+        return "i8", codes_from_i8(untile_codes_i8(ws[off:off + Mp * K].reshape(Mp, K), M))
+    raise ValueError(layout)

@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -270,3 +270,27 @@ def test_valid_call_without_device_reports_unsupported(lib):
     assert lib.w4a4_quantize_act_int4(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P,
                                       None) == W.ERR_UNSUPPORTED
     assert lib.w4a4_weights_tiled_to_ob(P, 8, 256, P, None) == W.ERR_UNSUPPORTED
+
+
+def test_workspace_layout_query(lib):
+    # Host logic only: where the forward leaves its codes and scales (codes,
+    # then scales); the codes layout is the one the GEMM of that call reads.
+    M, N, K = 40, 96, 4096
+    size = W.qlinear_workspace_size(M, N, K, 16)
+    cases = {("rowmajor", 4): "i8", ("tiled", 4): "packed_tiled",
+             ("tiled_ob", 4): "packed_tiled_ob", ("tiled", 8): "i8_tiled",
+             ("rowmajor", 8): "i8"}
+    for (wl, bits), want in cases.items():
+        co, cl, so = W.qlinear_workspace_layout(M, N, K, 16, wl, 0, bits)
+        assert cl == want
+        assert co % 256 == 0
+        assert so >= co + W.pad16(M) * K and so + 4 * M <= size
+    # decode-sized calls on offset-binary weights read plain packed codes
+    assert W.qlinear_workspace_layout(8, N, K, 0, "tiled_ob", 0, 4)[1] == "packed_tiled"
+    import ctypes
+    c, i = ctypes.c_size_t(0), ctypes.c_int(0)
+    f = lib.w4a4_qlinear_workspace_layout
+    assert f(0, N, K, 0, 0, 0, 4, ctypes.byref(c), ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
+    assert f(M, N, K, 0, 7, 0, 4, ctypes.byref(c), ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
+    assert f(M, N, K, 0, 0, 0, 5, ctypes.byref(c), ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
+    assert f(M, N, K, 0, 0, 0, 4, None, ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG

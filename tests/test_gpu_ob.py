@@ -21,7 +21,8 @@ import torch
 from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
-from layouts import ob_codes, ob_weights, split_ob, tile_weights, untile_weights
+from layouts import ob_codes, ob_weights, split_ob, tile_weights, untile_weights, workspace_codes
+from bars import check_y
 
 pytestmark = pytest.mark.gpu
 
@@ -175,20 +176,28 @@ def run_layer_ob(w, rows=None):
     Bd = dev(B.T) if B is not None else None
     wt = tile_weights(wq)
     print("layer ob", w.name, w.M, w.K, w.N, w.had_block, w.rank, flush=True)
+    M = X.shape[0]
+    ws_buf = W.qlinear_workspace(M, N, K, w.rank, DEV)
     y = host(W.qlinear_forward(Xd, dev(ob_weights(wt, N, K)), wsd, w.had_block, 0, Ad, Bd,
-                               w_layout="tiled_ob"))
+                               workspace=ws_buf, w_layout="tiled_ob"))
     y_plain = host(W.qlinear_forward(Xd, dev(wt), wsd, w.had_block, 0, Ad, Bd, w_layout="tiled"))
-    gxq, gsx = W.quantize_act_int4(Xd, w.had_block)
-    gxq, gsx = host(gxq), host(gsx)
+    wsb = host(ws_buf)
+    co, cl, so = W.qlinear_workspace_layout(M, N, K, w.rank, "tiled_ob", 0)
+    assert cl == ("packed_tiled" if M <= 32 else "packed_tiled_ob")
+    _, packed = workspace_codes(wsb, co, M, K, cl)
+    gc = O.unpack_int4(packed).astype(np.int16)
+    gsx = wsb[so:so + 4 * M].view(np.float32)
+    if cl == "packed_tiled_ob":   # the row sums of the odd channels' codes follow the tiles
+        sums = wsb[co + W.pad16(M) * (K // 2):].view(np.int32)[:M]
+        assert np.array_equal(sums, gc[:, 1::2].sum(axis=1))
     _, ps, pc, _ = O.quantize_activation(X, w.had_block)
-    gc = O.unpack_int4(gxq).astype(np.int16)
     y_codes = O.qlinear_from_codes(gc, gsx, wq, ws, 0, X, A, B)
     y_oracle = O.qlinear_forward(X, wq, ws, w.had_block, 0, A, B)
     rms = float(np.sqrt(np.mean(y_oracle.astype(np.float64) ** 2)))
     diff = gc - pc
     assert np.all(np.abs(diff) <= 1) and np.count_nonzero(diff) <= 1e-4 * diff.size
     assert np.all(np.abs(gsx.astype(np.float64) - ps) <= 1e-6 * ps)
-    assert np.max(np.abs(y.astype(np.float64) - y_codes)) <= 1e-3 * rms
+    check_y(y, y_codes, y_oracle)
     assert np.array_equal(y, y_plain)
     return float(np.max(np.abs(y - y_oracle)) / rms)
 

@@ -20,6 +20,7 @@ import torch
 from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
+from bars import check_y
 from layouts import tile_weights, tile_weights_residual, untile_weights_residual
 
 pytestmark = pytest.mark.gpu
@@ -136,8 +137,7 @@ def run_residual_layer(w, r, sample_rows=None):
     y_codes = O.residual_from_codes(gc[rows], gs[rows], q, ws.astype(np.float32), qr)
     y_oracle = O.qlinear_forward_residual(X[rows], wq, ws, qr, b)
     rms = float(np.sqrt(np.mean(y_oracle.astype(np.float64) ** 2)))
-    err = float(np.max(np.abs(y[rows].astype(np.float64) - y_codes)))
-    assert err <= 1e-3 * rms, (err, rms)
+    check_y(y[rows], y_codes, y_oracle)
     return float(np.max(np.abs(y[rows] - y_oracle)) / rms)
 
 
