@@ -88,8 +88,7 @@ class Layer:
             self.sets.append(c)
             self.sets8.append((wq8.clone() if ob else c[0],) + c[1:])
         self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
-        need = W.qlinear_workspace_size(wl.M, wl.N, wl.K, wl.rank)
-        self.ws = torch.empty((need,), dtype=torch.uint8, device=dev)
+        self.ws = W.qlinear_workspace(wl.M, wl.N, wl.K, wl.rank, dev)
         torch.cuda.synchronize()
 
     def forward(self, i: int = 0, act_bits: int = 4):
@@ -142,8 +141,11 @@ def gemm_kernel_name(layer: "Layer") -> str:
     return "qgemm_pipe_kernel" + (" (offset-binary)" if layer.w_layout == "tiled_ob" else "")
 
 
-def time_graph(fn, steps: int, warmup: int) -> float:
-    """Seconds per step: `steps` calls of fn(i) captured in one HIP graph."""
+WARM_SECONDS = 0.25   # untimed replays before a timed one: clocks ramp up under load
+
+
+def capture(fn, steps: int, warmup: int) -> "torch.cuda.CUDAGraph":
+    """`steps` calls of fn(i) captured in one HIP graph after `warmup` eager calls."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -155,9 +157,27 @@ def time_graph(fn, steps: int, warmup: int) -> float:
             for i in range(steps):
                 fn(i)
     torch.cuda.synchronize()
-    for _ in range(3):              # untimed replays: first-launch costs, clocks settle
+    return g
+
+
+def warm(g, seconds: float = WARM_SECONDS) -> None:
+    """Replays g (untimed) for about `seconds` of wall time, at least three
+    times: first-launch costs, and the clocks rise from idle under load."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 3 or time.perf_counter() - t0 < seconds:
         g.replay()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def time_graph(fn, steps: int, warmup: int) -> float:
+    """Seconds per step: `steps` calls of fn(i) captured in one HIP graph,
+    timed as one replay after the warm replays."""
+    g = capture(fn, steps, warmup)
+    warm(g)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     cur = torch.cuda.current_stream()
@@ -168,22 +188,12 @@ def time_graph(fn, steps: int, warmup: int) -> float:
     return start.elapsed_time(end) / 1e3 / steps
 
 
-def replay_stats(fn, steps: int, warmup: int, reps: int = 7) -> dict:
-    """Spread of the per-step time over `reps` further replays of one graph of
-    `steps` calls (each replay timed alone with events): median, p10, p90."""
-    for i in range(warmup):
-        fn(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(g, stream=s):
-            for i in range(steps):
-                fn(i)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
+def replay_stats(fn, steps: int, warmup: int, reps: int = 15) -> dict:
+    """Spread of the per-step time over `reps` replays of one graph of
+    `steps` calls (each replay timed alone with events, after the warm
+    replays): median, p10, p90."""
+    g = capture(fn, steps, warmup)
+    warm(g)
     cur = torch.cuda.current_stream()
     t = []
     for _ in range(reps):
@@ -199,19 +209,46 @@ def replay_stats(fn, steps: int, warmup: int, reps: int = 7) -> dict:
             "p90_ms_per_step": float(q[2]), "replays": reps, "steps_per_replay": steps}
 
 
-def environment() -> dict:
-    """ROCm and device identification, and the clocks rocm-smi reports."""
+def read_clocks() -> list:
+    """The current clock lines rocm-smi reports (informational)."""
     import subprocess
-    prop = torch.cuda.get_device_properties(0)
-    env = {"rocm": torch.version.hip, "torch": torch.__version__, "device": prop.name,
-           "compute_units": prop.multi_processor_count,
-           "arch": getattr(prop, "gcnArchName", None)}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=15)
-        env["clocks"] = [l.strip() for l in r.stdout.splitlines() if "clk" in l.lower()][:8]
+        return [l.strip() for l in r.stdout.splitlines() if "clk" in l.lower()][:8]
     except Exception as e:  # pragma: no cover - informational only
-        env["clocks"] = f"unavailable: {type(e).__name__}"
-    return env
+        return [f"unavailable: {type(e).__name__}"]
+
+
+def clocks_under_load(fn, steps: int, warmup: int, seconds: float = 1.5) -> list:
+    """Clock readings taken while the GPU replays the graph of fn back to back
+    (the clocks of the timed work, not of the idle device): a second thread
+    samples rocm-smi while this one keeps the device busy."""
+    import threading
+    g = capture(fn, steps, warmup)
+    warm(g)
+    samples = []
+    th = threading.Thread(target=lambda: samples.append(read_clocks()))
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while th.is_alive() or time.perf_counter() - t0 < seconds:
+        g.replay()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+        if time.perf_counter() - t0 > 30:
+            break
+    torch.cuda.synchronize()
+    th.join()
+    return samples[0] if samples else []
+
+
+def environment() -> dict:
+    """ROCm and device identification, and the clocks rocm-smi reports at idle."""
+    prop = torch.cuda.get_device_properties(0)
+    return {"rocm": torch.version.hip, "torch": torch.__version__, "device": prop.name,
+            "compute_units": prop.multi_processor_count,
+            "arch": getattr(prop, "gcnArchName", None), "clocks_idle": read_clocks()}
 
 
 def prefill_shapes(steps: int, warmup: int) -> dict:
@@ -296,7 +333,7 @@ def decode_forms(wl: synth.Workload, copies: int, steps: int, warmup: int) -> di
     Bt = torch.from_numpy(d["B"].T.copy()).to(dev)
     M, N, K, r, b = wl.M, wl.N, wl.K, wl.rank, wl.had_block
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
-    wsb = torch.empty((W.qlinear_workspace_size(M, N, K, r),), dtype=torch.uint8, device=dev)
+    wsb = W.qlinear_workspace(M, N, K, r, dev)
     base = 2 * M * K + 4 * M * N
     lr = 2 * (K * r + r * N)
     out = {}
@@ -448,6 +485,7 @@ def main() -> int:
     # W4A8 layers (8-bit activations beside the 4-bit weights), same workload.
     t_step8 = time_graph(lambda i: pre.forward(i, act_bits=8), args.steps, args.warmup)
     pre_stats = replay_stats(pre.forward, args.steps, args.warmup)
+    clocks_load = clocks_under_load(pre.forward, args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
     rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M  # X in, packed codes + scales out
@@ -474,6 +512,10 @@ def main() -> int:
             "metric": "W4A4 qlinear HBM GB/s (M=8)", "value": gbs, "unit": "GB/s",
             "ms_per_step": t_dec * 1e3, "frac_of_hbm": gbs / PEAK_HBM_GBS,
             "spread": dec_stats,
+            "roofline": {"bound": "hbm", "scope": "whole call (every kernel of one step)",
+                         "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "bytes_per_step": dec.algorithmic_bytes(),
+                         "us_per_step": t_dec * 1e6},
             "bytes_per_step": dec.algorithmic_bytes(), "weight_copies": copies,
             "kernels_us": {k: v * 1e6 for k, v in kd.items()},
             "w4a8": {"value": dec.algorithmic_bytes() / t_dec8 / 1e9, "unit": "GB/s",
@@ -527,8 +569,7 @@ def main() -> int:
         wq, ws = W.quantize_weight_residual_int4(Wd, b, r, torch.float16)
         del Wd, d
         y = torch.empty((rw.M, rw.N), dtype=torch.float32, device=dev)
-        wsb = torch.empty((W.qlinear_workspace_size(rw.M, rw.N, rw.K, 0),), dtype=torch.uint8,
-                          device=dev)
+        wsb = W.qlinear_workspace(rw.M, rw.N, rw.K, 0, dev)
         log(f"serq: {rw.name} with an in-GEMM residual of {r} channels, timing {args.steps} steps")
         t_res = time_graph(lambda i: W.qlinear_forward_residual(x, wq, ws, r, b, y=y, workspace=wsb),
                            args.steps, args.warmup)
@@ -563,8 +604,7 @@ def main() -> int:
         wq, ws = W.quantize_mxfp4(Wd, mw.had_block, "packed_tiled")
         del Wd, d
         y = torch.empty((mw.M, mw.N), dtype=torch.float32, device=dev)
-        wsb = torch.empty((W.qlinear_workspace_size(mw.M, mw.N, mw.K, 0),), dtype=torch.uint8,
-                          device=dev)
+        wsb = W.qlinear_workspace(mw.M, mw.N, mw.K, 0, dev)
         log(f"mxfp4: {mw.name} timing {args.steps} steps")
         t_mx = time_graph(lambda i: W.qlinear_forward_mxfp4(x, wq, ws, mw.N, mw.had_block, y=y,
                                                             workspace=wsb),
@@ -632,7 +672,7 @@ def main() -> int:
         "mxfp4": mxfp4,
         "prefill_shapes": shapes,
         "cpu_baseline": cpu,
-        "environment": environment(),
+        "environment": {**environment(), "clocks_under_prefill_load": clocks_load},
     }
     print(json.dumps(out), flush=True)
     return 0
