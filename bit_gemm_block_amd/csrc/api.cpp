@@ -350,7 +350,11 @@ int w4a4_qlinear_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank,
   return W4A4_OK;
 }
 
-namespace {
+}  // extern "C"
+
+namespace w4a4 {
+
+int hip_status(hipError_t e) { return hip_fail(e); }
 
 int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
@@ -447,22 +451,24 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
   return e == hipSuccess ? W4A4_OK : hip_fail(e);
 }
 
-}  // namespace
+}  // namespace w4a4
+
+extern "C" {
 
 int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
                          int64_t had_block, int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
-  return qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
-                      w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 7);
+  return w4a4::qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
+                            w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 7);
 }
 
 int w4a8_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
                          int64_t had_block, int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream) {
-  return qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
-                      w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
+  return w4a4::qlinear_impl(x, x_dtype, wq, w_layout, w_scale, w_scale_dtype, M, N, K, had_block,
+                            w_group, At, Bt, rank, y, workspace, ws_bytes, stream, 127);
 }
 
 // ---- MXFP4 -----------------------------------------------------------------

@@ -127,6 +127,17 @@ struct GemmArgs {
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
 
+// ---- the layer (api.cpp) ----------------------------------------------------
+// w4a4_qlinear_forward (qmax 7) and w4a8_qlinear_forward (qmax 127) with the
+// given workspace: validation, planning and launches; returns a w4a4_status.
+int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+                 const void* w_scale, int w_scale_dtype, int64_t M, int64_t N, int64_t K,
+                 int64_t had_block, int64_t w_group, const void* At, const void* Bt,
+                 int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream,
+                 int qmax);
+// Records e as the HIP error behind a W4A4_ERR_HIP and returns that status.
+int hip_status(hipError_t e);
+
 // ---- weight group sums (offq.hip) ------------------------------------------
 // out[n, g] = sum of the signed weight codes of row n over K-group g
 // (group a multiple of 8 dividing K); wq row-major [N, K/2] or tiled.

@@ -55,6 +55,8 @@ _SIGS = {
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
     "w4a8_qlinear_forward": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64, _I64,
                                     _P, _P, _I64, _P, _P, ctypes.c_size_t, _P]),
+    "w4a4_qlinear_forward_noalloc": (_INT, [_P, _INT, _P, _INT, _P, _INT, _I64, _I64, _I64, _I64,
+                                            _I64, _P, _P, _I64, _P, _P]),
     "w4a4_quantize_act_asym_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _INT, _P, _P,
                                            _P]),
     "w4a4_quantize_weight_residual_int4": (_INT, [_P, _INT, _I64, _I64, _I64, _I64, _P, _P, _INT,
@@ -359,6 +361,36 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
 
 
 # ---- asymmetric group-wise activations -------------------------------------
+NOALLOC_SCRATCH_BYTES = 32 << 20   # W4A4_NOALLOC_SCRATCH_BYTES of include/w4a4.h
+
+
+def qlinear_forward_noalloc(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                            had_block: int, w_group: int, At: Optional[torch.Tensor] = None,
+                            Bt: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                            w_layout: str = "rowmajor") -> torch.Tensor:
+    """qlinear_forward with its scratch in the library's fixed per-device
+    array instead of a workspace (the C call allocates nothing; y is
+    allocated here when not given)."""
+    _dev(x, "x")
+    _dev(wq, "wq")
+    _dev(w_scale, "w_scale")
+    wl = _WLAYOUTS[w_layout]
+    M, K = x.shape
+    N = w_scale.shape[0]
+    rank = 0 if At is None else At.shape[0]
+    if rank:
+        if Bt is None or tuple(At.shape) != (rank, K) or tuple(Bt.shape) != (N, rank):
+            raise ValueError("At must be [rank, K] and Bt [N, rank]")
+        _dev(At, "At")
+        _dev(Bt, "Bt")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _check("qlinear_forward_noalloc", lib().w4a4_qlinear_forward_noalloc(
+        _ptr(x), _dt(x), _ptr(wq), wl, _ptr(w_scale), _dt(w_scale), M, N, K, had_block, w_group,
+        _ptr(At), _ptr(Bt), rank, _ptr(y), _stream(x)))
+    return y
+
+
 def quantize_act_asym_int4(x: torch.Tensor, had_block: int, group: Optional[int] = None,
                            layout: str = "packed", xq: Optional[torch.Tensor] = None,
                            sx: Optional[torch.Tensor] = None, zx: Optional[torch.Tensor] = None):

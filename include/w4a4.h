@@ -296,6 +296,26 @@ int w4a4_qlinear_forward(const void* x, int x_dtype, const uint8_t* wq,
                          size_t ws_bytes, void* stream);
 
 /*
+ * w4a4_qlinear_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The activation codes, scales and X.A
+ * live in a fixed array of W4A4_NOALLOC_SCRATCH_BYTES inside the library:
+ * each GPU the library runs on holds its own copy from module load until the
+ * process ends, and every call on that GPU uses it, so calls that overlap in
+ * time on one GPU race (serialise them, e.g. on one stream).  The call
+ * allocates nothing.
+ *   Arguments, layouts and results as w4a4_qlinear_forward.
+ *   Returns W4A4_ERR_WORKSPACE, with nothing enqueued, when
+ *   w4a4_qlinear_workspace_size(M, N, K, rank) exceeds
+ *   W4A4_NOALLOC_SCRATCH_BYTES (at rank 0: M * K up to about 32 Mi).
+ */
+#define W4A4_NOALLOC_SCRATCH_BYTES (32u << 20)
+int w4a4_qlinear_forward_noalloc(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
+                                 const void* w_scale, int w_scale_dtype, int64_t M, int64_t N,
+                                 int64_t K, int64_t had_block, int64_t w_group, const void* At,
+                                 const void* Bt, int64_t rank, float* y, void* stream);
+
+/*
  * The W4A8 layer (DynamicPTQ page, "Metodología" §2): w4a4_qlinear_forward
  * with 8-bit per-token activation codes (w4a4_quantize_act_int8's rule) on
  * the same 4-bit weights, GEMM and epilogue.  Arguments, layouts, workspace

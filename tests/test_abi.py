@@ -22,7 +22,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = W.header_functions()
-    assert len(names) == 24
+    assert len(names) == 25
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(W._SIGS)
@@ -294,3 +294,19 @@ def test_workspace_layout_query(lib):
     assert f(M, N, K, 0, 7, 0, 4, ctypes.byref(c), ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
     assert f(M, N, K, 0, 0, 0, 5, ctypes.byref(c), ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
     assert f(M, N, K, 0, 0, 0, 4, None, ctypes.byref(i), ctypes.byref(c)) == W.ERR_INVALID_ARG
+
+
+def test_noalloc_argument_errors(lib):
+    # Checked on the host before any device call: sizes beyond the library's
+    # scratch array, negative sizes, and the empty no-op.
+    f = lib.w4a4_qlinear_forward_noalloc
+    import re
+    with open(W.HEADER) as fh:
+        m = re.search(r"#define W4A4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", fh.read())
+    assert m and int(m.group(1)) << int(m.group(2)) == W.NOALLOC_SCRATCH_BYTES
+    big = (4096, 4096, 16384)          # 64 MiB of int8 codes room
+    assert W.qlinear_workspace_size(*big, 0) > W.NOALLOC_SCRATCH_BYTES
+    assert f(P, W.F16, P, 1, P, W.F16, *big, 128, 0, None, None, 0, P, None) == W.ERR_WORKSPACE
+    assert f(P, W.F16, P, 1, P, W.F16, -1, 16, 256, 256, 0, None, None, 0, P, None) == W.ERR_INVALID_ARG
+    assert f(P, W.F16, P, 1, P, W.F16, 16, 16, 256, 256, 0, None, None, -1, P, None) == W.ERR_INVALID_ARG
+    assert f(None, W.F16, None, 1, None, W.F16, 0, 16, 256, 256, 0, None, None, 0, None, None) == W.OK
