@@ -160,18 +160,18 @@ hipError_t launch_f16(const _Float16* x, const _Float16* at, int64_t M, int64_t 
   const int col_groups = (rank + NCB * 16 - 1) / (NCB * 16);
   const dim3 grid(static_cast<unsigned>(row_tiles), static_cast<unsigned>(col_groups));
   constexpr int PF = NCB >= 4 ? 2 : 8 / NCB;
-  if constexpr (NCB == 1) {
-    if (row_tiles < 64) {
-      // Few workgroups: sixteen waves each split K so that every wave has a
-      // short range whose loads are all in flight at once.
-      hipLaunchKernelGGL((lowrank_f16_kernel<1, 16, PF>), grid, dim3(1024), 0, st, x, at, M, K,
-                         rank, t, pair);
-      return hipGetLastError();
-    }
+  if constexpr (NCB <= 4) {
+    // Sixteen waves split K, so that every wave has a short range whose
+    // loads are all in flight at once (with four waves the 4096-row
+    // projection was a chain of eight dependent load batches per wave).
+    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 16, PF>), grid, dim3(1024), 0, st, x, at, M, K,
+                       rank, t, pair);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 4, PF>), grid, dim3(256), 0, st, x, at, M, K,
+                       rank, t, pair);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL((lowrank_f16_kernel<NCB, 4, PF>), grid, dim3(256), 0, st, x, at, M, K, rank,
-                     t, pair);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -1069,18 +1069,48 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     swr[j] = (GROUPED || !want_y || n >= a.N) ? 1.f : load_scale(a.sw, n, a.sw_f16);
   }
 
+  // fp16 low-rank term: the first 32 ranks of the wave's Bt rows are loaded
+  // before the stores, and the loop below runs row blocks outermost, loading
+  // each row block's T pair (hi, lo) once: TM dependent loads per wave in
+  // place of one chain per output block.  Further ranks go through
+  // add_lowrank; the instructions and their order are add_lowrank's, so the
+  // result is the same.
+  constexpr bool LRP = LRMODE == LR_F16;
+  const half8 lr_z = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int lr_koff = (lane >> 4) * 8;
+  const bool lr_kok = want_y && lr_koff < a.rank;
+  half8 lr_b[LRP ? TN : 1];
+  if constexpr (LRP) {
+    const _Float16* bt = static_cast<const _Float16*>(a.B);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t nr = n0 + wn0 + j * 16 + (lane & 15);
+      lr_b[j] = (lr_kok && nr < a.N) ? *reinterpret_cast<const half8*>(bt + nr * a.rank + lr_koff)
+                                     : lr_z;
+    }
+  }
+
   // The common case (interior tile, Y only) runs a copy of the store loop
   // with no per-store checks.
   auto emit = [&](auto fast) {
     constexpr bool FAST = decltype(fast)::value;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int64_t n = nlane + j * 16;
-    const bool n_ok = n < a.N;
-    const float swn = swr[j];
-    const int32_t sbn = OB ? 128 * static_cast<int32_t>(epl[2 * BM + wn0 + (lane & 15) + j * 16]) : 0;
+  for (int i = 0; i < TM; ++i) {
+    half8 lr_hi = lr_z, lr_lo = lr_z;
+    if constexpr (LRP) {
+      const int64_t mr = m0 + wm0 + i * 16 + (lane & 15);
+      if (lr_kok && mr < a.M) {
+        const _Float16* th = static_cast<const _Float16*>(a.t);
+        lr_hi = *reinterpret_cast<const half8*>(th + mr * a.rank + lr_koff);
+        lr_lo = *reinterpret_cast<const half8*>(th + (a.M + mr) * a.rank + lr_koff);
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    for (int j = 0; j < TN; ++j) {
+      const int64_t n = nlane + j * 16;
+      const bool n_ok = n < a.N;
+      const float swn = swr[j];
+      const int32_t sbn = OB ? 128 * static_cast<int32_t>(epl[2 * BM + wn0 + (lane & 15) + j * 16]) : 0;
       if constexpr (OB) {
         // exact: the accumulator less 128 (row sum + column sum) is 16 sum qx qw
 #pragma unroll
@@ -1099,7 +1129,14 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
         else
           yv[r] = static_cast<float>(acc[i][j][r]) * (sxr[i][r] * swn);
       }
-      if constexpr (LRMODE != LR_NONE) {
+      if constexpr (LRP) {
+        if (want_y) {
+          yv = __builtin_amdgcn_mfma_f32_16x16x32_f16(lr_lo, lr_b[j], yv, 0, 0, 0);
+          yv = __builtin_amdgcn_mfma_f32_16x16x32_f16(lr_hi, lr_b[j], yv, 0, 0, 0);
+          if (a.rank > 32)
+            yv = add_lowrank<LRMODE>(a, yv, m0 + wm0 + i * 16, n0 + wn0 + j * 16, lane, 32);
+        }
+      } else if constexpr (LRMODE != LR_NONE) {
         if (want_y)
           yv = add_lowrank<LRMODE>(a, yv, m0 + wm0 + i * 16, n0 + wn0 + j * 16, lane);
       }
