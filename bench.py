@@ -47,6 +47,7 @@ from bit_gemm_block_amd import w4a4 as W  # noqa: E402
 
 PEAK_INT8_TOPS = 5000.0   # MI355X dense int8 matrix peak, TOP/s
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 (MXFP4) matrix peak, TFLOP/s
+PEAK_FP6_TOPS = 10100.0    # MI355X dense FP6 matrix peak (the int4 codes as E2M3), TOP/s
 PEAK_HBM_GBS = 8000.0     # MI355X HBM3E, GB/s
 LLC_BYTES = 256 << 20     # MI355X Infinity Cache
 
@@ -70,14 +71,18 @@ class Layer:
         Wd = torch.from_numpy(d["W"]).to(dev)
         sdt = torch.float16 if wl.w_scale_dtype == "float16" else torch.float32
         ob = w_layout == "tiled_ob"
+        f6 = w_layout == "tiled_f6"
         wq, ws = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt,
                                         layout="tiled" if ob else w_layout)
-        del Wd
         # Offset-binary weights are converted from the tiled ones; the W4A8
-        # layer keeps the tiled form (the offset-binary form serves 4-bit codes).
+        # layer keeps the tiled form (the offset-binary and FP6 forms serve
+        # 4-bit codes).
         wq8 = wq
         if ob:
             wq = W.weights_tiled_to_ob(wq, wl.N)
+        if f6:
+            wq8, _ = W.quantize_weight_int4(Wd, wl.had_block, wl.w_group, sdt, layout="tiled")
+        del Wd
         # Distinct copies of the weights (and low-rank factors) so a decode
         # loop streams them from HBM rather than from the last-level cache.
         self.sets = [(wq, ws, self.A, self.B)]
@@ -86,7 +91,7 @@ class Layer:
             c = (wq.clone(), ws.clone(), self.A.clone() if self.A is not None else None,
                  self.B.clone() if self.B is not None else None)
             self.sets.append(c)
-            self.sets8.append((wq8.clone() if ob else c[0],) + c[1:])
+            self.sets8.append((wq8.clone() if (ob or f6) else c[0],) + c[1:])
         self.y = torch.empty((wl.M, wl.N), dtype=torch.float32, device=dev)
         self.ws = W.qlinear_workspace(wl.M, wl.N, wl.K, wl.rank, dev)
         torch.cuda.synchronize()
@@ -94,7 +99,7 @@ class Layer:
     def forward(self, i: int = 0, act_bits: int = 4):
         if act_bits == 8:
             wq, ws, A, B = self.sets8[i % len(self.sets8)]
-            wl = "tiled" if self.w_layout == "tiled_ob" else self.w_layout
+            wl = "tiled" if self.w_layout in ("tiled_ob", "tiled_f6") else self.w_layout
         else:
             wq, ws, A, B = self.sets[i % len(self.sets)]
             wl = self.w_layout
@@ -125,17 +130,27 @@ class Layer:
         return 2 * self.wl.M * self.wl.N * self.wl.K
 
 
-def gemm_bytes(wl: synth.Workload, ob: bool = False) -> int:
-    """Bytes the GEMM must move once: packed codes and scales of X, packed
-    weights and their scales, float32 Y (offset-binary operands: plus one
-    int32 sum per row of X and of the weights)."""
+def gemm_bytes(wl: synth.Workload, w_layout: str = "tiled") -> int:
+    """Bytes the GEMM must move once: the codes and scales of X, the weight
+    codes and their scales, float32 Y.  Codes take 4 bits (6 bits in the FP6
+    layouts); offset-binary operands add one int32 sum per row of X and of
+    the weights."""
     sb = 2 if wl.w_scale_dtype == "float16" else 4
     nsc = wl.N if wl.w_group == 0 else wl.N * (wl.K // wl.w_group)
-    sums = 4 * (wl.M + wl.N) if ob else 0
-    return wl.M * wl.K // 2 + 4 * wl.M + wl.N * wl.K // 2 + nsc * sb + 4 * wl.M * wl.N + sums
+    sums = 4 * (wl.M + wl.N) if w_layout == "tiled_ob" else 0
+    cb = 3 / 4 if w_layout == "tiled_f6" else 1 / 2   # bytes per code
+    return int(cb * wl.M * wl.K) + 4 * wl.M + int(cb * wl.N * wl.K) + nsc * sb + \
+        4 * wl.M * wl.N + sums
+
+
+def gemm_peak(w_layout: str) -> float:
+    """Dense peak of the matrix instruction the GEMM runs on, TOP/s."""
+    return PEAK_FP6_TOPS if w_layout == "tiled_f6" else PEAK_INT8_TOPS
 
 
 def gemm_kernel_name(layer: "Layer") -> str:
+    if layer.w_layout == "tiled_f6":
+        return "qgemm_f6_kernel (FP6 E2M3 operands)"
     if layer.wl.M <= 32:
         return "qgemm_skinny_kernel"
     return "qgemm_pipe_kernel" + (" (offset-binary)" if layer.w_layout == "tiled_ob" else "")
@@ -251,16 +266,18 @@ def environment() -> dict:
             "arch": getattr(prop, "gcnArchName", None), "clocks_idle": read_clocks()}
 
 
-def prefill_shapes(steps: int, warmup: int) -> dict:
+def prefill_shapes(steps: int, warmup: int, w_layout: str) -> dict:
     """qlinear_forward TOP/s on the other prefill shapes: the grouped
     down-projection and the Llama-3-8B decoder linears (4096 tokens)."""
     out = {}
     for wl in [synth.DOWN_PROJ] + synth.LLAMA3_8B:
-        # offset-binary weights serve per-channel scales; grouped ones stay tiled
-        layer = Layer(wl, w_layout="tiled_ob" if wl.w_group == 0 else "tiled")
+        # FP6 weights serve every shape; else offset-binary weights serve
+        # per-channel scales and grouped ones stay tiled
+        lay = w_layout if w_layout == "tiled_f6" else "tiled_ob" if wl.w_group == 0 else "tiled"
+        layer = Layer(wl, w_layout=lay)
         t = time_graph(layer.forward, steps, warmup)
         tops = layer.ops() / t / 1e12
-        out[wl.name] = {"TOP/s": tops, "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
+        out[wl.name] = {"TOP/s": tops, "frac_of_matrix_peak": tops / gemm_peak(lay),
                         "ms_per_step": t * 1e3, "had_block": wl.had_block,
                         "w_group": wl.w_group, "rank": wl.rank, "w_layout": layer.w_layout}
         log(f"shape {wl.name}: {t * 1e6:.1f} us/step, {tops:.0f} TOP/s")
@@ -269,19 +286,21 @@ def prefill_shapes(steps: int, warmup: int) -> dict:
     return out
 
 
-def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
-    """Average duration of each kernel of the path, launched alone with the
-    same arguments and code layout as inside qlinear_forward: `steps`
-    launches replayed from one HIP graph, timed with events on the stream
-    they run on."""
+def kernel_launches(layer: Layer) -> dict:
+    """The kernels of the path as separate launches with the same arguments
+    and code layout as inside qlinear_forward (rotation + quantization into
+    the GEMM's code layout, then the GEMM)."""
     wl = layer.wl
     tiled = layer.w_layout in ("tiled", "tiled_ob")
-    # the code layout qlinear_forward hands the GEMM: packed tiles with tiled
-    # weights (offset-binary ones above 32 rows with offset-binary weights),
-    # int8 rows otherwise
+    # the code layout qlinear_forward hands the GEMM: FP6 tiles with FP6
+    # weights, packed tiles with tiled weights (offset-binary ones above 32
+    # rows with offset-binary weights), int8 rows otherwise
     ob = layer.w_layout == "tiled_ob" and wl.M > 32
-    lay = "packed_tiled_ob" if ob else "packed_tiled" if tiled else "i8"
-    if ob:
+    f6 = layer.w_layout == "tiled_f6"
+    lay = "f6_tiled" if f6 else "packed_tiled_ob" if ob else "packed_tiled" if tiled else "i8"
+    if f6:
+        xq = torch.empty((W.pad16(wl.M), 3 * wl.K // 4), dtype=torch.uint8, device="cuda:0")
+    elif ob:
         xq = torch.empty((W.ob_bytes(wl.M, wl.K),), dtype=torch.uint8, device="cuda:0")
     else:
         xq = torch.empty((W.pad16(wl.M) if tiled else wl.M, wl.K // 2 if tiled else wl.K),
@@ -289,15 +308,20 @@ def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
     sx = torch.empty((wl.M,), dtype=torch.float32, device="cuda:0")
     W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay)
     torch.cuda.synchronize()
-    out = {}
-    out["rotq"] = time_graph(
-        lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay), steps, warmup)
-    out["qgemm"] = time_graph(
-        lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
-                               layer.sets[i % len(layer.sets)][1], wl.w_group, y=layer.y,
-                               layout=lay, w_layout=layer.w_layout, M=wl.M, N=wl.N),
-        steps, warmup)
-    return out
+    return {
+        "rotq": lambda i: W.quantize_act_int4(layer.x, wl.had_block, xq, sx, layout=lay),
+        "qgemm": lambda i: W.qgemm_w4a4(xq, sx, layer.sets[i % len(layer.sets)][0],
+                                        layer.sets[i % len(layer.sets)][1], wl.w_group,
+                                        y=layer.y, layout=lay, w_layout=layer.w_layout,
+                                        M=wl.M, N=wl.N),
+    }
+
+
+def kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
+    """Average duration of each kernel of the path, launched alone:
+    `steps` launches replayed from one HIP graph, timed with events on the
+    stream they run on."""
+    return {k: time_graph(f, steps, warmup) for k, f in kernel_launches(layer).items()}
 
 
 def asym_kernel_times(layer: Layer, steps: int, warmup: int) -> dict:
@@ -368,7 +392,7 @@ def decode_forms(wl: synth.Workload, copies: int, steps: int, warmup: int) -> di
 CALIB_BYTES = 256 << 20   # the calibration copy reads and writes this much
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qgemm_prefill_traffic.txt")
 GEMM_SOURCES = [os.path.join(ROOT, "bit_gemm_block_amd", "csrc", f)
-                for f in ("qgemm.hip", "w4a4_internal.h")]
+                for f in ("qgemm.hip", "qgemm_f6.hip", "gemm_common.h", "w4a4_internal.h")]
 
 
 def gemm_source_hash() -> str:
@@ -380,23 +404,39 @@ def gemm_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def profile_kernels(steps: int, w_layout: str) -> None:
-    """Launch the prefill kernels alone (for hardware counters): rotate +
-    quantize and the GEMM `steps` times each, then a plain elementwise copy
-    of CALIB_BYTES, whose counter readings calibrate the byte counters."""
+def profile_kernels(steps: int, w_layout: str, decode_w_layout: str) -> None:
+    """Launch the kernels alone, eagerly, for hardware counters: the prefill
+    rotation + quantization and GEMM `steps` times each; the decode layer
+    (rotation launch with the low-rank and read-ahead roles, then the skinny
+    GEMM) `steps` times over weight copies that exceed the last-level cache;
+    then a plain elementwise copy of CALIB_BYTES, whose counter readings
+    calibrate the byte counters."""
     pre = Layer(synth.PREFILL, w_layout=w_layout)
-    kernel_times(pre, steps, 2)
+    for name, f in kernel_launches(pre).items():
+        for i in range(steps):
+            f(i)
+        torch.cuda.synchronize()
+    del pre
+    probe = synth.DECODE
+    per_set = probe.N * probe.K // 2 + probe.N * 2 + 2 * (probe.K + probe.N) * probe.rank * 2
+    dec = Layer(probe, copies=int(np.ceil(3 * LLC_BYTES / per_set)), w_layout=decode_w_layout)
+    for i in range(steps):
+        dec.forward(i)
+    torch.cuda.synchronize()
+    del dec
     src = torch.ones(CALIB_BYTES // 4, dtype=torch.int32, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(5):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    log(f"profiled {steps} launches of each prefill kernel and 5 copies of {CALIB_BYTES} bytes")
+    log(f"profiled {steps} launches of each prefill kernel, {steps} decode layers and 5 "
+        f"copies of {CALIB_BYTES} bytes")
 
 
-def read_traffic(algorithmic: float) -> dict | None:
+def read_traffic(algorithmic: float, w_layout: str) -> dict | None:
     """HBM bytes per GEMM launch from the committed counter summary, or None
-    when the summary is missing or the GEMM source changed since it was made."""
+    when the summary is missing, was taken on another weight layout, or the
+    GEMM source changed since it was made."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -405,7 +445,7 @@ def read_traffic(algorithmic: float) -> dict | None:
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("gemm_source_sha256_16") != gemm_source_hash():
+    if kv.get("gemm_source_sha256_16") != gemm_source_hash() or kv.get("w_layout") != w_layout:
         return None
     try:
         fetch = float(kv["gemm_fetch_bytes_per_launch"])
@@ -454,7 +494,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--w-layout", choices=["tiled_ob", "tiled", "rowmajor"], default="tiled_ob")
+    ap.add_argument("--w-layout", choices=["tiled_f6", "tiled_ob", "tiled", "rowmajor"],
+                    default="tiled_f6", help="weight layout of the prefill workloads")
+    ap.add_argument("--decode-w-layout", choices=["tiled_ob", "tiled", "rowmajor", "tiled_f6"],
+                    default="tiled_ob", help="weight layout of the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-offq", action="store_true")
@@ -473,12 +516,11 @@ def main() -> int:
         return 2
     W.lib()
     if args.profile_kernels:
-        profile_kernels(args.steps, args.w_layout)
+        profile_kernels(args.steps, args.w_layout, args.decode_w_layout)
         return 0
 
     # ---- prefill: the headline ------------------------------------------------
     pre = Layer(synth.PREFILL, w_layout=args.w_layout)
-    ob_pre = args.w_layout == "tiled_ob"
     log(f"prefill: {pre.wl.name} ({args.w_layout} weights) timing {args.steps} steps")
     t_step = time_graph(pre.forward, args.steps, args.warmup)
     kt = kernel_times(pre, args.steps, args.warmup)
@@ -488,7 +530,9 @@ def main() -> int:
     clocks_load = clocks_under_load(pre.forward, args.steps, args.warmup)
     tops = pre.ops() / t_step / 1e12
     gemm_tops = pre.ops() / kt["qgemm"] / 1e12
-    rot_bytes = pre.wl.M * pre.wl.K * 2 + pre.wl.M * pre.wl.K // 2 + 4 * pre.wl.M  # X in, packed codes + scales out
+    peak = gemm_peak(args.w_layout)
+    code_bytes = pre.wl.M * pre.wl.K * 3 // 4 if args.w_layout == "tiled_f6" else pre.wl.M * pre.wl.K // 2
+    rot_bytes = pre.wl.M * pre.wl.K * 2 + code_bytes + 4 * pre.wl.M  # X in, codes + scales out
     log(f"prefill: {t_step * 1e6:.2f} us/step, {tops:.1f} TOP/s; qgemm {kt['qgemm'] * 1e6:.2f} us "
         f"({gemm_tops:.1f} TOP/s), rotq {kt['rotq'] * 1e6:.2f} us "
         f"({rot_bytes / kt['rotq'] / 1e9:.0f} GB/s)")
@@ -499,7 +543,7 @@ def main() -> int:
         probe = synth.DECODE
         per_set = probe.N * probe.K // 2 + probe.N * 2 + 2 * (probe.K + probe.N) * probe.rank * 2
         copies = int(np.ceil(3 * LLC_BYTES / per_set))
-        dec = Layer(probe, copies=copies, w_layout=args.w_layout)
+        dec = Layer(probe, copies=copies, w_layout=args.decode_w_layout)
         log(f"decode: {dec.wl.name} with {copies} weight copies, timing {args.steps} steps")
         t_dec = time_graph(dec.forward, args.steps, args.warmup)
         dec_stats = replay_stats(dec.forward, args.steps, args.warmup)
@@ -631,7 +675,8 @@ def main() -> int:
         }
         del x, wq, ws, y, wsb, xq, xs
 
-    shapes = None if args.no_shapes else prefill_shapes(min(args.steps, 50), args.warmup)
+    shapes = None if args.no_shapes else prefill_shapes(min(args.steps, 50), args.warmup,
+                                                        args.w_layout)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -654,13 +699,16 @@ def main() -> int:
         "config": {"workload": pre.wl.name, "M": pre.wl.M, "N": pre.wl.N, "K": pre.wl.K,
                    "had_block": pre.wl.had_block, "w_group": pre.wl.w_group,
                    "rank": pre.wl.rank, "x_dtype": pre.wl.x_dtype,
-                   "w_layout": args.w_layout},
-        "frac_of_int8_peak": tops / PEAK_INT8_TOPS,
+                   "w_layout": args.w_layout,
+                   "matrix_operands": ("int4 codes as FP6 E2M3, float32 sums (exact integers)"
+                                       if args.w_layout == "tiled_f6"
+                                       else "int4 codes widened to int8, int32 sums")},
+        "frac_of_matrix_peak": tops / peak,
         "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(pre), "achieved": gemm_tops,
-                     "peak": PEAK_INT8_TOPS, "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
+                     "peak": peak, "unit": "TOP/s", "frac": gemm_tops / peak,
                      "ops_per_launch": pre.ops(), "us_per_launch": kt["qgemm"] * 1e6,
-                     "algorithmic_bytes_per_launch": gemm_bytes(pre.wl, ob_pre),
-                     "traffic": read_traffic(gemm_bytes(pre.wl, ob_pre))},
+                     "algorithmic_bytes_per_launch": gemm_bytes(pre.wl, args.w_layout),
+                     "traffic": read_traffic(gemm_bytes(pre.wl, args.w_layout), args.w_layout)},
         "spread": pre_stats,
         "kernels_us": {k: v * 1e6 for k, v in kt.items()},
         "rotq_gbs": rot_bytes / kt["rotq"] / 1e9,

@@ -82,9 +82,12 @@ int check_group(int64_t K, int64_t g, bool pow2_only) {
 }
 
 int plan_rotq(int64_t M, int64_t K, int64_t had_block, int64_t gsz, int max_lds,
-              w4a4::RotqPlan* p) {
+              w4a4::RotqPlan* p, bool f6 = false) {
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  return w4a4::rotq_plan(M, K, log2b, gsz, max_lds, p) ? W4A4_OK : W4A4_ERR_UNSUPPORTED;
+  // FP6 tiles pack 32 consecutive codes per instruction lane: at least 16
+  // elements per lane, two lanes per chunk.
+  return w4a4::rotq_plan(M, K, log2b, gsz, max_lds, p, f6 ? 16 : 8) ? W4A4_OK
+                                                                    : W4A4_ERR_UNSUPPORTED;
 }
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
@@ -137,6 +140,9 @@ bool wlayout_ok(int l) { return l == W4A4_WEIGHTS_ROWMAJOR || l == W4A4_WEIGHTS_
 // Entry points that also take the offset-binary layouts check with these.
 bool layout_ok_ob(int l) { return layout_ok(l) || l == W4A4_CODES_PACKED_TILED_OB; }
 bool wlayout_ok_ob(int l) { return wlayout_ok(l) || l == W4A4_WEIGHTS_TILED_OB; }
+// ... and these the FP6 tiled layouts as well.
+bool layout_ok_f6(int l) { return layout_ok_ob(l) || l == W4A4_CODES_F6_TILED; }
+bool wlayout_ok_f6(int l) { return wlayout_ok_ob(l) || l == W4A4_WEIGHTS_TILED_F6; }
 // Offset-binary buffers: the row sums follow the ceil(rows/16)*16 tiled rows.
 const int32_t* ob_sums(const uint8_t* q, int64_t rows, int64_t K) {
   return reinterpret_cast<const int32_t*>(q + (rows + 15) / 16 * 16 * (K / 2));
@@ -184,21 +190,23 @@ namespace {
 
 int quantize_act_impl(const void* x, int x_dtype, int64_t M, int64_t K, int64_t had_block,
                       uint8_t* xq, int codes_layout, float* x_scale, void* stream, int qmax) {
-  if (!dtype_ok(x_dtype) || !layout_ok_ob(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
+  if (!dtype_ok(x_dtype) || !layout_ok_f6(codes_layout) || M < 0) return W4A4_ERR_INVALID_ARG;
   if (qmax != 7 && !codes_i8(codes_layout)) return W4A4_ERR_INVALID_ARG;  // 8-bit codes
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   const bool ob = codes_layout == W4A4_CODES_PACKED_TILED_OB;
-  if ((codes_tiled(codes_layout) || ob) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  const bool f6 = codes_layout == W4A4_CODES_F6_TILED;
+  if ((codes_tiled(codes_layout) || ob || f6) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if (M == 0) return W4A4_OK;
   if (!x || !xq || !x_scale) return W4A4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(xq) || !aligned16(x_scale)) return W4A4_ERR_MISALIGNED;
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan, f6)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  const int mode = codes_layout == W4A4_CODES_I8              ? w4a4::ROTQ_QUANT_I8
+  const int mode = f6                                         ? w4a4::ROTQ_QUANT_F6
+                   : codes_layout == W4A4_CODES_I8              ? w4a4::ROTQ_QUANT_I8
                    : codes_layout == W4A4_CODES_I8_TILED     ? w4a4::ROTQ_QUANT_I8_TILED
                    : codes_layout == W4A4_CODES_PACKED_TILED ? w4a4::ROTQ_QUANT_TILED
                    : ob                                      ? w4a4::ROTQ_QUANT_TILED
@@ -226,11 +234,12 @@ int w4a4_quantize_act_int8(const void* x, int x_dtype, int64_t M, int64_t K, int
 int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, int64_t had_block,
                               int64_t w_group, uint8_t* wq, int w_layout, void* w_scale,
                               int scale_dtype, void* stream) {
-  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || !wlayout_ok(w_layout) || N < 0)
+  const bool f6 = w_layout == W4A4_WEIGHTS_TILED_F6;
+  if (!dtype_ok(w_dtype) || !dtype_ok(scale_dtype) || !(wlayout_ok(w_layout) || f6) || N < 0)
     return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
-  if (w_layout == W4A4_WEIGHTS_TILED && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+  if ((w_layout == W4A4_WEIGHTS_TILED || f6) && K % 128 != 0) return W4A4_ERR_UNSUPPORTED;
   if ((s = check_group(K, w_group, true)) != W4A4_OK) return s;
   if (N == 0) return W4A4_OK;
   if (!w || !wq || !w_scale) return W4A4_ERR_INVALID_ARG;
@@ -239,9 +248,10 @@ int w4a4_quantize_weight_int4(const void* w, int w_dtype, int64_t N, int64_t K, 
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   const int64_t gsz = w_group == 0 ? K : w_group;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(N, K, had_block, gsz, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(N, K, had_block, gsz, max_lds, &plan, f6)) != W4A4_OK) return s;
   const int log2b = had_block > 1 ? ilog2(had_block) : 0;
-  const int mode = w_layout == W4A4_WEIGHTS_TILED ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT;
+  const int mode = f6 ? w4a4::ROTQ_QUANT_F6
+                   : w_layout == W4A4_WEIGHTS_TILED ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT;
   hipError_t e = w4a4::launch_rotq(w, w_dtype == W4A4_F16, N, K, log2b, mode, gsz,
                                    scale_dtype == W4A4_F16, nullptr, wq, w_scale, plan,
                                    static_cast<hipStream_t>(stream));
@@ -266,12 +276,36 @@ int w4a4_lowrank_project(const void* x, int x_dtype, const void* At, int64_t M, 
 int w4a4_qgemm_w4a4(const uint8_t* xq, int codes_layout, const float* x_scale, const uint8_t* wq,
                     int w_layout, const void* w_scale, int w_scale_dtype, int64_t w_group,
                     int64_t M, int64_t N, int64_t K, float* y, int32_t* acc, void* stream) {
-  if (!dtype_ok(w_scale_dtype) || !layout_ok_ob(codes_layout) || !wlayout_ok_ob(w_layout) ||
+  if (!dtype_ok(w_scale_dtype) || !layout_ok_f6(codes_layout) || !wlayout_ok_f6(w_layout) ||
       M < 0 || N < 0 || K <= 0)
     return W4A4_ERR_INVALID_ARG;
   if (K % 64 != 0 || K > kMaxK) return W4A4_ERR_UNSUPPORTED;
   int s = check_group(K, w_group, false);
   if (s != W4A4_OK) return s;
+  // FP6 tiled codes go with FP6 tiled weights only
+  const bool f6 = w_layout == W4A4_WEIGHTS_TILED_F6;
+  if (f6 != (codes_layout == W4A4_CODES_F6_TILED)) return W4A4_ERR_INVALID_ARG;
+  if (f6) {
+    if (K % 128 != 0 || w_group % 128 != 0) return W4A4_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0) return W4A4_OK;
+    if (!xq || !wq || (!y && !acc)) return W4A4_ERR_INVALID_ARG;
+    if (y && (!x_scale || !w_scale)) return W4A4_ERR_INVALID_ARG;
+    if (!aligned16(xq) || !aligned16(wq) || (x_scale && !aligned16(x_scale)) ||
+        (w_scale && !aligned16(w_scale)) || (y && !aligned16(y)) || (acc && !aligned16(acc)))
+      return W4A4_ERR_MISALIGNED;
+    if ((s = device_check(nullptr)) != W4A4_OK) return s;
+    w4a4::GemmArgs g{};
+    g.xq = xq; g.sx = x_scale; g.wq = wq; g.sw = w_scale;
+    g.sw_f16 = w_scale_dtype == W4A4_F16;
+    g.group = static_cast<int>(w_group);
+    g.M = M; g.N = N; g.K = K;
+    g.y = y; g.acc = acc;
+    g.lr_mode = w4a4::LR_NONE;
+    g.tiled = 1;
+    g.f6 = 1;
+    hipError_t e = w4a4::launch_qgemm(g, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? W4A4_OK : hip_fail(e);
+  }
   const bool w_ob = w_layout == W4A4_WEIGHTS_TILED_OB;
   const bool a_ob = codes_layout == W4A4_CODES_PACKED_TILED_OB;
   const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
@@ -329,14 +363,17 @@ size_t w4a4_qlinear_workspace_size(int64_t M, int64_t N, int64_t K, int64_t rank
 int w4a4_qlinear_workspace_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int w_layout,
                                   int64_t w_group, int act_bits, size_t* codes_offset,
                                   int* codes_layout, size_t* scale_offset) {
-  if (M <= 0 || N <= 0 || K <= 0 || rank < 0 || w_group < 0 || !wlayout_ok_ob(w_layout) ||
+  if (M <= 0 || N <= 0 || K <= 0 || rank < 0 || w_group < 0 || !wlayout_ok_f6(w_layout) ||
       (act_bits != 4 && act_bits != 8) || !codes_offset || !codes_layout || !scale_offset)
     return W4A4_ERR_INVALID_ARG;
+  if (w_layout == W4A4_WEIGHTS_TILED_F6 && act_bits != 4) return W4A4_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(M, K, rank);
   const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
   const bool skinny = M <= 32 && (w_group == 0 || w_group % 128 == 0);
   int lay;
-  if (act_bits == 8)
+  if (w_layout == W4A4_WEIGHTS_TILED_F6)
+    lay = W4A4_CODES_F6_TILED;
+  else if (act_bits == 8)
     lay = tiled ? W4A4_CODES_I8_TILED : W4A4_CODES_I8;
   else if (!tiled)
     lay = W4A4_CODES_I8;
@@ -361,12 +398,14 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
                          int64_t had_block, int64_t w_group, const void* At, const void* Bt,
                          int64_t rank, float* y, void* workspace, size_t ws_bytes, void* stream,
                   int qmax) {
-  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok_ob(w_layout) || M < 0 ||
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_scale_dtype) || !wlayout_ok_f6(w_layout) || M < 0 ||
       N < 0 || rank < 0)
     return W4A4_ERR_INVALID_ARG;
   int s = check_k_had(K, had_block, false);
   if (s != W4A4_OK) return s;
   if ((s = check_group(K, w_group, false)) != W4A4_OK) return s;
+  const bool w_f6 = w_layout == W4A4_WEIGHTS_TILED_F6;
+  if (w_f6 && qmax != 7) return W4A4_ERR_UNSUPPORTED;  // FP6 tiles hold 4-bit codes
   const bool w_ob = w_layout == W4A4_WEIGHTS_TILED_OB;
   if (w_ob && (w_group != 0 || qmax != 7)) return W4A4_ERR_UNSUPPORTED;
   const bool tiled = w_layout != W4A4_WEIGHTS_ROWMAJOR;
@@ -383,7 +422,7 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
   int max_lds = 0;
   if ((s = device_check(&max_lds)) != W4A4_OK) return s;
   w4a4::RotqPlan plan;
-  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan)) != W4A4_OK) return s;
+  if ((s = plan_rotq(M, K, had_block, K, max_lds, &plan, w_f6)) != W4A4_OK) return s;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -406,7 +445,7 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
     ex.lr_rank = static_cast<int>(rank);
     ex.lr_t = t;
   }
-  const bool skinny = M <= 32 && (w_group == 0 || w_group % 128 == 0);
+  const bool skinny = !w_f6 && M <= 32 && (w_group == 0 || w_group % 128 == 0);
   // Offset-binary weights: offset-binary codes (and their row sums) for the
   // tiled GEMM; the decode kernel converts the weights and takes plain codes.
   const bool a_ob = w_ob && !skinny;
@@ -420,11 +459,11 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
     ex.pf_last = tiled ? unit_bytes : (N - 16 * (units - 1)) * (K / 2);
     ex.pf_blocks = static_cast<int>(8 * ((units + 15) / 16));
   }
-  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b,
-                                   tiled ? (packed_codes ? w4a4::ROTQ_QUANT_TILED
-                                                         : w4a4::ROTQ_QUANT_I8_TILED)
-                                         : w4a4::ROTQ_QUANT_I8,
-                                   K, false, nullptr, xq, sx, plan, st, &ex);
+  const int mode = w_f6 ? w4a4::ROTQ_QUANT_F6
+                   : tiled ? (packed_codes ? w4a4::ROTQ_QUANT_TILED : w4a4::ROTQ_QUANT_I8_TILED)
+                           : w4a4::ROTQ_QUANT_I8;
+  hipError_t e = w4a4::launch_rotq(x, f16, M, K, log2b, mode, K, false, nullptr, xq, sx, plan, st,
+                                   &ex);
   if (e != hipSuccess) return hip_fail(e);
   if (rank > 0 && !fuse_lr) {
     e = w4a4::launch_lowrank_project(x, f16, At, M, K, static_cast<int>(rank), t, f16, st);
@@ -443,6 +482,7 @@ int qlinear_impl(const void* x, int x_dtype, const uint8_t* wq, int w_layout,
   g.a_i8 = !packed_codes;
   g.tiled = tiled;
   g.w_ob = w_ob;
+  g.f6 = w_f6;
   if (a_ob) {
     g.ob_sa = ob_sums(xq, M, K);
     g.ob_sb = ob_sums(wq, N, K);

@@ -75,6 +75,7 @@ constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v >> 1); }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <typename T> struct Piece;
 template <> struct Piece<float> {
@@ -393,8 +394,9 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
   const int slot = row_wg * (a.K / gsz) + kfirst / gsz;
   const bool leader = valid && (kfirst % gsz) == 0;
   const int64_t si = row * (a.K / gsz) + kfirst / gsz;
-  // code[r] holds the code of element r in its low bits (two's complement:
-  // low nibble = q & 0xF, low byte = q & 0xFF).
+  // code[r] holds the bits of q + 1.5 * 2^23 for the code q of element r: its
+  // low bits are q in two's complement (low nibble = q & 0xF, low byte =
+  // q & 0xFF), and the float minus 1.5 * 2^23 is q.
   uint32_t code[R];
   uint32_t rpk[R / 8];  // packed residual codes (weights with a residual)
   const bool res_lane = kfirst < a.res_pad;
@@ -569,7 +571,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
         const float xt = v[r] * a.rs;
         float qf = rintf(__fdiv_rn(xt, s_eff));
         qf = fminf(fmaxf(qf, -a.fqmax), a.fqmax);
-        code[r] = static_cast<uint32_t>(static_cast<int>(qf));
+        code[r] = __float_as_uint(qf + kMagic);
       }
     }
     // 7. Residual codes of the first res_r channels, packed like the codes.
@@ -624,6 +626,43 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
       if (on) os = static_cast<int>(ssum[slot]);
     }
     if (leader) a.ob_sum[row] = os;
+  }
+  if (a.mode == ROTQ_QUANT_F6) {
+    // FP6 E2M3 tiles: chunk c of 32 consecutive codes (k = kfirst + 32 c) is
+    // one lane of the matrix instruction, lane 16 ((k % 128) / 32) + rin of
+    // tile (rblk, k / 128).  The packing instruction converts the exact
+    // integer values (scale 1) and interleaves its two 16-value halves:
+    // field 2u holds code u, field 2u + 1 code 16 + u.  With R = 16 a chunk
+    // spans two lanes, the even one holding its first half.
+    if constexpr (R >= 16) {
+      constexpr int NCH = R >= 32 ? R / 32 : 1;
+      const int64_t rblk6 = row >> 4, rin6 = row & 15;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        f32x16 lo, hi;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          if constexpr (R >= 32) {
+            lo[u] = __uint_as_float(code[32 * c + u]) - kMagic;
+            hi[u] = __uint_as_float(code[32 * c + 16 + u]) - kMagic;
+          } else {
+            const float own = __uint_as_float(code[u]) - kMagic;
+            const float other = __shfl_xor(own, 1);
+            lo[u] = (lam & 1) ? other : own;
+            hi[u] = (lam & 1) ? own : other;
+          }
+        }
+        const auto p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, 1.0f);
+        if (valid && (R >= 32 || (lam & 1) == 0)) {
+          const int64_t k = kfirst + 32 * c;
+          uint8_t* tile = a.q + (rblk6 * a.tile_stride + (k >> 7)) * 1536;
+          const int l6 = static_cast<int>(((k & 127) >> 5) * 16 + rin6);
+          *reinterpret_cast<uint4*>(tile + 16 * l6) = make_uint4(p[0], p[1], p[2], p[3]);
+          *reinterpret_cast<uint2*>(tile + 1024 + 8 * l6) = make_uint2(p[4], p[5]);
+        }
+      }
+    }
+    return;
   }
   if (!valid) return;
   const bool tiled = a.mode == ROTQ_QUANT_TILED || a.mode == ROTQ_QUANT_I8_TILED;
@@ -787,13 +826,14 @@ bool try_shape(const Shape& sh, bool wide, int64_t K, int log2b, int64_t gsz, in
 
 }  // namespace
 
-bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan) {
+bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan,
+               int min_r) {
   if (M <= kWideRows) {
     for (const Shape& sh : kWideMenu)
-      if (try_shape(sh, true, K, log2b, gsz, max_lds, plan)) return true;
+      if (sh.R >= min_r && try_shape(sh, true, K, log2b, gsz, max_lds, plan)) return true;
   }
   for (const Shape& sh : kMenu)
-    if (try_shape(sh, false, K, log2b, gsz, max_lds, plan)) return true;
+    if (sh.R >= min_r && try_shape(sh, false, K, log2b, gsz, max_lds, plan)) return true;
   return false;
 }
 

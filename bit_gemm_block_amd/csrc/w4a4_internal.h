@@ -19,8 +19,10 @@ struct RotqPlan {
   int nslots = 0;        // cross-segment reduction slots per workgroup
 };
 
-// Chooses the segment shape for (K, b, group); returns false if none fits.
-bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan);
+// Chooses the segment shape for (K, b, group), with at least min_r elements
+// per lane; returns false if none fits.
+bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPlan* plan,
+               int min_r = 8);
 
 // ROTQ_QUANT_I8 writes one int8 code per byte, each group of 8 elements in
 // the order 0,2,4,6,1,3,5,7 (the K order of the GEMM's nibble widening): the
@@ -32,7 +34,10 @@ enum RotqMode {
   ROTQ_QUANT = 1,
   ROTQ_QUANT_I8 = 2,
   ROTQ_QUANT_TILED = 3,
-  ROTQ_QUANT_I8_TILED = 4
+  ROTQ_QUANT_I8_TILED = 4,
+  // FP6 E2M3 codes in 16-row x 128-code tiles of 1536 bytes (see
+  // include/w4a4.h, W4A4_CODES_F6_TILED); needs a plan with R >= 16.
+  ROTQ_QUANT_F6 = 5
 };
 
 // x: [M, K] (f16 if x_f16 else f32).  mode ROTATE writes xrot [M, K] f32;
@@ -123,9 +128,18 @@ struct GemmArgs {
   int w_ob;
   const int32_t* ob_sa;
   const int32_t* ob_sb;
+  // FP6 E2M3 operands (xq and wq in the FP6 tiled layouts): launch_qgemm
+  // hands the call to launch_qgemm_f6.
+  int f6;
 };
 
 hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
+
+// ---- int4 GEMM on the FP6 matrix instruction (qgemm_f6.hip) -----------------
+// xq and wq in the FP6 tiled layouts (W4A4_CODES_F6_TILED and
+// W4A4_WEIGHTS_TILED_F6), K a multiple of 128, weight groups multiples of 128;
+// sx, sw, y, acc, the low-rank term and group as in GemmArgs.
+hipError_t launch_qgemm_f6(const GemmArgs& a, hipStream_t st);
 
 // ---- the layer (api.cpp) ----------------------------------------------------
 // w4a4_qlinear_forward (qmax 7) and w4a8_qlinear_forward (qmax 127) with the

@@ -21,13 +21,16 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "w4a4.h")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, F16 = 0, 1
-CODES_PACKED, CODES_I8, CODES_I8_TILED, CODES_PACKED_TILED, CODES_PACKED_TILED_OB = range(5)
-WEIGHTS_ROWMAJOR, WEIGHTS_TILED, WEIGHTS_TILED_OB = 0, 1, 2
+(CODES_PACKED, CODES_I8, CODES_I8_TILED, CODES_PACKED_TILED, CODES_PACKED_TILED_OB,
+ CODES_F6_TILED) = range(6)
+WEIGHTS_ROWMAJOR, WEIGHTS_TILED, WEIGHTS_TILED_OB, WEIGHTS_TILED_F6 = 0, 1, 2, 3
 _LAYOUTS = {"packed": CODES_PACKED, "i8": CODES_I8, "i8_tiled": CODES_I8_TILED,
-            "packed_tiled": CODES_PACKED_TILED, "packed_tiled_ob": CODES_PACKED_TILED_OB}
-_TILED_CODES = (CODES_I8_TILED, CODES_PACKED_TILED)
+            "packed_tiled": CODES_PACKED_TILED, "packed_tiled_ob": CODES_PACKED_TILED_OB,
+            "f6_tiled": CODES_F6_TILED}
+_TILED_CODES = (CODES_I8_TILED, CODES_PACKED_TILED, CODES_F6_TILED)
 _PACKED_CODES = (CODES_PACKED, CODES_PACKED_TILED)
-_WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED, "tiled_ob": WEIGHTS_TILED_OB}
+_WLAYOUTS = {"rowmajor": WEIGHTS_ROWMAJOR, "tiled": WEIGHTS_TILED, "tiled_ob": WEIGHTS_TILED_OB,
+             "tiled_f6": WEIGHTS_TILED_F6}
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -113,6 +116,16 @@ def pad16(n: int) -> int:
     return (n + 15) // 16 * 16
 
 
+def code_bytes_per_row(layout: str, K: int) -> int:
+    """Bytes per (padded) row of codes of K channels in a codes or weight
+    layout: K/2 packed nibbles, K int8 codes, or 3K/4 for the FP6 tiles."""
+    if layout in ("f6_tiled", "tiled_f6"):
+        return 3 * K // 4
+    if layout in ("i8", "i8_tiled"):
+        return K
+    return K // 2
+
+
 def ob_bytes(rows: int, K: int) -> int:
     """Bytes of an offset-binary tiled buffer (flat uint8): the tiles of
     pad16(rows) rows, then one int32 sum per padded row."""
@@ -171,7 +184,8 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
     the GEMM's K order), "i8_tiled" ([pad16(M), K] in 2 KB tiles) or
     "packed_tiled" ([pad16(M), K/2] in the weights' 1 KB tiles) or
     "packed_tiled_ob" (flat, ob_bytes(M, K): offset-binary tiles and the row
-    sums of the odd channels' codes), and one float32 scale per row."""
+    sums of the odd channels' codes) or "f6_tiled" ([pad16(M), 3K/4]: FP6
+    E2M3 tiles of 1536 bytes), and one float32 scale per row."""
     _dev(x, "x")
     M, K = x.shape
     lay = _LAYOUTS[layout]
@@ -179,7 +193,7 @@ def quantize_act_int4(x: torch.Tensor, had_block: int, xq: Optional[torch.Tensor
         xq = torch.empty((ob_bytes(M, K),), dtype=torch.uint8, device=x.device)
     elif xq is None:
         rows = pad16(M) if lay in _TILED_CODES else M
-        xq = torch.empty((rows, K // 2 if lay in _PACKED_CODES else K), dtype=torch.uint8,
+        xq = torch.empty((rows, code_bytes_per_row(layout, K)), dtype=torch.uint8,
                          device=x.device)
     if x_scale is None:
         x_scale = torch.empty((M,), dtype=torch.float32, device=x.device)
@@ -210,12 +224,13 @@ def quantize_weight_int4(w: torch.Tensor, had_block: int, w_group: int,
                          scale_dtype: torch.dtype = torch.float16,
                          layout: str = "rowmajor") -> Tuple[torch.Tensor, torch.Tensor]:
     """Packed codes in layout "rowmajor" ([N, K/2]) or "tiled" ([pad16(N),
-    K/2] in 1 KB tiles), and the scales [N] or [N, K/w_group]."""
+    K/2] in 1 KB tiles), or FP6 E2M3 codes in layout "tiled_f6" ([pad16(N),
+    3K/4] in 1536-byte tiles), and the scales [N] or [N, K/w_group]."""
     _dev(w, "w")
     N, K = w.shape
     wl = _WLAYOUTS[layout]
-    wq = torch.empty((pad16(N) if wl == WEIGHTS_TILED else N, K // 2), dtype=torch.uint8,
-                     device=w.device)
+    wq = torch.empty((N if wl == WEIGHTS_ROWMAJOR else pad16(N), code_bytes_per_row(layout, K)),
+                     dtype=torch.uint8, device=w.device)
     shape = (N,) if w_group == 0 else (N, K // w_group)
     ws = torch.empty(shape, dtype=scale_dtype, device=w.device)
     _check("quantize_weight_int4", lib().w4a4_quantize_weight_int4(
@@ -258,6 +273,10 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
         K = 2 * (wq.numel() // pad16(N) - 4)
         if wq.numel() != ob_bytes(N, K):
             raise ValueError("wq is not an offset-binary buffer of N rows")
+    elif wl == WEIGHTS_TILED_F6:
+        K = 4 * wq.shape[1] // 3
+        if wq.shape[0] < pad16(N) or wq.shape[1] != 3 * K // 4:
+            raise ValueError("wq is not an FP6 tiled buffer of N rows")
     else:
         K = 2 * wq.shape[1]
         if wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N):
@@ -266,7 +285,7 @@ def qgemm_w4a4(xq: torch.Tensor, x_scale: Optional[torch.Tensor], wq: torch.Tens
         if xq.numel() != ob_bytes(M, K):
             raise ValueError("xq is not an offset-binary buffer of M rows and K channels")
     else:
-        if xq.shape[1] != (K // 2 if lay in _PACKED_CODES else K):
+        if xq.shape[1] != code_bytes_per_row(layout, K):
             raise ValueError("xq and wq disagree on K")
         if xq.shape[0] < (pad16(M) if lay in _TILED_CODES else M):
             raise ValueError("xq has too few rows")
@@ -339,7 +358,8 @@ def qlinear_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, ha
     if wl == WEIGHTS_TILED_OB:
         if wq.numel() != ob_bytes(N, K):
             raise ValueError("wq is not an offset-binary buffer matching w_scale and x")
-    elif wq.shape[0] < (pad16(N) if wl == WEIGHTS_TILED else N) or wq.shape[1] != K // 2:
+    elif (wq.shape[0] < (N if wl == WEIGHTS_ROWMAJOR else pad16(N)) or
+          wq.shape[1] != code_bytes_per_row(w_layout, K)):
         raise ValueError("wq does not match w_scale and x")
     rank = 0 if At is None else At.shape[0]
     if rank:

@@ -81,7 +81,8 @@ typedef enum {
   W4A4_CODES_I8 = 1,
   W4A4_CODES_I8_TILED = 2,
   W4A4_CODES_PACKED_TILED = 3,
-  W4A4_CODES_PACKED_TILED_OB = 4
+  W4A4_CODES_PACKED_TILED_OB = 4,
+  W4A4_CODES_F6_TILED = 5
 } w4a4_codes_layout;
 
 /* Tiled layouts (K a multiple of 128).  Rows are taken in blocks of 16 and K
@@ -106,7 +107,8 @@ typedef enum {
 typedef enum {
   W4A4_WEIGHTS_ROWMAJOR = 0,
   W4A4_WEIGHTS_TILED = 1,
-  W4A4_WEIGHTS_TILED_OB = 2
+  W4A4_WEIGHTS_TILED_OB = 2,
+  W4A4_WEIGHTS_TILED_F6 = 3
 } w4a4_weight_layout;
 
 /* Offset-binary tiled layouts: the same 16-row x 128-code tiles, with one
@@ -129,6 +131,25 @@ typedef enum {
  * the epilogue corrects exactly.  Offset-binary weights are produced from
  * tiled ones by w4a4_weights_tiled_to_ob and serve per-channel weight scales
  * (w_group 0) of the int4 layer and GEMM. */
+
+/* FP6 tiled layouts: the same 4-bit codes (SERQ page, "Resumen técnico"
+ * §1-2), each stored as the FP6 E2M3 number of equal value (OCP
+ * microscaling formats: sign bit 5, exponent bits 4:3 with bias 1, mantissa
+ * bits 2:0; every integer in [-7, 7] is exact, e.g. 3 = 0b010100 and
+ * -7 = 0b111110).  They are the operand format of the gfx950 FP6 matrix
+ * instruction, whose float32 sums of these products are exact integers, so
+ * the GEMM takes them with no conversion; they cost 6 bits per code instead
+ * of 4.  Rows in blocks of 16, K (a multiple of 128) in steps of 128; tile
+ * (b, t) is 1536 bytes at (b*(K/128) + t)*1536.  Lane l = 16g + r of a tile
+ * holds codes [128t + 32g, +32) of row 16b + r as 192 bits, field p (bits
+ * [6p, 6p+6)) being code 128t + 32g + p/2 + 16*(p%2); the tile's bytes
+ * [16l, 16l + 16) are the lane's bits [0, 128), its bytes
+ * [1024 + 8l, 1024 + 8l + 8) the bits [128, 192).
+ *   W4A4_CODES_F6_TILED (activations, [ceil(M/16)*16, 3K/4] bytes)
+ *   W4A4_WEIGHTS_TILED_F6 (weights, [ceil(N/16)*16, 3K/4] bytes)
+ * Produced by w4a4_quantize_act_int4 and w4a4_quantize_weight_int4, used
+ * together by w4a4_qgemm_w4a4 and by the int4 layer (per-channel or grouped
+ * weight scales, any M, not the 8-bit activations of W4A8). */
 
 /* ABI version of the loaded library (W4A4_ABI_VERSION when built). */
 int w4a4_abi_version(void);

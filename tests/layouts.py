@@ -134,10 +134,79 @@ def split_ob(flat, rows, K):
     return flat[:nb].reshape(Rp, K // 2), flat[nb:nb + 4 * Rp].view(np.int32)[:rows]
 
 
+# FP6 E2M3 (OCP microscaling formats): sign bit 5, exponent bits 4:3 with
+# bias 1, mantissa bits 2:0; exponent 0 is subnormal (m / 8).
+def e2m3_value(c):
+    """Value of each 6-bit E2M3 code (any of the 64)."""
+    c = np.asarray(c, np.int64)
+    e, m = (c >> 3) & 3, (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * np.exp2(e - 1.0))
+    return np.where(c & 32, -mag, mag)
+
+
+def e2m3_code(q):
+    """The E2M3 code of each integer q in [-7, 7] (0 as +0), found by search
+    over the 32 non-negative codes."""
+    q = np.asarray(q, np.int64)
+    table = {int(v): c for c, v in enumerate(e2m3_value(np.arange(32))) if float(v).is_integer()}
+    mag = np.vectorize(lambda a: table[int(a)])(np.abs(q)) if q.size else np.zeros(q.shape, np.int64)
+    return np.where(q < 0, mag | 32, mag).astype(np.uint8)
+
+
+def _f6_lane_fields(codes32):
+    """[..., 32] codes of one instruction lane -> [..., 32] fields in field
+    order: field 2u is code u, field 2u + 1 code 16 + u."""
+    f = np.empty_like(codes32)
+    f[..., 0::2] = codes32[..., :16]
+    f[..., 1::2] = codes32[..., 16:]
+    return f
+
+
+def tile_f6(q, rng=None):
+    """Codes [R, K] in [-7, 7] -> the FP6 tiled layout [pad16(R), 3K/4]
+    (W4A4_CODES_F6_TILED / W4A4_WEIGHTS_TILED_F6).  Padding rows get random
+    6-bit codes."""
+    R, K = q.shape
+    Rp = pad16(R)
+    c = np.empty((Rp, K), np.uint8)
+    c[:R] = e2m3_code(q)
+    c[R:] = (rng or np.random.default_rng(3)).integers(0, 64, (Rp - R, K), dtype=np.uint8)
+    # [blk, r, t, g, 32] -> [blk, t, g, r, 32] = tile (blk, t), lane 16 g + r
+    lanes = c.reshape(Rp // 16, 16, K // 128, 4, 32).transpose(0, 2, 3, 1, 4)
+    fields = _f6_lane_fields(lanes.reshape(Rp // 16, K // 128, 64, 32))
+    bits = ((fields[..., None] >> np.arange(6)) & 1).astype(np.uint8)
+    lane_bytes = np.packbits(bits.reshape(Rp // 16, K // 128, 64, 192), axis=-1, bitorder="little")
+    tile = np.concatenate([lane_bytes[..., :16].reshape(Rp // 16, K // 128, 1024),
+                           lane_bytes[..., 16:].reshape(Rp // 16, K // 128, 512)], axis=-1)
+    return np.ascontiguousarray(tile).reshape(Rp, 3 * K // 4)
+
+
+def untile_f6_codes(tiled, R, K):
+    """FP6 tiled bytes [pad16(R), 3K/4] -> the 6-bit codes [R, K] row-major."""
+    Rp = pad16(R)
+    t = np.asarray(tiled, np.uint8).reshape(Rp // 16, K // 128, 1536)
+    lane_bytes = np.concatenate([t[..., :1024].reshape(Rp // 16, K // 128, 64, 16),
+                                 t[..., 1024:].reshape(Rp // 16, K // 128, 64, 8)], axis=-1)
+    bits = np.unpackbits(lane_bytes, axis=-1, bitorder="little").reshape(Rp // 16, K // 128, 64, 32, 6)
+    fields = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    codes32 = np.concatenate([fields[..., 0::2], fields[..., 1::2]], axis=-1)
+    c = codes32.reshape(Rp // 16, K // 128, 4, 16, 32).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(c).reshape(Rp, K)[:R]
+
+
+def untile_f6(tiled, R, K):
+    """FP6 tiled bytes -> the integer codes [R, K] (int8); every code must be
+    an integer in [-7, 7]."""
+    v = e2m3_value(untile_f6_codes(tiled, R, K))
+    assert np.all(v == np.round(v)) and np.all(np.abs(v) <= 7)
+    return v.astype(np.int8)
+
+
 def workspace_codes(ws, off, M, K, layout):
     """The activation codes a layer call left in its workspace (flat uint8
     bytes, codes at byte offset `off`, stored in `layout`), rearranged row-major:
-    ("packed", [M, K/2] uint8 packed bytes) or ("i8", [M, K] int8 codes)."""
+    ("packed", [M, K/2] uint8 packed bytes) or ("i8", [M, K] int8 codes; FP6
+    tiles are decoded to their integer values)."""
     ws = np.asarray(ws, np.uint8)
     Mp = pad16(M)
     if layout in ("packed_tiled", "packed_tiled_ob"):
@@ -151,4 +220,6 @@ def workspace_codes(ws, off, M, K, layout):
         return "i8", codes_from_i8(ws[off:off + M * K].reshape(M, K))
     if layout == "i8_tiled":
         return "i8", codes_from_i8(untile_codes_i8(ws[off:off + Mp * K].reshape(Mp, K), M))
+    if layout == "f6_tiled":
+        return "i8", untile_f6(ws[off:off + Mp * (3 * K // 4)].reshape(Mp, 3 * K // 4), M, K)
     raise ValueError(layout)

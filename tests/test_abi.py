@@ -41,7 +41,8 @@ def test_quantize_act_argument_errors(lib):
     f = lib.w4a4_quantize_act_int4
     L = W.CODES_PACKED
     assert f(P, 7, 4, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG          # dtype
-    assert f(P, W.F16, 4, 256, 0, P, 5, P, None) == W.ERR_INVALID_ARG      # layout
+    assert f(P, W.F16, 4, 256, 0, P, 6, P, None) == W.ERR_INVALID_ARG      # layout
+    assert f(P, W.F16, 4, 192, 0, P, W.CODES_F6_TILED, P, None) == W.ERR_UNSUPPORTED  # K % 128
     assert f(P, W.F16, -1, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG     # M < 0
     assert f(P, W.F16, 4, 0, 0, P, L, P, None) == W.ERR_INVALID_ARG        # K = 0
     assert f(None, W.F16, 4, 256, 0, P, L, P, None) == W.ERR_INVALID_ARG   # null x
@@ -60,6 +61,7 @@ def test_int8_activation_quantizer_argument_errors(lib):
     f = lib.w4a4_quantize_act_int8
     assert f(P, W.F16, 4, 256, 0, P, W.CODES_PACKED, P, None) == W.ERR_INVALID_ARG         # 4-bit layout
     assert f(P, W.F16, 4, 256, 0, P, W.CODES_PACKED_TILED, P, None) == W.ERR_INVALID_ARG
+    assert f(P, W.F16, 4, 256, 0, P, W.CODES_F6_TILED, P, None) == W.ERR_INVALID_ARG   # FP6: 4-bit
     assert f(P, W.F16, 4, 192, 0, P, W.CODES_I8_TILED, P, None) == W.ERR_UNSUPPORTED       # K % 128
     assert f(P, W.F16, 4, 256, 3, P, W.CODES_I8, P, None) == W.ERR_UNSUPPORTED             # b
     assert f(Q, W.F16, 4, 256, 0, P, W.CODES_I8, P, None) == W.ERR_MISALIGNED
@@ -134,8 +136,12 @@ def test_qlinear_argument_errors(lib):
     assert f(*bad) == W.ERR_MISALIGNED
     bad = list(args); bad[10] = 100
     assert f(*bad) == W.ERR_UNSUPPORTED
-    bad = list(args); bad[3] = 3                                      # weight layout
+    bad = list(args); bad[3] = 4                                      # weight layout
     assert f(*bad) == W.ERR_INVALID_ARG
+    bad = list(args); bad[3] = W.WEIGHTS_TILED_F6                     # FP6: 4-bit codes only
+    assert lib.w4a8_qlinear_forward(*bad) == W.ERR_UNSUPPORTED
+    bad = list(args); bad[3] = W.WEIGHTS_TILED_F6; bad[10] = 64       # FP6: groups of 128 k
+    assert f(*bad) == W.ERR_UNSUPPORTED
     bad = list(args); bad[3] = W.WEIGHTS_TILED_OB; bad[10] = 128      # offset-binary: no groups
     assert f(*bad) == W.ERR_UNSUPPORTED
     bad = list(args); bad[3] = W.WEIGHTS_TILED_OB                     # offset-binary: no W4A8

@@ -96,3 +96,43 @@ def test_offset_binary_pairing_gives_the_corrected_integer_product():
     # the sums are those of the odd (activations) and even (weights) channels
     assert np.array_equal(sa, qx[:, 1::2].sum(axis=1))
     assert np.array_equal(sb, qw[:, 0::2].sum(axis=1))
+
+
+def test_e2m3_values_from_the_format_definition():
+    from layouts import e2m3_value, e2m3_code
+    # sign bit 5, exponent bits 4:3 (bias 1), mantissa 2:0; exponent 0 subnormal
+    cases = {0b000000: 0.0, 0b000001: 0.125, 0b000111: 0.875, 0b001000: 1.0, 0b010000: 2.0,
+             0b010100: 3.0, 0b011000: 4.0, 0b011010: 5.0, 0b011100: 6.0, 0b011110: 7.0,
+             0b011111: 7.5, 0b111110: -7.0, 0b101100: -1.5}
+    for c, v in cases.items():
+        assert e2m3_value(c) == v, c
+    assert np.signbit(e2m3_value(0b100000))  # -0
+    q = np.arange(-7, 8)
+    assert np.array_equal(e2m3_value(e2m3_code(q)), q)
+    assert e2m3_code(np.array([3]))[0] == 0b010100 and e2m3_code(np.array([-7]))[0] == 0b111110
+
+
+def test_f6_tiles_put_fields_where_the_header_says():
+    from layouts import tile_f6, untile_f6, untile_f6_codes, e2m3_code
+    rng = np.random.default_rng(11)
+    R, K = 21, 256
+    q = rng.integers(-7, 8, (R, K)).astype(np.int8)
+    t = tile_f6(q)
+    assert t.shape == (32, 3 * K // 4)
+    assert np.array_equal(untile_f6(t, R, K), q)
+    flat = t.reshape(-1)
+    for m in range(R):
+        for k in range(0, K, 7):
+            b, r, tt, g, u = m // 16, m % 16, k // 128, (k % 128) // 32, k % 32
+            p = 2 * u if u < 16 else 2 * (u - 16) + 1
+            lane = 16 * g + r
+            tile = (b * (K // 128) + tt) * 1536
+            val = 0
+            for j in range(6):
+                bit = 6 * p + j
+                off = tile + 16 * lane + bit // 8 if bit < 128 else tile + 1024 + 8 * lane + (bit - 128) // 8
+                val |= ((int(flat[off]) >> (bit % 8)) & 1) << j
+            assert val == e2m3_code(q[m:m + 1, k])[0], (m, k)
+    # zero codes are +0 (code 0) in every field
+    assert np.array_equal(untile_f6_codes(tile_f6(np.zeros((R, K), np.int8)), R, K),
+                          np.zeros((R, K)))
