@@ -11,10 +11,13 @@
 // registers right before v_mfma_i32_16x16x64_i8.  A nibble moved to the top
 // of its byte is a valid signed int8 equal to 16*q, so the widening is one
 // AND (high nibbles) or one shift+AND (low nibbles) per 8 codes, and the
-// accumulator holds 256 * acc, which stays below 2^31 for K <= 65536
-// (256 * 64 * K).  Low and high nibbles of a dword feed different int8
-// lanes of the instruction, i.e. the K order inside one instruction is
-// permuted; A and B use the same permutation, so the dot products are exact.
+// accumulator holds 256 * acc.  With codes down to -8, |acc| <= 64 K, so the
+// int32 holds it exactly for K < 2^17; the library accepts K <= 16384 (the
+// rotation kernel keeps a row of K values in one workgroup, 256 lanes x 64),
+// and the in-GEMM residual form 8 K + r_pad < 2^17.  Low and high nibbles
+// of a dword feed different int8 lanes of the instruction, i.e. the K order
+// inside one instruction is permuted; A and B use the same permutation, so
+// the dot products are exact.
 //
 // Large M: a 256-thread workgroup owns a (32 TM) x (32 TN) output tile; its
 // four waves form a 2 x 2 grid of (16 TM) x (16 TN) wave tiles.  K advances

@@ -25,7 +25,9 @@
  *             A non-OK status means nothing was enqueued.
  * Sizes:      M (tokens) and N (output channels) may be 0 (nothing is
  *             enqueued); K must be a positive multiple of 64 and at most
- *             16384.
+ *             16384 (the rotation kernel holds a row of K values in one
+ *             workgroup); the in-GEMM residual form also needs
+ *             8 K + (r rounded up to 128) < 2^17.
  * dtypes:     W4A4_F32 = float32, W4A4_F16 = IEEE binary16.
  * Packing:    int4 codes are two's-complement nibbles, element 2j in the low
  *             nibble of byte j: a [R, K] code matrix is stored as uint8
@@ -38,7 +40,10 @@
  *             and ties to even; a zero scale gives all-zero codes.
  * Errors:     no exceptions cross the ABI; every call returns a w4a4_status.
  * Threads:    the library is stateless apart from a per-device cache of the
- *             device check; calls are reentrant.
+ *             device check and, for w4a4_qlinear_forward_noalloc only, one
+ *             fixed scratch array per device that every such call on that
+ *             device shares (its calls must not overlap); all other calls are
+ *             reentrant.
  */
 #ifndef W4A4_H
 #define W4A4_H
