@@ -162,6 +162,34 @@ def _f6_lane_fields(codes32):
     return f
 
 
+def _fields_to_lane_bytes(fields):
+    """[..., 32] 6-bit fields -> [..., 24] bytes: field p at bits [6p, 6p + 6)
+    of the lane's 192-bit little-endian value (three 64-bit words)."""
+    f = fields.astype(np.uint64)
+    words = np.zeros(f.shape[:-1] + (3,), np.uint64)
+    for p in range(32):
+        bit = 6 * p
+        w, off = bit // 64, bit % 64
+        words[..., w] |= (f[..., p] << np.uint64(off)) & np.uint64(0xFFFFFFFFFFFFFFFF)
+        if off > 58:   # the field continues in the next word
+            words[..., w + 1] |= f[..., p] >> np.uint64(64 - off)
+    return words.astype("<u8").view(np.uint8).reshape(f.shape[:-1] + (24,))
+
+
+def _lane_bytes_to_fields(lane_bytes):
+    """Inverse of _fields_to_lane_bytes: [..., 24] bytes -> [..., 32] fields."""
+    words = np.ascontiguousarray(lane_bytes).view("<u8").astype(np.uint64)
+    out = np.empty(words.shape[:-1] + (32,), np.uint8)
+    for p in range(32):
+        bit = 6 * p
+        w, off = bit // 64, bit % 64
+        v = words[..., w] >> np.uint64(off)
+        if off > 58:
+            v |= words[..., w + 1] << np.uint64(64 - off)
+        out[..., p] = (v & np.uint64(63)).astype(np.uint8)
+    return out
+
+
 def tile_f6(q, rng=None):
     """Codes [R, K] in [-7, 7] -> the FP6 tiled layout [pad16(R), 3K/4]
     (W4A4_CODES_F6_TILED / W4A4_WEIGHTS_TILED_F6).  Padding rows get random
@@ -174,8 +202,7 @@ def tile_f6(q, rng=None):
     # [blk, r, t, g, 32] -> [blk, t, g, r, 32] = tile (blk, t), lane 16 g + r
     lanes = c.reshape(Rp // 16, 16, K // 128, 4, 32).transpose(0, 2, 3, 1, 4)
     fields = _f6_lane_fields(lanes.reshape(Rp // 16, K // 128, 64, 32))
-    bits = ((fields[..., None] >> np.arange(6)) & 1).astype(np.uint8)
-    lane_bytes = np.packbits(bits.reshape(Rp // 16, K // 128, 64, 192), axis=-1, bitorder="little")
+    lane_bytes = _fields_to_lane_bytes(fields)
     tile = np.concatenate([lane_bytes[..., :16].reshape(Rp // 16, K // 128, 1024),
                            lane_bytes[..., 16:].reshape(Rp // 16, K // 128, 512)], axis=-1)
     return np.ascontiguousarray(tile).reshape(Rp, 3 * K // 4)
@@ -187,8 +214,7 @@ def untile_f6_codes(tiled, R, K):
     t = np.asarray(tiled, np.uint8).reshape(Rp // 16, K // 128, 1536)
     lane_bytes = np.concatenate([t[..., :1024].reshape(Rp // 16, K // 128, 64, 16),
                                  t[..., 1024:].reshape(Rp // 16, K // 128, 64, 8)], axis=-1)
-    bits = np.unpackbits(lane_bytes, axis=-1, bitorder="little").reshape(Rp // 16, K // 128, 64, 32, 6)
-    fields = (bits.astype(np.int64) << np.arange(6)).sum(axis=-1)
+    fields = _lane_bytes_to_fields(lane_bytes)
     codes32 = np.concatenate([fields[..., 0::2], fields[..., 1::2]], axis=-1)
     c = codes32.reshape(Rp // 16, K // 128, 4, 16, 32).transpose(0, 3, 1, 2, 4)
     return np.ascontiguousarray(c).reshape(Rp, K)[:R]
@@ -197,9 +223,12 @@ def untile_f6_codes(tiled, R, K):
 def untile_f6(tiled, R, K):
     """FP6 tiled bytes -> the integer codes [R, K] (int8); every code must be
     an integer in [-7, 7]."""
-    v = e2m3_value(untile_f6_codes(tiled, R, K))
-    assert np.all(v == np.round(v)) and np.all(np.abs(v) <= 7)
-    return v.astype(np.int8)
+    v = e2m3_value(np.arange(64))
+    ok = (v == np.round(v)) & (np.abs(v) <= 7)
+    table = np.where(ok, v, 99).astype(np.int8)   # 99: not a code
+    q = table[untile_f6_codes(tiled, R, K)]
+    assert not np.any(q == 99)
+    return q
 
 
 def workspace_codes(ws, off, M, K, layout):

@@ -1,9 +1,11 @@
 """Full-size parity of every workload the benchmark times, on sampled rows.
 
-Each case runs qlinear_forward at its real size, in the launch configuration
-bench.py times: weights rotated and quantized on the GPU into the tiled
-layout (then converted to the offset-binary layout when the scales are per
-channel), the activations rotated and quantized inside the call.  The
+Each case runs qlinear_forward at its real size, in the launch configurations
+bench.py times: weights rotated and quantized on the GPU into the FP6 tiled
+layout (the prefill workloads' form), and into the int4 tiled layout (then
+converted to the offset-binary layout when the scales are per channel: the
+decode workload's form and the other int4 forms); the activations rotated and
+quantized inside the call.  The
 reference is the CPU oracle's epilogue evaluated on the codes and scales the
 call itself left in its workspace and on the GPU's own weight codes, for rows
 0 (the BOS-like token), 1, 40 random rows and the last row.
@@ -23,7 +25,7 @@ import torch
 from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
-from layouts import untile_weights, workspace_codes
+from layouts import untile_f6, untile_weights, workspace_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -43,11 +45,14 @@ def sample_rows(M, seed):
     return np.unique(np.r_[0, 1, np.random.default_rng(seed).integers(0, M, 40), M - 1])
 
 
-def gpu_weights(w, Wt_dev):
-    """The benchmark's weight preparation: fused rotation into tiled int4,
-    offset-binary for per-channel scales.  Returns (operand, layout, scales,
-    row-major packed codes read back)."""
+def gpu_weights(w, Wt_dev, form="int4"):
+    """The benchmark's weight preparation: fused rotation into FP6 tiles
+    (form "f6"), or into tiled int4, offset-binary for per-channel scales.
+    Returns (operand, layout, scales, row-major packed codes read back)."""
     sdt = torch.float16 if w.w_scale_dtype == "float16" else torch.float32
+    if form == "f6":
+        wf, ws = W.quantize_weight_int4(Wt_dev, w.had_block, w.w_group, sdt, layout="tiled_f6")
+        return wf, "tiled_f6", ws, O.pack_int4(untile_f6(host(wf), w.N, w.K))
     wt, ws = W.quantize_weight_int4(Wt_dev, w.had_block, w.w_group, sdt, layout="tiled")
     packed = untile_weights(host(wt), w.N)
     if w.w_group == 0:
@@ -76,12 +81,12 @@ def check_rows(y, y_codes, y_oracle, label):
     assert float(e.max()) <= 1e-3 * rms
 
 
-def run_full(w, seed):
-    print("full-size layer", w.name, flush=True)
+def run_full(w, seed, form="int4"):
+    print("full-size layer", w.name, form, flush=True)
     d = synth.make_inputs(w)
     X, Wt, A, B = d["X"], d["W"], d["A"], d["B"]
     Xd = dev(X)
-    op, wl, ws, gpacked = gpu_weights(w, dev(Wt))
+    op, wl, ws, gpacked = gpu_weights(w, dev(Wt), form)
     opacked, os_, _ = O.prepare_weight(Wt, w.had_block, w.w_group, w.w_scale_dtype)
     check_weights(gpacked, host(ws), opacked, os_)
     Ad = dev(A.T) if A is not None else None
@@ -105,17 +110,24 @@ def run_full(w, seed):
     gws = host(ws)
     y_codes = O.qlinear_from_codes(gc, gsx, gpacked, gws, w.w_group, Xr, A, B)
     y_oracle = O.qlinear_forward(Xr, opacked, os_, w.had_block, w.w_group, A, B)
-    check_rows(y, y_codes, y_oracle, w.name)
+    check_rows(y, y_codes, y_oracle, f"{w.name} {form}")
 
 
-@pytest.mark.parametrize("name", ["downproj_4096x14336x4096_g128",
-                                  "llama3_8b_qkv_4096x4096x6144",
-                                  "llama3_8b_o_4096x4096x4096",
-                                  "llama3_8b_gateup_4096x4096x28672",
-                                  "llama3_8b_down_4096x14336x4096",
-                                  "prefill_2048x4096x4096",
-                                  "decode_8x4096x4096_r64"])
+PREFILL_WORKLOADS = ["downproj_4096x14336x4096_g128", "llama3_8b_qkv_4096x4096x6144",
+                     "llama3_8b_o_4096x4096x4096", "llama3_8b_gateup_4096x4096x28672",
+                     "llama3_8b_down_4096x14336x4096", "prefill_2048x4096x4096"]
+
+
+@pytest.mark.parametrize("name", PREFILL_WORKLOADS)
+def test_layer_full_size_as_benchmarked_f6(name):
+    # the prefill workloads as bench.py times them: FP6 tiled weights
+    run_full(synth.by_name(name), seed=len(name) + 1, form="f6")
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", PREFILL_WORKLOADS + ["decode_8x4096x4096_r64"])
 def test_layer_full_size_as_benchmarked(name):
+    # the decode workload as bench.py times it, and the int4 operand forms
     w = synth.by_name(name)
     run_full(w, seed=len(name))
     torch.cuda.empty_cache()
@@ -123,12 +135,15 @@ def test_layer_full_size_as_benchmarked(name):
 
 @pytest.mark.parametrize("N,K,b,g", [(4096, 4096, 4096, 0), (6144, 4096, 128, 0),
                                      (4096, 14336, 128, 128), (512, 14336, 128, 0)])
-def test_quantize_weight_tiled_fused_rotation(N, K, b, g):
+@pytest.mark.parametrize("layout", ["tiled", "tiled_f6"])
+def test_quantize_weight_tiled_fused_rotation(N, K, b, g, layout):
     # The benchmark's weight preparation path (rotation fused into the tiled
     # quantizer) against the oracle's dense rotation and quantizer.
     rng = np.random.default_rng(N + K + b)
     Wt = (0.02 * rng.standard_normal((N, K))).astype(np.float32)
     Wt[:, 11] *= 40
-    wt, ws = W.quantize_weight_int4(dev(Wt), b, g, torch.float16, layout="tiled")
+    wt, ws = W.quantize_weight_int4(dev(Wt), b, g, torch.float16, layout=layout)
     opacked, os_, _ = O.prepare_weight(Wt, b, g, "float16")
-    check_weights(untile_weights(host(wt), N), host(ws), opacked, os_)
+    got = (untile_weights(host(wt), N) if layout == "tiled"
+           else O.pack_int4(untile_f6(host(wt), N, K)))
+    check_weights(got, host(ws), opacked, os_)

@@ -10,7 +10,7 @@ import torch
 from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
-from layouts import ob_weights, tile_weights
+from layouts import ob_weights, tile_f6, tile_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -28,9 +28,10 @@ def host(t):
 
 def operands(w, wl):
     d = synth.make_inputs(w)
-    wq, ws, _ = O.prepare_weight(d["W"], w.had_block, w.w_group, w.w_scale_dtype)
+    wq, ws, qw = O.prepare_weight(d["W"], w.had_block, w.w_group, w.w_scale_dtype)
     op = {"rowmajor": wq, "tiled": tile_weights(wq),
-          "tiled_ob": ob_weights(tile_weights(wq), w.N, w.K) if w.w_group == 0 else None}[wl]
+          "tiled_ob": ob_weights(tile_weights(wq), w.N, w.K) if w.w_group == 0 else None,
+          "tiled_f6": tile_f6(qw)}[wl]
     At = dev(d["A"].T) if d["A"] is not None else None
     Bt = dev(d["B"].T) if d["B"] is not None else None
     return d, wq, ws, dev(op), At, Bt
@@ -59,8 +60,11 @@ def test_noalloc_equals_workspace_forward_two_calls():
 
 
 def test_noalloc_equals_workspace_forward_forms():
-    # row-major and tiled weights, a weight group, fp32 input, low-rank terms
+    # row-major, tiled and FP6 tiled weights, a weight group, fp32 input,
+    # low-rank terms
     for w, wl in [(synth.small("na3", 300, 1024, 260, had_block=256, rank=16), "tiled"),
+                  (synth.small("na6", 200, 2048, 384, had_block=128, w_group=128, rank=32),
+                   "tiled_f6"),
                   (synth.small("na4", 65, 14336, 96, had_block=128, w_group=128, rank=32), "tiled"),
                   (synth.small("na5", 40, 384, 100, x_dtype="float32", w_scale_dtype="float32"),
                    "rowmajor"),
