@@ -31,7 +31,8 @@
 // (NWM = 4) one workgroup fills a CU: a 256 x 128 tile reads 25% fewer
 // operand bytes per product than two 128 x 128 ones, and four stages keep
 // more iterations of copies in flight to cover stages whose lines miss the
-// L2.  Weight groups (multiples of 128 codes) are flushed into a float
+// L2; with 64 x 128 wave tiles (TN = 8) the 256 x 256 tile reads a third
+// fewer than 256 x 128.  Weight groups (multiples of 128 codes) are flushed into a float
 // accumulator, y = sx sum_g sw_g acc_g, with the group scales of the tile's
 // columns staged in LDS before the loop.
 #include "w4a4_internal.h"
@@ -205,7 +206,11 @@ __global__ void __launch_bounds__(128 * NWM) qgemm_f6_kernel(GemmArgs a) {
     __syncthreads();
   }
 
-  if constexpr (!GROUPED) {
+  // One fragment set per iteration, read right before its instructions, when
+  // the accumulators take too many registers for a second set: weight groups
+  // (group and float accumulators) and 64 x 128 wave tiles.
+  constexpr bool SB = GROUPED || TM * TN > 16;
+  if constexpr (!SB) {
     // Prologue: the first STAGES stages in flight, stage 0 visible, its
     // fragments read.
 #pragma unroll
@@ -263,10 +268,9 @@ __global__ void __launch_bounds__(128 * NWM) qgemm_f6_kernel(GemmArgs a) {
       }
     }
   } else {
-    // Weight groups: the group and float accumulators take twice the
-    // registers, so one fragment set is read per iteration, right before its
-    // instructions (the other waves of the SIMD cover the read latency).
-    // Prologue: stages 0 .. STAGES - 2 in flight.
+    // One fragment set, read right before the instructions (the other waves
+    // of the SIMD cover the read latency).  Prologue: stages 0 .. STAGES - 2
+    // in flight.
 #pragma unroll
     for (int sidx = 0; sidx < STAGES - 1; ++sidx)
       if (sidx < nkt) issue(sidx, stage(sidx));
@@ -415,7 +419,9 @@ hipError_t launch_f6(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();                                                              \
   }
   W4A4_F6_CASE(false, LR_NONE) W4A4_F6_CASE(false, LR_F16) W4A4_F6_CASE(false, LR_F32)
-  W4A4_F6_CASE(true, LR_NONE) W4A4_F6_CASE(true, LR_F16) W4A4_F6_CASE(true, LR_F32)
+  if constexpr (TM * TN <= 16) {  // grouped wave tiles of at most 64 x 64 (registers)
+    W4A4_F6_CASE(true, LR_NONE) W4A4_F6_CASE(true, LR_F16) W4A4_F6_CASE(true, LR_F32)
+  }
 #undef W4A4_F6_CASE
   return hipErrorInvalidValue;
 }
@@ -443,11 +449,22 @@ hipError_t launch_qgemm_f6(const GemmArgs& a, hipStream_t st) {
     if (3 * 37888 + shm <= 163840) return launch_f6<4, 4, 4, 3>(ya, st);
     return launch_f6<4, 4, 4, 2>(ya, st);
   }
-  // Per-channel scales: eight-wave 256 x 128 tiles with four stages for long
-  // K or many tile rounds (K = 14336: 4% faster; 4096 x 28672: 6%), two
-  // four-wave 128 x 128 workgroups per CU with three stages otherwise (the
-  // 2048- and 4096-row products with K = 4096: 3-5% faster).
+  // Per-channel scales, largest tile first:
+  // * eight waves of 64 x 128 (256 x 256 tiles, one workgroup per CU, three
+  //   stages of 48 KB) when the tiles fill at least 90% of their rounds on
+  //   the 256 CUs: a third fewer operand bytes per product than 256 x 128
+  //   (4096 x 28672 x 4096: 19% faster, 4096 x 4096 x 14336: 11%,
+  //   4096 x 4096 x 4096: 7%; 384 tiles, 1.5 rounds: 3% slower);
+  // * eight waves of 64 x 64 (256 x 128 tiles, four stages) for long K or
+  //   many tiles;
+  // * two four-wave 128 x 128 workgroups per CU (three stages) otherwise
+  //   (the 2048- and 4096-row products with K = 4096: 3-5% faster).
+  constexpr int64_t kCUs = 256;  // MI355X
   const int64_t tiles8 = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+  const int64_t tiles16 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int64_t rounds16 = (tiles16 + kCUs - 1) / kCUs;
+  if (tiles16 >= kCUs && 10 * tiles16 >= 9 * rounds16 * kCUs)
+    return launch_f6<4, 8, 4, 3>(ya, st);
   if (a.K >= 8192 || tiles8 >= 2048) return launch_f6<4, 4, 4, 4>(ya, st);
   return launch_f6<4, 4, 2, 3>(ya, st);
 }
