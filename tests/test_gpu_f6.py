@@ -61,7 +61,7 @@ def test_quantize_act_f6_exact(M, K, b, dt):
 
 
 @pytest.mark.parametrize("M,K,b", [(130, 4096, 4096), (37, 4096, 4096), (9, 14336, 128),
-                                   (300, 1024, 256)])
+                                   (300, 1024, 256), (4100, 4096, 128)])
 def test_quantize_act_f6_fused_matches_packed(M, K, b):
     w = synth.small("qf6f", M, K, 8, n_outlier=3, bos_factor=500.0)
     Xd = dev(synth.make_inputs(w)["X"])
