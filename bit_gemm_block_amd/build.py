@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libw4a4.so")
 
-SOURCES = ["api.cpp", "rotq.hip", "qgemm.hip", "qgemm_f6.hip", "lowrank.hip", "offq.hip",
+SOURCES = ["api.cpp", "rotq.hip", "rotq_mfma.hip", "qgemm.hip", "qgemm_f6.hip", "lowrank.hip", "offq.hip",
            "noalloc.hip"]
 
 # No fast-math and no denormal flushing: the quantizer's float32 division and

@@ -61,7 +61,7 @@ def test_quantize_act_f6_exact(M, K, b, dt):
 
 
 @pytest.mark.parametrize("M,K,b", [(130, 4096, 4096), (37, 4096, 4096), (9, 14336, 128),
-                                   (300, 1024, 256), (4100, 4096, 128)])
+                                   (300, 1024, 256), (60, 4096, 128)])
 def test_quantize_act_f6_fused_matches_packed(M, K, b):
     w = synth.small("qf6f", M, K, 8, n_outlier=3, bos_factor=500.0)
     Xd = dev(synth.make_inputs(w)["X"])
@@ -70,6 +70,32 @@ def test_quantize_act_f6_fused_matches_packed(M, K, b):
     xp, sp = W.quantize_act_int4(Xd, b, layout="packed")
     assert np.array_equal(host(sf), host(sp))
     assert np.array_equal(untile_f6(host(xf), M, K), O.unpack_int4(host(xp)))
+
+
+@pytest.mark.parametrize("M,K", [(65, 2048), (130, 4096), (4100, 4096), (200, 14336),
+                                 (77, 16384), (1000, 6144)])
+def test_quantize_act_f6_b128_matrix_rotation(M, K):
+    # FP6 codes of fp16 rows with b = 128 (more than 64 rows): the transform
+    # runs on the fp16 matrix instruction, so its float32 sums round in
+    # another order than the butterflies'; against the oracle the codes meet
+    # the fused-path bar (at most 0.01% differ, each by one step) and the
+    # scales agree within 1e-6.  A wrong lane exchange or tile offset would
+    # move whole 8-code units and fail the bar at once.
+    w = synth.small("qm128", M, K, 8, n_outlier=3, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    print("quantize_act f6 b128 matrix", M, K, flush=True)
+    xq, sx = W.quantize_act_int4(dev(X), 128, layout="f6_tiled")
+    _, ps, pc, _ = O.quantize_activation(O.rotate(X, 128), 0)
+    got = untile_f6(host(xq), M, K).astype(np.int16)
+    diff = got - pc.astype(np.int16)
+    assert np.all(np.abs(diff) <= 1)
+    assert np.count_nonzero(diff) <= 1e-4 * diff.size
+    assert np.all(np.abs(host(sx).astype(np.float64) - ps) <= 1e-6 * ps)
+    # the packed codes of the butterfly kernel meet the same bar against these
+    xp, sp = W.quantize_act_int4(dev(X), 128, layout="packed")
+    d2 = got - O.unpack_int4(host(xp)).astype(np.int16)
+    assert np.all(np.abs(d2) <= 1)
+    assert np.count_nonzero(d2) <= 2e-4 * d2.size
 
 
 @pytest.mark.parametrize("N,K,b,g,sdt", [(4096, 4096, 4096, 0, torch.float16),

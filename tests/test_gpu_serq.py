@@ -21,7 +21,7 @@ from oracle import w4a4_oracle as O
 from bit_gemm_block_amd import synth
 from bit_gemm_block_amd import w4a4 as W
 from bars import check_y
-from layouts import tile_weights, tile_weights_residual, untile_weights_residual
+from layouts import tile_weights, tile_weights_residual, untile_weights_residual, workspace_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -126,9 +126,14 @@ def run_residual_layer(w, r, sample_rows=None):
     wqd = dev(ext_weights(q, qr))
     Xd = dev(X)
     print("residual layer", w.name, w.M, w.K, w.N, b, r, flush=True)
-    y = host(W.qlinear_forward_residual(Xd, wqd, dev(ws), r, b))
-    gxq, gsx = W.quantize_act_int4(Xd, b)
-    gc, gs = O.unpack_int4(host(gxq)), host(gsx)
+    ws_buf = W.qlinear_workspace(w.M, w.N, w.K, 0, DEV)
+    y = host(W.qlinear_forward_residual(Xd, wqd, dev(ws), r, b, workspace=ws_buf))
+    # the codes and scales the layer left in its workspace
+    wsb = host(ws_buf)
+    co, cl, so = W.qlinear_workspace_layout(w.M, w.N, w.K, 0, "tiled", 0)
+    assert cl == "packed_tiled"
+    _, packed = workspace_codes(wsb, co, w.M, w.K, cl)
+    gc, gs = O.unpack_int4(packed), wsb[so:so + 4 * w.M].view(np.float32)
     rows = np.arange(w.M) if sample_rows is None else sample_rows
     _, ps, pc, _ = O.quantize_activation(X[rows], b)
     diff = gc[rows].astype(np.int16) - pc
