@@ -61,6 +61,7 @@
 // of two the quotient is formed as y / (s / rs), the same real number.
 #include "w4a4_internal.h"
 #include "lowrank_rows.h"
+#include "rotq_mfma.h"
 
 #include <hip/hip_fp16.h>
 #include <type_traits>
@@ -894,14 +895,20 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
                        int64_t gsz, bool scale_f16, float* xrot, uint8_t* q, void* scale,
                        const RotqPlan& plan, hipStream_t st, const RotqExtras* ex) {
   // Tiled 4-bit codes (FP6, or packed plain or offset-binary) of fp16 rows
-  // with b = 128 and one float32 scale per row: the transform on the matrix
-  // instruction (rotq_mfma.hip).
+  // with one float32 scale per row: the transform on the matrix instruction
+  // (rotq_mfma.hip), for b = 128 and for 256 <= b <= 4096.
   const bool plain_ex = !ex || (ex->qmax == 7 && !ex->asym_zero && ex->res_r == 0 && !ex->mx_scale &&
                                 ex->lr_rank == 0 && !ex->pf);
   const bool tiled4 = mode == ROTQ_QUANT_F6 || mode == ROTQ_QUANT_TILED;
-  if (x_f16 && tiled4 && log2b == 7 && gsz == K && !scale_f16 && plain_ex && rotq128_ok(M, K))
-    return launch_rotq128(static_cast<const _Float16*>(x), M, K, mode == ROTQ_QUANT_F6, q,
-                          static_cast<float*>(scale), ex ? ex->ob_sum : nullptr, st);
+  if (x_f16 && tiled4 && gsz == K && !scale_f16 && plain_ex) {
+    const _Float16* xh = static_cast<const _Float16*>(x);
+    float* sf = static_cast<float*>(scale);
+    int32_t* ob = ex ? ex->ob_sum : nullptr;
+    if (log2b == 7 && rotq128_ok(M, K))
+      return launch_rotq128(xh, M, K, mode == ROTQ_QUANT_F6, q, sf, ob, st);
+    if (rotq_kron_ok(M, K, log2b))
+      return launch_rotq_kron(xh, M, K, log2b, mode == ROTQ_QUANT_F6, q, sf, ob, st);
+  }
   RotqKArgs ka{};
   ka.x = x;
   ka.M = M;

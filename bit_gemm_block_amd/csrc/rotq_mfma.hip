@@ -32,7 +32,29 @@
 // which lane groups g = 0..3 hold 8 each (mb = 2 j, 2 j + 1): a 4 x 4
 // transpose of 8-value units across the lane groups, by v_permlane32_swap
 // (lane groups 0,1 <-> 2,3) then v_permlane16_swap (0 <-> 1, 2 <-> 3).
-#include "w4a4_internal.h"
+//
+// Larger blocks, b = 128 n with n = 2^P sub-blocks of 128 (2 <= n <= 32):
+// Sylvester's construction gives H_b = H_n (x) H_128 (entry
+// (128 j + e, 128 j' + e') is (-1)^(j.j') (-1)^(e.e')), so the rotation is the
+// transform of every sub-block of 128, then the n-point transform across the
+// sub-blocks at each of the 128 positions.  A wave takes 4096 elements of the
+// row, 32 sub-blocks, as two chains h of the product above (sub-block
+// 16 h + c in lane column c).  The transform across sub-blocks has one bit in
+// the registers (the chain, for n = 32) and up to four in the lane column.
+// A lane stage is one v_fmac_f32_dpp per value, v += sgn * v[partner], the
+// partner read through a lane permutation within each 16-lane row: xor 1 and
+// xor 2 (quad permutations), xor 7 (half-row mirror), xor 8 (row rotation by
+// 8).  (A uniform add or subtract gives both lanes of a pair the same linear
+// form of their two values; the per-lane sign gives the low lane the sum and
+// the high lane the difference, negated.)  With partner masks 1, 2, 7, 8 the
+// stages are the Walsh-Hadamard butterflies in the coordinates of the column
+// index over the basis {1, 2, 7, 8}: a lane's sign at stage s is its s-th
+// coordinate, the product is H_16 with its columns permuted by the Gram matrix
+// of the basis, and loading sub-block pi(c) into column c undoes that
+// permutation.  At the end a lane holds its outputs times (-1)^(sum of its
+// coordinates); the quantizer puts that sign back into the codes.  The host
+// derives pi, the coordinates and the final signs from the four masks.
+#include "rotq_mfma.h"
 
 #include <hip/hip_fp16.h>
 
@@ -45,19 +67,26 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 
 constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: x + kMagic - kMagic = rint(x) for |x| < 2^22
 
-struct Rot128Args {
+struct RotArgs {
   const _Float16* x;  // [M, K]
   int64_t M, K;
-  float rs;           // float32(1 / sqrt(128))
+  float rs;           // float32(1 / sqrt(b))
+  float sqrt_b;       // sqrt(b) when it is a power of two (the divisor fold)
   uint8_t* q;         // the code tiles
   float* scale;       // [M]
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
-  int64_t tile_stride;  // tiles per 16-row block (K / 128)
+  int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
+  uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
+  uint64_t sel_tbl;   // 4 bits per column: bit s is the column's sign at lane stage s
+  uint32_t sig_tbl;   // bit c: column c holds its outputs negated after the stages
 };
 
 // Output layouts.
 enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2 };
+
+template <int OUT>
+constexpr int64_t kTileBytes = OUT == OUT_F6 ? 1536 : 1024;
 
 __device__ __forceinline__ h8 neg8(h8 v) {
   h8 r;
@@ -66,53 +95,44 @@ __device__ __forceinline__ h8 neg8(h8 v) {
   return r;
 }
 
-template <int W, int OUT>  // W waves per row: K = 2048 W
-__global__ void __launch_bounds__(64 * W) rotq128_kernel(Rot128Args a) {
-  __shared__ float wmax[W];
-  __shared__ int wsum[W];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
-  // whole 16-row blocks, so that every line of a code tile is written from
-  // one L2.
-  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
-  if (row >= a.M) return;
-  const _Float16* src = a.x + row * a.K + 2048 * w + 128 * c + 8 * g;
+// The +-1 operands A of the 128-point transform: F0[t] is the Hadamard sign
+// of (r & t) and (r3 & g0); F1 adds (g1) for odd output blocks; N0, N1 their
+// negations.
+struct HFrag {
+  h8 f0, f1, n0, n1;
+};
 
-  h8 xb[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
-
-  // F0[t] = H sign of (r & t) and (r3 & g0); F1 adds (g1) for odd mb.
-  const int r = lane & 15;
-  h8 f0, f1;
+__device__ __forceinline__ HFrag h128_fragments(int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  HFrag f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int par = (__builtin_popcount(r & t & 7) + ((r >> 3) & g & 1)) & 1;
-    f0[t] = par ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
-    f1[t] = ((g >> 1) & 1) ? -f0[t] : f0[t];
+    f.f0[t] = par ? static_cast<_Float16>(-1.0f) : static_cast<_Float16>(1.0f);
+    f.f1[t] = ((g >> 1) & 1) ? -f.f0[t] : f.f0[t];
   }
-  const h8 n0 = neg8(f0), n1 = neg8(f1);
+  f.n0 = neg8(f.f0);
+  f.n1 = neg8(f.f1);
+  return f;
+}
 
-  f4 acc[8];
+// acc[mb]: lane 16 g + c holds y_c[16 mb + 4 g + i], y_c = H x_c, for the 16
+// blocks whose operand B xb this lane holds.
+__device__ __forceinline__ void h128_product(const HFrag& f, const h8 (&xb)[4], f4 (&acc)[8]) {
 #pragma unroll
   for (int mb = 0; mb < 8; ++mb) {
     acc[mb] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       const bool neg = (((mb >> 1) & kc & 1) ^ ((mb >> 2) & (kc >> 1) & 1)) != 0;
-      const h8 av = (mb & 1) ? (neg ? n1 : f1) : (neg ? n0 : f0);
+      const h8 av = (mb & 1) ? (neg ? f.n1 : f.f1) : (neg ? f.n0 : f.f0);
       acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, xb[kc], acc[mb], 0, 0, 0);
     }
   }
+}
 
-  // Row absmax of y (x~ = RN(y rs) is monotone in |y|).
-  float m = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[mb][i]));
+template <int W>
+__device__ __forceinline__ float row_max(float m, float* wmax, int lane, int w) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   if (W > 1) {
@@ -121,31 +141,34 @@ __global__ void __launch_bounds__(64 * W) rotq128_kernel(Rot128Args a) {
 #pragma unroll
     for (int v = 0; v < W; ++v) m = fmaxf(m, wmax[v]);
   }
+  return m;
+}
 
-  // Scale and codes, as the butterfly kernel's quantizer (fp16 input keeps
-  // every scale inside the range where the refined reciprocal is exact).
-  const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, 7.0f);
-  if (threadIdx.x == 0) a.scale[row] = s;
-  const float rc = s == 0.f ? 0.f : __frcp_rn(s);
-  // cm holds q + 1.5 * 2^23 for the code q: minus that constant it is q as a
-  // float (the FP6 packing instruction's input), and its low nibble is q in
-  // two's complement.
-  float cm[8][4];
+template <int W>
+__device__ __forceinline__ int row_sum(int os, int* wsum, int lane, int w) {
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int o = 1; o < 64; o <<= 1) os += __shfl_xor(os, o);
+  if (W > 1) {
+    if (lane == 0) wsum[w] = os;
+    __syncthreads();
+    os = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float xt = acc[mb][i] * a.rs;
-      float q = xt * rc;
-      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
-      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
-      cm[mb][i] = q + kMagic;
-    }
+    for (int v = 0; v < W; ++v) os += wsum[v];
+  }
+  return os;
+}
 
-  // Unit j of this lane (the 8 codes of chunk j: mb = 2 j + v / 4, i' = v % 4)
+// Writes the codes of the 16 blocks of one product into their tiles.  cm[mb][i]
+// holds the code q of y_c[16 mb + 4 g + i] in the form its tile takes: q as a
+// float for FP6 (the packing instruction's input), q + 1.5 * 2^23 for the
+// nibble tiles (whose low nibble is q in two's complement).  Returns, for
+// offset-binary tiles, this lane's sum of the codes at odd channels.
+template <int OUT>
+__device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* tile, int g, int rin) {
+  // Unit j of this lane (the 8 codes of chunk j: mb = 2 j + v / 4, i = v % 4)
   // goes to lane group j.  After the two swaps, B[s][v] is unit (this lane
-  // group) of source group s.
+  // group) of source group s, and this lane holds codes [32 g, 32 g + 32) of
+  // its block, chunk offset 16 (v / 4) + 4 s + v % 4 in B[s][v].
   uint32_t u[4][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -163,10 +186,6 @@ __global__ void __launch_bounds__(64 * W) rotq128_kernel(Rot128Args a) {
     b[2][v] = t23[0];
     b[3][v] = t23[1];
   }
-  // This lane now holds codes [32 g, 32 g + 32) of block 16 w + c of the
-  // row; chunk offset 16 (v / 4) + 4 s + v % 4 is B[s][v].
-  const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // tile of block 16 w + c
-  const int rin = static_cast<int>(row & 15);
   if constexpr (OUT == OUT_F6) {
     // lane 16 g + (row % 16) of the 1536-byte FP6 tile
     f16v lo, hi;
@@ -174,14 +193,14 @@ __global__ void __launch_bounds__(64 * W) rotq128_kernel(Rot128Args a) {
     for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        lo[4 * sg + t] = __uint_as_float(b[sg][t]) - kMagic;
-        hi[4 * sg + t] = __uint_as_float(b[sg][4 + t]) - kMagic;
+        lo[4 * sg + t] = __uint_as_float(b[sg][t]);
+        hi[4 * sg + t] = __uint_as_float(b[sg][4 + t]);
       }
     const auto p = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, 1.0f);
-    uint8_t* tile = a.q + blk * 1536;
     const int l6 = 16 * g + rin;
     *reinterpret_cast<uint4*>(tile + 16 * l6) = make_uint4(p[0], p[1], p[2], p[3]);
     *reinterpret_cast<uint2*>(tile + 1024 + 8 * l6) = make_uint2(p[4], p[5]);
+    return 0;
   } else {
     // Nibble 8 d + e of the lane's 16 bytes is chunk offset 8 d + e: dword d
     // takes B[2 (d % 2) + e / 4][4 (d / 2) + e % 4]; the 16 bytes go to
@@ -195,30 +214,259 @@ __global__ void __launch_bounds__(64 * W) rotq128_kernel(Rot128Args a) {
         v = __builtin_amdgcn_alignbit(b[2 * (d & 1) + (e >> 2)][4 * (d >> 1) + (e & 3)], v, 4);
       pk[d] = v;
     }
+    int os = 0;
     if constexpr (OUT == OUT_PACKED_OB) {
-      // Row sum of the codes at odd channels (the high nibbles, as int8 16 q),
-      // then the low nibbles offset by 8.
+      // The codes at odd channels (the high nibbles, as int8 16 q), then the
+      // low nibbles offset by 8.
       int os16 = 0;
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         os16 = __builtin_amdgcn_sdot4(static_cast<int>(pk[d] & 0xF0F0F0F0u), 0x01010101, os16, false);
-      int os = os16 >> 4;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) os += __shfl_xor(os, o);
-      if (W > 1) {
-        if (lane == 0) wsum[w] = os;
-        __syncthreads();
-        os = 0;
-#pragma unroll
-        for (int v = 0; v < W; ++v) os += wsum[v];
-      }
-      if (threadIdx.x == 0) a.ob_sum[row] = os;
+      os = os16 >> 4;
 #pragma unroll
       for (int d = 0; d < 4; ++d) pk[d] ^= 0x08080808u;
     }
-    *reinterpret_cast<uint4*>(a.q + blk * 1024 + (16 * g + rin) * 16) =
-        make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(tile + (16 * g + rin) * 16) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    return os;
   }
+}
+
+template <int W, int OUT>  // W waves per row: K = 2048 W
+__global__ void __launch_bounds__(64 * W, 2) rotq128_kernel(RotArgs a) {
+  __shared__ float wmax[W];
+  __shared__ int wsum[W];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
+  // whole 16-row blocks, so that every line of a code tile is written from
+  // one L2.
+  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
+  if (row >= a.M) return;
+  const _Float16* src = a.x + row * a.K + 2048 * w + 128 * c + 8 * g;
+
+  h8 xb[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
+  f4 acc[8];
+  h128_product(h128_fragments(lane), xb, acc);
+
+  // Row absmax of y (x~ = RN(y rs) is monotone in |y|).
+  float m = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[mb][i]));
+  m = row_max<W>(m, wmax, lane, w);
+
+  // Scale and codes, as the butterfly kernel's quantizer (fp16 input keeps
+  // every scale inside the range where the refined reciprocal is exact).
+  const float amax = m * a.rs;
+  const float s = __fdiv_rn(amax, 7.0f);
+  if (threadIdx.x == 0) a.scale[row] = s;
+  const float rc = s == 0.f ? 0.f : __frcp_rn(s);
+  float cm[8][4];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float xt = acc[mb][i] * a.rs;
+      float q = xt * rc;
+      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+      cm[mb][i] = OUT == OUT_F6 ? __builtin_rintf(q) : q + kMagic;
+    }
+
+  const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // tile of block 16 w + c
+  const int os = store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, static_cast<int>(row & 15));
+  if constexpr (OUT == OUT_PACKED_OB) {
+    const int tot = row_sum<W>(os, wsum, lane, w);
+    if (threadIdx.x == 0) a.ob_sum[row] = tot;
+  }
+}
+
+// One lane stage over the 64 values: v += sgn * v[lane ^ mask] within each
+// 16-lane row.  Inline asm, since the compiler splits the permuted operand into
+// a separate move; the s_nop covers the two wait states that a permuted read
+// needs after the VALU write of its register.
+#define W4A4_FMAC_DPP8(CTRL, V, SG)                                                 \
+  asm("s_nop 1\n\t"                                                                 \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t"           \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"               \
+      : "+v"((V)[0]), "+v"((V)[1]), "+v"((V)[2]), "+v"((V)[3]), "+v"((V)[4]),      \
+        "+v"((V)[5]), "+v"((V)[6]), "+v"((V)[7])                                    \
+      : "v"(SG))
+
+template <int S>  // partner masks 1, 2, 7, 8
+__device__ __forceinline__ void lane_stage(float (&y)[64], int sel) {
+  const float sg = ((sel >> S) & 1) ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 64; k += 8) {
+    float* v = y + k;
+    if constexpr (S == 0)
+      W4A4_FMAC_DPP8("quad_perm:[1,0,3,2]", v, sg);
+    else if constexpr (S == 1)
+      W4A4_FMAC_DPP8("quad_perm:[2,3,0,1]", v, sg);
+    else if constexpr (S == 2)
+      W4A4_FMAC_DPP8("row_half_mirror", v, sg);
+    else
+      W4A4_FMAC_DPP8("row_ror:8", v, sg);
+  }
+}
+#undef W4A4_FMAC_DPP8
+
+// W waves per row, each taking 4096 elements (K = 4096 W); b = 128 * 2^P.
+// (At least two waves per SIMD: the register cap keeps the accumulators out of
+// the AGPRs, which would take a copy per value.)
+template <int W, int OUT, int P>
+__global__ void __launch_bounds__(64 * W, 2) rotq_kron_kernel(RotArgs a) {
+  constexpr int kLaneStages = P < 4 ? P : 4;
+  // sqrt(b) a power of two: x~ / s = y / (s sqrt(b)) with both sides exact.
+  constexpr bool kFold = (P & 1) != 0;
+  __shared__ float wmax[W];
+  __shared__ int wsum[W];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;  // as rotq128_kernel
+  if (row >= a.M) return;
+  const int pc = static_cast<int>((a.pi_tbl >> (4 * c)) & 15u);
+  const _Float16* src = a.x + row * a.K + 4096 * w + 128 * pc + 8 * g;
+
+  h8 xb[2][4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+      xb[h][kc] = *reinterpret_cast<const h8*>(src + 2048 * h + 32 * kc);
+  const HFrag f = h128_fragments(lane);
+  f4 acc[2][8];
+  h128_product(f, xb[0], acc[0]);
+  h128_product(f, xb[1], acc[1]);
+  float y[64];  // y[32 h + 4 mb + i]
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[32 * h + 4 * mb + i] = acc[h][mb][i];
+
+  // The stages across sub-blocks.  The first one after the products is
+  // ordinary code, which waits on the matrix results; the inline asm after it
+  // reads registers that ordinary VALU code wrote.
+  const int sel = static_cast<int>((a.sel_tbl >> (4 * c)) & 15u);
+  if constexpr (P == 5) {
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float t = y[k] + y[32 + k];
+      y[32 + k] = y[k] - y[32 + k];
+      y[k] = t;
+    }
+    lane_stage<0>(y, sel);
+  } else {
+    const float sg = (sel & 1) ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < 64; ++k)
+      y[k] = __builtin_fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[k]), 0xB1, 0xF, 0xF, true)),
+                            sg, y[k]);  // quad_perm [1,0,3,2]: lane ^ 1
+  }
+  if constexpr (kLaneStages > 1) lane_stage<1>(y, sel);
+  if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
+  if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
+
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) m = fmaxf(m, fabsf(y[k]));
+  m = row_max<W>(m, wmax, lane, w);
+
+  // The quantizer of rotq128_kernel.  A lane holds its values times sgn; with
+  // the divisor and its reciprocal times sgn too, every step below gives the
+  // same float as on the unsigned value (rounding is symmetric), so q is the
+  // quotient of the true value.
+  const float amax = m * a.rs;
+  const float s = __fdiv_rn(amax, 7.0f);
+  if (threadIdx.x == 0) a.scale[row] = s;
+  const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
+  const float sd = (kFold ? s * a.sqrt_b : s) * sgn;
+  const float rc = s == 0.f ? 0.f : __frcp_rn(sd);
+  const int rin = static_cast<int>(row & 15);
+  int os = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float cm[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xt = kFold ? y[32 * h + 4 * mb + i] : y[32 * h + 4 * mb + i] * a.rs;
+        float q = xt * rc;
+        q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
+        q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
+        cm[mb][i] = OUT == OUT_F6 ? __builtin_rintf(q) : q + kMagic;
+      }
+    const int64_t blk = (row >> 4) * a.tile_stride + 32 * w + 16 * h + c;  // sub-block 32 w + 16 h + c
+    os += store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, rin);
+  }
+  if constexpr (OUT == OUT_PACKED_OB) {
+    const int tot = row_sum<W>(os, wsum, lane, w);
+    if (threadIdx.x == 0) a.ob_sum[row] = tot;
+  }
+}
+
+int parity(int v) { return __builtin_popcount(static_cast<unsigned>(v)) & 1; }
+
+// Load permutation, per-stage signs and final signs of the lane stages with
+// partner masks 1, 2, 7, 8 (the first `stages` of them, which span the low
+// `stages` bits of the column index).
+void kron_tables(int stages, RotArgs* a) {
+  static constexpr int kMask[4] = {1, 2, 7, 8};
+  const int n = 1 << stages;
+  int coord[16] = {};
+  for (int v = 0; v < n; ++v) {
+    int i = 0;
+    for (int s = 0; s < stages; ++s)
+      if ((v >> s) & 1) i ^= kMask[s];
+    coord[i] = v;  // the masks are a basis of [0, n), so each i is hit once
+  }
+  a->pi_tbl = a->sel_tbl = 0;
+  a->sig_tbl = 0;
+  for (int c = 0; c < 16; ++c) {
+    const int lo = c & (n - 1), hi = c & ~(n - 1);
+    int pj = 0;
+    for (int j = 0; j < n; ++j) {  // (-1)^(coord(i).coord(lo)) = (-1)^(i.j) for every i
+      bool ok = true;
+      for (int i = 0; i < n && ok; ++i) ok = parity(coord[i] & coord[lo]) == parity(i & j);
+      if (ok) {
+        pj = j;
+        break;
+      }
+    }
+    a->pi_tbl |= static_cast<uint64_t>(hi | pj) << (4 * c);
+    a->sel_tbl |= static_cast<uint64_t>(coord[lo]) << (4 * c);
+    a->sig_tbl |= static_cast<uint32_t>(parity(coord[lo])) << c;
+  }
+}
+
+RotArgs base_args(const _Float16* x, int64_t M, int64_t K, int log2b, uint8_t* q, float* scale,
+                  int32_t* ob_sum) {
+  RotArgs a{};
+  a.x = x;
+  a.M = M;
+  a.K = K;
+  a.rs = static_cast<float>(1.0 / __builtin_sqrt(static_cast<double>(int64_t{1} << log2b)));
+  a.sqrt_b = static_cast<float>(int64_t{1} << (log2b / 2));
+  a.q = q;
+  a.scale = scale;
+  a.ob_sum = ob_sum;
+  a.tile_stride = K / 128;
+  a.rows_per_xcd = ((M + 15) / 16 + 7) / 8 * 16;
+  return a;
 }
 
 }  // namespace
@@ -229,16 +477,7 @@ bool rotq128_ok(int64_t M, int64_t K) {
 
 hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint8_t* q,
                           float* scale, int32_t* ob_sum, hipStream_t st) {
-  Rot128Args a;
-  a.x = x;
-  a.M = M;
-  a.K = K;
-  a.rs = static_cast<float>(1.0 / __builtin_sqrt(128.0));
-  a.q = q;
-  a.scale = scale;
-  a.ob_sum = ob_sum;
-  a.tile_stride = K / 128;
-  a.rows_per_xcd = ((M + 15) / 16 + 7) / 8 * 16;
+  const RotArgs a = base_args(x, M, K, 7, q, scale, ob_sum);
   const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
   const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
   switch (K / 2048) {
@@ -257,6 +496,45 @@ hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint
     default:
       return hipErrorInvalidValue;
   }
+}
+
+bool rotq_kron_ok(int64_t M, int64_t K, int log2b) {
+  return M > 64 && K % 4096 == 0 && K >= 4096 && K <= 16384 && log2b >= 8 && log2b <= 12;
+}
+
+hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
+                            uint8_t* q, float* scale, int32_t* ob_sum, hipStream_t st) {
+  if (!rotq_kron_ok(M, K, log2b)) return hipErrorInvalidValue;
+  RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
+  const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
+  kron_tables(p < 4 ? p : 4, &a);
+  const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
+  const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
+#define W4A4_KRON(WW, OO)                                                                          \
+  switch (p) {                                                                                     \
+    case 1: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 1>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 2: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 2>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 3: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 3>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 4: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 4>), grid, dim3(64 * WW), 0, st, a); break; \
+    default: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 5>), grid, dim3(64 * WW), 0, st, a); break; \
+  }                                                                                                \
+  return hipGetLastError();
+#define W4A4_KRON_W(WW)                        \
+  case WW:                                     \
+    if (out == OUT_F6) {                       \
+      W4A4_KRON(WW, OUT_F6)                    \
+    } else if (out == OUT_PACKED) {            \
+      W4A4_KRON(WW, OUT_PACKED)                \
+    } else {                                   \
+      W4A4_KRON(WW, OUT_PACKED_OB)             \
+    }
+  switch (K / 4096) {
+    W4A4_KRON_W(1) W4A4_KRON_W(2) W4A4_KRON_W(3) W4A4_KRON_W(4)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef W4A4_KRON_W
+#undef W4A4_KRON
 }
 
 }  // namespace w4a4

@@ -141,14 +141,6 @@ hipError_t launch_qgemm(const GemmArgs& a, hipStream_t st);
 // sx, sw, y, acc, the low-rank term and group as in GemmArgs.
 hipError_t launch_qgemm_f6(const GemmArgs& a, hipStream_t st);
 
-// Rotation with b = 128 on the fp16 matrix instruction, quantized with one
-// float32 scale per row (fp16 x, more than 64 rows, K a multiple of 2048 up
-// to 16384) into FP6 tiles (f6) or packed tiles (offset-binary, with the row
-// sums, when ob_sum is given).
-bool rotq128_ok(int64_t M, int64_t K);
-hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint8_t* q,
-                          float* scale, int32_t* ob_sum, hipStream_t st);
-
 // ---- the layer (api.cpp) ----------------------------------------------------
 // w4a4_qlinear_forward (qmax 7) and w4a8_qlinear_forward (qmax 127) with the
 // given workspace: validation, planning and launches; returns a w4a4_status.

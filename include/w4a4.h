@@ -141,7 +141,8 @@ typedef enum {
  * §1-2), each stored as the FP6 E2M3 number of equal value (OCP
  * microscaling formats: sign bit 5, exponent bits 4:3 with bias 1, mantissa
  * bits 2:0; every integer in [-7, 7] is exact, e.g. 3 = 0b010100 and
- * -7 = 0b111110).  They are the operand format of the gfx950 FP6 matrix
+ * -7 = 0b111110; code 0 may be stored as either zero, 0b000000 or
+ * 0b100000).  They are the operand format of the gfx950 FP6 matrix
  * instruction, whose float32 sums of these products are exact integers, so
  * the GEMM takes them with no conversion; they cost 6 bits per code instead
  * of 4.  Rows in blocks of 16, K (a multiple of 128) in steps of 128; tile

@@ -60,12 +60,17 @@ def test_quantize_act_f6_exact(M, K, b, dt):
     assert np.array_equal(untile_f6(host(xq), M, K), pc)
 
 
-@pytest.mark.parametrize("M,K,b", [(130, 4096, 4096), (37, 4096, 4096), (9, 14336, 128),
-                                   (300, 1024, 256), (60, 4096, 128)])
-def test_quantize_act_f6_fused_matches_packed(M, K, b):
-    w = synth.small("qf6f", M, K, 8, n_outlier=3, bos_factor=500.0)
+@pytest.mark.parametrize("M,K,b,dt", [(130, 4096, 4096, "float32"), (37, 4096, 4096, "float16"),
+                                      (9, 14336, 128, "float16"), (300, 1024, 256, "float16"),
+                                      (60, 4096, 128, "float16")])
+def test_quantize_act_f6_fused_matches_packed(M, K, b, dt):
+    # The butterfly kernel's FP6 mode against its packed mode.  (fp16 rows,
+    # more than 64 of them, with b = 128 or with K a multiple of 4096 take the
+    # matrix-instruction rotation instead: test_gpu_rot_kron.py and the b = 128
+    # test below.)
+    w = synth.small("qf6f", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
     Xd = dev(synth.make_inputs(w)["X"])
-    print("quantize_act f6 fused", M, K, b, flush=True)
+    print("quantize_act f6 fused", M, K, b, dt, flush=True)
     xf, sf = W.quantize_act_int4(Xd, b, layout="f6_tiled")
     xp, sp = W.quantize_act_int4(Xd, b, layout="packed")
     assert np.array_equal(host(sf), host(sp))
