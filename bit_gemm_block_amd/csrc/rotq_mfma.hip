@@ -77,6 +77,7 @@ struct RotArgs {
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
   int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
+  int64_t rows_per_wg;   // rotq_kron_kernel: rows per workgroup
   uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
   uint64_t sel_tbl;   // 4 bits per column: bit s is the column's sign at lane stage s
   uint32_t sig_tbl;   // bit c: column c holds its outputs negated after the stages
@@ -285,7 +286,7 @@ __global__ void __launch_bounds__(64 * W, 2) rotq128_kernel(RotArgs a) {
   }
 }
 
-// One lane stage over the 64 values: v += sgn * v[lane ^ mask] within each
+// One lane stage over the 32 values: v += sgn * v[lane ^ mask] within each
 // 16-lane row.  Inline asm, since the compiler splits the permuted operand into
 // a separate move; the s_nop covers the two wait states that a permuted read
 // needs after the VALU write of its register.
@@ -304,10 +305,10 @@ __global__ void __launch_bounds__(64 * W, 2) rotq128_kernel(RotArgs a) {
       : "v"(SG))
 
 template <int S>  // partner masks 1, 2, 7, 8
-__device__ __forceinline__ void lane_stage(float (&y)[64], int sel) {
+__device__ __forceinline__ void lane_stage(float (&y)[32], int sel) {
   const float sg = ((sel >> S) & 1) ? -1.f : 1.f;
 #pragma unroll
-  for (int k = 0; k < 64; k += 8) {
+  for (int k = 0; k < 32; k += 8) {
     float* v = y + k;
     if constexpr (S == 0)
       W4A4_FMAC_DPP8("quad_perm:[1,0,3,2]", v, sg);
@@ -321,101 +322,124 @@ __device__ __forceinline__ void lane_stage(float (&y)[64], int sel) {
 }
 #undef W4A4_FMAC_DPP8
 
-// W waves per row, each taking 4096 elements (K = 4096 W); b = 128 * 2^P.
-// (At least two waves per SIMD: the register cap keeps the accumulators out of
-// the AGPRs, which would take a copy per value.)
-template <int W, int OUT, int P>
-__global__ void __launch_bounds__(64 * W, 2) rotq_kron_kernel(RotArgs a) {
+// WV waves per row, each taking one chain of 16 sub-blocks, 2048 elements
+// (K = 2048 WV); b = 128 * 2^P.  For b = 4096 the sub-block bit 4 pairs waves
+// 2 v and 2 v + 1, which exchange their products through LDS.  A workgroup
+// takes rows_per_wg consecutive rows and loads the next row as soon as the
+// products of the current one have read their operands, so that its loads
+// overlap the current row's stages, quantizer and stores.  (At least two waves
+// per SIMD: the register cap keeps the accumulators out of the AGPRs, which
+// would take a copy per value.)
+template <int WV, int OUT, int P>
+__global__ void __launch_bounds__(64 * WV, 2) rotq_kron_kernel(RotArgs a) {
   constexpr int kLaneStages = P < 4 ? P : 4;
+  constexpr bool kPair = P == 5;
   // sqrt(b) a power of two: x~ / s = y / (s sqrt(b)) with both sides exact.
   constexpr bool kFold = (P & 1) != 0;
-  __shared__ float wmax[W];
-  __shared__ int wsum[W];
+  __shared__ float wmax[2][WV];  // by row parity: one barrier per row suffices
+  __shared__ int wsum[2][WV];
+  // The products of each wave for the pair exchange.  One buffer: the absmax
+  // barrier of a row separates its reads from the next row's writes.
+  __shared__ f4 exch[kPair ? WV * 8 * 64 : 1];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;  // as rotq128_kernel
-  if (row >= a.M) return;
+  // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
+  // whole 16-row blocks (as rotq128_kernel), and each of its workgroups a run
+  // of rows_per_wg rows inside that range.
+  const int64_t xcd_first = (blockIdx.x % 8) * a.rows_per_xcd;
+  const int64_t first = xcd_first + (blockIdx.x / 8) * a.rows_per_wg;
+  int64_t end = first + a.rows_per_wg;
+  if (end > xcd_first + a.rows_per_xcd) end = xcd_first + a.rows_per_xcd;
+  if (end > a.M) end = a.M;
+  if (first >= end) return;
   const int pc = static_cast<int>((a.pi_tbl >> (4 * c)) & 15u);
-  const _Float16* src = a.x + row * a.K + 4096 * w + 128 * pc + 8 * g;
+  const int64_t lane_off = 2048 * w + 128 * pc + 8 * g;
 
-  h8 xb[2][4];
+  h8 xb[4];
+  auto load_row = [&](int64_t r) {
+    const _Float16* src = a.x + r * a.K + lane_off;
 #pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-      xb[h][kc] = *reinterpret_cast<const h8*>(src + 2048 * h + 32 * kc);
+    for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
+  };
+  load_row(first);
   const HFrag f = h128_fragments(lane);
-  f4 acc[2][8];
-  h128_product(f, xb[0], acc[0]);
-  h128_product(f, xb[1], acc[1]);
-  float y[64];  // y[32 h + 4 mb + i]
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[32 * h + 4 * mb + i] = acc[h][mb][i];
-
-  // The stages across sub-blocks.  The first one after the products is
-  // ordinary code, which waits on the matrix results; the inline asm after it
-  // reads registers that ordinary VALU code wrote.
   const int sel = static_cast<int>((a.sel_tbl >> (4 * c)) & 15u);
-  if constexpr (P == 5) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float t = y[k] + y[32 + k];
-      y[32 + k] = y[k] - y[32 + k];
-      y[k] = t;
-    }
-    lane_stage<0>(y, sel);
-  } else {
-    const float sg = (sel & 1) ? -1.f : 1.f;
-#pragma unroll
-    for (int k = 0; k < 64; ++k)
-      y[k] = __builtin_fmaf(__int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(y[k]), 0xB1, 0xF, 0xF, true)),
-                            sg, y[k]);  // quad_perm [1,0,3,2]: lane ^ 1
-  }
-  if constexpr (kLaneStages > 1) lane_stage<1>(y, sel);
-  if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
-  if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
-
-  float m = 0.f;
-#pragma unroll
-  for (int k = 0; k < 64; ++k) m = fmaxf(m, fabsf(y[k]));
-  m = row_max<W>(m, wmax, lane, w);
-
-  // The quantizer of rotq128_kernel.  A lane holds its values times sgn; with
-  // the divisor and its reciprocal times sgn too, every step below gives the
-  // same float as on the unsigned value (rounding is symmetric), so q is the
-  // quotient of the true value.
-  const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, 7.0f);
-  if (threadIdx.x == 0) a.scale[row] = s;
   const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
-  const float sd = (kFold ? s * a.sqrt_b : s) * sgn;
-  const float rc = s == 0.f ? 0.f : __frcp_rn(sd);
-  const int rin = static_cast<int>(row & 15);
-  int os = 0;
+
+  for (int64_t row = first; row < end; ++row) {
+    const int par = static_cast<int>((row - first) & 1);
+    f4 acc[8];
+    h128_product(f, xb, acc);
+    if (row + 1 < end) load_row(row + 1);
+    float y[32];  // y[4 mb + i]
+
+    // The stages across sub-blocks.  The first one after the products is
+    // ordinary code, which waits on the matrix results; the inline asm after
+    // it reads registers that ordinary VALU code wrote.
+    if constexpr (kPair) {
+      // bit 4: the even wave of the pair takes the sum, the odd one the
+      // difference (even minus odd): own * (+-1) + other
+      const float so = (w & 1) ? -1.f : 1.f;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+      for (int mb = 0; mb < 8; ++mb) exch[(w * 8 + mb) * 64 + lane] = acc[mb];
+      __syncthreads();
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const f4 o = exch[((w ^ 1) * 8 + mb) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[4 * mb + i] = __builtin_fmaf(acc[mb][i], so, o[i]);
+      }
+      lane_stage<0>(y, sel);
+    } else {
+      const float sg = (sel & 1) ? -1.f : 1.f;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = acc[mb][i];
+          y[4 * mb + i] = __builtin_fmaf(
+              __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)), sg,
+              v);  // quad_perm [1,0,3,2]: lane ^ 1
+        }
+    }
+    if constexpr (kLaneStages > 1) lane_stage<1>(y, sel);
+    if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
+    if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
+
+    float m = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(y[k]));
+    m = row_max<WV>(m, wmax[par], lane, w);
+
+    // Scale as in rotq128_kernel; each code is x~ * RN(1 / s) rounded once to
+    // an integer (one fma with 1.5 * 2^23, the same instruction for every
+    // layout), without the refinement to the correctly rounded quotient: the
+    // exact product is within one unit in the last place of the quotient
+    // (|q| < 8), below the float32 rounding that the transform's own sums
+    // leave in x~, and the quantizer takes one or two instructions per value
+    // instead of six.  |q| < 7 (1 + 2^-23), so no clamp.  A lane holds its
+    // values times sgn; the reciprocal times sgn takes it out (exactly:
+    // rounding is symmetric).
+    const float amax = m * a.rs;
+    const float s = __fdiv_rn(amax, 7.0f);
+    if (threadIdx.x == 0) a.scale[row] = s;
+    const float rc = s == 0.f ? 0.f : __frcp_rn((kFold ? s * a.sqrt_b : s) * sgn);
     float cm[8][4];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float xt = kFold ? y[32 * h + 4 * mb + i] : y[32 * h + 4 * mb + i] * a.rs;
-        float q = xt * rc;
-        q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
-        q = __builtin_fmaf(__builtin_fmaf(-q, sd, xt), rc, q);
-        cm[mb][i] = OUT == OUT_F6 ? __builtin_rintf(q) : q + kMagic;
+        const float xt = kFold ? y[4 * mb + i] : y[4 * mb + i] * a.rs;
+        const float t = __builtin_fmaf(xt, rc, kMagic);  // 1.5 * 2^23 + code
+        cm[mb][i] = OUT == OUT_F6 ? t - kMagic : t;
       }
-    const int64_t blk = (row >> 4) * a.tile_stride + 32 * w + 16 * h + c;  // sub-block 32 w + 16 h + c
-    os += store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, rin);
-  }
-  if constexpr (OUT == OUT_PACKED_OB) {
-    const int tot = row_sum<W>(os, wsum, lane, w);
-    if (threadIdx.x == 0) a.ob_sum[row] = tot;
+    const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // sub-block 16 w + c
+    const int os = store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, static_cast<int>(row & 15));
+    if constexpr (OUT == OUT_PACKED_OB) {
+      const int tot = row_sum<WV>(os, wsum[par], lane, w);
+      if (threadIdx.x == 0) a.ob_sum[row] = tot;
+    }
   }
 }
 
@@ -498,8 +522,16 @@ hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint
   }
 }
 
+// Four resident waves per SIMD: at 2048 rows of K = 4096 every wave takes half
+// of one row and all loads are in flight at once.  (Two waves per SIMD, each
+// taking half of two rows with the second row's loads overlapping the first
+// row's work, were slower: the VALU work after the loads, not the loads, sets
+// the time, and four waves hide its dependency stalls better.)
+constexpr int kKronWavesPerSimd = 4;
+
 bool rotq_kron_ok(int64_t M, int64_t K, int log2b) {
-  return M > 64 && K % 4096 == 0 && K >= 4096 && K <= 16384 && log2b >= 8 && log2b <= 12;
+  const int64_t step = log2b == 12 ? 4096 : 2048;
+  return M > 64 && K % step == 0 && K >= step && K <= 16384 && log2b >= 8 && log2b <= 12;
 }
 
 hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
@@ -508,7 +540,13 @@ hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, 
   RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
   const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
   kron_tables(p < 4 ? p : 4, &a);
-  const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
+  const int WV = static_cast<int>(K / 2048);
+  // Workgroups per XCD for kKronWavesPerSimd waves on each of its 128 SIMDs;
+  // each takes an equal run of the XCD's rows.
+  const int64_t wg_target = 128 * kKronWavesPerSimd / WV;
+  a.rows_per_wg = (a.rows_per_xcd + wg_target - 1) / wg_target;
+  const int64_t wg_per_xcd = (a.rows_per_xcd + a.rows_per_wg - 1) / a.rows_per_wg;
+  const dim3 grid(static_cast<unsigned>(8 * wg_per_xcd));
   const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
 #define W4A4_KRON(WW, OO)                                                                          \
   switch (p) {                                                                                     \
@@ -516,7 +554,12 @@ hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, 
     case 2: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 2>), grid, dim3(64 * WW), 0, st, a); break; \
     case 3: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 3>), grid, dim3(64 * WW), 0, st, a); break; \
     case 4: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 4>), grid, dim3(64 * WW), 0, st, a); break; \
-    default: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 5>), grid, dim3(64 * WW), 0, st, a); break; \
+    default:                                                                                       \
+      if constexpr (WW % 2 == 0)                                                                   \
+        hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 5>), grid, dim3(64 * WW), 0, st, a);          \
+      else                                                                                         \
+        return hipErrorInvalidValue;                                                               \
+      break;                                                                                       \
   }                                                                                                \
   return hipGetLastError();
 #define W4A4_KRON_W(WW)                        \
@@ -528,8 +571,9 @@ hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, 
     } else {                                   \
       W4A4_KRON(WW, OUT_PACKED_OB)             \
     }
-  switch (K / 4096) {
-    W4A4_KRON_W(1) W4A4_KRON_W(2) W4A4_KRON_W(3) W4A4_KRON_W(4)
+  switch (WV) {
+    W4A4_KRON_W(1) W4A4_KRON_W(2) W4A4_KRON_W(3) W4A4_KRON_W(4) W4A4_KRON_W(5) W4A4_KRON_W(6)
+    W4A4_KRON_W(7) W4A4_KRON_W(8)
     default:
       return hipErrorInvalidValue;
   }

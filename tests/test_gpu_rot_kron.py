@@ -82,8 +82,9 @@ def test_quantize_act_kron_matrix_rotation(M, K, b, layout):
 
 def test_quantize_act_kron_zero_and_constant_rows():
     # An all-zero row takes scale 0 and codes 0; a row with one non-zero
-    # element rotates to +-v / 64 everywhere (codes +-7 exactly, no rounding
-    # near a tie), so any sign slip in the stages shows as a flipped code.
+    # element rotates to +-v / 64 everywhere (codes +-7: the product with the
+    # reciprocal of the scale is within 2^-21 of 7, far from a tie), so any
+    # sign slip in the stages shows as a flipped code.
     M, K, b = 96, 4096, 4096
     X = np.zeros((M, K), np.float16)
     rng = np.random.default_rng(5)
