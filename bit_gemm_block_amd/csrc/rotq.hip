@@ -896,7 +896,7 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
                        const RotqPlan& plan, hipStream_t st, const RotqExtras* ex) {
   // Tiled 4-bit codes (FP6, or packed plain or offset-binary) of fp16 rows
   // with one float32 scale per row: the transform on the matrix instruction
-  // (rotq_mfma.hip), for b = 128 and for 256 <= b <= 4096.
+  // (rotq_mfma.hip), for 128 <= b <= 4096.
   const bool plain_ex = !ex || (ex->qmax == 7 && !ex->asym_zero && ex->res_r == 0 && !ex->mx_scale &&
                                 ex->lr_rank == 0 && !ex->pf);
   const bool tiled4 = mode == ROTQ_QUANT_F6 || mode == ROTQ_QUANT_TILED;
@@ -904,10 +904,8 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
     const _Float16* xh = static_cast<const _Float16*>(x);
     float* sf = static_cast<float*>(scale);
     int32_t* ob = ex ? ex->ob_sum : nullptr;
-    if (log2b == 7 && rotq128_ok(M, K))
-      return launch_rotq128(xh, M, K, mode == ROTQ_QUANT_F6, q, sf, ob, st);
-    if (rotq_kron_ok(M, K, log2b))
-      return launch_rotq_kron(xh, M, K, log2b, mode == ROTQ_QUANT_F6, q, sf, ob, st);
+    if (rotq_mfma_ok(M, K, log2b))
+      return launch_rotq_mfma(xh, M, K, log2b, mode == ROTQ_QUANT_F6, q, sf, ob, st);
   }
   RotqKArgs ka{};
   ka.x = x;

@@ -11,15 +11,11 @@
 
 namespace w4a4 {
 
-// b = 128: K a multiple of 2048 up to 16384.
-bool rotq128_ok(int64_t M, int64_t K);
-hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint8_t* q,
-                          float* scale, int32_t* ob_sum, hipStream_t st);
-
-// b = 2^log2b with 256 <= b <= 4096 (the transform of 16 sub-blocks of 128,
-// then the Kronecker factor across them): K a multiple of 4096 up to 16384.
-bool rotq_kron_ok(int64_t M, int64_t K, int log2b);
-hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
+// b = 2^log2b with 128 <= b <= 4096 (the transform of 16 sub-blocks of 128
+// at a time, then for b > 128 the Kronecker factor across them): K a multiple
+// of 2048 (of 4096 for b = 4096) up to 16384.
+bool rotq_mfma_ok(int64_t M, int64_t K, int log2b);
+hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
                             uint8_t* q, float* scale, int32_t* ob_sum, hipStream_t st);
 
 }  // namespace w4a4

@@ -1,23 +1,17 @@
-// rotq_mfma.hip — block Hadamard rotation with b = 128 on the fp16 matrix
-// instruction, fused with per-token absmax int4 quantization into the tiled
-// code layouts of the layer: FP6 E2M3 tiles, or packed nibble tiles (plain or
-// offset-binary, with the row sums of the odd channels' codes) (SERQ page,
-// "Resumen técnico" §1-2: rotate, then quantize each token on the fly).
+// rotq_mfma.hip — block Hadamard rotation (128 <= b <= 4096) on the fp16
+// matrix instruction, fused with per-token absmax int4 quantization into the
+// tiled code layouts of the layer: FP6 E2M3 tiles, or packed nibble tiles
+// (plain or offset-binary, with the row sums of the odd channels' codes)
+// (SERQ page, "Resumen técnico" §1-2: rotate, then quantize each token on the
+// fly).
 //
-// With b = 128 the rotation of a row is 128-point transforms of its blocks,
-// y_c = H x_c (H the Sylvester matrix, entries +-1).  Sixteen blocks at a
-// time are one product H [128 x 128] . X^T [128 x 16] of exact fp16 operands
-// (fp16 X, H = +-1) with float32 accumulation, 32 instructions of
-// v_mfma_f32_16x16x32_f16, where the butterflies would take 7 VALU
-// instructions per element.  Everything after the transform is the
-// quantizer of the butterfly kernel: x~ = RN(y / sqrt(b)) as y * rs,
-// s = RN(max|x~| / 7), each code rint of the correctly rounded quotient
-// x~ / s (reciprocal plus two refinement steps; exact for every scale fp16
-// input can produce), so the two kernels differ only where the float32
-// sums of the transform round differently.
-//
-// A workgroup takes one row; wave w takes its elements [2048 w, 2048 w + 2048)
-// as sixteen blocks c of 128:
+// The 128-point part: the rotation of 16 blocks of 128 is one product
+// H [128 x 128] . X^T [128 x 16] of exact fp16 operands (fp16 X, H = +-1, the
+// Sylvester matrix) with float32 accumulation, 32 instructions of
+// v_mfma_f32_16x16x32_f16 (22 after the compiler shares chain prefixes),
+// where butterflies would take 7 VALU instructions per element.  Wave w of
+// a row's workgroup takes its elements [2048 w, 2048 w + 2048) as sixteen
+// blocks c of 128:
 //   * operand B of K-step kc: lane 16 g + c holds x[128 c + 32 kc + 8 g, +8)
 //     (one 16-byte load);
 //   * operand A of output block mb, K-step kc: lane 16 g + r holds
@@ -27,33 +21,35 @@
 //     mb1 & kc0, mb2 & kc1 (bits 5-6), so A = +-(mb0 ? F1 : F0) with F0, F1
 //     built once per lane;
 //   * output: lane 16 g + c holds y_c[16 mb + 4 g + i'], i' < 4.
-// The row's absmax is reduced over lanes and waves.  For the tiles, lane
-// 16 j + c must hold the 32 consecutive codes [32 j, 32 j + 32) of block c,
-// which lane groups g = 0..3 hold 8 each (mb = 2 j, 2 j + 1): a 4 x 4
-// transpose of 8-value units across the lane groups, by v_permlane32_swap
-// (lane groups 0,1 <-> 2,3) then v_permlane16_swap (0 <-> 1, 2 <-> 3).
 //
-// Larger blocks, b = 128 n with n = 2^P sub-blocks of 128 (2 <= n <= 32):
+// Larger blocks, b = 128 n with n = 2^P sub-blocks (2 <= n <= 32):
 // Sylvester's construction gives H_b = H_n (x) H_128 (entry
 // (128 j + e, 128 j' + e') is (-1)^(j.j') (-1)^(e.e')), so the rotation is the
-// transform of every sub-block of 128, then the n-point transform across the
-// sub-blocks at each of the 128 positions.  A wave takes 4096 elements of the
-// row, 32 sub-blocks, as two chains h of the product above (sub-block
-// 16 h + c in lane column c).  The transform across sub-blocks has one bit in
-// the registers (the chain, for n = 32) and up to four in the lane column.
-// A lane stage is one v_fmac_f32_dpp per value, v += sgn * v[partner], the
-// partner read through a lane permutation within each 16-lane row: xor 1 and
-// xor 2 (quad permutations), xor 7 (half-row mirror), xor 8 (row rotation by
-// 8).  (A uniform add or subtract gives both lanes of a pair the same linear
-// form of their two values; the per-lane sign gives the low lane the sum and
-// the high lane the difference, negated.)  With partner masks 1, 2, 7, 8 the
-// stages are the Walsh-Hadamard butterflies in the coordinates of the column
-// index over the basis {1, 2, 7, 8}: a lane's sign at stage s is its s-th
-// coordinate, the product is H_16 with its columns permuted by the Gram matrix
-// of the basis, and loading sub-block pi(c) into column c undoes that
-// permutation.  At the end a lane holds its outputs times (-1)^(sum of its
-// coordinates); the quantizer puts that sign back into the codes.  The host
-// derives pi, the coordinates and the final signs from the four masks.
+// 128-point transform of every sub-block, then the n-point transform across
+// the sub-blocks at each of the 128 positions.  Sub-block bits 0-3 lie in the
+// lane column; for n = 32, bit 4 pairs waves 2 v and 2 v + 1, which exchange
+// their products through LDS.  A lane stage is one v_fmac_f32_dpp per value,
+// v += sgn * v[partner], the partner read through a lane permutation within
+// each 16-lane row: xor 1 and xor 2 (quad permutations), xor 7 (half-row
+// mirror), xor 8 (row rotation by 8).  (A uniform add or subtract gives both
+// lanes of a pair the same linear form of their two values; the per-lane sign
+// gives the low lane the sum and the high lane the difference, negated.)
+// With partner masks 1, 2, 7, 8 the stages are the Walsh-Hadamard butterflies
+// in the coordinates of the column index over the basis {1, 2, 7, 8}: a
+// lane's sign at stage s is its s-th coordinate, the product is H_16 with its
+// columns permuted by the Gram matrix of the basis, and loading sub-block
+// pi(c) into column c undoes that permutation.  At the end a lane holds its
+// outputs times (-1)^(sum of its coordinates); the quantizer takes that sign
+// back out.  The host derives pi, the coordinates and the final signs from
+// the four masks.
+//
+// Then x~ = RN(y / sqrt(b)) as y * rs, s = RN(max|x~| / 7), and each code is
+// x~ * RN(1 / s) rounded once to an integer.  The row's absmax is reduced
+// over lanes and waves.  For the tiles, lane 16 j + c must hold the 32
+// consecutive codes [32 j, 32 j + 32) of block c, which lane groups
+// g = 0..3 hold 8 each (mb = 2 j, 2 j + 1): a 4 x 4 transpose of 8-value
+// units across the lane groups, by v_permlane32_swap (lane groups 0,1 <->
+// 2,3) then v_permlane16_swap (0 <-> 1, 2 <-> 3).
 #include "rotq_mfma.h"
 
 #include <hip/hip_fp16.h>
@@ -77,7 +73,6 @@ struct RotArgs {
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
   int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
-  int64_t rows_per_wg;   // rotq_kron_kernel: rows per workgroup
   uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
   uint64_t sel_tbl;   // 4 bits per column: bit s is the column's sign at lane stage s
   uint32_t sig_tbl;   // bit c: column c holds its outputs negated after the stages
@@ -232,60 +227,6 @@ __device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* til
   }
 }
 
-template <int W, int OUT>  // W waves per row: K = 2048 W
-__global__ void __launch_bounds__(64 * W, 2) rotq128_kernel(RotArgs a) {
-  __shared__ float wmax[W];
-  __shared__ int wsum[W];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
-  // whole 16-row blocks, so that every line of a code tile is written from
-  // one L2.
-  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
-  if (row >= a.M) return;
-  const _Float16* src = a.x + row * a.K + 2048 * w + 128 * c + 8 * g;
-
-  h8 xb[4];
-#pragma unroll
-  for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
-  f4 acc[8];
-  h128_product(h128_fragments(lane), xb, acc);
-
-  // Row absmax of y (x~ = RN(y rs) is monotone in |y|).
-  float m = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(acc[mb][i]));
-  m = row_max<W>(m, wmax, lane, w);
-
-  // Scale and codes, as the butterfly kernel's quantizer (fp16 input keeps
-  // every scale inside the range where the refined reciprocal is exact).
-  const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, 7.0f);
-  if (threadIdx.x == 0) a.scale[row] = s;
-  const float rc = s == 0.f ? 0.f : __frcp_rn(s);
-  float cm[8][4];
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float xt = acc[mb][i] * a.rs;
-      float q = xt * rc;
-      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
-      q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
-      cm[mb][i] = OUT == OUT_F6 ? __builtin_rintf(q) : q + kMagic;
-    }
-
-  const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // tile of block 16 w + c
-  const int os = store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, static_cast<int>(row & 15));
-  if constexpr (OUT == OUT_PACKED_OB) {
-    const int tot = row_sum<W>(os, wsum, lane, w);
-    if (threadIdx.x == 0) a.ob_sum[row] = tot;
-  }
-}
-
 // One lane stage over the 32 values: v += sgn * v[lane ^ mask] within each
 // 16-lane row.  Inline asm, since the compiler splits the permuted operand into
 // a separate move; the s_nop covers the two wait states that a permuted read
@@ -323,123 +264,110 @@ __device__ __forceinline__ void lane_stage(float (&y)[32], int sel) {
 #undef W4A4_FMAC_DPP8
 
 // WV waves per row, each taking one chain of 16 sub-blocks, 2048 elements
-// (K = 2048 WV); b = 128 * 2^P.  For b = 4096 the sub-block bit 4 pairs waves
-// 2 v and 2 v + 1, which exchange their products through LDS.  A workgroup
-// takes rows_per_wg consecutive rows and loads the next row as soon as the
-// products of the current one have read their operands, so that its loads
-// overlap the current row's stages, quantizer and stores.  (At least two waves
-// per SIMD: the register cap keeps the accumulators out of the AGPRs, which
-// would take a copy per value.)
+// (K = 2048 WV); b = 128 * 2^P (P = 0: the 128-point transform alone).  For
+// b = 4096 the sub-block bit 4 pairs waves 2 v and 2 v + 1, which exchange
+// their products through LDS.  One row per workgroup, all rows launched at
+// once.  (At least two waves per SIMD: the register cap keeps the
+// accumulators out of the AGPRs, which would take a copy per value.)
 template <int WV, int OUT, int P>
-__global__ void __launch_bounds__(64 * WV, 2) rotq_kron_kernel(RotArgs a) {
+__global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
   constexpr int kLaneStages = P < 4 ? P : 4;
   constexpr bool kPair = P == 5;
   // sqrt(b) a power of two: x~ / s = y / (s sqrt(b)) with both sides exact.
   constexpr bool kFold = (P & 1) != 0;
-  __shared__ float wmax[2][WV];  // by row parity: one barrier per row suffices
-  __shared__ int wsum[2][WV];
-  // The products of each wave for the pair exchange.  One buffer: the absmax
-  // barrier of a row separates its reads from the next row's writes.
-  __shared__ f4 exch[kPair ? WV * 8 * 64 : 1];
+  __shared__ float wmax[WV];
+  __shared__ int wsum[WV];
+  __shared__ f4 exch[kPair ? WV * 8 * 64 : 1];  // each wave's products, for the pair stage
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
   // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
-  // whole 16-row blocks (as rotq128_kernel), and each of its workgroups a run
-  // of rows_per_wg rows inside that range.
-  const int64_t xcd_first = (blockIdx.x % 8) * a.rows_per_xcd;
-  const int64_t first = xcd_first + (blockIdx.x / 8) * a.rows_per_wg;
-  int64_t end = first + a.rows_per_wg;
-  if (end > xcd_first + a.rows_per_xcd) end = xcd_first + a.rows_per_xcd;
-  if (end > a.M) end = a.M;
-  if (first >= end) return;
+  // whole 16-row blocks, so that every line of a code tile is written from
+  // one L2.
+  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
+  if (row >= a.M) return;
   const int pc = static_cast<int>((a.pi_tbl >> (4 * c)) & 15u);
-  const int64_t lane_off = 2048 * w + 128 * pc + 8 * g;
+  const _Float16* src = a.x + row * a.K + 2048 * w + 128 * pc + 8 * g;
 
   h8 xb[4];
-  auto load_row = [&](int64_t r) {
-    const _Float16* src = a.x + r * a.K + lane_off;
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
-  };
-  load_row(first);
-  const HFrag f = h128_fragments(lane);
+  for (int kc = 0; kc < 4; ++kc) xb[kc] = *reinterpret_cast<const h8*>(src + 32 * kc);
+  f4 acc[8];
+  h128_product(h128_fragments(lane), xb, acc);
   const int sel = static_cast<int>((a.sel_tbl >> (4 * c)) & 15u);
-  const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
+  float y[32];  // y[4 mb + i]
 
-  for (int64_t row = first; row < end; ++row) {
-    const int par = static_cast<int>((row - first) & 1);
-    f4 acc[8];
-    h128_product(f, xb, acc);
-    if (row + 1 < end) load_row(row + 1);
-    float y[32];  // y[4 mb + i]
-
-    // The stages across sub-blocks.  The first one after the products is
-    // ordinary code, which waits on the matrix results; the inline asm after
-    // it reads registers that ordinary VALU code wrote.
-    if constexpr (kPair) {
-      // bit 4: the even wave of the pair takes the sum, the odd one the
-      // difference (even minus odd): own * (+-1) + other
-      const float so = (w & 1) ? -1.f : 1.f;
+  // The stages across sub-blocks.  The first one after the products is
+  // ordinary code, which waits on the matrix results; the inline asm after it
+  // reads registers that ordinary VALU code wrote.
+  if constexpr (kPair) {
+    // bit 4: the even wave of the pair takes the sum, the odd one the
+    // difference (even minus odd): own * (+-1) + other
+    const float so = (w & 1) ? -1.f : 1.f;
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) exch[(w * 8 + mb) * 64 + lane] = acc[mb];
-      __syncthreads();
+    for (int mb = 0; mb < 8; ++mb) exch[(w * 8 + mb) * 64 + lane] = acc[mb];
+    __syncthreads();
 #pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const f4 o = exch[((w ^ 1) * 8 + mb) * 64 + lane];
+    for (int mb = 0; mb < 8; ++mb) {
+      const f4 o = exch[((w ^ 1) * 8 + mb) * 64 + lane];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[4 * mb + i] = __builtin_fmaf(acc[mb][i], so, o[i]);
-      }
-      lane_stage<0>(y, sel);
-    } else {
-      const float sg = (sel & 1) ? -1.f : 1.f;
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[mb][i];
-          y[4 * mb + i] = __builtin_fmaf(
-              __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)), sg,
-              v);  // quad_perm [1,0,3,2]: lane ^ 1
-        }
+      for (int i = 0; i < 4; ++i) y[4 * mb + i] = __builtin_fmaf(acc[mb][i], so, o[i]);
     }
-    if constexpr (kLaneStages > 1) lane_stage<1>(y, sel);
-    if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
-    if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
-
-    float m = 0.f;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(y[k]));
-    m = row_max<WV>(m, wmax[par], lane, w);
-
-    // Scale as in rotq128_kernel; each code is x~ * RN(1 / s) rounded once to
-    // an integer (one fma with 1.5 * 2^23, the same instruction for every
-    // layout), without the refinement to the correctly rounded quotient: the
-    // exact product is within one unit in the last place of the quotient
-    // (|q| < 8), below the float32 rounding that the transform's own sums
-    // leave in x~, and the quantizer takes one or two instructions per value
-    // instead of six.  |q| < 7 (1 + 2^-23), so no clamp.  A lane holds its
-    // values times sgn; the reciprocal times sgn takes it out (exactly:
-    // rounding is symmetric).
-    const float amax = m * a.rs;
-    const float s = __fdiv_rn(amax, 7.0f);
-    if (threadIdx.x == 0) a.scale[row] = s;
-    const float rc = s == 0.f ? 0.f : __frcp_rn((kFold ? s * a.sqrt_b : s) * sgn);
-    float cm[8][4];
+    lane_stage<0>(y, sel);
+  } else if constexpr (P >= 1) {
+    const float sg = (sel & 1) ? -1.f : 1.f;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float xt = kFold ? y[4 * mb + i] : y[4 * mb + i] * a.rs;
-        const float t = __builtin_fmaf(xt, rc, kMagic);  // 1.5 * 2^23 + code
-        cm[mb][i] = OUT == OUT_F6 ? t - kMagic : t;
+        const float v = acc[mb][i];
+        y[4 * mb + i] = __builtin_fmaf(
+            __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)), sg,
+            v);  // quad_perm [1,0,3,2]: lane ^ 1
       }
-    const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // sub-block 16 w + c
-    const int os = store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, static_cast<int>(row & 15));
-    if constexpr (OUT == OUT_PACKED_OB) {
-      const int tot = row_sum<WV>(os, wsum[par], lane, w);
-      if (threadIdx.x == 0) a.ob_sum[row] = tot;
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) y[4 * mb + i] = acc[mb][i];
+  }
+  if constexpr (kLaneStages > 1) lane_stage<1>(y, sel);
+  if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
+  if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
+
+  float m = 0.f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(y[k]));
+  m = row_max<WV>(m, wmax, lane, w);
+
+  // s = RN(max|x~| / 7) (x~ = RN(y rs) is monotone in |y|); each code is
+  // x~ * RN(1 / s) rounded once to an integer (one fma with 1.5 * 2^23, the
+  // same instruction for every layout), without the refinement to the
+  // correctly rounded quotient: the exact product is within one unit in the
+  // last place of the quotient (|q| < 8), below the float32 rounding that the
+  // transform's own sums leave in x~, and the quantizer takes one or two
+  // instructions per value instead of six.  |q| < 7 (1 + 2^-23), so no clamp.
+  // A lane holds its values times sgn; the reciprocal times sgn takes it out
+  // (exactly: rounding is symmetric).
+  const float amax = m * a.rs;
+  const float s = __fdiv_rn(amax, 7.0f);
+  if (threadIdx.x == 0) a.scale[row] = s;
+  const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
+  const float rc = s == 0.f ? 0.f : __frcp_rn((kFold ? s * a.sqrt_b : s) * sgn);
+  float cm[8][4];
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float xt = kFold ? y[4 * mb + i] : y[4 * mb + i] * a.rs;
+      const float t = __builtin_fmaf(xt, rc, kMagic);  // 1.5 * 2^23 + code
+      cm[mb][i] = OUT == OUT_F6 ? t - kMagic : t;
     }
+  const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // sub-block 16 w + c
+  const int os = store_codes<OUT>(cm, a.q + blk * kTileBytes<OUT>, g, static_cast<int>(row & 15));
+  if constexpr (OUT == OUT_PACKED_OB) {
+    const int tot = row_sum<WV>(os, wsum, lane, w);
+    if (threadIdx.x == 0) a.ob_sum[row] = tot;
   }
 }
 
@@ -495,90 +423,52 @@ RotArgs base_args(const _Float16* x, int64_t M, int64_t K, int log2b, uint8_t* q
 
 }  // namespace
 
-bool rotq128_ok(int64_t M, int64_t K) {
-  return M > 64 && K % 2048 == 0 && K >= 2048 && K <= 16384;
-}
-
-hipError_t launch_rotq128(const _Float16* x, int64_t M, int64_t K, bool f6, uint8_t* q,
-                          float* scale, int32_t* ob_sum, hipStream_t st) {
-  const RotArgs a = base_args(x, M, K, 7, q, scale, ob_sum);
-  const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
-  const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
-  switch (K / 2048) {
-#define W4A4_R128(WW)                                                                        \
-  case WW:                                                                                   \
-    if (out == OUT_F6)                                                                       \
-      hipLaunchKernelGGL((rotq128_kernel<WW, OUT_F6>), grid, dim3(64 * WW), 0, st, a);       \
-    else if (out == OUT_PACKED)                                                              \
-      hipLaunchKernelGGL((rotq128_kernel<WW, OUT_PACKED>), grid, dim3(64 * WW), 0, st, a);   \
-    else                                                                                     \
-      hipLaunchKernelGGL((rotq128_kernel<WW, OUT_PACKED_OB>), grid, dim3(64 * WW), 0, st, a); \
-    return hipGetLastError();
-    W4A4_R128(1) W4A4_R128(2) W4A4_R128(3) W4A4_R128(4) W4A4_R128(5) W4A4_R128(6)
-    W4A4_R128(7) W4A4_R128(8)
-#undef W4A4_R128
-    default:
-      return hipErrorInvalidValue;
-  }
-}
-
-// Four resident waves per SIMD: at 2048 rows of K = 4096 every wave takes half
-// of one row and all loads are in flight at once.  (Two waves per SIMD, each
-// taking half of two rows with the second row's loads overlapping the first
-// row's work, were slower: the VALU work after the loads, not the loads, sets
-// the time, and four waves hide its dependency stalls better.)
-constexpr int kKronWavesPerSimd = 4;
-
-bool rotq_kron_ok(int64_t M, int64_t K, int log2b) {
+bool rotq_mfma_ok(int64_t M, int64_t K, int log2b) {
   const int64_t step = log2b == 12 ? 4096 : 2048;
-  return M > 64 && K % step == 0 && K >= step && K <= 16384 && log2b >= 8 && log2b <= 12;
+  return M > 64 && K % step == 0 && K >= step && K <= 16384 && log2b >= 7 && log2b <= 12;
 }
 
-hipError_t launch_rotq_kron(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
+hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
                             uint8_t* q, float* scale, int32_t* ob_sum, hipStream_t st) {
-  if (!rotq_kron_ok(M, K, log2b)) return hipErrorInvalidValue;
+  if (!rotq_mfma_ok(M, K, log2b)) return hipErrorInvalidValue;
   RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
   const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
   kron_tables(p < 4 ? p : 4, &a);
   const int WV = static_cast<int>(K / 2048);
-  // Workgroups per XCD for kKronWavesPerSimd waves on each of its 128 SIMDs;
-  // each takes an equal run of the XCD's rows.
-  const int64_t wg_target = 128 * kKronWavesPerSimd / WV;
-  a.rows_per_wg = (a.rows_per_xcd + wg_target - 1) / wg_target;
-  const int64_t wg_per_xcd = (a.rows_per_xcd + a.rows_per_wg - 1) / a.rows_per_wg;
-  const dim3 grid(static_cast<unsigned>(8 * wg_per_xcd));
+  const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
   const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
-#define W4A4_KRON(WW, OO)                                                                          \
+#define W4A4_ROT(WW, OO)                                                                          \
   switch (p) {                                                                                     \
-    case 1: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 1>), grid, dim3(64 * WW), 0, st, a); break; \
-    case 2: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 2>), grid, dim3(64 * WW), 0, st, a); break; \
-    case 3: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 3>), grid, dim3(64 * WW), 0, st, a); break; \
-    case 4: hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 4>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 0: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 1: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 1>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 2: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 2>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 3: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 3>), grid, dim3(64 * WW), 0, st, a); break; \
+    case 4: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 4>), grid, dim3(64 * WW), 0, st, a); break; \
     default:                                                                                       \
       if constexpr (WW % 2 == 0)                                                                   \
-        hipLaunchKernelGGL((rotq_kron_kernel<WW, OO, 5>), grid, dim3(64 * WW), 0, st, a);          \
+        hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 5>), grid, dim3(64 * WW), 0, st, a);          \
       else                                                                                         \
         return hipErrorInvalidValue;                                                               \
       break;                                                                                       \
   }                                                                                                \
   return hipGetLastError();
-#define W4A4_KRON_W(WW)                        \
+#define W4A4_ROT_W(WW)                        \
   case WW:                                     \
     if (out == OUT_F6) {                       \
-      W4A4_KRON(WW, OUT_F6)                    \
+      W4A4_ROT(WW, OUT_F6)                    \
     } else if (out == OUT_PACKED) {            \
-      W4A4_KRON(WW, OUT_PACKED)                \
+      W4A4_ROT(WW, OUT_PACKED)                \
     } else {                                   \
-      W4A4_KRON(WW, OUT_PACKED_OB)             \
+      W4A4_ROT(WW, OUT_PACKED_OB)             \
     }
   switch (WV) {
-    W4A4_KRON_W(1) W4A4_KRON_W(2) W4A4_KRON_W(3) W4A4_KRON_W(4) W4A4_KRON_W(5) W4A4_KRON_W(6)
-    W4A4_KRON_W(7) W4A4_KRON_W(8)
+    W4A4_ROT_W(1) W4A4_ROT_W(2) W4A4_ROT_W(3) W4A4_ROT_W(4) W4A4_ROT_W(5) W4A4_ROT_W(6)
+    W4A4_ROT_W(7) W4A4_ROT_W(8)
     default:
       return hipErrorInvalidValue;
   }
-#undef W4A4_KRON_W
-#undef W4A4_KRON
+#undef W4A4_ROT_W
+#undef W4A4_ROT
 }
 
 }  // namespace w4a4
