@@ -71,6 +71,7 @@ struct RotArgs {
   uint8_t* q;         // the code tiles
   float* scale;       // [M]
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
+  uint8_t* mx_scale;  // MXFP4: E8M0 scale bytes, 64 per 16 x 128 tile
   int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
   uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
@@ -79,7 +80,7 @@ struct RotArgs {
 };
 
 // Output layouts.
-enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2 };
+enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2, OUT_MX = 3 };
 
 template <int OUT>
 constexpr int64_t kTileBytes = OUT == OUT_F6 ? 1536 : 1024;
@@ -127,10 +128,34 @@ __device__ __forceinline__ void h128_product(const HFrag& f, const h8 (&xb)[4], 
   }
 }
 
+// Reductions over the 64 lanes of a wave without LDS round trips: within each
+// 16-lane row, data-parallel moves pair each lane with lane ^ 1, lane ^ 2,
+// its half-row mirror (lane ^ 7) and its row mirror (lane ^ 15), each step
+// joining two disjoint groups whose lanes agree; then the 32- and 16-lane
+// swaps of the value with itself join the four rows.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  auto bits = [](T x) { return __builtin_bit_cast(uint32_t, x); };
+  auto val = [](uint32_t x) { return __builtin_bit_cast(T, x); };
+  v = op(v, val(dpp_mov<0xB1>(bits(v))));   // quad_perm [1,0,3,2]
+  v = op(v, val(dpp_mov<0x4E>(bits(v))));   // quad_perm [2,3,0,1]
+  v = op(v, val(dpp_mov<0x141>(bits(v))));  // row_half_mirror
+  v = op(v, val(dpp_mov<0x140>(bits(v))));  // row_mirror
+  const auto s32 = __builtin_amdgcn_permlane32_swap(bits(v), bits(v), false, false);
+  v = op(val(s32[0]), val(s32[1]));
+  const auto s16 = __builtin_amdgcn_permlane16_swap(bits(v), bits(v), false, false);
+  return op(val(s16[0]), val(s16[1]));
+}
+
+// Maximum over the W waves of a row.
 template <int W>
 __device__ __forceinline__ float row_max(float m, float* wmax, int lane, int w) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+  m = wave_reduce(m, [](float x, float y) { return fmaxf(x, y); });
   if (W > 1) {
     if (lane == 0) wmax[w] = m;
     __syncthreads();
@@ -142,8 +167,7 @@ __device__ __forceinline__ float row_max(float m, float* wmax, int lane, int w) 
 
 template <int W>
 __device__ __forceinline__ int row_sum(int os, int* wsum, int lane, int w) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) os += __shfl_xor(os, o);
+  os = wave_reduce(os, [](int x, int y) { return x + y; });
   if (W > 1) {
     if (lane == 0) wsum[w] = os;
     __syncthreads();
@@ -159,18 +183,18 @@ __device__ __forceinline__ int row_sum(int os, int* wsum, int lane, int w) {
 // float for FP6 (the packing instruction's input), q + 1.5 * 2^23 for the
 // nibble tiles (whose low nibble is q in two's complement).  Returns, for
 // offset-binary tiles, this lane's sum of the codes at odd channels.
-template <int OUT>
-__device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* tile, int g, int rin) {
-  // Unit j of this lane (the 8 codes of chunk j: mb = 2 j + v / 4, i = v % 4)
-  // goes to lane group j.  After the two swaps, B[s][v] is unit (this lane
-  // group) of source group s, and this lane holds codes [32 g, 32 g + 32) of
-  // its block, chunk offset 16 (v / 4) + 4 s + v % 4 in B[s][v].
+// The 4 x 4 unit transpose across the lane groups.  in[mb][i] is this lane's
+// value at position 16 mb + 4 g + i of its block; unit j (the 8 values of
+// chunk j: mb = 2 j + v / 4, i = v % 4) goes to lane group j.  After the two
+// swaps, b[s][v] is unit (this lane group) of source group s, and this lane
+// holds positions [32 g, 32 g + 32) of its block, chunk offset
+// 16 (v / 4) + 4 s + v % 4 in b[s][v].
+__device__ __forceinline__ void unit_transpose(const float (&in)[8][4], uint32_t (&b)[4][8]) {
   uint32_t u[4][8];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int v = 0; v < 8; ++v) u[j][v] = __float_as_uint(cm[2 * j + (v >> 2)][v & 3]);
-  uint32_t b[4][8];
+    for (int v = 0; v < 8; ++v) u[j][v] = __float_as_uint(in[2 * j + (v >> 2)][v & 3]);
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const auto s02 = __builtin_amdgcn_permlane32_swap(u[0][v], u[2][v], false, false);
@@ -182,6 +206,12 @@ __device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* til
     b[2][v] = t23[0];
     b[3][v] = t23[1];
   }
+}
+
+template <int OUT>
+__device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* tile, int g, int rin) {
+  uint32_t b[4][8];
+  unit_transpose(cm, b);
   if constexpr (OUT == OUT_F6) {
     // lane 16 g + (row % 16) of the 1536-byte FP6 tile
     f16v lo, hi;
@@ -335,6 +365,53 @@ __global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
   if constexpr (kLaneStages > 2) lane_stage<2>(y, sel);
   if constexpr (kLaneStages > 3) lane_stage<3>(y, sel);
 
+  if constexpr (OUT == OUT_MX) {
+    // MXFP4 (the butterfly kernel's rule): after the unit transpose a lane
+    // holds one 32-element block, positions [32 g, 32 g + 32) of sub-block
+    // 16 w + c.  e = max(floor(log2(max|x~|)) - 2, -127), max|x~| =
+    // RN(max|y| rs); each element x~ 2^-e (exact) to E2M1 by the hardware
+    // conversion, with the sign of the quotient.  The lane's sign sgn goes
+    // into the multiplier.
+    float yv[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yv[mb][i] = y[4 * mb + i];
+    uint32_t bt[4][8];
+    unit_transpose(yv, bt);
+    float bm = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int v = 0; v < 8; ++v) bm = fmaxf(bm, fabsf(__uint_as_float(bt[s4][v])));
+    const float amax = bm * a.rs;
+    const int e = max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 129, -127);
+    const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
+    const float srs = sgn * a.rs;
+    const float mul = ldexpf(kFold ? srs : 1.f, -e);  // exact: a power of two
+    // element o (chunk offset) is bt[(o / 4) % 4][4 (o / 16) + o % 4]; elements
+    // 2 k and 2 k + 1 go to byte k of the 16 (low nibble first)
+    auto q2 = [&](int o) {
+      const int s4 = (o >> 2) & 3, v = 4 * (o >> 4) + (o & 3);
+      const float x0 = __uint_as_float(bt[s4][v]), x1 = __uint_as_float(bt[s4][v + 1]);
+      return kFold ? float2{x0 * mul, x1 * mul} : float2{(x0 * srs) * mul, (x1 * srs) * mul};
+    };
+    uint32_t pk[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const float2 e0 = q2(8 * d), e1 = q2(8 * d + 2), e2 = q2(8 * d + 4), e3 = q2(8 * d + 6);
+      uint32_t v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, e0.x, e0.y, 1.0f, 0);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, e1.x, e1.y, 1.0f, 1);
+      v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, e2.x, e2.y, 1.0f, 2);
+      pk[d] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, e3.x, e3.y, 1.0f, 3);
+    }
+    const int rin = static_cast<int>(row & 15);
+    const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;  // sub-block 16 w + c
+    *reinterpret_cast<uint4*>(a.q + blk * 1024 + (16 * g + rin) * 16) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    a.mx_scale[blk * 64 + g * 16 + rin] = static_cast<uint8_t>(e + 127);
+    return;
+  }
+
   float m = 0.f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(y[k]));
@@ -429,14 +506,16 @@ bool rotq_mfma_ok(int64_t M, int64_t K, int log2b) {
 }
 
 hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
-                            uint8_t* q, float* scale, int32_t* ob_sum, hipStream_t st) {
+                            uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
+                            hipStream_t st) {
   if (!rotq_mfma_ok(M, K, log2b)) return hipErrorInvalidValue;
   RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
+  a.mx_scale = mx_scale;
   const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
   kron_tables(p < 4 ? p : 4, &a);
   const int WV = static_cast<int>(K / 2048);
   const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
-  const int out = f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
+  const int out = mx_scale ? OUT_MX : f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
 #define W4A4_ROT(WW, OO)                                                                          \
   switch (p) {                                                                                     \
     case 0: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0>), grid, dim3(64 * WW), 0, st, a); break; \
@@ -458,8 +537,10 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
       W4A4_ROT(WW, OUT_F6)                    \
     } else if (out == OUT_PACKED) {            \
       W4A4_ROT(WW, OUT_PACKED)                \
-    } else {                                   \
+    } else if (out == OUT_PACKED_OB) {         \
       W4A4_ROT(WW, OUT_PACKED_OB)             \
+    } else {                                   \
+      W4A4_ROT(WW, OUT_MX)                    \
     }
   switch (WV) {
     W4A4_ROT_W(1) W4A4_ROT_W(2) W4A4_ROT_W(3) W4A4_ROT_W(4) W4A4_ROT_W(5) W4A4_ROT_W(6)

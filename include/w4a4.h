@@ -394,6 +394,11 @@ int w4a4_qgemm_mxfp4(const uint8_t* xq, const uint8_t* x_scale, const uint8_t* w
  * w4a4_quantize_mxfp4 (same had_block, tiled), plus the optional rank-r term
  * as in w4a4_qlinear_forward.
  *   workspace: at least w4a4_qlinear_workspace_size(M, N, K, rank) bytes.
+ *   It leaves the activation codes there in the W4A4_CODES_PACKED_TILED
+ *   layout at the codes offset that w4a4_qlinear_workspace_layout reports
+ *   for tiled int4 weights, and their E8M0 scale tiles (the tiled layout of
+ *   w4a4_quantize_mxfp4) at the next multiple of 256 bytes after the codes'
+ *   ceil(M / 16) * 16 * K / 2 bytes.
  */
 int w4a4_qlinear_forward_mxfp4(const void* x, int x_dtype, const uint8_t* wq,
                                const uint8_t* w_scale, int64_t M, int64_t N, int64_t K,

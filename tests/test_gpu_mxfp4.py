@@ -97,8 +97,12 @@ def test_quantize_mxfp4_row_major_small_k():
     assert np.array_equal(e, pe) and np.array_equal(codes, pc)
 
 
-@pytest.mark.parametrize("M,K,b", [(64, 4096, 128), (48, 14336, 128), (100, 4096, 4096), (8, 2048, 256)])
+@pytest.mark.parametrize("M,K,b", [(64, 4096, 128), (48, 14336, 128), (100, 4096, 4096), (8, 2048, 256),
+                                   (130, 4096, 128), (2048, 4096, 4096), (300, 8192, 1024),
+                                   (97, 6144, 2048), (77, 16384, 4096), (1000, 14336, 128)])
 def test_quantize_mxfp4_fused_rotation(M, K, b):
+    # fp16 rows, more than 64 of them: the rotation on the matrix instruction
+    # (the tiled layout; the row-major one keeps the butterfly kernel)
     w = synth.small("mxf", M, K, 8, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
     codes, e = gpu_mx(X, b, "packed_tiled")
@@ -108,6 +112,22 @@ def test_quantize_mxfp4_fused_rotation(M, K, b):
     assert np.count_nonzero(diff) <= 1e-4 * diff.size
     step = np.repeat(np.exp2(np.maximum(e, pe)), 32, axis=1)
     assert np.all(np.abs(dg - do) <= 2 * step)
+
+
+@pytest.mark.parametrize("M,K,b", [(130, 4096, 4096), (300, 4096, 128), (65, 8192, 512)])
+def test_quantize_mxfp4_matrix_rotation_matches_butterfly(M, K, b):
+    # the tiled layout (matrix instruction) against the row-major one
+    # (butterflies) on the same input: the same rule on float32 sums that
+    # round in another order, so at most 0.02% of the values differ, each by
+    # at most two E2M1 steps of the larger scale
+    w = synth.small("mxm", M, K, 8, n_outlier=4, bos_factor=500.0)
+    X = synth.make_inputs(w)["X"]
+    ct, et = gpu_mx(X, b, "packed_tiled")
+    cr, er = gpu_mx(X, b, "packed")
+    vt, vr = O.mxfp4_values(ct, et), O.mxfp4_values(cr, er)
+    assert np.count_nonzero(vt != vr) <= 2e-4 * vt.size
+    step = np.repeat(np.exp2(np.maximum(et, er)), 32, axis=1)
+    assert np.all(np.abs(vt - vr) <= 2 * step)
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (7, 33, 256), (130, 260, 1024), (2048, 4096, 4096),
@@ -139,14 +159,24 @@ def run_mx_layer(w, sample_rows=None):
     Ad = dev(A.T) if A is not None else None
     Bd = dev(B.T) if B is not None else None
     print("mxfp4 layer", w.name, w.M, w.K, w.N, b, w.rank, flush=True)
-    y = host(W.qlinear_forward_mxfp4(Xd, wq, ws, w.N, b, Ad, Bd))
+    ws_buf = W.qlinear_workspace(w.M, w.N, w.K, w.rank, DEV)
+    y = host(W.qlinear_forward_mxfp4(Xd, wq, ws, w.N, b, Ad, Bd, workspace=ws_buf))
     wc = nibbles(untile_weights(host(wq), w.N))
     we = untile_mx_scales(host(ws), w.N, w.K).astype(np.int64) - 127
     pwc, pwe = O.quantize_mxfp4(O.rotate(Wt, b))
     dw = O.mxfp4_values(wc, we) != O.mxfp4_values(pwc, pwe)
     assert np.count_nonzero(dw) <= 1e-4 * dw.size
     rows = np.arange(w.M) if sample_rows is None else sample_rows
-    xc, xe = gpu_mx(X, b, "packed")
+    # the codes and scale tiles the layer left in its workspace
+    wsb = host(ws_buf)
+    co, _, _ = W.qlinear_workspace_layout(w.M, w.N, w.K, w.rank, "tiled", 0)
+    Mp = W.pad16(w.M)
+    so = co + (Mp * w.K // 2 + 255) // 256 * 256
+    xc = nibbles(untile_weights(wsb[co:co + Mp * w.K // 2].reshape(Mp, w.K // 2), w.M))
+    xe = untile_mx_scales(wsb[so:so + Mp * w.K // 32], w.M, w.K).astype(np.int64) - 127
+    pxc, pxe = O.quantize_mxfp4(O.rotate(X[rows], b)) if b > 1 else O.quantize_mxfp4(X[rows])
+    dx = O.mxfp4_values(xc[rows], xe[rows]) != O.mxfp4_values(pxc, pxe)
+    assert np.count_nonzero(dx) <= 1e-4 * dx.size + 1
     y_codes = O.mxfp4_gemm(xc[rows], xe[rows], wc, we)
     lr = O.lowrank(X[rows], A, B)
     if lr is not None:

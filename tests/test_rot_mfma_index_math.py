@@ -232,3 +232,27 @@ def test_kron_signed_quotient_equals_unsigned():
         rc = f(f(1.0) / s)
         assert quot(z, s, rc) == quot(f(-z), f(-s), f(-rc))
         assert quot(z, s, rc) != quot(f(-z), s, f(-rc)) or quot(z, s, rc) == 0
+
+
+def test_wave_reduction_pattern_reaches_every_lane():
+    # The kernel's 64-lane reductions: lane ^ 1, lane ^ 2 (quad permutations),
+    # the half-row mirror and the row mirror within each 16-lane row, then the
+    # 32- and 16-lane swaps of the value with itself.  Every lane must end
+    # with the maximum (and the sum) of all 64.
+    def half_mirror(lane):
+        return (lane & ~7) + 7 - (lane & 7)
+
+    def mirror(lane):
+        return (lane & ~15) + 15 - (lane & 15)
+
+    rng = np.random.default_rng(9)
+    for op, ident in ((np.maximum, None), (np.add, None)):
+        v = rng.integers(-1000, 1000, 64).astype(np.int64)
+        want = op.reduce(v)
+        for part in (lambda l: l ^ 1, lambda l: l ^ 2, half_mirror, mirror):
+            v = op(v, v[[part(l) for l in LANES]])
+        a, b = swap32(v, v)
+        v = op(a, b)
+        a, b = swap16(v, v)
+        v = op(a, b)
+        assert np.all(v == want)
