@@ -905,14 +905,21 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
     float* sf = static_cast<float*>(scale);
     int32_t* ob = ex ? ex->ob_sum : nullptr;
     if (rotq_mfma_ok(M, K, log2b))
-      return launch_rotq_mfma(xh, M, K, log2b, mode == ROTQ_QUANT_F6, q, sf, ob, nullptr, st);
+      return launch_rotq_mfma(xh, M, K, log2b, mode == ROTQ_QUANT_F6 ? ROT_OUT_F6 : ROT_OUT_PACKED, 7,
+                              q, sf, ob, nullptr, st);
   }
-  // MXFP4 codes into the tiled layouts, same conditions otherwise.
-  const bool mx_ex = ex && ex->mx_scale && ex->qmax == 7 && !ex->asym_zero && ex->res_r == 0 &&
-                     ex->lr_rank == 0 && !ex->pf;
-  if (x_f16 && mode == ROTQ_QUANT_TILED && gsz == K && mx_ex && rotq_mfma_ok(M, K, log2b))
-    return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, false, q, nullptr,
+  // MXFP4 codes, or int8 tiles (qmax 7 or 127), same conditions otherwise.
+  const bool bare_ex = !ex || (!ex->asym_zero && ex->res_r == 0 && ex->lr_rank == 0 && !ex->pf &&
+                               !ex->ob_sum);
+  const int qmax = ex ? ex->qmax : 7;
+  if (x_f16 && mode == ROTQ_QUANT_TILED && gsz == K && bare_ex && ex && ex->mx_scale && qmax == 7 &&
+      rotq_mfma_ok(M, K, log2b))
+    return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, ROT_OUT_MX, 7, q, nullptr,
                             nullptr, ex->mx_scale, st);
+  if (x_f16 && mode == ROTQ_QUANT_I8_TILED && gsz == K && !scale_f16 && bare_ex &&
+      !(ex && ex->mx_scale) && rotq_mfma_ok(M, K, log2b))
+    return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, ROT_OUT_I8, qmax, q,
+                            static_cast<float*>(scale), nullptr, nullptr, st);
   RotqKArgs ka{};
   ka.x = x;
   ka.M = M;

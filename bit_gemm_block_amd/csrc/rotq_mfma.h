@@ -1,9 +1,10 @@
 // rotq_mfma.h — block Hadamard rotation on the fp16 matrix instruction, fused
 // with the activation quantizer into the tiled code layouts: per-token absmax
-// int4 codes with one float32 scale per row in FP6 tiles or packed tiles
-// (plain, or offset-binary with the row sums of the odd channels' codes)
-// (SERQ page, "Resumen técnico" §1-2), or MXFP4 codes with their E8M0 scale
-// tiles (SERQ page, "Metodología" item 2).  For fp16 rows, more than 64 of
+// int4 codes with one float32 scale per row in FP6 tiles, packed tiles
+// (plain, or offset-binary with the row sums of the odd channels' codes) or
+// int8 tiles (SERQ page, "Resumen técnico" §1-2; 8-bit codes for the W4A8
+// layer), or MXFP4 codes with their E8M0 scale tiles (SERQ page,
+// "Metodología" item 2).  For fp16 rows, more than 64 of
 // them; every other form of the rotation runs the butterfly kernel.
 #pragma once
 
@@ -16,11 +17,13 @@ namespace w4a4 {
 // at a time, then for b > 128 the Kronecker factor across them): K a multiple
 // of 2048 (of 4096 for b = 4096) up to 16384.
 bool rotq_mfma_ok(int64_t M, int64_t K, int log2b);
-// Output: mx_scale given, MXFP4 codes in packed tiles and their E8M0 scale
-// tiles (scale unused); else FP6 tiles (f6) or packed tiles (offset-binary,
-// with the row sums, when ob_sum is given), with one float32 scale per row.
-hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
-                            uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
+// Outputs: FP6 tiles, packed tiles (offset-binary, with the row sums, when
+// ob_sum is given) or int8 tiles (qmax 7 or 127), each with one float32
+// scale per row; or MXFP4 codes in packed tiles with their E8M0 scale tiles
+// (mx_scale; scale unused).
+enum RotMfmaOut { ROT_OUT_F6, ROT_OUT_PACKED, ROT_OUT_I8, ROT_OUT_MX };
+hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, RotMfmaOut out_kind,
+                            int qmax, uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
                             hipStream_t st);
 
 }  // namespace w4a4

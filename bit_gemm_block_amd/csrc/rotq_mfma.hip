@@ -67,6 +67,7 @@ struct RotArgs {
   const _Float16* x;  // [M, K]
   int64_t M, K;
   float rs;           // float32(1 / sqrt(b))
+  float qmax;         // largest code: 7, or 127 for int8 tiles
   float sqrt_b;       // sqrt(b) when it is a power of two (the divisor fold)
   uint8_t* q;         // the code tiles
   float* scale;       // [M]
@@ -80,10 +81,10 @@ struct RotArgs {
 };
 
 // Output layouts.
-enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2, OUT_MX = 3 };
+enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2, OUT_MX = 3, OUT_I8 = 4 };
 
 template <int OUT>
-constexpr int64_t kTileBytes = OUT == OUT_F6 ? 1536 : 1024;
+constexpr int64_t kTileBytes = OUT == OUT_F6 ? 1536 : OUT == OUT_I8 ? 2048 : 1024;
 
 __device__ __forceinline__ h8 neg8(h8 v) {
   h8 r;
@@ -181,7 +182,7 @@ __device__ __forceinline__ int row_sum(int os, int* wsum, int lane, int w) {
 // Writes the codes of the 16 blocks of one product into their tiles.  cm[mb][i]
 // holds the code q of y_c[16 mb + 4 g + i] in the form its tile takes: q as a
 // float for FP6 (the packing instruction's input), q + 1.5 * 2^23 for the
-// nibble tiles (whose low nibble is q in two's complement).  Returns, for
+// nibble and byte tiles (whose low nibble or byte is q in two's complement).  Returns, for
 // offset-binary tiles, this lane's sum of the codes at odd channels.
 // The 4 x 4 unit transpose across the lane groups.  in[mb][i] is this lane's
 // value at position 16 mb + 4 g + i of its block; unit j (the 8 values of
@@ -212,7 +213,28 @@ template <int OUT>
 __device__ __forceinline__ int store_codes(const float (&cm)[8][4], uint8_t* tile, int g, int rin) {
   uint32_t b[4][8];
   unit_transpose(cm, b);
-  if constexpr (OUT == OUT_F6) {
+  if constexpr (OUT == OUT_I8) {
+    // The 2 KB int8 tile: codes [32 g + 16 h, +16) of row r are the 16 bytes
+    // at ((4 h + g) 16 + r) 16, each group of 8 in the order 0,2,4,6,1,3,5,7.
+    // Element e of group q of half h is chunk offset 16 h + 8 q + e, that is
+    // b[2 q + e / 4][4 h + e % 4]: dword 2 q takes e = 0, 2, 4, 6 and dword
+    // 2 q + 1 takes e = 1, 3, 5, 7.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t d[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int odd = 0; odd < 2; ++odd) {
+          const uint32_t lo = __builtin_amdgcn_perm(b[2 * q][4 * h + 2 + odd], b[2 * q][4 * h + odd], 0x0C0C0400u);
+          const uint32_t hi =
+              __builtin_amdgcn_perm(b[2 * q + 1][4 * h + 2 + odd], b[2 * q + 1][4 * h + odd], 0x04000C0Cu);
+          d[2 * q + odd] = lo | hi;
+        }
+      *reinterpret_cast<uint4*>(tile + ((4 * h + g) * 16 + rin) * 16) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+    return 0;
+  } else if constexpr (OUT == OUT_F6) {
     // lane 16 g + (row % 16) of the 1536-byte FP6 tile
     f16v lo, hi;
 #pragma unroll
@@ -427,7 +449,7 @@ __global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
   // A lane holds its values times sgn; the reciprocal times sgn takes it out
   // (exactly: rounding is symmetric).
   const float amax = m * a.rs;
-  const float s = __fdiv_rn(amax, 7.0f);
+  const float s = __fdiv_rn(amax, a.qmax);
   if (threadIdx.x == 0) a.scale[row] = s;
   const float sgn = ((a.sig_tbl >> c) & 1u) ? -1.f : 1.f;
   const float rc = s == 0.f ? 0.f : __frcp_rn((kFold ? s * a.sqrt_b : s) * sgn);
@@ -505,17 +527,25 @@ bool rotq_mfma_ok(int64_t M, int64_t K, int log2b) {
   return M > 64 && K % step == 0 && K >= step && K <= 16384 && log2b >= 7 && log2b <= 12;
 }
 
-hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
-                            uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
+hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, RotMfmaOut out_kind,
+                            int qmax, uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
                             hipStream_t st) {
   if (!rotq_mfma_ok(M, K, log2b)) return hipErrorInvalidValue;
+  if ((out_kind == ROT_OUT_MX) != (mx_scale != nullptr) || (ob_sum && out_kind != ROT_OUT_PACKED) ||
+      (qmax != 7 && !(qmax == 127 && out_kind == ROT_OUT_I8)))
+    return hipErrorInvalidValue;
   RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
   a.mx_scale = mx_scale;
+  a.qmax = static_cast<float>(qmax);
   const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
   kron_tables(p < 4 ? p : 4, &a);
   const int WV = static_cast<int>(K / 2048);
   const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
-  const int out = mx_scale ? OUT_MX : f6 ? OUT_F6 : ob_sum ? OUT_PACKED_OB : OUT_PACKED;
+  const int out = out_kind == ROT_OUT_MX   ? OUT_MX
+                  : out_kind == ROT_OUT_F6 ? OUT_F6
+                  : out_kind == ROT_OUT_I8 ? OUT_I8
+                  : ob_sum                 ? OUT_PACKED_OB
+                                           : OUT_PACKED;
 #define W4A4_ROT(WW, OO)                                                                          \
   switch (p) {                                                                                     \
     case 0: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0>), grid, dim3(64 * WW), 0, st, a); break; \
@@ -539,6 +569,8 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
       W4A4_ROT(WW, OUT_PACKED)                \
     } else if (out == OUT_PACKED_OB) {         \
       W4A4_ROT(WW, OUT_PACKED_OB)             \
+    } else if (out == OUT_I8) {                \
+      W4A4_ROT(WW, OUT_I8)                    \
     } else {                                   \
       W4A4_ROT(WW, OUT_MX)                    \
     }

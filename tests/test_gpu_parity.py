@@ -544,15 +544,20 @@ def test_quantize_act_int8_ties_and_extremes():
     assert np.array_equal(codes_from_i8(host(xq)), pc)
 
 
-@pytest.mark.parametrize("M,K,b", [(64, 4096, 4096), (48, 14336, 128), (8, 4096, 4096)])
-def test_quantize_act_int8_fused_rotation(M, K, b):
+@pytest.mark.parametrize("M,K,b,layout", [(64, 4096, 4096, "i8"), (48, 14336, 128, "i8"), (8, 4096, 4096, "i8"),
+                                          (130, 4096, 4096, "i8_tiled"), (2048, 4096, 4096, "i8_tiled"),
+                                          (300, 6144, 128, "i8_tiled"), (97, 8192, 1024, "i8_tiled")])
+def test_quantize_act_int8_fused_rotation(M, K, b, layout):
     # fp32 FWHT against the float64 rotation: every flip is one step and at
-    # most 0.01% of the codes flip (the 4-bit bar; measured ~4e-6 here).
+    # most 0.01% of the codes flip (the 4-bit bar; measured ~4e-6 here).  The
+    # tiled cases of fp16 rows (more than 64) take the rotation on the matrix
+    # instruction.
     w = synth.small("f8", M, K, 8, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
-    xq, sx = W.quantize_act_int8(dev(X), b)
+    xq, sx = W.quantize_act_int8(dev(X), b, layout=layout)
     _, ps, pc, _ = O.quantize_activation(X, b, qmax=127)
-    diff = codes_from_i8(host(xq)).astype(np.int16) - pc
+    got = host(xq) if layout == "i8" else untile_codes_i8(host(xq), M)
+    diff = codes_from_i8(got).astype(np.int16) - pc
     print("int8 fused rotation: fraction of codes one step off =", np.count_nonzero(diff) / diff.size)
     assert np.all(np.abs(diff) <= 1)
     assert np.count_nonzero(diff) <= 1e-4 * diff.size

@@ -256,3 +256,24 @@ def test_wave_reduction_pattern_reaches_every_lane():
         a, b = swap16(v, v)
         v = op(a, b)
         assert np.all(v == want)
+
+
+def test_int8_tile_bytes_follow_the_documented_order():
+    # After the unit transpose, chunk offset o of a lane is b[s][v] with
+    # o = 16 (v / 4) + 4 s + v % 4.  The kernel's int8 store: half h, dword
+    # 2 q + odd takes bytes b[2q][4h + odd], b[2q][4h + 2 + odd],
+    # b[2q + 1][4h + odd], b[2q + 1][4h + 2 + odd].  The 32 bytes must be the
+    # documented W4A4_CODES_I8 order of codes 0..31 (each group of 8 as
+    # 0,2,4,6,1,3,5,7), which tests/layouts.py writes independently.
+    from layouts import i8_from_codes
+    b = np.zeros((4, 8), np.int64)
+    for s in range(4):
+        for v in range(8):
+            b[s, v] = 16 * (v >> 2) + 4 * s + (v & 3)
+    out = []
+    for h in range(2):
+        for q in range(2):
+            for odd in range(2):
+                out += [b[2 * q][4 * h + odd], b[2 * q][4 * h + 2 + odd],
+                        b[2 * q + 1][4 * h + odd], b[2 * q + 1][4 * h + 2 + odd]]
+    assert out == list(i8_from_codes(np.arange(32).reshape(1, 32))[0])
