@@ -916,6 +916,12 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
       rotq_mfma_ok(M, K, log2b))
     return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, ROT_OUT_MX, 7, q, nullptr,
                             nullptr, ex->mx_scale, st);
+  // Asymmetric codes per block of 128 (b = group = 128) into packed tiles.
+  if (x_f16 && mode == ROTQ_QUANT_TILED && log2b == 7 && gsz == 128 && !scale_f16 && ex &&
+      ex->asym_zero && qmax == 7 && ex->res_r == 0 && !ex->mx_scale && ex->lr_rank == 0 && !ex->pf &&
+      !ex->ob_sum && rotq_mfma_ok(M, K, log2b))
+    return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, ROT_OUT_ASYM, 7, q,
+                            static_cast<float*>(scale), ex->asym_zero, nullptr, st);
   if (x_f16 && mode == ROTQ_QUANT_I8_TILED && gsz == K && !scale_f16 && bare_ex &&
       !(ex && ex->mx_scale) && rotq_mfma_ok(M, K, log2b))
     return launch_rotq_mfma(static_cast<const _Float16*>(x), M, K, log2b, ROT_OUT_I8, qmax, q,

@@ -3,8 +3,9 @@
 // int4 codes with one float32 scale per row in FP6 tiles, packed tiles
 // (plain, or offset-binary with the row sums of the odd channels' codes) or
 // int8 tiles (SERQ page, "Resumen técnico" §1-2; 8-bit codes for the W4A8
-// layer), or MXFP4 codes with their E8M0 scale tiles (SERQ page,
-// "Metodología" item 2).  For fp16 rows, more than 64 of
+// layer), MXFP4 codes with their E8M0 scale tiles (SERQ page,
+// "Metodología" item 2), or asymmetric codes per block of 128 (OffQ page,
+// "Metodología" steps 2-3).  For fp16 rows, more than 64 of
 // them; every other form of the rotation runs the butterfly kernel.
 #pragma once
 
@@ -17,13 +18,15 @@ namespace w4a4 {
 // at a time, then for b > 128 the Kronecker factor across them): K a multiple
 // of 2048 (of 4096 for b = 4096) up to 16384.
 bool rotq_mfma_ok(int64_t M, int64_t K, int log2b);
-// Outputs: FP6 tiles, packed tiles (offset-binary, with the row sums, when
-// ob_sum is given) or int8 tiles (qmax 7 or 127), each with one float32
-// scale per row; or MXFP4 codes in packed tiles with their E8M0 scale tiles
-// (mx_scale; scale unused).
-enum RotMfmaOut { ROT_OUT_F6, ROT_OUT_PACKED, ROT_OUT_I8, ROT_OUT_MX };
+// Outputs: FP6 tiles, packed tiles (offset-binary, with the row sums in i32,
+// when i32 is given) or int8 tiles (qmax 7 or 127), each with one float32
+// scale per row; MXFP4 codes in packed tiles with their E8M0 scale tiles
+// (mx_scale; scale unused); or, for b = 128, asymmetric codes of every
+// (row, block of 128) in packed tiles with float32 scales (scale) and int32
+// zero points (i32), [M, K / 128] each.
+enum RotMfmaOut { ROT_OUT_F6, ROT_OUT_PACKED, ROT_OUT_I8, ROT_OUT_MX, ROT_OUT_ASYM };
 hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, RotMfmaOut out_kind,
-                            int qmax, uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
+                            int qmax, uint8_t* q, float* scale, int32_t* i32, uint8_t* mx_scale,
                             hipStream_t st);
 
 }  // namespace w4a4

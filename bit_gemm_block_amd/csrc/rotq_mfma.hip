@@ -73,6 +73,7 @@ struct RotArgs {
   float* scale;       // [M]
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
   uint8_t* mx_scale;  // MXFP4: E8M0 scale bytes, 64 per 16 x 128 tile
+  int32_t* zero;      // asymmetric codes: zero points [M, K / 128] (scale: [M, K / 128])
   int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
   uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
@@ -81,7 +82,7 @@ struct RotArgs {
 };
 
 // Output layouts.
-enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2, OUT_MX = 3, OUT_I8 = 4 };
+enum { OUT_F6 = 0, OUT_PACKED = 1, OUT_PACKED_OB = 2, OUT_MX = 3, OUT_I8 = 4, OUT_ASYM = 5 };
 
 template <int OUT>
 constexpr int64_t kTileBytes = OUT == OUT_F6 ? 1536 : OUT == OUT_I8 ? 2048 : 1024;
@@ -434,6 +435,60 @@ __global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
     return;
   }
 
+  if constexpr (OUT == OUT_ASYM) {
+    // Asymmetric codes of each (row, block of 128) (the butterfly kernel's
+    // rule, b = 128): the group is sub-block 16 w + c, which the four lane
+    // groups of column c hold, 32 values each.  s = RN((hi - lo) / 15),
+    // z = rint(RN(-lo / s)), q = clamp(rint(x~ / s) + z, 0, 15) with the
+    // correctly rounded quotient (a large z makes its last bits matter),
+    // stored as q - 8; a group without spread spans [min(c, 0), max(c, 0)].
+    float ymax = y[0], ymin = y[0];
+#pragma unroll
+    for (int k = 1; k < 32; ++k) {
+      ymax = fmaxf(ymax, y[k]);
+      ymin = fminf(ymin, y[k]);
+    }
+    auto join = [](float v, auto op) {  // over the lanes c, c + 16, c + 32, c + 48
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = op(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      return op(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    };
+    ymax = join(ymax, [](float p, float q) { return fmaxf(p, q); });
+    ymin = join(ymin, [](float p, float q) { return fminf(p, q); });
+    float lo = ymin * a.rs, hi = ymax * a.rs;
+    if (hi == lo) {
+      lo = fminf(lo, 0.f);
+      hi = fmaxf(hi, 0.f);
+    }
+    const float s = __fdiv_rn(hi - lo, 15.f);
+    const bool live = s > 0.f;
+    const float zf = live ? rintf(__fdiv_rn(-lo, s)) : 0.f;
+    const int64_t si = row * (a.K / 128) + 16 * w + c;
+    if (g == 0) {
+      a.scale[si] = s;
+      a.zero[si] = static_cast<int>(zf);
+    }
+    const float rc = live ? __frcp_rn(s) : 0.f;
+    float cm[8][4];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float xt = y[4 * mb + i] * a.rs;
+        float q = xt * rc;
+        q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+        q = __builtin_fmaf(__builtin_fmaf(-q, s, xt), rc, q);
+        // rint(q) + z is exact whenever it lands near [0, 15]; farther out
+        // the clamp decides.  (q - 8) + 1.5 * 2^23 has q - 8 in its low nibble.
+        const float qc = __builtin_amdgcn_fmed3f(rintf(q) + zf, 0.f, 15.f);
+        cm[mb][i] = qc + (kMagic - 8.f);
+      }
+    const int64_t blk = (row >> 4) * a.tile_stride + 16 * w + c;
+    store_codes<OUT_PACKED>(cm, a.q + blk * 1024, g, static_cast<int>(row & 15));
+    return;
+  }
+
   float m = 0.f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) m = fmaxf(m, fabsf(y[k]));
@@ -528,24 +583,28 @@ bool rotq_mfma_ok(int64_t M, int64_t K, int log2b) {
 }
 
 hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, RotMfmaOut out_kind,
-                            int qmax, uint8_t* q, float* scale, int32_t* ob_sum, uint8_t* mx_scale,
+                            int qmax, uint8_t* q, float* scale, int32_t* i32, uint8_t* mx_scale,
                             hipStream_t st) {
   if (!rotq_mfma_ok(M, K, log2b)) return hipErrorInvalidValue;
-  if ((out_kind == ROT_OUT_MX) != (mx_scale != nullptr) || (ob_sum && out_kind != ROT_OUT_PACKED) ||
+  if ((out_kind == ROT_OUT_MX) != (mx_scale != nullptr) ||
+      (i32 && out_kind != ROT_OUT_PACKED && out_kind != ROT_OUT_ASYM) ||
+      (out_kind == ROT_OUT_ASYM && (!i32 || log2b != 7)) ||
       (qmax != 7 && !(qmax == 127 && out_kind == ROT_OUT_I8)))
     return hipErrorInvalidValue;
-  RotArgs a = base_args(x, M, K, log2b, q, scale, ob_sum);
+  RotArgs a = base_args(x, M, K, log2b, q, scale, out_kind == ROT_OUT_PACKED ? i32 : nullptr);
   a.mx_scale = mx_scale;
+  a.zero = out_kind == ROT_OUT_ASYM ? i32 : nullptr;
   a.qmax = static_cast<float>(qmax);
   const int p = log2b - 7;  // log2 of the sub-blocks per rotation block
   kron_tables(p < 4 ? p : 4, &a);
   const int WV = static_cast<int>(K / 2048);
   const dim3 grid(static_cast<unsigned>(8 * a.rows_per_xcd));
-  const int out = out_kind == ROT_OUT_MX   ? OUT_MX
-                  : out_kind == ROT_OUT_F6 ? OUT_F6
-                  : out_kind == ROT_OUT_I8 ? OUT_I8
-                  : ob_sum                 ? OUT_PACKED_OB
-                                           : OUT_PACKED;
+  const int out = out_kind == ROT_OUT_MX     ? OUT_MX
+                  : out_kind == ROT_OUT_F6   ? OUT_F6
+                  : out_kind == ROT_OUT_I8   ? OUT_I8
+                  : out_kind == ROT_OUT_ASYM ? OUT_ASYM
+                  : a.ob_sum                 ? OUT_PACKED_OB
+                                             : OUT_PACKED;
 #define W4A4_ROT(WW, OO)                                                                          \
   switch (p) {                                                                                     \
     case 0: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0>), grid, dim3(64 * WW), 0, st, a); break; \
@@ -561,6 +620,9 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
       break;                                                                                       \
   }                                                                                                \
   return hipGetLastError();
+#define W4A4_ROT_P0(WW, OO)                                                                  \
+  hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0>), grid, dim3(64 * WW), 0, st, a);           \
+  return hipGetLastError();
 #define W4A4_ROT_W(WW)                        \
   case WW:                                     \
     if (out == OUT_F6) {                       \
@@ -571,6 +633,8 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
       W4A4_ROT(WW, OUT_PACKED_OB)             \
     } else if (out == OUT_I8) {                \
       W4A4_ROT(WW, OUT_I8)                    \
+    } else if (out == OUT_ASYM) {              \
+      W4A4_ROT_P0(WW, OUT_ASYM)               \
     } else {                                   \
       W4A4_ROT(WW, OUT_MX)                    \
     }
@@ -581,6 +645,7 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
       return hipErrorInvalidValue;
   }
 #undef W4A4_ROT_W
+#undef W4A4_ROT_P0
 #undef W4A4_ROT
 }
 

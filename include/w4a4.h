@@ -520,6 +520,12 @@ int w4a4_qgemm_asym(const uint8_t* xq, const float* x_scale, const int32_t* x_ze
  *   w4a4_quantize_weight_int4 with the same had_block; w_gsum from
  *   w4a4_weight_group_sums with group = had_block.
  *   workspace: at least w4a4_qlinear_workspace_size(M, N, K, rank) bytes.
+ *   It leaves the activation codes there in the W4A4_CODES_PACKED_TILED
+ *   layout at the codes offset that w4a4_qlinear_workspace_layout reports
+ *   for tiled int4 weights; the float32 group scales [M, K / had_block] at
+ *   the next multiple of 256 bytes after the codes' ceil(M / 16) * 16 * K / 2
+ *   bytes, and the int32 zero points [M, K / had_block] at the next multiple
+ *   of 256 bytes after the scales.
  *   Other arguments and errors as w4a4_qlinear_forward.
  */
 int w4a4_qlinear_forward_asym(const void* x, int x_dtype, const uint8_t* wq,

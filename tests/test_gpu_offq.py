@@ -42,8 +42,13 @@ def gpu_codes(xq, M, layout):
     """uint4 codes q from the stored nibbles q - 8."""
     b = host(xq)
     if layout == "packed_tiled":
-        b = untile_weights(b, M)
+        return gpu_codes_tiled_bytes(b, M)
     return (O.unpack_int4(b).astype(np.int16) + 8).astype(np.uint8)
+
+
+def gpu_codes_tiled_bytes(b, M):
+    """uint4 codes q from packed tiled bytes of the nibbles q - 8."""
+    return (O.unpack_int4(untile_weights(b, M)).astype(np.int16) + 8).astype(np.uint8)
 
 
 # --------------------------------------------------------------------------
@@ -99,14 +104,19 @@ def test_quantize_act_asym_edge_groups():
     assert np.abs(zp).max() > 1000  # offsets were absorbed by zero points beyond the code range
 
 
-@pytest.mark.parametrize("M,K,b,dt", [(64, 4096, 128, "float16"), (48, 14336, 128, "float16"),
-                                      (8, 4096, 4096, "float16"), (100, 2048, 256, "float32")])
-def test_quantize_act_asym_fused_rotation(M, K, b, dt):
+@pytest.mark.parametrize("M,K,b,dt,layout", [
+    (64, 4096, 128, "float16", "packed"), (48, 14336, 128, "float16", "packed"),
+    (8, 4096, 4096, "float16", "packed"), (100, 2048, 256, "float32", "packed"),
+    (130, 4096, 128, "float16", "packed_tiled"), (2048, 4096, 128, "float16", "packed_tiled"),
+    (300, 14336, 128, "float16", "packed_tiled"), (65, 2048, 128, "float16", "packed_tiled")])
+def test_quantize_act_asym_fused_rotation(M, K, b, dt, layout):
+    # The tiled cases of fp16 rows (more than 64, b = 128) take the rotation
+    # on the matrix instruction.
     w = synth.small("af", M, K, 8, x_dtype=dt, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
-    xq, sx, zx = W.quantize_act_asym_int4(dev(X), b, b)
+    xq, sx, zx = W.quantize_act_asym_int4(dev(X), b, b, layout=layout)
     q, s, z = O.quantize_act_asym(O.rotate(X, b), b)
-    gq = gpu_codes(xq, M, "packed").astype(np.int64)
+    gq = gpu_codes(xq, M, layout).astype(np.int64)
     gz, gs = host(zx).astype(np.int64), host(sx).astype(np.float64)
     eff = (gq - np.repeat(gz, b, axis=1)) - (q.astype(np.int64) - np.repeat(z, b, axis=1))
     assert np.all(np.abs(eff) <= 1)
@@ -195,9 +205,17 @@ def run_asym_layer(w, sample_rows=None):
     Ad = dev(A.T) if A is not None else None
     Bd = dev(B.T) if B is not None else None
     print("asym layer", w.name, w.M, w.K, w.N, b, w.rank, flush=True)
-    y = host(W.qlinear_forward_asym(Xd, wqd, dev(ws), gsum, b, Ad, Bd))
-    xq, sx, zx = W.quantize_act_asym_int4(Xd, b, b)
-    gq, gs, gz = gpu_codes(xq, w.M, "packed"), host(sx), host(zx).astype(np.int64)
+    ws_buf = W.qlinear_workspace(w.M, w.N, w.K, w.rank, DEV)
+    y = host(W.qlinear_forward_asym(Xd, wqd, dev(ws), gsum, b, Ad, Bd, workspace=ws_buf))
+    # the codes, group scales and zero points the layer left in its workspace
+    wsb = host(ws_buf)
+    co, _, _ = W.qlinear_workspace_layout(w.M, w.N, w.K, w.rank, "tiled", 0)
+    Mp, G = W.pad16(w.M), w.K // b
+    so = co + (Mp * w.K // 2 + 255) // 256 * 256
+    zo = so + (w.M * G * 4 + 255) // 256 * 256
+    gq = gpu_codes_tiled_bytes(wsb[co:co + Mp * w.K // 2].reshape(Mp, w.K // 2), w.M)
+    gs = wsb[so:so + 4 * w.M * G].view(np.float32).reshape(w.M, G)
+    gz = wsb[zo:zo + 4 * w.M * G].view(np.int32).reshape(w.M, G).astype(np.int64)
     rows = np.arange(w.M) if sample_rows is None else sample_rows
     Xr = X[rows]
     q, s, z = O.quantize_act_asym(O.rotate(Xr, b), b)
