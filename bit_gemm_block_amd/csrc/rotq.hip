@@ -61,6 +61,7 @@
 // of two the quotient is formed as y / (s / rs), the same real number.
 #include "w4a4_internal.h"
 #include "lowrank_rows.h"
+#include "decode_roles.h"
 #include "rotq_mfma.h"
 
 #include <hip/hip_fp16.h>
@@ -171,41 +172,8 @@ struct RotqKArgs {
   const void* lr_at;      // then lr_rank blocks: column j of T = X . A (fp16, M <= 16)
   int lr_rank;
   void* lr_t;
-  const uint8_t* pf;      // then pf_blocks blocks read pf_units units of pf_unit bytes
-  int64_t pf_unit;        // (unit g is what the GEMM workgroup g will read)
-  int64_t pf_units;
-  int64_t pf_last;        // bytes of the last unit
-  int pf_blocks;
-  uint32_t pf_magic;      // the loaded words are folded and compared with this
+  ReadAhead ra;           // then ra.blocks blocks read the weights ahead (decode_roles.h)
 };
-
-// Reads the units g = x + 8 (p / 8 + t * (blocks / 8)) of the prefetch area,
-// where x is the XCD this block is assumed to run on (workgroups are placed
-// on the eight XCDs round-robin by index): the GEMM workgroup g runs on XCD
-// g mod 8, so its operand lands in that XCD's L2 and in the shared
-// last-level cache.  The loaded words are folded into a value that is
-// stored to LDS only if it equals a runtime constant, which keeps the loads.
-__device__ __forceinline__ void prefetch_role(const RotqKArgs& a, int p, int64_t launch_index,
-                                              uint32_t* sink) {
-  const int x = static_cast<int>(launch_index & 7);
-  const int per_xcd = a.pf_blocks / 8;
-  uint32_t fold = 0u;
-  for (int64_t g = x + 8 * static_cast<int64_t>(p / 8); g < a.pf_units; g += 8 * per_xcd) {
-    const int64_t bytes = g == a.pf_units - 1 ? a.pf_last : a.pf_unit;
-    const uint8_t* base = a.pf + g * a.pf_unit;
-    for (int64_t off0 = 0; off0 < bytes; off0 += 4 * 4096) {
-      uint4 w[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t off = off0 + u * 4096 + 16 * threadIdx.x;
-        w[u] = off + 16 <= bytes ? *reinterpret_cast<const uint4*>(base + off) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) fold ^= w[u].x ^ w[u].y ^ w[u].z ^ w[u].w;
-    }
-  }
-  if (fold == a.pf_magic) sink[0] = fold;
-}
 
 // Order-preserving map of float32 onto uint32 (unsigned compare = float
 // compare), for LDS atomic max of signed values, and its inverse.
@@ -256,7 +224,7 @@ __global__ void __launch_bounds__(256) rotq_kernel(RotqKArgs a) {
                               static_cast<const _Float16*>(a.lr_at), a.M, a.K, a.lr_rank, a.lr_t,
                               1, e, lds);
     } else {
-      prefetch_role(a, e - a.lr_rank, blockIdx.x, reinterpret_cast<uint32_t*>(lds));
+      read_ahead_role(a.ra, e - a.lr_rank, blockIdx.x, reinterpret_cast<uint32_t*>(lds));
     }
     return;
   }
@@ -796,17 +764,17 @@ constexpr int64_t kWideRows = 64;  // at most this many rows use the wide menu
 
 template <typename TIn>
 hipError_t launch_typed(const RotqKArgs& ka, const RotqPlan& p, int64_t M, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(ka.nrot_blocks + ka.lr_rank + ka.pf_blocks));
+  const dim3 grid(static_cast<unsigned>(ka.nrot_blocks + ka.lr_rank + ka.ra.blocks));
   // The low-rank and read-ahead roles are written for 256 threads (their K
   // and byte strides, and the four-wave reduction); the rotation blocks leave
   // threads past the plan's count idle.
-  const dim3 block((ka.lr_rank > 0 || ka.pf_blocks > 0) ? 256 : p.threads);
+  const dim3 block((ka.lr_rank > 0 || ka.ra.blocks > 0) ? 256 : p.threads);
   // Specialized quantizer for symmetric codes with float32 scales, fp16 input,
   // no extra roles and no MXFP4, asymmetric or residual output, on the
   // segment shapes of more than 64 rows.
   const bool plain = std::is_same<TIn, _Float16>::value && ka.mode != ROTQ_ROTATE && !ka.mx &&
                      !ka.asym && ka.res_pad == 0 && !ka.scale_f16 && ka.lr_rank == 0 &&
-                     ka.pf_blocks == 0;
+                     ka.ra.blocks == 0;
   if (plain) {
     uint32_t rsb;
     __builtin_memcpy(&rsb, &ka.rs, 4);
@@ -891,6 +859,17 @@ bool rotq_plan(int64_t M, int64_t K, int log2b, int64_t gsz, int max_lds, RotqPl
   return false;
 }
 
+static ReadAhead read_ahead_of(const RotqExtras& ex) {
+  ReadAhead r;
+  r.pf = ex.pf;
+  r.unit = ex.pf_unit;
+  r.units = ex.pf_units;
+  r.last = ex.pf_last;
+  r.blocks = ex.pf_blocks / 8 * 8;
+  r.magic = 0x9E3779B9u;
+  return r;
+}
+
 hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2b, int mode,
                        int64_t gsz, bool scale_f16, float* xrot, uint8_t* q, void* scale,
                        const RotqPlan& plan, hipStream_t st, const RotqExtras* ex) {
@@ -900,6 +879,18 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
   const bool plain_ex = !ex || (ex->qmax == 7 && !ex->asym_zero && ex->res_r == 0 && !ex->mx_scale &&
                                 ex->lr_rank == 0 && !ex->pf);
   const bool tiled4 = mode == ROTQ_QUANT_F6 || mode == ROTQ_QUANT_TILED;
+  // Decode launches with the low-rank or read-ahead roles (int4 codes of fp16
+  // rows into FP6 or packed tiles, one float32 scale per row).
+  const bool has_lr = ex && ex->lr_rank > 0 && x_f16 && M <= 16;
+  const bool has_pf = ex && ex->pf && ex->pf_units > 0 && ex->pf_blocks >= 8;
+  if (x_f16 && tiled4 && gsz == K && !scale_f16 && (has_lr || has_pf) && ex->qmax == 7 &&
+      !ex->asym_zero && ex->res_r == 0 && !ex->mx_scale && !ex->ob_sum &&
+      rotq_mfma_roles_ok(M, K, log2b))
+    return launch_rotq_mfma_roles(static_cast<const _Float16*>(x), M, K, log2b, mode == ROTQ_QUANT_F6,
+                                  q, static_cast<float*>(scale),
+                                  has_lr ? static_cast<const _Float16*>(ex->lr_at) : nullptr,
+                                  has_lr ? ex->lr_rank : 0, has_lr ? ex->lr_t : nullptr,
+                                  has_pf ? read_ahead_of(*ex) : ReadAhead{}, st);
   if (x_f16 && tiled4 && gsz == K && !scale_f16 && plain_ex) {
     const _Float16* xh = static_cast<const _Float16*>(x);
     float* sf = static_cast<float*>(scale);
@@ -957,14 +948,7 @@ hipError_t launch_rotq(const void* x, bool x_f16, int64_t M, int64_t K, int log2
       ka.lr_rank = ex->lr_rank;
       ka.lr_t = ex->lr_t;
     }
-    if (ex->pf && ex->pf_units > 0 && ex->pf_blocks >= 8) {
-      ka.pf = ex->pf;
-      ka.pf_unit = ex->pf_unit;
-      ka.pf_units = ex->pf_units;
-      ka.pf_last = ex->pf_last;
-      ka.pf_blocks = ex->pf_blocks / 8 * 8;
-      ka.pf_magic = 0x9E3779B9u;
-    }
+    if (ex->pf && ex->pf_units > 0 && ex->pf_blocks >= 8) ka.ra = read_ahead_of(*ex);
   }
   if (x_f16) return launch_typed<_Float16>(ka, plan, M, st);
   return launch_typed<float>(ka, plan, M, st);

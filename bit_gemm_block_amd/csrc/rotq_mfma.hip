@@ -54,6 +54,8 @@
 
 #include <hip/hip_fp16.h>
 
+#include "lowrank_rows.h"
+
 namespace w4a4 {
 namespace {
 
@@ -74,6 +76,13 @@ struct RotArgs {
   int32_t* ob_sum;    // offset-binary packed tiles: [M] sums of the odd channels' codes
   uint8_t* mx_scale;  // MXFP4: E8M0 scale bytes, 64 per 16 x 128 tile
   int32_t* zero;      // asymmetric codes: zero points [M, K / 128] (scale: [M, K / 128])
+  // Decode launches (ROLES): blocks [0, M) take row blockIdx.x, then lr_rank
+  // blocks compute column j of T = X . A, then ra.blocks read the weights
+  // ahead; every block has 256 threads.
+  const _Float16* lr_at;
+  int lr_rank;
+  void* lr_t;
+  ReadAhead ra;
   int64_t tile_stride;   // tiles per 16-row block (K / 128)
   int64_t rows_per_xcd;  // a multiple of 16
   uint64_t pi_tbl;    // 4 bits per lane column c: the sub-block that column c loads
@@ -322,8 +331,8 @@ __device__ __forceinline__ void lane_stage(float (&y)[32], int sel) {
 // their products through LDS.  One row per workgroup, all rows launched at
 // once.  (At least two waves per SIMD: the register cap keeps the
 // accumulators out of the AGPRs, which would take a copy per value.)
-template <int WV, int OUT, int P>
-__global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
+template <int WV, int OUT, int P, bool ROLES = false>
+__global__ void __launch_bounds__(ROLES ? 256 : 64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
   constexpr int kLaneStages = P < 4 ? P : 4;
   constexpr bool kPair = P == 5;
   // sqrt(b) a power of two: x~ / s = y / (s sqrt(b)) with both sides exact.
@@ -334,11 +343,34 @@ __global__ void __launch_bounds__(64 * WV, 2) rotq_mfma_kernel(RotArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
-  // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
-  // whole 16-row blocks, so that every line of a code tile is written from
-  // one L2.
-  const int64_t row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
-  if (row >= a.M) return;
+  int64_t row;
+  if constexpr (ROLES) {
+    // Decode launch: the roles after the M rotation blocks (whole workgroups,
+    // so no barrier is split), then one row per block.
+    __shared__ float role_lds[64];
+    if (static_cast<int64_t>(blockIdx.x) >= a.M) {
+      const int e = static_cast<int>(blockIdx.x - a.M);
+      if (e < a.lr_rank)
+        lowrank_rows_body<16>(a.x, a.lr_at, a.M, a.K, a.lr_rank, a.lr_t, 1, e, role_lds);
+      else
+        read_ahead_role(a.ra, e - a.lr_rank, blockIdx.x, reinterpret_cast<uint32_t*>(role_lds));
+      return;
+    }
+    row = blockIdx.x;
+    if (w >= WV) {
+      // Waves past the row's: take part in the row's barriers, then leave.
+      constexpr int kBarriers = (kPair ? 1 : 0) + (WV > 1 ? 1 : 0) + (OUT == OUT_PACKED_OB && WV > 1 ? 1 : 0);
+#pragma unroll
+      for (int k = 0; k < kBarriers; ++k) __syncthreads();
+      return;
+    }
+  } else {
+    // Workgroup b runs on XCD b % 8 (round robin); each XCD takes a range of
+    // whole 16-row blocks, so that every line of a code tile is written from
+    // one L2.
+    row = (blockIdx.x % 8) * a.rows_per_xcd + blockIdx.x / 8;
+    if (row >= a.M) return;
+  }
   const int pc = static_cast<int>((a.pi_tbl >> (4 * c)) & 15u);
   const _Float16* src = a.x + row * a.K + 2048 * w + 128 * pc + 8 * g;
 
@@ -530,7 +562,7 @@ int parity(int v) { return __builtin_popcount(static_cast<unsigned>(v)) & 1; }
 // Load permutation, per-stage signs and final signs of the lane stages with
 // partner masks 1, 2, 7, 8 (the first `stages` of them, which span the low
 // `stages` bits of the column index).
-void kron_tables(int stages, RotArgs* a) {
+void derive_kron_tables(int stages, RotArgs* a) {
   static constexpr int kMask[4] = {1, 2, 7, 8};
   const int n = 1 << stages;
   int coord[16] = {};
@@ -559,6 +591,28 @@ void kron_tables(int stages, RotArgs* a) {
   }
 }
 
+// The tables for 0-4 stages, derived once.
+void kron_tables(int stages, RotArgs* a) {
+  struct Tables {
+    uint64_t pi[5], sel[5];
+    uint32_t sig[5];
+  };
+  static const Tables t = [] {
+    Tables r{};
+    for (int n = 0; n < 5; ++n) {
+      RotArgs x{};
+      derive_kron_tables(n, &x);
+      r.pi[n] = x.pi_tbl;
+      r.sel[n] = x.sel_tbl;
+      r.sig[n] = x.sig_tbl;
+    }
+    return r;
+  }();
+  a->pi_tbl = t.pi[stages];
+  a->sel_tbl = t.sel[stages];
+  a->sig_tbl = t.sig[stages];
+}
+
 RotArgs base_args(const _Float16* x, int64_t M, int64_t K, int log2b, uint8_t* q, float* scale,
                   int32_t* ob_sum) {
   RotArgs a{};
@@ -579,7 +633,7 @@ RotArgs base_args(const _Float16* x, int64_t M, int64_t K, int log2b, uint8_t* q
 
 bool rotq_mfma_ok(int64_t M, int64_t K, int log2b) {
   const int64_t step = log2b == 12 ? 4096 : 2048;
-  return M > 64 && K % step == 0 && K >= step && K <= 16384 && log2b >= 7 && log2b <= 12;
+  return M > 0 && K % step == 0 && K >= step && K <= 16384 && log2b >= 7 && log2b <= 12;
 }
 
 hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, RotMfmaOut out_kind,
@@ -647,6 +701,57 @@ hipError_t launch_rotq_mfma(const _Float16* x, int64_t M, int64_t K, int log2b, 
 #undef W4A4_ROT_W
 #undef W4A4_ROT_P0
 #undef W4A4_ROT
+}
+
+bool rotq_mfma_roles_ok(int64_t M, int64_t K, int log2b) {
+  const int64_t step = log2b == 12 ? 4096 : 2048;
+  return M > 0 && M <= 64 && K % step == 0 && K >= step && K <= 8192 && log2b >= 7 && log2b <= 12;
+}
+
+hipError_t launch_rotq_mfma_roles(const _Float16* x, int64_t M, int64_t K, int log2b, bool f6,
+                                  uint8_t* q, float* scale, const _Float16* lr_at, int lr_rank,
+                                  void* lr_t, const ReadAhead& ra, hipStream_t st) {
+  if (!rotq_mfma_roles_ok(M, K, log2b) || (lr_rank > 0 && M > 16) || ra.blocks % 8 != 0)
+    return hipErrorInvalidValue;
+  RotArgs a = base_args(x, M, K, log2b, q, scale, nullptr);
+  a.lr_at = lr_at;
+  a.lr_rank = lr_rank;
+  a.lr_t = lr_t;
+  a.ra = ra;
+  a.qmax = 7.f;
+  const int p = log2b - 7;
+  kron_tables(p < 4 ? p : 4, &a);
+  const int WV = static_cast<int>(K / 2048);
+  const dim3 grid(static_cast<unsigned>(M + lr_rank + ra.blocks));
+#define W4A4_ROLES(WW, OO)                                                                            \
+  switch (p) {                                                                                        \
+    case 0: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 0, true>), grid, dim3(256), 0, st, a); break; \
+    case 1: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 1, true>), grid, dim3(256), 0, st, a); break; \
+    case 2: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 2, true>), grid, dim3(256), 0, st, a); break; \
+    case 3: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 3, true>), grid, dim3(256), 0, st, a); break; \
+    case 4: hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 4, true>), grid, dim3(256), 0, st, a); break; \
+    default:                                                                                          \
+      if constexpr (WW % 2 == 0)                                                                      \
+        hipLaunchKernelGGL((rotq_mfma_kernel<WW, OO, 5, true>), grid, dim3(256), 0, st, a);           \
+      else                                                                                            \
+        return hipErrorInvalidValue;                                                                  \
+      break;                                                                                          \
+  }                                                                                                   \
+  return hipGetLastError();
+#define W4A4_ROLES_W(WW)   \
+  case WW:                  \
+    if (f6) {               \
+      W4A4_ROLES(WW, OUT_F6) \
+    } else {                \
+      W4A4_ROLES(WW, OUT_PACKED) \
+    }
+  switch (WV) {
+    W4A4_ROLES_W(1) W4A4_ROLES_W(2) W4A4_ROLES_W(3) W4A4_ROLES_W(4)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef W4A4_ROLES_W
+#undef W4A4_ROLES
 }
 
 }  // namespace w4a4

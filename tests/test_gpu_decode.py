@@ -3,9 +3,9 @@ weights with per-channel scales: the rotation launch (with the low-rank
 projection and the weight read-ahead folded in) and the skinny GEMM.
 
 Besides the layer bars of tests/test_gpu_parity.py:
-* Y on tiled and offset-binary weights equals, bit for bit, Y on row-major
-  weights (int8 codes, another GEMM kernel: the same codes, the same exact
-  integer sums and the same float32 epilogue arithmetic);
+* Y on tiled weights equals, bit for bit, Y on offset-binary tiled weights
+  (another GEMM kernel: the same codes, the same exact integer sums and the
+  same float32 epilogue arithmetic);
 * a captured HIP graph of several calls, replayed with eager work and
   synchronisations in between, gives the eager result on every replay;
 * two different inputs through one workspace, alternately, each give their
@@ -60,9 +60,10 @@ def test_decode_layer_tiled(M, K, N, b, r, dt, wl):
     wsd = dev(ws)
     ws_buf = W.qlinear_workspace(M, N, K, r, DEV)
     y = host(W.qlinear_forward(X, ops[wl], wsd, b, 0, At, Bt, workspace=ws_buf, w_layout=wl))
-    # row-major weights: same codes, same arithmetic
-    y_rm = host(W.qlinear_forward(X, ops["rowmajor"], wsd, b, 0, At, Bt, w_layout="rowmajor"))
-    assert np.array_equal(y, y_rm)
+    # the other tiled weight layout: same codes, same arithmetic
+    other = "tiled_ob" if wl == "tiled" else "tiled"
+    y_other = host(W.qlinear_forward(X, ops[other], wsd, b, 0, At, Bt, w_layout=other))
+    assert np.array_equal(y, y_other)
     wsb = host(ws_buf)
     co, cl, so = W.qlinear_workspace_layout(M, N, K, r, wl, 0)
     _, packed = workspace_codes(wsb, co, M, K, cl)
@@ -121,9 +122,10 @@ def test_decode_back_to_back_sizes():
         X = dev(d["X"])
         y = host(W.qlinear_forward(X, ops["tiled_ob"], dev(ws), w.had_block, 0, At, Bt,
                                    workspace=ws_buf, w_layout="tiled_ob"))
-        y_rm = host(W.qlinear_forward(X, ops["rowmajor"], dev(ws), w.had_block, 0, At, Bt,
-                                      w_layout="rowmajor"))
-        assert np.array_equal(y, y_rm)
+        # the same call with a workspace of its own
+        y_own = host(W.qlinear_forward(X, ops["tiled_ob"], dev(ws), w.had_block, 0, At, Bt,
+                                       w_layout="tiled_ob"))
+        assert np.array_equal(y, y_own)
     del w_big
 
 
@@ -137,8 +139,8 @@ def test_decode_alternating_inputs(wl):
     X1 = dev(d["X"])
     X2 = dev(np.ascontiguousarray(d["X"][::-1] * np.float16(-0.5)))
     wsd = dev(ws)
-    refs = [host(W.qlinear_forward(X, ops["rowmajor"], wsd, 4096, 0, At, Bt, w_layout="rowmajor"))
-            for X in (X1, X2)]
+    refs = [host(W.qlinear_forward(X, ops[wl], wsd, 4096, 0, At, Bt, w_layout=wl))
+            for X in (X1, X2)]   # each with a workspace of its own
     assert not np.array_equal(refs[0], refs[1])
     ws_buf = W.qlinear_workspace(w.M, w.N, w.K, w.rank, DEV)
     for i in range(8):

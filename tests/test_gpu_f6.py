@@ -62,25 +62,25 @@ def test_quantize_act_f6_exact(M, K, b, dt):
 
 @pytest.mark.parametrize("M,K,b,dt", [(130, 4096, 4096, "float32"), (37, 4096, 4096, "float16"),
                                       (9, 14336, 128, "float16"), (300, 1024, 256, "float16"),
-                                      (60, 4096, 128, "float16")])
+                                      (60, 4096, 128, "float16"), (12, 2048, 256, "float32")])
 def test_quantize_act_f6_fused_matches_packed(M, K, b, dt):
-    # The butterfly kernel's FP6 mode against its packed mode.  (fp16 rows,
-    # more than 64 of them, with b = 128 or with K a multiple of 4096 take the
-    # matrix-instruction rotation instead: test_gpu_rot_kron.py and the b = 128
-    # test below.)
+    # FP6 tiles against packed tiles of the same call: the same kernel (the
+    # matrix-instruction rotation for fp16 rows with K a multiple of 2048, of
+    # 4096 for b = 4096; the butterfly kernel otherwise) and the same
+    # arithmetic, so the same codes and scales.
     w = synth.small("qf6f", M, K, 8, x_dtype=dt, n_outlier=3, bos_factor=500.0)
     Xd = dev(synth.make_inputs(w)["X"])
     print("quantize_act f6 fused", M, K, b, dt, flush=True)
     xf, sf = W.quantize_act_int4(Xd, b, layout="f6_tiled")
-    xp, sp = W.quantize_act_int4(Xd, b, layout="packed")
+    xp, sp = W.quantize_act_int4(Xd, b, layout="packed_tiled")
     assert np.array_equal(host(sf), host(sp))
-    assert np.array_equal(untile_f6(host(xf), M, K), O.unpack_int4(host(xp)))
+    assert np.array_equal(untile_f6(host(xf), M, K), O.unpack_int4(untile_weights(host(xp), M)))
 
 
 @pytest.mark.parametrize("M,K", [(65, 2048), (130, 4096), (4100, 4096), (200, 14336),
                                  (77, 16384), (1000, 6144)])
 def test_quantize_act_f6_b128_matrix_rotation(M, K):
-    # FP6 codes of fp16 rows with b = 128 (more than 64 rows): the transform
+    # FP6 codes of fp16 rows with b = 128: the transform
     # runs on the fp16 matrix instruction, so its float32 sums round in
     # another order than the butterflies'; against the oracle the codes meet
     # the fused-path bar (at most 0.01% differ, each by one step) and the
@@ -235,7 +235,7 @@ def run_layer_f6(w, rows=None):
     (65, 14336, 96, 128, 128, 0, "float16"), (300, 1024, 1030, 256, 0, 40, "float16"),
     (40, 384, 100, 128, 128, 0, "float32"), (20, 4096, 520, 128, 0, 24, "float16"),
     (130, 1024, 260, 128, 256, 16, "float32"), (8, 4096, 4096, 4096, 0, 64, "float16"),
-    (257, 2048, 384, 128, 128, 32, "float16")])
+    (257, 2048, 384, 128, 128, 32, "float16"), (16, 2048, 64, 128, 0, 8, "float16")])
 def test_qlinear_f6_ragged(M, K, N, b, g, r, dt):
     w = synth.small("rf6", M, K, N, x_dtype=dt, had_block=b, w_group=g, rank=r,
                     w_scale_dtype="float16" if dt == "float16" else "float32")

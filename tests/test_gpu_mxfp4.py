@@ -101,8 +101,8 @@ def test_quantize_mxfp4_row_major_small_k():
                                    (130, 4096, 128), (2048, 4096, 4096), (300, 8192, 1024),
                                    (97, 6144, 2048), (77, 16384, 4096), (1000, 14336, 128)])
 def test_quantize_mxfp4_fused_rotation(M, K, b):
-    # fp16 rows, more than 64 of them: the rotation on the matrix instruction
-    # (the tiled layout; the row-major one keeps the butterfly kernel)
+    # fp16 rows with K a multiple of 2048: the rotation on the matrix
+    # instruction (the tiled layout; the row-major one keeps the butterfly kernel)
     w = synth.small("mxf", M, K, 8, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]
     codes, e = gpu_mx(X, b, "packed_tiled")

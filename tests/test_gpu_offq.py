@@ -110,7 +110,7 @@ def test_quantize_act_asym_edge_groups():
     (130, 4096, 128, "float16", "packed_tiled"), (2048, 4096, 128, "float16", "packed_tiled"),
     (300, 14336, 128, "float16", "packed_tiled"), (65, 2048, 128, "float16", "packed_tiled")])
 def test_quantize_act_asym_fused_rotation(M, K, b, dt, layout):
-    # The tiled cases of fp16 rows (more than 64, b = 128) take the rotation
+    # The tiled cases of fp16 rows (b = 128, K a multiple of 2048) take the rotation
     # on the matrix instruction.
     w = synth.small("af", M, K, 8, x_dtype=dt, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]

@@ -550,7 +550,7 @@ def test_quantize_act_int8_ties_and_extremes():
 def test_quantize_act_int8_fused_rotation(M, K, b, layout):
     # fp32 FWHT against the float64 rotation: every flip is one step and at
     # most 0.01% of the codes flip (the 4-bit bar; measured ~4e-6 here).  The
-    # tiled cases of fp16 rows (more than 64) take the rotation on the matrix
+    # tiled cases of fp16 rows take the rotation on the matrix
     # instruction.
     w = synth.small("f8", M, K, 8, n_outlier=4, bos_factor=500.0)
     X = synth.make_inputs(w)["X"]

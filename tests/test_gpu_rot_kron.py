@@ -3,7 +3,7 @@
 instruction, then H_n across the n = b / 128 sub-blocks with lane and register
 stages; Sylvester's construction gives H_b = H_n (x) H_128) against the CPU
 oracle, through the C ABI.  It runs for the tiled 4-bit codes of fp16 rows with
-one scale per row, more than 64 rows and K a multiple of 4096.
+one scale per row, and K a multiple of 4096 here (2048 for b up to 2048).
 
 Bars (the fused-path bar, as for the butterfly kernel: the float32 sums of the
 transform round in another order than the oracle's float64 ones):
