@@ -12,13 +12,12 @@
 //
 // fp32 inputs: LDS-tiled float32 FMA, T written as float32.
 #include "w4a4_internal.h"
+#include "gemm_common.h"
 #include "lowrank_rows.h"
 
 namespace w4a4 {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int NCB, int KW, int PF>
 __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __restrict__ x,
@@ -90,6 +89,129 @@ __global__ void __launch_bounds__(64 * KW) lowrank_f16_kernel(const _Float16* __
               static_cast<_Float16*>(t)[M * rank + m * rank + j] = lo;
             } else {
               static_cast<float*>(t)[m * rank + j] = s[i];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Prefill sizes (fp16, rank <= 16 NCB <= 32, K a multiple of 512): one
+// workgroup of four waves per 16 rows of X, fed by direct-to-LDS copies.
+// Stage s holds channels [512 s, 512 s + 512) of the 16 rows of X and of the
+// 16 NCB rows of At, each row one contiguous 1 KB run (the register-loaded
+// kernel above reads 16 rows x 64 bytes per load instruction, and At once per
+// 16 rows of X, which bounded it at about 7 TB/s from the L2); rows lie
+// 1040 bytes apart in LDS, so that the fragment reads of 16 rows fall in
+// distinct banks.  Three stages are in flight.  Wave w multiplies K steps
+// [4 w, 4 w + 4) of every stage; the waves' partial tiles are summed in LDS
+// in a fixed order.  Rows past M and columns past rank read the last valid
+// row (their results are not stored).
+template <int NCB>
+__global__ void __launch_bounds__(256) lowrank_stage_kernel(const _Float16* __restrict__ x,
+                                                            const _Float16* __restrict__ at,
+                                                            int64_t M, int64_t K, int rank,
+                                                            void* __restrict__ t, int pair_out) {
+  constexpr int ROWS = 16 + 16 * NCB;  // X rows, then At rows
+  constexpr int RS = 1040;             // LDS bytes per row
+  constexpr int STAGE = ROWS * RS;
+  constexpr int CPW = ROWS / 4;        // copies per wave per stage
+  constexpr int STAGES = 3;
+  static_assert((STAGES - 1) * CPW < 64, "in-flight copies exceed vmcnt");
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[STAGE];
+  __shared__ f32x4 red[4][NCB][64];
+  auto stage = [&](int sidx) -> uint8_t* { return sidx == 0 ? st0 : sidx == 1 ? st1 : st2; };
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int nst = static_cast<int>(K / 512);
+
+  // Copy q of this wave: stage row wave + 4 q.
+  const uint8_t* src[CPW];
+#pragma unroll
+  for (int q = 0; q < CPW; ++q) {
+    const int row = wave + 4 * q;
+    const _Float16* p;
+    if (row < 16) {
+      const int64_t m = m0 + row < M ? m0 + row : M - 1;
+      p = x + m * K;
+    } else {
+      const int j = row - 16 < rank ? row - 16 : rank - 1;
+      p = at + static_cast<int64_t>(j) * K;
+    }
+    src[q] = reinterpret_cast<const uint8_t*>(p) + 16 * lane;
+  }
+  auto issue = [&](int s, uint8_t* buf) {
+    const uint32_t b = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
+#pragma unroll
+    for (int q = 0; q < CPW; ++q) dma16(src[q] + static_cast<int64_t>(s) * 1024, b + (wave + 4 * q) * RS);
+  };
+
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int r = lane & 15, g = lane >> 4;
+  auto compute = [&](const uint8_t* buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int off = (4 * wave + u) * 64 + 16 * g;
+      const half8 xa = *reinterpret_cast<const half8*>(buf + r * RS + off);
+      half8 ab[NCB];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) ab[c] = *reinterpret_cast<const half8*>(buf + (16 + 16 * c + r) * RS + off);
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ab[c], acc[c], 0, 0, 0);
+    }
+  };
+  // Stage s: once it has landed and the barrier has retired every wave's
+  // reads of stage s - 1, that buffer takes stage s + 2.
+  auto iterate = [&](int s, int sbuf, bool steady) {
+    if (steady || s + 2 <= nst)
+      wait_vmcnt<CPW>();
+    else
+      wait_vmcnt<0>();
+    stage_barrier();
+    if (steady || s + 2 < nst) issue(s + 2, stage((sbuf + 2) % 3));
+    compute(stage(sbuf));
+  };
+  issue(0, st0);
+  if (nst > 1) issue(1, st1);
+  int s0 = 0;
+  for (; s0 + 6 <= nst; s0 += 3) {
+    iterate(s0, 0, true);
+    iterate(s0 + 1, 1, true);
+    iterate(s0 + 2, 2, true);
+  }
+#pragma unroll
+  for (int u = 0; u < 6; ++u)
+    if (s0 + u < nst) iterate(s0 + u, u % 3, false);
+
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) red[wave][c][lane] = acc[c];
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      f32x4 sum = red[0][c][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) sum += red[w][c][lane];
+      const int j = c * 16 + (lane & 15);
+      if (j < rank) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + (lane >> 4) * 4 + i;
+          if (m < M) {
+            if (pair_out) {
+              const _Float16 hi = static_cast<_Float16>(sum[i]);
+              const _Float16 lo = static_cast<_Float16>(sum[i] - static_cast<float>(hi));
+              static_cast<_Float16*>(t)[m * rank + j] = hi;
+              static_cast<_Float16*>(t)[M * rank + m * rank + j] = lo;
+            } else {
+              static_cast<float*>(t)[m * rank + j] = sum[i];
             }
           }
         }
@@ -192,6 +314,15 @@ hipError_t launch_lowrank_project(const void* x, bool x_f16, const void* at, int
     if (M <= 16) {
       hipLaunchKernelGGL((lowrank_rows_kernel<16>), dim3(rank), dim3(256), 0, st, xh, ah, M, K,
                          rank, t, pair);
+      return hipGetLastError();
+    }
+    // Prefill sizes: the staged kernel.
+    if (row_tiles >= 64 && rank <= 32 && K % 512 == 0) {
+      const dim3 grid(static_cast<unsigned>(row_tiles));
+      if (rank <= 16)
+        hipLaunchKernelGGL((lowrank_stage_kernel<1>), grid, dim3(256), 0, st, xh, ah, M, K, rank, t, pair);
+      else
+        hipLaunchKernelGGL((lowrank_stage_kernel<2>), grid, dim3(256), 0, st, xh, ah, M, K, rank, t, pair);
       return hipGetLastError();
     }
     // Few row tiles: one 16-column block per workgroup for parallelism.
