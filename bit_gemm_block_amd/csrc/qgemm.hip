@@ -105,7 +105,10 @@ __device__ __forceinline__ int a8_off(int r, int h, int g) {
 
 // The first LR_PRE 32-wide rank chunks of the fp16 low-rank operands of one
 // 16x16 output block, loaded ahead of the main loop by the waves that run
-// the epilogue (so that these loads overlap the weight stream).
+// the epilogue (so that these loads overlap the weight stream).  The loads
+// are unconditional, from clamped indices (rows past M or N give outputs that
+// are not stored), so that no select of a loaded value makes the wave wait
+// here; rank chunks past the rank are zeroed when the term is applied.
 constexpr int LR_PRE = 2;
 struct LowRankPre {
   half8 hi[LR_PRE], lo[LR_PRE], bb[LR_PRE];
@@ -113,28 +116,32 @@ struct LowRankPre {
 
 __device__ __forceinline__ void load_lowrank_pre(const GemmArgs& a, int64_t mblk, int64_t nblk,
                                                  int lane, LowRankPre& p) {
-  const int64_t mr = mblk + (lane & 15);
-  const int64_t nr = nblk + (lane & 15);
+  const int64_t mr0 = mblk + (lane & 15);
+  const int64_t nr0 = nblk + (lane & 15);
+  const int64_t mr = mr0 < a.M ? mr0 : a.M - 1;
+  const int64_t nr = nr0 < a.N ? nr0 : a.N - 1;
   const int koff = (lane >> 4) * 8;
   const _Float16* th = static_cast<const _Float16*>(a.t);
   const _Float16* tl = th + a.M * a.rank;
   const _Float16* bt = static_cast<const _Float16*>(a.B);
-  const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int q = 0; q < LR_PRE; ++q) {
-    const int j = q * 32 + koff;
-    const bool jok = j < a.rank;
-    p.hi[q] = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(th + mr * a.rank + j) : z;
-    p.lo[q] = (jok && mr < a.M) ? *reinterpret_cast<const half8*>(tl + mr * a.rank + j) : z;
-    p.bb[q] = (jok && nr < a.N) ? *reinterpret_cast<const half8*>(bt + nr * a.rank + j) : z;
+    const int j0 = q * 32 + koff;
+    const int j = j0 < a.rank ? j0 : a.rank - 8;  // the rank is a multiple of 8
+    p.hi[q] = *reinterpret_cast<const half8*>(th + mr * a.rank + j);
+    p.lo[q] = *reinterpret_cast<const half8*>(tl + mr * a.rank + j);
+    p.bb[q] = *reinterpret_cast<const half8*>(bt + nr * a.rank + j);
   }
 }
 
-__device__ __forceinline__ f32x4 apply_lowrank_pre(const LowRankPre& p, f32x4 v) {
+__device__ __forceinline__ f32x4 apply_lowrank_pre(const GemmArgs& a, const LowRankPre& p, int lane,
+                                                   f32x4 v) {
+  const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int q = 0; q < LR_PRE; ++q) {
-    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.lo[q], p.bb[q], v, 0, 0, 0);
-    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.hi[q], p.bb[q], v, 0, 0, 0);
+    const half8 bb = q * 32 + (lane >> 4) * 8 < a.rank ? p.bb[q] : z;
+    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.lo[q], bb, v, 0, 0, 0);
+    v = __builtin_amdgcn_mfma_f32_16x16x32_f16(p.hi[q], bb, v, 0, 0, 0);
   }
   return v;
 }
@@ -1290,18 +1297,28 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
   const int64_t p_end = npairs * (wave + 1) / KW;
 
   // The epilogue waves load their scales and low-rank operands first, so
-  // that these loads overlap the weight stream instead of following it.
-  float sx_pre[4] = {0.f, 0.f, 0.f, 0.f};
-  float sw_pre = 1.f;
+  // that these loads overlap the weight stream instead of following it.  The
+  // scales are loaded as raw bits from clamped indices, unconditionally, and
+  // converted and masked only in the epilogue: arithmetic on them here (or a
+  // select of the loaded value) made the wave wait for each load in turn
+  // before issuing its weight loads, about 1 us per launch.
+  uint32_t sx_bits[4] = {0u, 0u, 0u, 0u};
+  uint32_t sw_bits = 0u;
   LowRankPre lrp;
   if (wave < MB && want_y) {
     const int64_t mblk = wave * 16;
     const int64_t n = n0 + (lane & 15);
-    if (!GROUPED && n < a.N) sw_pre = load_scale(a.sw, n, a.sw_f16);
+    const int64_t nc = n < a.N ? n : a.N - 1;
+    if (!GROUPED) {
+      if (a.sw_f16)
+        sw_bits = reinterpret_cast<const uint16_t*>(a.sw)[nc];
+      else
+        sw_bits = reinterpret_cast<const uint32_t*>(a.sw)[nc];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t m = mblk + (lane >> 4) * 4 + r;
-      sx_pre[r] = m < a.M ? a.sx[m] * (AI8 ? kInv16 : kInv256) : 0.f;
+      sx_bits[r] = reinterpret_cast<const uint32_t*>(a.sx)[m < a.M ? m : a.M - 1];
     }
     if constexpr (LRMODE == LR_F16) load_lowrank_pre(a, mblk, n0, lane, lrp);
   }
@@ -1431,11 +1448,21 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_kernel(GemmArgs a) {
 #pragma unroll
         for (int w = 1; w < KW; ++w) fsum += fred[w][b][lane];
       }
+      float sx_pre[4];
+      float sw_pre = 1.f;
+      if (!GROUPED && n0 + (lane & 15) < a.N)
+        sw_pre = a.sw_f16 ? __half2float(__ushort_as_half(static_cast<unsigned short>(sw_bits)))
+                          : __uint_as_float(sw_bits);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mblk + (lane >> 4) * 4 + r;
+        sx_pre[r] = m < a.M ? __uint_as_float(sx_bits[r]) * (AI8 ? kInv16 : kInv256) : 0.f;
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         yv[r] = GROUPED ? fsum[r] * sx_pre[r] : static_cast<float>(total[r]) * (sx_pre[r] * sw_pre);
       if constexpr (LRMODE == LR_F16) {
-        yv = apply_lowrank_pre(lrp, yv);
+        yv = apply_lowrank_pre(a, lrp, lane, yv);
         yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane, 32 * LR_PRE);
       } else {
         yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
