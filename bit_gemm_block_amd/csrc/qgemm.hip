@@ -1509,6 +1509,31 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
   const int p_begin = static_cast<int>(static_cast<int64_t>(nsteps) * wave / KW);
   const int p_end = static_cast<int>(static_cast<int64_t>(nsteps) * (wave + 1) / KW);
 
+  // The epilogue waves load their scales and low-rank operands first, as
+  // raw bits from clamped indices (the skinny kernel's rule), so that these
+  // loads overlap the weight stream instead of following it.
+  uint32_t sw_bits = 0u;
+  uint32_t sx_bits[4] = {0u, 0u, 0u, 0u};
+  LowRankPre lrp;
+  if (wave < MB && want_y) {
+    const int64_t mblk = wave * 16;
+    const int64_t nc = nrow < a.N ? nrow : a.N - 1;
+    if constexpr (XM != XMX) {
+      if (a.sw_f16)
+        sw_bits = reinterpret_cast<const uint16_t*>(a.sw)[nc];
+      else
+        sw_bits = reinterpret_cast<const uint32_t*>(a.sw)[nc];
+    }
+    if constexpr (XM == XRES) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t m = mblk + (lane >> 4) * 4 + r;
+        sx_bits[r] = reinterpret_cast<const uint32_t*>(a.sx)[m < a.M ? m : a.M - 1];
+      }
+    }
+    if constexpr (LRMODE == LR_F16) load_lowrank_pre(a, mblk, n0, lane, lrp);
+  }
+
   i32x4 acc[MB], accr[XM == XRES ? MB : 1];
   f32x4 facc[FL ? MB : 1];
 #pragma unroll
@@ -1639,12 +1664,15 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
     }
     f32x4 yv = f32x4{0.f, 0.f, 0.f, 0.f};
     if (want_y) {
-      const float swn = (XM != XMX && n_ok) ? load_scale(a.sw, nrow, a.sw_f16) : 1.f;
+      float swn = 1.f;
+      if (XM != XMX && n_ok)
+        swn = a.sw_f16 ? __half2float(__ushort_as_half(static_cast<unsigned short>(sw_bits)))
+                       : __uint_as_float(sw_bits);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t m = mblk + (lane >> 4) * 4 + r;
         if constexpr (XM == XRES) {
-          const float sx = m < a.M ? a.sx[m] * (kInv256 * 0.125f) : 0.f;
+          const float sx = m < a.M ? __uint_as_float(sx_bits[r]) * (kInv256 * 0.125f) : 0.f;
           yv[r] = static_cast<float>(total[r]) * (sx * swn);
         } else if constexpr (XM == XMX) {
           yv[r] = fsum[r];
@@ -1656,7 +1684,12 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
           yv[r] = (fsum[r] - corr) * swn;
         }
       }
-      yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
+      if constexpr (LRMODE == LR_F16) {
+        yv = apply_lowrank_pre(a, lrp, lane, yv);
+        yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane, 32 * LR_PRE);
+      } else {
+        yv = add_lowrank<LRMODE>(a, yv, mblk, n0, lane);
+      }
     }
     const int64_t n = n0 + (lane & 15);
     if (n < a.N) {
