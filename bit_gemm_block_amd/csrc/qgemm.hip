@@ -1542,6 +1542,33 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
     if constexpr (XM == XRES) accr[b] = i32x4{0, 0, 0, 0};
     if constexpr (FL) facc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // One batch of steps (weights, codes and, for MXFP4, their scale bytes)
+  // into registers.  The first batch is issued before the asymmetric groups'
+  // staging below, so that the weights are in flight during its round trip.
+  uint4 wv[CH], xv[CH][MB];
+  int ws_[XM == XMX ? CH : 1], xs_[XM == XMX ? CH : 1][MB];
+  auto load_batch = [&](int p0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int p = p0 + c;
+      const bool ok = p < p_end;
+      const int pa = (XM == XRES && p >= nkt) ? p - nkt : p;     // code step
+      wv[c] = ok ? *reinterpret_cast<const uint4*>(a.wq + (n0 / 16 * nsteps + p) * 1024 + 16 * lane)
+                 : make_uint4(0, 0, 0, 0);
+      if constexpr (XM == XMX)
+        ws_[c] = ok ? a.mx_ws[(n0 / 16 * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
+#pragma unroll
+      for (int b = 0; b < MB; ++b) {
+        const int64_t mb = b < mlast ? b : mlast;
+        xv[c][b] = ok ? *reinterpret_cast<const uint4*>(a.xq + (mb * nkt + pa) * 1024 + 16 * lane)
+                      : make_uint4(0, 0, 0, 0);
+        if constexpr (XM == XMX)
+          xs_[c][b] = ok ? a.mx_xs[(mb * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
+      }
+    }
+  };
+  if (p_begin < p_end) load_batch(p_begin);
+
   // Asymmetric groups: the rows' scales (times 1/256) and offsets
   // s (z - 8), and the columns' weight sums, staged in LDS as [group][row]
   // and [group][column] before the loop (dynamic LDS of 4 (2 * 16 MB + 16) G
@@ -1579,26 +1606,7 @@ __global__ void __launch_bounds__(64 * KW) qgemm_skinny_x_kernel(GemmArgs a) {
   };
 
   for (int p0 = p_begin; p0 < p_end; p0 += CH) {
-    uint4 wv[CH], xv[CH][MB];
-    int ws_[XM == XMX ? CH : 1], xs_[XM == XMX ? CH : 1][MB];
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int p = p0 + c;
-      const bool ok = p < p_end;
-      const int pa = (XM == XRES && p >= nkt) ? p - nkt : p;     // code step
-      wv[c] = ok ? *reinterpret_cast<const uint4*>(a.wq + (n0 / 16 * nsteps + p) * 1024 + 16 * lane)
-                 : make_uint4(0, 0, 0, 0);
-      if constexpr (XM == XMX)
-        ws_[c] = ok ? a.mx_ws[(n0 / 16 * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
-#pragma unroll
-      for (int b = 0; b < MB; ++b) {
-        const int64_t mb = b < mlast ? b : mlast;
-        xv[c][b] = ok ? *reinterpret_cast<const uint4*>(a.xq + (mb * nkt + pa) * 1024 + 16 * lane)
-                      : make_uint4(0, 0, 0, 0);
-        if constexpr (XM == XMX)
-          xs_[c][b] = ok ? a.mx_xs[(mb * nkt + p) * 64 + (lane >> 4) * 16 + (lane & 15)] : 127;
-      }
-    }
+    if (p0 != p_begin) load_batch(p0);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int p = p0 + c;
