@@ -49,7 +49,10 @@ def prepared(w):
     (8, 4096, 4096, 4096, 64, "float16"), (1, 4096, 520, 4096, 0, "float16"),
     (16, 4096, 100, 128, 8, "float16"), (5, 2048, 300, 2048, 16, "float16"),
     (8, 8192, 96, 4096, 64, "float16"), (3, 4096, 64, 256, 0, "float32"),
-    (12, 2048, 33, 128, 0, "float32"), (8, 12288, 40, 4096, 32, "float16")])
+    (12, 2048, 33, 128, 0, "float32"), (8, 12288, 40, 4096, 32, "float16"),
+    # a partial last rank chunk, ranks past the preloaded 64, two 16-row blocks
+    (8, 4096, 96, 4096, 40, "float16"), (20, 4096, 64, 4096, 72, "float16"),
+    (32, 2048, 130, 128, 24, "float16")])
 @pytest.mark.parametrize("wl", ["tiled", "tiled_ob"])
 def test_decode_layer_tiled(M, K, N, b, r, dt, wl):
     w = synth.small("dec1", M, K, N, x_dtype=dt, had_block=b, rank=r,

@@ -191,7 +191,8 @@ def run_mx_layer(w, sample_rows=None):
     (1, 256, 64, 256, 0, "float16"), (130, 1024, 260, 128, 16, "float16"),
     (33, 4096, 100, 4096, 64, "float16"), (65, 14336, 96, 128, 32, "float16"),
     (40, 384, 100, 128, 0, "float32"), (16, 512, 48, 128, 8, "float32"),
-    (8, 6144, 96, 128, 64, "float16"), (8, 12288, 64, 128, 64, "float16")])
+    (8, 6144, 96, 128, 64, "float16"), (8, 12288, 64, 128, 64, "float16"),
+    (8, 4096, 96, 4096, 40, "float16"), (24, 2048, 100, 128, 72, "float16")])
 def test_qlinear_mxfp4_ragged(M, K, N, b, r, dt):
     w = synth.small("mxl", M, K, N, x_dtype=dt, had_block=b, rank=r)
     run_mx_layer(w)

@@ -237,6 +237,7 @@ def run_asym_layer(w, sample_rows=None):
     (1, 256, 64, 128, 0, "float16"), (130, 1024, 260, 128, 16, "float16"),
     (33, 4096, 100, 4096, 64, "float16"), (65, 14336, 96, 128, 32, "float16"),
     (20, 4096, 520, 256, 24, "float16"), (300, 1024, 1030, 512, 40, "float16"),
+    (8, 4096, 96, 128, 40, "float16"), (24, 2048, 100, 128, 72, "float16"),
     (40, 384, 100, 128, 0, "float32"), (16, 512, 48, 128, 8, "float32"),
     (33, 4096, 100, 4096, 0, "float16"), (130, 1024, 260, 1024, 0, "float32"),
     (8, 6144, 96, 128, 64, "float16"), (8, 12288, 64, 128, 64, "float16")])

@@ -149,7 +149,8 @@ def run_residual_layer(w, r, sample_rows=None):
 @pytest.mark.parametrize("M,K,N,b,r,dt", [
     (1, 256, 64, 256, 32, "float16"), (130, 1024, 260, 128, 128, "float16"),
     (33, 4096, 100, 4096, 64, "float16"), (65, 14336, 96, 128, 200, "float16"),
-    (40, 384, 100, 128, 5, "float32"), (300, 1024, 1030, 256, 0, "float16")])
+    (40, 384, 100, 128, 5, "float32"), (300, 1024, 1030, 256, 0, "float16"),
+    (8, 4096, 96, 4096, 40, "float16"), (17, 2048, 100, 128, 72, "float16")])
 def test_qlinear_residual_ragged(M, K, N, b, r, dt):
     w = synth.small("res", M, K, N, x_dtype=dt, had_block=b,
                     w_scale_dtype="float16" if dt == "float16" else "float32")
