@@ -859,13 +859,25 @@ __global__ void __launch_bounds__(256) qgemm_pipe_kernel(GemmArgs a) {
     const int G = AG1 ? 1 : static_cast<int>(ngroups);
     uint32_t* rmax = reinterpret_cast<uint32_t*>(gsc) + (AG1 ? 0 : BM * G);
     stage_barrier();
-    for (int e = tid; e < BM * G; e += 256) {
-      const int row = e / G, g = e % G;
+    // Row maxima of |s (z - 8)|: 256 / BM consecutive threads per row, each
+    // over every (256 / BM)-th group, joined by lane swaps (LDS atomics on
+    // the row words serialised the 32-plus updates of each row: 10 us of the
+    // 4096^3 layer).  Non-negative floats order as their bit patterns, so
+    // the words are the ones an unsigned maximum of the bits gives.
+    static_assert(256 % BM == 0, "whole rows per workgroup");
+    {
+      constexpr int TPR = 256 / BM;
+      const int row = tid / TPR, part = tid % TPR;
       const int64_t m = m0 + row;
+      float mx = 0.f;
       if (m < a.M) {
-        const float o = a.sx[m * G + g] * static_cast<float>(a.zx[m * G + g] - 8);
-        atomicMax(&rmax[row], __float_as_uint(fabsf(o)));
+#pragma unroll 4
+        for (int g = part; g < G; g += TPR)
+          mx = fmaxf(mx, fabsf(a.sx[m * G + g] * static_cast<float>(a.zx[m * G + g] - 8)));
       }
+#pragma unroll
+      for (int off = 1; off < TPR; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      if (part == 0) rmax[row] = __float_as_uint(mx);
     }
     __syncthreads();
     auto row_exp = [&](int row) -> int {
